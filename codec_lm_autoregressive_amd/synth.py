@@ -1,0 +1,250 @@
+"""Seeded synthetic inputs for the Qwen3-TTS 12 Hz frame step.
+
+This module only draws random numbers and lays them out: model dimensions,
+weights, prompt embeddings, prompt lengths. It holds none of the method's
+arithmetic. Both the HIP path (through the tests and the benchmark) and the
+CPU oracle are fed from here, so that they see the same inputs.
+
+Recipe (the pages publish no weights, so random ones of the right shape stand
+in for the checkpoints):
+  * linear weights, embedding tables and heads ~ N(0, 0.02);
+  * RMSNorm gains = 1 + N(0, 0.02) (a literal N(0, 0.02) gain would shrink
+    every activation ~50x per norm and turn every logit into a near-tie);
+  * prompt embeddings ~ N(0, 1);
+  * trailing text embeddings and tts_pad ~ N(0, 0.02), the scale of the code
+    embedding rows they are summed with in the feedback (at N(0, 1) the pad
+    row would swamp the 16 code rows and the talker input would barely depend
+    on the codes just drawn);
+  * for bf16 configurations every weight tensor is rounded to bf16
+    (round-to-nearest-even) and handed out as float32 holding the bf16 value.
+Each tensor family draws from its own PCG64 stream, derived from the seed and
+the tensor's name, so one tensor never depends on the order others are drawn.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+
+# Codec ids of the 12 Hz talker vocabulary (Qwen3-TTS ncnn port discussion,
+# section 1 "structure"): 0..2047 acoustic codes, pad 2148, bos 2149, eos 2150.
+TALKER_VOCAB = 3072
+CODEBOOK = 2048
+N_GROUPS = 16
+EOS_ID = 2150
+SUPPRESS_BEGIN = 2048
+SUPPRESS_END = 3072
+
+
+def _dec(layers, hidden, n_heads, n_kv_heads, head_dim, intermediate,
+         rope_theta=1.0e6, rms_eps=1.0e-6):
+    return dict(layers=layers, hidden=hidden, n_heads=n_heads,
+                n_kv_heads=n_kv_heads, head_dim=head_dim,
+                intermediate=intermediate, rope_theta=rope_theta,
+                rms_eps=rms_eps)
+
+
+def dims(name: str) -> dict:
+    """Model dimensions of a named workload.
+
+    tiny     - 4-layer talker / 2-layer predictor, hidden 512, GQA 8/4, d 64
+    qwen06b  - 0.6B-shaped: 28/5 layers, hidden 1024, GQA 16/8, d 128, I 3072
+    qwen17b  - 1.7B-class talker (hidden 2048, I 6144) with a 1024-wide
+               predictor behind a 2048->1024 input projection
+    """
+    base = dict(talker_vocab=TALKER_VOCAB, codebook=CODEBOOK,
+                n_groups=N_GROUPS, eos_id=EOS_ID,
+                suppress_begin=SUPPRESS_BEGIN, suppress_end=SUPPRESS_END)
+    if name == "tiny":
+        t = _dec(4, 512, 8, 4, 64, 1536)
+        p = _dec(2, 512, 8, 4, 64, 1536)
+        return dict(base, talker=t, predictor=p, pred_in_proj=False)
+    if name == "qwen06b":
+        t = _dec(28, 1024, 16, 8, 128, 3072)
+        p = _dec(5, 1024, 16, 8, 128, 3072)
+        return dict(base, talker=t, predictor=p, pred_in_proj=False)
+    if name == "qwen17b":
+        t = _dec(28, 2048, 16, 8, 128, 6144)
+        p = _dec(5, 1024, 16, 8, 128, 3072)
+        return dict(base, talker=t, predictor=p, pred_in_proj=True)
+    raise KeyError(name)
+
+
+def small_dims(layers_t=2, layers_p=2, hidden=64, n_heads=4, n_kv_heads=2,
+               head_dim=16, intermediate=96, vocab=TALKER_VOCAB,
+               codebook=CODEBOOK, pred_in_proj=False, pred_hidden=None):
+    """A reduced shape for fast tests (vocabulary kept at its real size)."""
+    hp = hidden if pred_hidden is None else pred_hidden
+    return dict(talker_vocab=vocab, codebook=codebook, n_groups=N_GROUPS,
+                eos_id=EOS_ID, suppress_begin=SUPPRESS_BEGIN,
+                suppress_end=SUPPRESS_END,
+                talker=_dec(layers_t, hidden, n_heads, n_kv_heads, head_dim,
+                            intermediate),
+                predictor=_dec(layers_p, hp, n_heads, n_kv_heads, head_dim,
+                               intermediate),
+                pred_in_proj=pred_in_proj)
+
+
+def _stream(seed: int, name: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([seed, zlib.crc32(name.encode())]))
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of float32 values that already hold bf16 values."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal(seed, name, shape, std, mean=0.0):
+    g = _stream(seed, name)
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if mean != 0.0:
+        x += np.float32(mean)
+    return x
+
+
+def _decoder_weights(seed, prefix, d, in_hidden=None):
+    H = d["hidden"]
+    nq, nkv, hd, inter = d["n_heads"], d["n_kv_heads"], d["head_dim"], d["intermediate"]
+    layers = []
+    for i in range(d["layers"]):
+        p = f"{prefix}.{i}."
+        layers.append(dict(
+            attn_norm=_normal(seed, p + "attn_norm", (H,), 0.02, 1.0),
+            wq=_normal(seed, p + "wq", (nq * hd, H), 0.02),
+            wk=_normal(seed, p + "wk", (nkv * hd, H), 0.02),
+            wv=_normal(seed, p + "wv", (nkv * hd, H), 0.02),
+            q_norm=_normal(seed, p + "q_norm", (hd,), 0.02, 1.0),
+            k_norm=_normal(seed, p + "k_norm", (hd,), 0.02, 1.0),
+            wo=_normal(seed, p + "wo", (H, nq * hd), 0.02),
+            mlp_norm=_normal(seed, p + "mlp_norm", (H,), 0.02, 1.0),
+            w_gate=_normal(seed, p + "w_gate", (inter, H), 0.02),
+            w_up=_normal(seed, p + "w_up", (inter, H), 0.02),
+            w_down=_normal(seed, p + "w_down", (H, inter), 0.02),
+        ))
+    return layers
+
+
+def make_weights(dm: dict, seed: int = 0, dtype: str = "bf16") -> dict:
+    """All weights of talker + code predictor, float32 arrays.
+
+    Layout is nn.Linear's [out, in], row-major.  pred_embeds holds the 15
+    predictor tables stacked as [15*codebook, talker_hidden]; pred_heads the
+    15 heads stacked as [15*codebook, pred_hidden].
+    """
+    t, p = dm["talker"], dm["predictor"]
+    H, Hp = t["hidden"], p["hidden"]
+    V, C, G = dm["talker_vocab"], dm["codebook"], dm["n_groups"]
+    w = dict(
+        talker_layers=_decoder_weights(seed, "talker", t),
+        talker_norm=_normal(seed, "talker.norm", (H,), 0.02, 1.0),
+        talker_codec_embed=_normal(seed, "talker.codec_embed", (V, H), 0.02),
+        talker_codec_head=_normal(seed, "talker.codec_head", (V, H), 0.02),
+        pred_layers=_decoder_weights(seed, "pred", p),
+        pred_norm=_normal(seed, "pred.norm", (Hp,), 0.02, 1.0),
+        pred_embeds=_normal(seed, "pred.embeds", ((G - 1) * C, H), 0.02),
+        pred_heads=_normal(seed, "pred.heads", ((G - 1) * C, Hp), 0.02),
+        pred_in_proj=(_normal(seed, "pred.in_proj", (Hp, H), 0.02)
+                      if dm["pred_in_proj"] else None),
+    )
+    if dtype == "bf16":
+        w = map_arrays(w, bf16_round)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return w
+
+
+def map_arrays(w, fn):
+    """Apply fn to every array of a weight tree (dicts / lists / None kept)."""
+    if isinstance(w, dict):
+        return {k: map_arrays(v, fn) for k, v in w.items()}
+    if isinstance(w, list):
+        return [map_arrays(v, fn) for v in w]
+    if w is None:
+        return None
+    return fn(w)
+
+
+def prompt_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Per-row prompt lengths, uniform on the integers lo..hi inclusive."""
+    if lo == hi:
+        return np.full(B, lo, dtype=np.int32)
+    g = _stream(seed, "prompt_lengths")
+    return g.integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def make_prompts(lens, hidden: int, seed: int) -> np.ndarray:
+    """Packed prompt embeddings [sum(lens), hidden], N(0, 1)."""
+    return _normal(seed, "prompt", (int(np.sum(lens)), hidden), 1.0)
+
+
+def make_text(lens, hidden: int, seed: int) -> np.ndarray:
+    """Packed trailing text embeddings [sum(lens), hidden], N(0, 0.02)."""
+    return _normal(seed, "text", (int(np.sum(lens)), hidden), 0.02)
+
+
+def make_tts_pad(hidden: int, seed: int) -> np.ndarray:
+    """The tts_pad embedding [hidden], N(0, 0.02)."""
+    return _normal(seed, "tts_pad", (hidden,), 0.02)
+
+
+def split_rows(packed: np.ndarray, lens) -> list:
+    """Cut a packed [sum(lens), H] array into per-row views."""
+    out, o = [], 0
+    for n in lens:
+        out.append(packed[o:o + int(n)])
+        o += int(n)
+    return out
+
+
+# Sampling settings of the workloads (Qwen3-TTS pages: repetition penalty 1.05,
+# min_new_tokens 2, suppress 2048..3071 except EOS; temperature 0.9, top-k 50,
+# top-p 0.8 for the sampling workloads).
+GREEDY = dict(do_sample=False, temperature=1.0, top_k=0, top_p=1.0,
+              repetition_penalty=1.05, min_new_tokens=2)
+SAMPLING = dict(do_sample=True, temperature=0.9, top_k=50, top_p=0.8,
+                repetition_penalty=1.05, min_new_tokens=2)
+# The code predictor has no penalty, min-new or suppress processors.
+PRED_GREEDY = dict(do_sample=False, temperature=1.0, top_k=0, top_p=1.0,
+                   repetition_penalty=1.0, min_new_tokens=0)
+PRED_SAMPLING = dict(do_sample=True, temperature=0.9, top_k=50, top_p=0.8,
+                     repetition_penalty=1.0, min_new_tokens=0)
+
+
+def workload(name: str) -> dict:
+    """The five synthetic workloads (shape, batch, prompt lengths, frames, sampling)."""
+    if name == "tiny_fp32_b1":
+        return dict(model="tiny", dtype="f32", B=1, prompt=(8, 8), frames=4,
+                    talker=GREEDY, predictor=PRED_GREEDY, max_positions=64)
+    if name == "qwen06b_bf16_b1":
+        return dict(model="qwen06b", dtype="bf16", B=1, prompt=(32, 32),
+                    frames=100, talker=GREEDY, predictor=PRED_GREEDY,
+                    max_positions=160)
+    if name == "qwen06b_bf16_b8_sampling":
+        return dict(model="qwen06b", dtype="bf16", B=8, prompt=(32, 256),
+                    frames=200, talker=SAMPLING, predictor=PRED_SAMPLING,
+                    max_positions=512)
+    if name == "qwen17b_bf16_b1":
+        return dict(model="qwen17b", dtype="bf16", B=1, prompt=(64, 64),
+                    frames=250, talker=GREEDY, predictor=PRED_GREEDY,
+                    max_positions=320)
+    if name == "qwen17b_bf16_b8":
+        return dict(model="qwen17b", dtype="bf16", B=8, prompt=(64, 64),
+                    frames=250, talker=GREEDY, predictor=PRED_GREEDY,
+                    max_positions=320)
+    if name == "qwen06b_bf16_b64_sampling":
+        return dict(model="qwen06b", dtype="bf16", B=64, prompt=(128, 512),
+                    frames=1024, talker=SAMPLING, predictor=PRED_SAMPLING,
+                    max_positions=1536)
+    raise KeyError(name)
