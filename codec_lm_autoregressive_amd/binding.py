@@ -1,0 +1,296 @@
+"""ctypes binding of libqt.so (include/qt.h), argument marshalling only.
+
+Every step of the frame runs in the HIP library; this module only turns
+Python / numpy / torch objects into the C structures and device pointers the
+ABI takes. torch provides device memory and the stream. The library must be
+built (codec_lm_autoregressive_amd.build); importing the binding without it
+raises - there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqt.so")
+
+QT_OK, QT_E_INVALID, QT_E_RANGE, QT_E_CAPACITY, QT_E_NOMEM, QT_E_HIP, QT_E_NAN, QT_E_STATE = range(8)
+QT_DTYPE_F32, QT_DTYPE_BF16 = 0, 1
+STATUS_NAMES = {0: "QT_OK", 1: "QT_E_INVALID", 2: "QT_E_RANGE", 3: "QT_E_CAPACITY", 4: "QT_E_NOMEM",
+                5: "QT_E_HIP", 6: "QT_E_NAN", 7: "QT_E_STATE"}
+
+
+class QtError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class DecoderDims(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("rope_theta", C.c_float), ("rms_eps", C.c_float)]
+
+
+class Config(C.Structure):
+    _fields_ = [("talker", DecoderDims), ("predictor", DecoderDims), ("talker_vocab", C.c_int32),
+                ("n_groups", C.c_int32), ("codebook", C.c_int32), ("eos_id", C.c_int32),
+                ("suppress_begin", C.c_int32), ("suppress_end", C.c_int32), ("pred_in_proj", C.c_int32),
+                ("weight_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("max_batch", C.c_int32),
+                ("max_positions", C.c_int32)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
+                                          "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class Weights(C.Structure):
+    _fields_ = [("talker_layers", C.POINTER(LayerWeights)), ("talker_norm", C.c_void_p),
+                ("talker_codec_embed", C.c_void_p), ("talker_codec_head", C.c_void_p),
+                ("pred_layers", C.POINTER(LayerWeights)), ("pred_norm", C.c_void_p),
+                ("pred_embeds", C.c_void_p), ("pred_heads", C.c_void_p), ("pred_in_proj", C.c_void_p)]
+
+
+class Sampling(C.Structure):
+    _fields_ = [("do_sample", C.c_int32), ("temperature", C.c_float), ("top_k", C.c_int32),
+                ("top_p", C.c_float), ("repetition_penalty", C.c_float), ("min_new_tokens", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with python -m codec_lm_autoregressive_amd.build")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, u64, f32 = C.c_void_p, C.c_int32, C.c_uint64, C.c_float
+        sig = {
+            "qt_config_check": ([C.POINTER(Config)], i32),
+            "qt_workspace_bytes": ([C.POINTER(Config), C.POINTER(C.c_size_t)], i32),
+            "qt_create": ([C.POINTER(Config), C.POINTER(Weights), vp, C.c_size_t, vp, C.POINTER(vp)], i32),
+            "qt_prefill": ([vp, i32, vp, vp, vp, vp, vp, C.POINTER(Sampling), C.POINTER(Sampling), u64, i32], i32),
+            "qt_step_frame": ([vp, vp, vp], i32),
+            "qt_generate": ([vp, i32, vp, vp, vp, vp, vp, C.POINTER(Sampling), C.POINTER(Sampling), u64, i32,
+                             vp, vp, vp], i32),
+            "qt_destroy": ([vp], None),
+            "qt_last_error": ([vp], C.c_char_p),
+            "qt_debug_step_forced": ([vp, vp, vp, vp, vp], i32),
+            "qt_debug_talker_logits": ([vp, vp], i32),
+            "qt_debug_select": ([vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, C.POINTER(Sampling), u64, i32,
+                                 i32, vp, vp, vp], i32),
+            "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, i32], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status, ctx=None):
+    if status != QT_OK:
+        raise QtError(status, lib().qt_last_error(ctx).decode())
+
+
+def _dec(d):
+    return DecoderDims(d["layers"], d["hidden"], d["n_heads"], d["n_kv_heads"], d["head_dim"],
+                       d["intermediate"], d["rope_theta"], d["rms_eps"])
+
+
+def make_config(dm, weight_dtype="bf16", kv_dtype=None, max_batch=1, max_positions=256):
+    wd = QT_DTYPE_BF16 if weight_dtype == "bf16" else QT_DTYPE_F32
+    kd = wd if kv_dtype is None else (QT_DTYPE_BF16 if kv_dtype == "bf16" else QT_DTYPE_F32)
+    return Config(_dec(dm["talker"]), _dec(dm["predictor"]), dm["talker_vocab"], dm["n_groups"], dm["codebook"],
+                  dm["eos_id"], dm["suppress_begin"], dm["suppress_end"], int(bool(dm["pred_in_proj"])),
+                  wd, kd, max_batch, max_positions)
+
+
+def sampling(s):
+    return Sampling(int(bool(s["do_sample"])), s["temperature"], s["top_k"], s["top_p"],
+                    s["repetition_penalty"], s["min_new_tokens"])
+
+
+def config_check(cfg):
+    return lib().qt_config_check(C.byref(cfg))
+
+
+def workspace_bytes(cfg):
+    n = C.c_size_t(0)
+    _check(lib().qt_workspace_bytes(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(C.c_void_p) if a is not None else None
+
+
+def to_device_weight(a, dtype, device="cuda"):
+    """numpy float32 array (holding bf16 values for bf16) -> device tensor of the ABI element type."""
+    import torch
+    if dtype == "bf16":
+        from .synth import bf16_bits
+        return torch.from_numpy(bf16_bits(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class Engine:
+    """One qt_ctx on the current device, on a private torch stream."""
+
+    def __init__(self, dm, weights, dtype="bf16", kv_dtype=None, max_batch=1, max_positions=256,
+                 use_workspace=True):
+        import torch
+        self.torch = torch
+        self.dm = dm
+        self.dtype = dtype
+        self.cfg = make_config(dm, dtype, kv_dtype, max_batch, max_positions)
+        self.stream = torch.cuda.Stream()
+        L = lib()
+        dev = {}
+
+        def up(a):
+            t = to_device_weight(a, dtype)
+            dev[id(t)] = t
+            return _ptr(t)
+
+        def layers(ws):
+            arr = (LayerWeights * len(ws))()
+            for i, lw in enumerate(ws):
+                arr[i] = LayerWeights(*[up(lw[n]) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
+                                                              "wo", "mlp_norm", "w_gate", "w_up", "w_down")])
+            return arr
+
+        with torch.cuda.stream(self.stream):
+            tl = layers(weights["talker_layers"])
+            pl = layers(weights["pred_layers"])
+            w = Weights(tl, up(weights["talker_norm"]), up(weights["talker_codec_embed"]),
+                        up(weights["talker_codec_head"]), pl, up(weights["pred_norm"]),
+                        up(weights["pred_embeds"]), up(weights["pred_heads"]),
+                        up(weights["pred_in_proj"]) if weights.get("pred_in_proj") is not None else None)
+            torch.cuda.synchronize()
+            self.ws_bytes = workspace_bytes(self.cfg)
+            self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+                              if use_workspace else None)
+            ctx = C.c_void_p()
+            _check(L.qt_create(C.byref(self.cfg), C.byref(w), _ptr(self.workspace),
+                               self.ws_bytes if use_workspace else 0,
+                               C.c_void_p(self.stream.cuda_stream), C.byref(ctx)))
+        self.ctx = ctx
+        dev.clear()  # the library holds its own repacked copy
+        torch.cuda.synchronize()
+        self.B = 0
+        self._keep = []
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            lib().qt_destroy(self.ctx)
+            self.ctx = None
+
+    __del__ = close
+
+    # ---- generation
+    def prefill(self, prompt, lens, tts_pad, talker, predictor, seed, max_frames, text=None, text_lens=None):
+        """prompt: packed [sum(lens), H] (numpy or device tensor); tts_pad [H]; text packed or None."""
+        torch = self.torch
+        dev = lambda a: a if isinstance(a, torch.Tensor) else torch.from_numpy(  # noqa: E731
+            np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        with torch.cuda.stream(self.stream):
+            p = dev(prompt)
+            pad = dev(tts_pad)
+            tx = dev(text) if text is not None else None
+        torch.cuda.synchronize()
+        self._keep = [p, pad, tx]  # the library reads text / pad in every frame
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        tl = np.ascontiguousarray(text_lens, dtype=np.int32) if text_lens is not None else None
+        self.B = int(lens.size)
+        ts, ps = sampling(talker), sampling(predictor)
+        _check(lib().qt_prefill(self.ctx, self.B, _ptr(p), _np_ptr(lens), _ptr(tx), _np_ptr(tl), _ptr(pad),
+                                C.byref(ts), C.byref(ps), C.c_uint64(seed), int(max_frames)), self.ctx)
+
+    def step_frame(self):
+        codes = np.zeros((self.B, 16), dtype=np.int32)
+        state = np.zeros(self.B, dtype=np.uint8)
+        _check(lib().qt_step_frame(self.ctx, _np_ptr(codes), _np_ptr(state)), self.ctx)
+        return codes, state
+
+    def generate(self, prompt, lens, tts_pad, talker, predictor, seed, max_frames, text=None, text_lens=None):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            p = prompt if isinstance(prompt, torch.Tensor) else torch.from_numpy(
+                np.ascontiguousarray(prompt, dtype=np.float32)).cuda()
+            pad = tts_pad if isinstance(tts_pad, torch.Tensor) else torch.from_numpy(
+                np.ascontiguousarray(tts_pad, dtype=np.float32)).cuda()
+            tx = None if text is None else (text if isinstance(text, torch.Tensor) else torch.from_numpy(
+                np.ascontiguousarray(text, dtype=np.float32)).cuda())
+        torch.cuda.synchronize()
+        self._keep = [p, pad, tx]
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        tl = np.ascontiguousarray(text_lens, dtype=np.int32) if text_lens is not None else None
+        B = int(lens.size)
+        self.B = B
+        codes = np.zeros((B, max_frames, 16), dtype=np.int32)
+        n = np.zeros(B, dtype=np.int32)
+        fin = np.zeros(B, dtype=np.uint8)
+        ts, ps = sampling(talker), sampling(predictor)
+        _check(lib().qt_generate(self.ctx, B, _ptr(p), _np_ptr(lens), _ptr(tx), _np_ptr(tl), _ptr(pad),
+                                 C.byref(ts), C.byref(ps), C.c_uint64(seed), int(max_frames),
+                                 _np_ptr(codes), _np_ptr(n), _np_ptr(fin)), self.ctx)
+        return codes, n, fin
+
+    # ---- test entry points
+    def step_forced(self, forced):
+        forced = np.ascontiguousarray(forced, dtype=np.int32)
+        tl = np.zeros((self.B, self.dm["talker_vocab"]), dtype=np.float32)
+        pl = np.zeros((self.B, 15, self.dm["codebook"]), dtype=np.float32)
+        ch = np.zeros((self.B, 16), dtype=np.int32)
+        _check(lib().qt_debug_step_forced(self.ctx, _np_ptr(forced), _np_ptr(tl), _np_ptr(pl), _np_ptr(ch)),
+               self.ctx)
+        return tl, pl, ch
+
+    def talker_logits(self):
+        out = np.zeros((self.B, self.dm["talker_vocab"]), dtype=np.float32)
+        _check(lib().qt_debug_talker_logits(self.ctx, _np_ptr(out)), self.ctx)
+        return out
+
+    def last_error(self):
+        return lib().qt_last_error(self.ctx).decode()
+
+
+def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", reps=1, stream=None):
+    """Y = op(W · norm(X)) on the device (torch tensors: W int16 bf16 bits or float32)."""
+    import torch
+    N, K = W.shape
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.zeros((M, N // 2 if epilogue == 2 else N), dtype=torch.float32, device=X.device)
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(lib().qt_debug_linear(C.c_void_p(s), QT_DTYPE_BF16 if wdtype == "bf16" else QT_DTYPE_F32,
+                                 _ptr(W), N, K, _ptr(X), M, _ptr(gain), eps, epilogue, _ptr(Y), reps))
+    return Y
+
+
+def debug_select(logits, samp, seen=None, noise=None, probs=None, processors=False, eos=2150,
+                 suppress=(2048, 3072), seed=0, stream_id=0, sel_index=0, want_processed=False):
+    """Run the selection kernel on device tensors [B, V]; returns (codes, processed, status)."""
+    import torch
+    B, V = logits.shape
+    out = torch.zeros(B, dtype=torch.int32, device=logits.device)
+    st = torch.zeros(1, dtype=torch.int32, device=logits.device)
+    proc = torch.zeros((B, V), dtype=torch.float32, device=logits.device) if want_processed else None
+    sm = sampling(samp)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().qt_debug_select(C.c_void_p(s), B, V, _ptr(logits), _ptr(seen), _ptr(noise), _ptr(probs),
+                                 int(bool(processors)), eos, suppress[0], suppress[1], C.byref(sm),
+                                 C.c_uint64(seed), stream_id, sel_index, _ptr(out), _ptr(proc), _ptr(st)))
+    torch.cuda.synchronize()
+    return out, proc, st

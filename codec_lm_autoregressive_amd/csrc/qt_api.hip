@@ -1,0 +1,898 @@
+// C-ABI layer of the Qwen3-TTS 12 Hz frame step: validation, workspace
+// layout, weight repacking, prompt prefill, the per-frame kernel sequence
+// (replayed as one hipGraph per batch size), and the test entry points.
+#include "qt.h"
+#include "qt_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+using namespace qt;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+constexpr int kGroups = 16;       // codes per frame
+constexpr int kPredPositions = 16;
+constexpr int kPrefillChunk = 1024;
+constexpr int kMaxVocab = 6144;
+
+void set_err(char* buf, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, 512, fmt, ap);
+  va_end(ap);
+}
+
+size_t esize(int dt) { return dt == QT_DTYPE_BF16 ? 2 : 4; }
+
+// overflow-checked size arithmetic
+struct Sz {
+  bool ovf = false;
+  size_t mul(size_t a, size_t b) {
+    size_t r;
+    if (__builtin_mul_overflow(a, b, &r)) { ovf = true; return 0; }
+    return r;
+  }
+  size_t mul(std::initializer_list<size_t> xs) {
+    size_t r = 1;
+    for (size_t x : xs) r = mul(r, x);
+    return r;
+  }
+};
+
+bool dims_ok(const qt_decoder_dims& d, char* err, const char* who) {
+  if (d.layers < 1 || d.layers > 1024) { set_err(err, "%s.layers must be in 1..1024", who); return false; }
+  if (d.hidden < 64 || d.hidden > 16384 || d.hidden % 64) { set_err(err, "%s.hidden must be a multiple of 64 in 64..16384", who); return false; }
+  if (d.n_kv_heads < 1 || d.n_heads < 1 || d.n_heads % d.n_kv_heads) { set_err(err, "%s.n_heads must be a positive multiple of n_kv_heads", who); return false; }
+  if (d.n_heads / d.n_kv_heads > 8) { set_err(err, "%s: at most 8 q heads per kv head", who); return false; }
+  if (d.head_dim != 16 && d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) {
+    set_err(err, "%s.head_dim must be 16, 32, 64, 128 or 256", who); return false;
+  }
+  if ((d.n_heads * d.head_dim) % 64 || (d.n_heads * d.head_dim) > 65536) { set_err(err, "%s: n_heads*head_dim must be a multiple of 64", who); return false; }
+  if (d.intermediate < 64 || d.intermediate > 65536 || d.intermediate % 64) { set_err(err, "%s.intermediate must be a multiple of 64 in 64..65536", who); return false; }
+  if (!(d.rope_theta > 0.f) || !std::isfinite(d.rope_theta)) { set_err(err, "%s.rope_theta must be positive", who); return false; }
+  if (!(d.rms_eps > 0.f) || !std::isfinite(d.rms_eps)) { set_err(err, "%s.rms_eps must be positive", who); return false; }
+  return true;
+}
+
+qt_status check_config(const qt_config* c, char* err) {
+  if (!c) { set_err(err, "config is NULL"); return QT_E_INVALID; }
+  if (!dims_ok(c->talker, err, "talker") || !dims_ok(c->predictor, err, "predictor")) return QT_E_INVALID;
+  if (c->n_groups != kGroups) { set_err(err, "n_groups must be 16"); return QT_E_INVALID; }
+  if (c->talker_vocab < 2 || c->talker_vocab > kMaxVocab) { set_err(err, "talker_vocab must be in 2..%d", kMaxVocab); return QT_E_INVALID; }
+  if (c->codebook < 2 || c->codebook > kMaxVocab) { set_err(err, "codebook must be in 2..%d", kMaxVocab); return QT_E_INVALID; }
+  if (c->codebook > c->talker_vocab) { set_err(err, "codebook must not exceed talker_vocab"); return QT_E_INVALID; }
+  if (c->eos_id < 0 || c->eos_id >= c->talker_vocab) { set_err(err, "eos_id out of range"); return QT_E_INVALID; }
+  if (c->suppress_begin < 0 || c->suppress_begin > c->suppress_end || c->suppress_end > c->talker_vocab) {
+    set_err(err, "suppress range must satisfy 0 <= begin <= end <= talker_vocab"); return QT_E_INVALID;
+  }
+  if (c->pred_in_proj != 0 && c->pred_in_proj != 1) { set_err(err, "pred_in_proj must be 0 or 1"); return QT_E_INVALID; }
+  if (!c->pred_in_proj && c->predictor.hidden != c->talker.hidden) {
+    set_err(err, "predictor.hidden must equal talker.hidden without pred_in_proj"); return QT_E_INVALID;
+  }
+  if ((c->weight_dtype != QT_DTYPE_F32 && c->weight_dtype != QT_DTYPE_BF16) ||
+      (c->kv_dtype != QT_DTYPE_F32 && c->kv_dtype != QT_DTYPE_BF16)) {
+    set_err(err, "weight_dtype / kv_dtype must be QT_DTYPE_F32 or QT_DTYPE_BF16"); return QT_E_INVALID;
+  }
+  if (c->max_batch < 1 || c->max_batch > 4096) { set_err(err, "max_batch must be in 1..4096"); return QT_E_INVALID; }
+  if (c->max_positions < 2 || c->max_positions > (1 << 20)) { set_err(err, "max_positions must be in 2..2^20"); return QT_E_INVALID; }
+  return QT_OK;
+}
+
+bool sampling_ok(const qt_sampling* s, char* err, const char* who) {
+  if (!s) { set_err(err, "%s sampling settings are NULL", who); return false; }
+  if (s->do_sample != 0 && s->do_sample != 1) { set_err(err, "%s.do_sample must be 0 or 1", who); return false; }
+  if (!(s->temperature > 0.f) || !std::isfinite(s->temperature)) { set_err(err, "%s.temperature must be > 0", who); return false; }
+  if (s->top_k < 0) { set_err(err, "%s.top_k must be >= 0", who); return false; }
+  if (!(s->top_p > 0.f) || s->top_p > 1.f) { set_err(err, "%s.top_p must be in (0, 1]", who); return false; }
+  if (!(s->repetition_penalty > 0.f) || !std::isfinite(s->repetition_penalty)) { set_err(err, "%s.repetition_penalty must be > 0", who); return false; }
+  if (s->min_new_tokens < 0) { set_err(err, "%s.min_new_tokens must be >= 0", who); return false; }
+  return true;
+}
+
+struct Dec {
+  int L, H, nq, nkv, d, I, qkv, nqd;
+  float theta, eps;
+  static Dec of(const qt_decoder_dims& x) {
+    Dec d;
+    d.L = x.layers; d.H = x.hidden; d.nq = x.n_heads; d.nkv = x.n_kv_heads; d.d = x.head_dim;
+    d.I = x.intermediate; d.qkv = (x.n_heads + 2 * x.n_kv_heads) * x.head_dim; d.nqd = x.n_heads * x.head_dim;
+    d.theta = x.rope_theta; d.eps = x.rms_eps;
+    return d;
+  }
+};
+
+// Workspace plan: every buffer's byte offset, 256-byte aligned.
+struct Plan {
+  Sz sz;
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    size_t b = (bytes + 255) & ~(size_t)255;
+    if (__builtin_add_overflow(off, b, &off)) sz.ovf = true;
+    return o;
+  }
+};
+
+struct LayerBuf { size_t wqkv, wo, wgu, wd, attn_norm, q_norm, k_norm, mlp_norm; };
+
+struct Layout {
+  std::vector<LayerBuf> tl, pl;
+  size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj;
+  size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
+  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p;
+  size_t rowstate, seen, runs, idx, frame_out, req;
+  size_t total;
+  int tmax, seen_words, max_runs;
+  bool ovf;
+};
+
+Layout plan_layout(const qt_config& c) {
+  Layout L;
+  Plan p;
+  const Dec t = Dec::of(c.talker), q = Dec::of(c.predictor);
+  const size_t es = esize(c.weight_dtype), kvs = esize(c.kv_dtype);
+  const size_t V = c.talker_vocab, C = c.codebook, B = c.max_batch, MP = c.max_positions;
+  auto layer = [&](const Dec& d) {
+    LayerBuf b;
+    b.wqkv = p.take(p.sz.mul({(size_t)d.qkv, (size_t)d.H, es}));
+    b.wo = p.take(p.sz.mul({(size_t)d.H, (size_t)d.nqd, es}));
+    b.wgu = p.take(p.sz.mul({2, (size_t)d.I, (size_t)d.H, es}));
+    b.wd = p.take(p.sz.mul({(size_t)d.H, (size_t)d.I, es}));
+    b.attn_norm = p.take((size_t)d.H * 4);
+    b.q_norm = p.take((size_t)d.d * 4);
+    b.k_norm = p.take((size_t)d.d * 4);
+    b.mlp_norm = p.take((size_t)d.H * 4);
+    return b;
+  };
+  for (int i = 0; i < t.L; ++i) L.tl.push_back(layer(t));
+  for (int i = 0; i < q.L; ++i) L.pl.push_back(layer(q));
+  L.talker_norm = p.take((size_t)t.H * 4);
+  L.temb = p.take(p.sz.mul({V, (size_t)t.H, es}));
+  L.thead = p.take(p.sz.mul({V, (size_t)t.H, es}));
+  L.pred_norm = p.take((size_t)q.H * 4);
+  L.pemb = p.take(p.sz.mul({15, C, (size_t)t.H, es}));
+  L.phead = p.take(p.sz.mul({15, C, (size_t)q.H, es}));
+  L.pproj = c.pred_in_proj ? p.take(p.sz.mul({(size_t)q.H, (size_t)t.H, es})) : 0;
+  L.cos_t = p.take(p.sz.mul({MP, (size_t)t.d / 2, 4}));
+  L.sin_t = p.take(p.sz.mul({MP, (size_t)t.d / 2, 4}));
+  L.cos_p = p.take((size_t)kPredPositions * q.d / 2 * 4);
+  L.sin_p = p.take((size_t)kPredPositions * q.d / 2 * 4);
+  const size_t kvt = p.sz.mul({(size_t)t.L, B, (size_t)t.nkv, MP, (size_t)t.d, kvs});
+  L.kc_t = p.take(kvt);
+  L.vc_t = p.take(kvt);
+  const size_t kvp = p.sz.mul({(size_t)q.L, B, (size_t)q.nkv, (size_t)kPredPositions, (size_t)q.d, kvs});
+  L.kc_p = p.take(kvp);
+  L.vc_p = p.take(kvp);
+  L.tmax = std::max(kPrefillChunk, 2 * c.max_batch);
+  const size_t T = L.tmax;
+  const size_t Hm = std::max(t.H, q.H), QKVm = std::max(t.qkv, q.qkv), NQm = std::max(t.nqd, q.nqd),
+               Im = std::max(t.I, q.I);
+  L.x_t = p.take(p.sz.mul({T, (size_t)t.H, 4}));
+  L.qkv = p.take(p.sz.mul({T, QKVm, 4}));
+  L.attn = p.take(p.sz.mul({T, NQm, 4}));
+  L.act = p.take(p.sz.mul({T, Im, 4}));
+  L.x_p = p.take(p.sz.mul({2 * B, (size_t)q.H, 4}));
+  L.xin_w = c.pred_in_proj ? p.take(p.sz.mul({2 * B, (size_t)t.H, 4})) : 0;
+  L.h = p.take(p.sz.mul({B, (size_t)t.H, 4}));
+  L.xlast = p.take(p.sz.mul({B, (size_t)t.H, 4}));
+  L.logits_t = p.take(p.sz.mul({B, V, 4}));
+  L.logits_p = p.take(p.sz.mul({15, B, C, 4}));
+  (void)Hm;
+  // row state: code0_next, finished, pos, text_off, text_len [B]; frame_k; own/forced [B,16]
+  L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
+  L.seen_words = (int)((V + 31) / 32);
+  L.seen = p.take(p.sz.mul({B, (size_t)L.seen_words, 4}));
+  L.max_runs = (int)std::min<size_t>((size_t)1 << 30, 3 * B + (B * MP) / kPrefillChunk + 2 + B);
+  L.runs = p.take(p.sz.mul({(size_t)L.max_runs, sizeof(Run)}));
+  L.idx = p.take(B * 4);
+  L.frame_out = p.take(p.sz.mul({1 + B + B * kGroups, 4}));
+  L.req = p.take(sizeof(ReqParams));
+  L.total = p.off;
+  L.ovf = p.sz.ovf;
+  return L;
+}
+
+struct DevLayer {
+  void *wqkv, *wo, *wgu, *wd;
+  float *attn_norm, *q_norm, *k_norm, *mlp_norm;
+};
+
+}  // namespace
+
+struct qt_ctx {
+  qt_config cfg;
+  Dec t, p;
+  Layout lay;
+  hipStream_t stream = nullptr;       // caller's stream
+  hipStream_t cap = nullptr;          // private stream for graph capture
+  hipEvent_t ev = nullptr;
+  int device = 0;
+  char err[512] = "";
+  char* ws = nullptr;
+  bool own_ws = false;
+  std::vector<DevLayer> tl, pl;
+  float *talker_norm, *pred_norm;
+  void *temb, *thead, *pemb, *phead, *pproj;
+  float *cos_t, *sin_t, *cos_p, *sin_p;
+  void *kc_t, *vc_t, *kc_p, *vc_p;
+  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p;
+  int *code0_next, *finished, *pos, *text_off, *text_len, *frame_k, *own, *forced;
+  uint32_t* seen;
+  Run* runs;
+  int* idx;
+  int* frame_out;                     // [status | state B | codes B*16]
+  ReqParams* req;                     // per-request settings (device)
+  int* hout = nullptr;                // pinned host mirror of frame_out
+  // generation state
+  int B = 0;
+  bool prefilled = false, failed = false;
+  int frames_done = 0, max_frames = 0;
+  std::vector<uint8_t> done;
+  qt_sampling ts{}, ps{};
+  uint64_t seed = 0;
+  const float* text = nullptr;
+  const float* pad = nullptr;
+  bool has_text = false;
+  // graph of one frame for the current B
+  hipGraphExec_t gexec = nullptr;
+  int graph_B = -1;
+  int eager_frames = 0;
+};
+
+namespace {
+
+template <typename T> T* at(qt_ctx* c, size_t off) { return (T*)(c->ws + off); }
+
+#define HIPCK(call)                                                                   \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) {                                                           \
+      set_err(ctx->err, "%s failed: %s", #call, hipGetErrorString(e_));               \
+      return QT_E_HIP;                                                                \
+    }                                                                                 \
+  } while (0)
+
+#define QTCK(call)                \
+  do {                            \
+    qt_status r_ = (call);        \
+    if (r_ != QT_OK) return r_;   \
+  } while (0)
+
+void host_rope(int max_pos, int d, float theta, std::vector<float>& cs, std::vector<float>& sn) {
+  const int half = d / 2;
+  std::vector<float> inv(half);
+  for (int i = 0; i < half; ++i) inv[i] = (float)std::pow((double)theta, -(2.0 * i) / d);
+  cs.resize((size_t)max_pos * half);
+  sn.resize((size_t)max_pos * half);
+  for (int p = 0; p < max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const float ang = (float)p * inv[i];  // float32 product
+      cs[(size_t)p * half + i] = (float)std::cos((double)ang);
+      sn[(size_t)p * half + i] = (float)std::sin((double)ang);
+    }
+}
+
+qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLayer& o, hipStream_t s) {
+  const int wd = ctx->cfg.weight_dtype;
+  const size_t es = esize(wd);
+  if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.q_norm || !w.k_norm || !w.wo || !w.mlp_norm || !w.w_gate ||
+      !w.w_up || !w.w_down) {
+    set_err(ctx->err, "a layer weight pointer is NULL");
+    return QT_E_INVALID;
+  }
+  // fused q/k/v rows
+  HIPCK(launch_convert(w.wq, wd, d.H, o.wqkv, wd, d.H, (long)d.nq * d.d, d.H, s));
+  HIPCK(launch_convert(w.wk, wd, d.H, (char*)o.wqkv + (size_t)d.nq * d.d * d.H * es, wd, d.H, (long)d.nkv * d.d, d.H, s));
+  HIPCK(launch_convert(w.wv, wd, d.H, (char*)o.wqkv + (size_t)(d.nq + d.nkv) * d.d * d.H * es, wd, d.H,
+                       (long)d.nkv * d.d, d.H, s));
+  HIPCK(launch_convert(w.wo, wd, d.nqd, o.wo, wd, d.nqd, d.H, d.nqd, s));
+  // gate / up interleaved by row: row 2j = gate j, row 2j+1 = up j
+  HIPCK(launch_convert(w.w_gate, wd, d.H, o.wgu, wd, 2L * d.H, d.I, d.H, s));
+  HIPCK(launch_convert(w.w_up, wd, d.H, (char*)o.wgu + (size_t)d.H * es, wd, 2L * d.H, d.I, d.H, s));
+  HIPCK(launch_convert(w.w_down, wd, d.I, o.wd, wd, d.I, d.H, d.I, s));
+  HIPCK(launch_convert(w.attn_norm, wd, d.H, o.attn_norm, DT_F32, d.H, 1, d.H, s));
+  HIPCK(launch_convert(w.q_norm, wd, d.d, o.q_norm, DT_F32, d.d, 1, d.d, s));
+  HIPCK(launch_convert(w.k_norm, wd, d.d, o.k_norm, DT_F32, d.d, 1, d.d, s));
+  HIPCK(launch_convert(w.mlp_norm, wd, d.H, o.mlp_norm, DT_F32, d.H, 1, d.H, s));
+  return QT_OK;
+}
+
+// ---- the decoder stack over M tokens
+qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
+                     int pos_base, hipStream_t s) {
+  const Dec& d = talker ? ctx->t : ctx->p;
+  std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
+  const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
+  const size_t kvs = esize(ctx->cfg.kv_dtype);
+  const long row_stride = (long)d.nkv * maxpos * d.d;
+  const size_t layer_kv = (size_t)ctx->cfg.max_batch * row_stride * kvs;
+  char* kc = (char*)(talker ? ctx->kc_t : ctx->kc_p);
+  char* vc = (char*)(talker ? ctx->vc_t : ctx->vc_p);
+  for (int l = 0; l < d.L; ++l) {
+    const DevLayer& w = layers[l];
+    LinearArgs a{};
+    a.wdtype = ctx->cfg.weight_dtype;
+    a.eps = d.eps;
+    // q/k/v = W_qkv · RMSNorm(x)
+    a.W = w.wqkv; a.N = d.qkv; a.K = d.H; a.X = x; a.ldx = d.H; a.M = M; a.gain = w.attn_norm;
+    a.Y = ctx->qkv; a.ldy = d.qkv; a.epi = EPI_STORE;
+    HIPCK(launch_linear(a, s));
+    AttnArgs t{};
+    t.qkv = ctx->qkv; t.ld_qkv = d.qkv; t.out = ctx->attn; t.ld_out = d.nqd;
+    t.q_gain = w.q_norm; t.k_gain = w.k_norm; t.eps = d.eps; t.scale = (float)(1.0 / std::sqrt((double)d.d));
+    t.cos = talker ? ctx->cos_t : ctx->cos_p; t.sin = talker ? ctx->sin_t : ctx->sin_p;
+    t.kc = kc + l * layer_kv; t.vc = vc + l * layer_kv; t.kvdtype = ctx->cfg.kv_dtype;
+    t.row_stride = row_stride; t.max_pos = maxpos;
+    t.runs = runs; t.n_runs = n_runs; t.row_pos = row_pos; t.pos_base = pos_base;
+    t.nq = d.nq; t.nkv = d.nkv; t.d = d.d;
+    HIPCK(launch_attention(t, s));
+    // x += W_o · attn
+    a.W = w.wo; a.N = d.H; a.K = d.nqd; a.X = ctx->attn; a.ldx = d.nqd; a.gain = nullptr;
+    a.Y = x; a.ldy = d.H; a.epi = EPI_RESIDUAL;
+    HIPCK(launch_linear(a, s));
+    // act = silu(W_g · RMSNorm(x)) * (W_u · RMSNorm(x))
+    a.W = w.wgu; a.N = 2 * d.I; a.K = d.H; a.X = x; a.ldx = d.H; a.gain = w.mlp_norm;
+    a.Y = ctx->act; a.ldy = d.I; a.epi = EPI_SWIGLU;
+    HIPCK(launch_linear(a, s));
+    // x += W_d · act
+    a.W = w.wd; a.N = d.H; a.K = d.I; a.X = ctx->act; a.ldx = d.I; a.gain = nullptr;
+    a.Y = x; a.ldy = d.H; a.epi = EPI_RESIDUAL;
+    HIPCK(launch_linear(a, s));
+  }
+  return QT_OK;
+}
+
+SelectArgs select_base(qt_ctx* ctx, const qt_sampling& sm, bool talker) {
+  SelectArgs a{};
+  a.req = ctx->req; a.which = talker ? 0 : 1;
+  a.B = ctx->B;
+  a.V = talker ? ctx->cfg.talker_vocab : ctx->cfg.codebook;
+  a.processors = talker ? 1 : 0;
+  a.seen = ctx->seen; a.seen_words = ctx->lay.seen_words;
+  a.penalty = sm.repetition_penalty; a.min_new = sm.min_new_tokens;
+  a.eos = ctx->cfg.eos_id; a.sup_b = ctx->cfg.suppress_begin; a.sup_e = ctx->cfg.suppress_end;
+  a.do_sample = sm.do_sample; a.temperature = sm.temperature; a.top_k = sm.top_k; a.top_p = sm.top_p;
+  a.seed = ctx->seed;
+  a.status = ctx->frame_out;
+  return a;
+}
+
+// One frame for all rows; forced != nullptr selects teacher forcing.
+qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
+  const int B = ctx->B;
+  const Dec &T = ctx->t, &P = ctx->p;
+  const int C = ctx->cfg.codebook;
+  const bool proj = ctx->cfg.pred_in_proj != 0;
+  const int wd = ctx->cfg.weight_dtype;
+  int* codes = ctx->frame_out + 1 + ctx->cfg.max_batch;
+  int* state = ctx->frame_out + 1;
+  Run* runs_decode = ctx->runs;
+  Run* runs_pass0 = ctx->runs + ctx->cfg.max_batch;
+  Run* runs_step = ctx->runs + 2 * ctx->cfg.max_batch;
+
+  FrameStartArgs fs{};
+  fs.B = B; fs.eos = ctx->cfg.eos_id; fs.V = ctx->cfg.talker_vocab;
+  fs.code0_next = ctx->code0_next; fs.finished = ctx->finished; fs.forced = forced; fs.forced_ld = kGroups;
+  fs.seen = ctx->seen; fs.seen_words = ctx->lay.seen_words; fs.codes = codes;
+  fs.temb = ctx->temb; fs.tdtype = wd; fs.H = T.H; fs.h = ctx->h;
+  fs.pass0 = proj ? ctx->xin_w : ctx->x_p; fs.pass0_ld = T.H;
+  fs.fb = ctx->x_t; fs.fb_ld = T.H; fs.status = ctx->frame_out;
+  HIPCK(launch_frame_start(fs, s));
+
+  LinearArgs pa{};
+  pa.wdtype = wd; pa.W = ctx->pproj; pa.N = P.H; pa.K = T.H; pa.X = ctx->xin_w; pa.ldx = T.H;
+  pa.Y = ctx->x_p; pa.ldy = P.H; pa.epi = EPI_STORE;
+
+  for (int st = 0; st < 15; ++st) {
+    const int M = st == 0 ? 2 * B : B;
+    if (proj) { pa.M = M; HIPCK(launch_linear(pa, s)); }
+    if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s)); }
+    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s)); }
+    // head st on the last token of each row
+    LinearArgs ha{};
+    ha.wdtype = wd; ha.W = (const char*)ctx->phead + (size_t)st * C * P.H * esize(wd); ha.N = C; ha.K = P.H;
+    ha.X = st == 0 ? ctx->x_p + P.H : ctx->x_p; ha.ldx = st == 0 ? 2L * P.H : P.H; ha.M = B;
+    ha.gain = ctx->pred_norm; ha.eps = P.eps;
+    ha.Y = ctx->logits_p + (size_t)st * ctx->cfg.max_batch * C; ha.ldy = C; ha.epi = EPI_STORE;
+    HIPCK(launch_linear(ha, s));
+    SelectArgs sa = select_base(ctx, ctx->ps, false);
+    sa.logits = ha.Y; sa.ld = C;
+    sa.stream = st + 1; sa.ctr = ctx->frame_k; sa.ctr_add = 0;
+    sa.forced = forced; sa.forced_ld = kGroups; sa.forced_col = st + 1;
+    sa.used = codes; sa.used_ld = kGroups; sa.used_col = st + 1;
+    sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = st + 1;
+    sa.epi = 1;
+    sa.tab = ctx->pemb; sa.tab_dtype = wd; sa.tab_dim = T.H; sa.tab_off = (long)st * C;
+    sa.next_in = st < 14 ? (proj ? ctx->xin_w : ctx->x_p) : nullptr; sa.next_ld = T.H;
+    sa.fb = ctx->x_t; sa.fb_ld = T.H;
+    sa.add_text = st == 14; sa.text_off = ctx->text_off; sa.text_len = ctx->text_len;
+    sa.frame_k = ctx->frame_k;
+    HIPCK(launch_select(sa, s));
+  }
+  // talker step at position P_r + k
+  QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s));
+  LinearArgs ta{};
+  ta.wdtype = wd; ta.W = ctx->thead; ta.N = ctx->cfg.talker_vocab; ta.K = T.H; ta.X = ctx->x_t; ta.ldx = T.H; ta.M = B;
+  ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = ctx->cfg.talker_vocab; ta.epi = EPI_STORE;
+  ta.norm_out = ctx->h; ta.ld_norm = T.H;
+  HIPCK(launch_linear(ta, s));
+  SelectArgs sa = select_base(ctx, ctx->ts, true);
+  sa.logits = ctx->logits_t; sa.ld = ctx->cfg.talker_vocab;
+  sa.stream = 0; sa.ctr = ctx->frame_k; sa.ctr_add = 1;
+  sa.used = ctx->code0_next; sa.used_ld = 1; sa.used_col = 0;
+  sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = 0;
+  sa.epi = forced ? 0 : 2; sa.finished = ctx->finished; sa.state = state;
+  sa.frame_k = ctx->frame_k;
+  HIPCK(launch_select(sa, s));
+  HIPCK(launch_frame_advance(ctx->frame_k, ctx->pos, B, s));
+  return QT_OK;
+}
+
+qt_status read_status(qt_ctx* ctx) {
+  const int st = ctx->hout[0];
+  if (st & ST_NONFINITE) {
+    ctx->failed = true;
+    set_err(ctx->err, "non-finite logit on the device (frame %d)", ctx->frames_done);
+    return QT_E_NAN;
+  }
+  if (st & ST_RANGE) {
+    ctx->failed = true;
+    set_err(ctx->err, "code id out of range on the device (frame %d)", ctx->frames_done);
+    return QT_E_RANGE;
+  }
+  return QT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qt_status qt_config_check(const qt_config* cfg) { return check_config(cfg, g_err); }
+
+qt_status qt_workspace_bytes(const qt_config* cfg, size_t* bytes) {
+  qt_status s = check_config(cfg, g_err);
+  if (s != QT_OK) return s;
+  if (!bytes) { set_err(g_err, "bytes is NULL"); return QT_E_INVALID; }
+  Layout L = plan_layout(*cfg);
+  if (L.ovf) { set_err(g_err, "workspace size overflows size_t"); return QT_E_CAPACITY; }
+  *bytes = L.total;
+  return QT_OK;
+}
+
+const char* qt_last_error(const qt_ctx* ctx) { return ctx ? ctx->err : g_err; }
+
+qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, size_t ws_bytes, void* hip_stream,
+                    qt_ctx** out) {
+  qt_status s = check_config(cfg, g_err);
+  if (s != QT_OK) return s;
+  if (!out) { set_err(g_err, "out is NULL"); return QT_E_INVALID; }
+  *out = nullptr;
+  if (!w || !w->talker_layers || !w->pred_layers || !w->talker_norm || !w->talker_codec_embed ||
+      !w->talker_codec_head || !w->pred_norm || !w->pred_embeds || !w->pred_heads) {
+    set_err(g_err, "a weight pointer is NULL");
+    return QT_E_INVALID;
+  }
+  if (cfg->pred_in_proj && !w->pred_in_proj) { set_err(g_err, "pred_in_proj weights are NULL"); return QT_E_INVALID; }
+  Layout L = plan_layout(*cfg);
+  if (L.ovf) { set_err(g_err, "workspace size overflows size_t"); return QT_E_CAPACITY; }
+  if (workspace && ws_bytes < L.total) {
+    set_err(g_err, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    return QT_E_NOMEM;
+  }
+  qt_ctx* ctx = new (std::nothrow) qt_ctx();
+  if (!ctx) { set_err(g_err, "out of host memory"); return QT_E_NOMEM; }
+  ctx->cfg = *cfg;
+  ctx->t = Dec::of(cfg->talker);
+  ctx->p = Dec::of(cfg->predictor);
+  ctx->lay = L;
+  ctx->stream = (hipStream_t)hip_stream;
+  auto fail = [&](qt_status st) {
+    snprintf(g_err, sizeof g_err, "%s", ctx->err);
+    qt_destroy(ctx);
+    return st;
+  };
+  if (hipGetDevice(&ctx->device) != hipSuccess) { set_err(ctx->err, "no HIP device"); return fail(QT_E_HIP); }
+  if (workspace) {
+    ctx->ws = (char*)workspace;
+  } else {
+    if (hipMalloc((void**)&ctx->ws, L.total) != hipSuccess) {
+      set_err(ctx->err, "hipMalloc of %zu bytes failed", L.total);
+      return fail(QT_E_NOMEM);
+    }
+    ctx->own_ws = true;
+  }
+  if (hipStreamCreateWithFlags(&ctx->cap, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ctx->ev, hipEventDisableTiming) != hipSuccess) {
+    set_err(ctx->err, "stream/event creation failed");
+    return fail(QT_E_HIP);
+  }
+  if (hipHostMalloc((void**)&ctx->hout, (1 + cfg->max_batch + (size_t)cfg->max_batch * kGroups) * sizeof(int)) !=
+      hipSuccess) {
+    set_err(ctx->err, "pinned host allocation failed");
+    return fail(QT_E_NOMEM);
+  }
+  for (const LayerBuf& b : L.tl)
+    ctx->tl.push_back({at<void>(ctx, b.wqkv), at<void>(ctx, b.wo), at<void>(ctx, b.wgu), at<void>(ctx, b.wd),
+                       at<float>(ctx, b.attn_norm), at<float>(ctx, b.q_norm), at<float>(ctx, b.k_norm),
+                       at<float>(ctx, b.mlp_norm)});
+  for (const LayerBuf& b : L.pl)
+    ctx->pl.push_back({at<void>(ctx, b.wqkv), at<void>(ctx, b.wo), at<void>(ctx, b.wgu), at<void>(ctx, b.wd),
+                       at<float>(ctx, b.attn_norm), at<float>(ctx, b.q_norm), at<float>(ctx, b.k_norm),
+                       at<float>(ctx, b.mlp_norm)});
+  ctx->talker_norm = at<float>(ctx, L.talker_norm);
+  ctx->temb = at<void>(ctx, L.temb);
+  ctx->thead = at<void>(ctx, L.thead);
+  ctx->pred_norm = at<float>(ctx, L.pred_norm);
+  ctx->pemb = at<void>(ctx, L.pemb);
+  ctx->phead = at<void>(ctx, L.phead);
+  ctx->pproj = cfg->pred_in_proj ? at<void>(ctx, L.pproj) : nullptr;
+  ctx->cos_t = at<float>(ctx, L.cos_t); ctx->sin_t = at<float>(ctx, L.sin_t);
+  ctx->cos_p = at<float>(ctx, L.cos_p); ctx->sin_p = at<float>(ctx, L.sin_p);
+  ctx->kc_t = at<void>(ctx, L.kc_t); ctx->vc_t = at<void>(ctx, L.vc_t);
+  ctx->kc_p = at<void>(ctx, L.kc_p); ctx->vc_p = at<void>(ctx, L.vc_p);
+  ctx->x_t = at<float>(ctx, L.x_t); ctx->qkv = at<float>(ctx, L.qkv); ctx->attn = at<float>(ctx, L.attn);
+  ctx->act = at<float>(ctx, L.act); ctx->x_p = at<float>(ctx, L.x_p);
+  ctx->xin_w = cfg->pred_in_proj ? at<float>(ctx, L.xin_w) : nullptr;
+  ctx->h = at<float>(ctx, L.h); ctx->xlast = at<float>(ctx, L.xlast);
+  ctx->logits_t = at<float>(ctx, L.logits_t); ctx->logits_p = at<float>(ctx, L.logits_p);
+  int* rs = at<int>(ctx, L.rowstate);
+  const int MB = cfg->max_batch;
+  ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->text_off = rs + 3 * MB;
+  ctx->text_len = rs + 4 * MB; ctx->own = rs + 5 * MB; ctx->forced = rs + 5 * MB + kGroups * MB;
+  ctx->frame_k = rs + 5 * MB + 2 * kGroups * MB;
+  ctx->seen = at<uint32_t>(ctx, L.seen);
+  ctx->runs = at<Run>(ctx, L.runs);
+  ctx->idx = at<int>(ctx, L.idx);
+  ctx->frame_out = at<int>(ctx, L.frame_out);
+  ctx->req = at<ReqParams>(ctx, L.req);
+
+  hipStream_t st = ctx->stream;
+  for (int i = 0; i < ctx->t.L; ++i) {
+    qt_status r = pack_layer(ctx, w->talker_layers[i], ctx->t, ctx->tl[i], st);
+    if (r != QT_OK) return fail(r);
+  }
+  for (int i = 0; i < ctx->p.L; ++i) {
+    qt_status r = pack_layer(ctx, w->pred_layers[i], ctx->p, ctx->pl[i], st);
+    if (r != QT_OK) return fail(r);
+  }
+  const int wd = cfg->weight_dtype;
+  const Dec &T = ctx->t, &P = ctx->p;
+  const long V = cfg->talker_vocab, C = cfg->codebook;
+  auto conv = [&](const void* src, void* dst, int ddt, long rows, int n) -> bool {
+    return launch_convert(src, wd, n, dst, ddt, n, rows, n, st) == hipSuccess;
+  };
+  bool ok = conv(w->talker_norm, ctx->talker_norm, DT_F32, 1, T.H) && conv(w->talker_codec_embed, ctx->temb, wd, V, T.H) &&
+            conv(w->talker_codec_head, ctx->thead, wd, V, T.H) && conv(w->pred_norm, ctx->pred_norm, DT_F32, 1, P.H) &&
+            conv(w->pred_embeds, ctx->pemb, wd, 15 * C, T.H) && conv(w->pred_heads, ctx->phead, wd, 15 * C, P.H) &&
+            (!cfg->pred_in_proj || conv(w->pred_in_proj, ctx->pproj, wd, P.H, T.H));
+  if (!ok) { set_err(ctx->err, "weight repack launch failed"); return fail(QT_E_HIP); }
+  std::vector<float> cs, sn;
+  host_rope(cfg->max_positions, T.d, T.theta, cs, sn);
+  if (hipMemcpyAsync(ctx->cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(ctx->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    set_err(ctx->err, "rope table upload failed");
+    return fail(QT_E_HIP);
+  }
+  host_rope(kPredPositions, P.d, P.theta, cs, sn);
+  if (hipMemcpyAsync(ctx->cos_p, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(ctx->sin_p, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    set_err(ctx->err, "rope table upload failed");
+    return fail(QT_E_HIP);
+  }
+  *out = ctx;
+  return QT_OK;
+}
+
+void qt_destroy(qt_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->stream || ctx->cap) (void)hipDeviceSynchronize();
+  if (ctx->gexec) (void)hipGraphExecDestroy(ctx->gexec);
+  if (ctx->own_ws && ctx->ws) (void)hipFree(ctx->ws);
+  if (ctx->hout) (void)hipHostFree(ctx->hout);
+  if (ctx->ev) (void)hipEventDestroy(ctx->ev);
+  if (ctx->cap) (void)hipStreamDestroy(ctx->cap);
+  delete ctx;
+}
+
+qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t* prompt_lens, const float* text,
+                     const int32_t* text_lens, const float* tts_pad, const qt_sampling* talker,
+                     const qt_sampling* predictor, uint64_t seed, int32_t max_frames) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  const qt_config& c = ctx->cfg;
+  if (B < 1 || B > c.max_batch) { set_err(ctx->err, "B=%d outside 1..max_batch=%d", B, c.max_batch); return QT_E_CAPACITY; }
+  if (!prompt || !prompt_lens || !tts_pad) { set_err(ctx->err, "prompt, prompt_lens and tts_pad must not be NULL"); return QT_E_INVALID; }
+  if (max_frames < 1) { set_err(ctx->err, "max_frames must be >= 1"); return QT_E_INVALID; }
+  if (!sampling_ok(talker, ctx->err, "talker") || !sampling_ok(predictor, ctx->err, "predictor")) return QT_E_INVALID;
+  long total = 0, text_total = 0;
+  for (int r = 0; r < B; ++r) {
+    if (prompt_lens[r] < 1) { set_err(ctx->err, "prompt_lens[%d]=%d must be >= 1", r, prompt_lens[r]); return QT_E_RANGE; }
+    if ((long)prompt_lens[r] + max_frames > c.max_positions) {
+      set_err(ctx->err, "row %d: prompt %d + max_frames %d exceeds max_positions %d", r, prompt_lens[r], max_frames, c.max_positions);
+      return QT_E_CAPACITY;
+    }
+    total += prompt_lens[r];
+    if (text_lens) {
+      if (text_lens[r] < 0) { set_err(ctx->err, "text_lens[%d] must be >= 0", r); return QT_E_RANGE; }
+      text_total += text_lens[r];
+    }
+  }
+  if (text_total > 0 && !text) { set_err(ctx->err, "text is NULL but text_lens are positive"); return QT_E_INVALID; }
+  if (total > (1L << 30)) { set_err(ctx->err, "total prompt length too large"); return QT_E_CAPACITY; }
+
+  ctx->B = B; ctx->prefilled = false; ctx->failed = false; ctx->frames_done = 0; ctx->max_frames = max_frames;
+  ctx->done.assign(B, 0); ctx->ts = *talker; ctx->ps = *predictor; ctx->seed = seed;
+  ctx->text = text; ctx->pad = tts_pad; ctx->has_text = text_total > 0;
+  ctx->eager_frames = 0;
+  const Dec& T = ctx->t;
+  hipStream_t s = ctx->stream;
+
+  // host-side run tables
+  const int MB = c.max_batch;
+  std::vector<Run> runs((size_t)3 * MB, Run{0, 0, 0, 0});
+  for (int r = 0; r < B; ++r) {
+    runs[r] = Run{r, r, 1, 0};                 // talker decode (pos from the device)
+    runs[MB + r] = Run{r, 2 * r, 2, 0};        // predictor pass 0: positions 0, 1
+    runs[2 * MB + r] = Run{r, r, 1, 0};        // predictor step s: position s + 1
+  }
+  std::vector<long> start(B + 1, 0);
+  for (int r = 0; r < B; ++r) start[r + 1] = start[r] + prompt_lens[r];
+  struct Chunk { long t0; int n; int run0, nrun; int last0, nlast, lastrow0; };
+  std::vector<Chunk> chunks;
+  std::vector<int> lastidx;
+  for (long t0 = 0; t0 < total; t0 += kPrefillChunk) {
+    Chunk ch{t0, (int)std::min<long>(kPrefillChunk, total - t0), (int)runs.size(), 0, (int)lastidx.size(), 0, -1};
+    for (int r = 0; r < B; ++r) {
+      const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
+      if (a >= b) continue;
+      runs.push_back(Run{r, (int)(a - t0), (int)(b - a), (int)(a - start[r])});
+      ch.nrun++;
+      if (start[r + 1] - 1 >= t0 && start[r + 1] - 1 < t0 + ch.n) {
+        if (ch.lastrow0 < 0) ch.lastrow0 = r;
+        lastidx.push_back((int)(start[r + 1] - 1 - t0));
+        ch.nlast++;
+      }
+    }
+    chunks.push_back(ch);
+  }
+  if ((int)runs.size() > ctx->lay.max_runs) { set_err(ctx->err, "internal: run table overflow"); return QT_E_CAPACITY; }
+  std::vector<int> rowinit((size_t)5 * MB, 0);
+  long to = 0;
+  for (int r = 0; r < B; ++r) {
+    rowinit[2 * MB + r] = prompt_lens[r];                 // pos
+    rowinit[3 * MB + r] = (int)to;                        // text_off
+    rowinit[4 * MB + r] = text_lens ? text_lens[r] : 0;   // text_len
+    to += text_lens ? text_lens[r] : 0;
+  }
+  ReqParams rq{};
+  const qt_sampling* sm[2] = {talker, predictor};
+  for (int i = 0; i < 2; ++i)
+    rq.samp[i] = SampParams{sm[i]->do_sample, sm[i]->temperature, sm[i]->top_k, sm[i]->top_p,
+                            sm[i]->repetition_penalty, sm[i]->min_new_tokens};
+  rq.seed = seed; rq.max_frames = max_frames; rq.has_text = text_total > 0; rq.text = text; rq.pad = tts_pad;
+  HIPCK(hipMemcpyAsync(ctx->req, &rq, sizeof rq, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->runs, runs.data(), runs.size() * sizeof(Run), hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->idx, lastidx.data(), lastidx.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->code0_next, rowinit.data(), rowinit.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCK(launch_fill_i32(ctx->frame_k, 0, 1, s));
+  HIPCK(launch_fill_i32((int*)ctx->seen, 0, (long)MB * ctx->lay.seen_words, s));
+  HIPCK(launch_fill_i32(ctx->frame_out, 0, 1 + MB + (long)MB * kGroups, s));
+  HIPCK(launch_fill_i32(ctx->own, 0, (long)MB * kGroups, s));
+
+  for (const Chunk& ch : chunks) {
+    HIPCK(hipMemcpyAsync(ctx->x_t, prompt + ch.t0 * T.H, (size_t)ch.n * T.H * 4, hipMemcpyDeviceToDevice, s));
+    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s);
+    if (r != QT_OK) return r;
+    if (ch.nlast > 0)
+      HIPCK(launch_copy_rows(ctx->x_t, T.H, ctx->idx + ch.last0, ch.nlast, ctx->xlast + (size_t)ch.lastrow0 * T.H, T.H,
+                             T.H, s));
+  }
+  LinearArgs ta{};
+  ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H; ta.X = ctx->xlast; ta.ldx = T.H;
+  ta.M = B; ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = c.talker_vocab;
+  ta.epi = EPI_STORE; ta.norm_out = ctx->h; ta.ld_norm = T.H;
+  HIPCK(launch_linear(ta, s));
+  SelectArgs sa = select_base(ctx, ctx->ts, true);
+  sa.logits = ctx->logits_t; sa.ld = c.talker_vocab; sa.stream = 0; sa.ctr = nullptr; sa.ctr_add = 0;
+  sa.used = ctx->code0_next; sa.used_ld = 1; sa.used_col = 0;
+  sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = 0;
+  sa.epi = 2; sa.finished = ctx->finished; sa.state = ctx->frame_out + 1;
+  sa.frame_k = nullptr;
+  HIPCK(launch_select(sa, s));
+  HIPCK(hipMemcpyAsync(ctx->hout, ctx->frame_out, (1 + MB) * sizeof(int), hipMemcpyDeviceToHost, s));
+  HIPCK(hipStreamSynchronize(s));
+  qt_status r = read_status(ctx);
+  if (r != QT_OK) return r;
+  for (int i = 0; i < B; ++i) ctx->done[i] = ctx->hout[1 + i] == 1;
+  ctx->prefilled = true;
+  return QT_OK;
+}
+
+static qt_status frame_common(qt_ctx* ctx, const int* forced_dev) {
+  hipStream_t s = ctx->stream;
+  const int MB = ctx->cfg.max_batch;
+  if (forced_dev) {
+    qt_status r = enqueue_frame(ctx, s, forced_dev);
+    if (r != QT_OK) return r;
+  } else {
+    // the first frame after a prefill runs eagerly; later frames replay one captured graph
+    if (ctx->gexec && ctx->graph_B == ctx->B) {
+      HIPCK(hipGraphLaunch(ctx->gexec, s));
+    } else if (ctx->eager_frames == 0) {
+      qt_status r = enqueue_frame(ctx, s, nullptr);
+      if (r != QT_OK) return r;
+      ctx->eager_frames++;
+    } else {
+      if (ctx->gexec) { (void)hipGraphExecDestroy(ctx->gexec); ctx->gexec = nullptr; }
+      HIPCK(hipStreamSynchronize(s));
+      hipGraph_t g = nullptr;
+      HIPCK(hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal));
+      qt_status r = enqueue_frame(ctx, ctx->cap, nullptr);
+      hipError_t e = hipStreamEndCapture(ctx->cap, &g);
+      if (r != QT_OK) { if (g) (void)hipGraphDestroy(g); return r; }
+      if (e != hipSuccess) { set_err(ctx->err, "graph capture failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+      e = hipGraphInstantiate(&ctx->gexec, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if (e != hipSuccess) { ctx->gexec = nullptr; set_err(ctx->err, "graph instantiate failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+      ctx->graph_B = ctx->B;
+      HIPCK(hipGraphLaunch(ctx->gexec, s));
+    }
+  }
+  HIPCK(hipMemcpyAsync(ctx->hout, ctx->frame_out, (1 + MB + (size_t)MB * kGroups) * sizeof(int), hipMemcpyDeviceToHost, s));
+  HIPCK(hipEventRecord(ctx->ev, s));
+  HIPCK(hipEventSynchronize(ctx->ev));
+  return read_status(ctx);
+}
+
+qt_status qt_step_frame(qt_ctx* ctx, int32_t* codes, uint8_t* state) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!codes || !state) { set_err(ctx->err, "codes and state must not be NULL"); return QT_E_INVALID; }
+  if (!ctx->prefilled || ctx->failed) { set_err(ctx->err, "qt_step_frame needs a successful qt_prefill first"); return QT_E_STATE; }
+  bool any = false;
+  for (int r = 0; r < ctx->B; ++r) any |= !ctx->done[r];
+  if (!any || ctx->frames_done >= ctx->max_frames) { set_err(ctx->err, "every row has finished"); return QT_E_STATE; }
+  qt_status r = frame_common(ctx, nullptr);
+  if (r != QT_OK) return r;
+  const int MB = ctx->cfg.max_batch;
+  for (int i = 0; i < ctx->B; ++i) {
+    const int st = ctx->hout[1 + i];
+    state[i] = (uint8_t)(ctx->done[i] ? 3 : st);
+    if (!ctx->done[i] && (st == 1 || st == 2)) ctx->done[i] = 1;
+    memcpy(codes + (size_t)i * kGroups, ctx->hout + 1 + MB + (size_t)i * kGroups, kGroups * sizeof(int));
+  }
+  ctx->frames_done++;
+  return QT_OK;
+}
+
+qt_status qt_generate(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t* prompt_lens, const float* text,
+                      const int32_t* text_lens, const float* tts_pad, const qt_sampling* talker,
+                      const qt_sampling* predictor, uint64_t seed, int32_t max_frames, int32_t* codes,
+                      int32_t* n_frames, uint8_t* finish) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!codes || !n_frames || !finish) { set_err(ctx->err, "codes, n_frames and finish must not be NULL"); return QT_E_INVALID; }
+  qt_status r = qt_prefill(ctx, B, prompt, prompt_lens, text, text_lens, tts_pad, talker, predictor, seed, max_frames);
+  if (r != QT_OK) return r;
+  std::vector<int32_t> fc((size_t)B * kGroups);
+  std::vector<uint8_t> st(B);
+  for (int i = 0; i < B; ++i) {
+    n_frames[i] = 0;
+    finish[i] = ctx->done[i] ? 1 : 0;
+  }
+  while (true) {
+    bool any = false;
+    for (int i = 0; i < B; ++i) any |= !ctx->done[i];
+    if (!any) break;
+    r = qt_step_frame(ctx, fc.data(), st.data());
+    if (r != QT_OK) return r;
+    for (int i = 0; i < B; ++i) {
+      if (st[i] == 3) continue;
+      memcpy(codes + ((size_t)i * max_frames + n_frames[i]) * kGroups, fc.data() + (size_t)i * kGroups,
+             kGroups * sizeof(int32_t));
+      n_frames[i]++;
+      if (st[i] == 1 || st[i] == 2) finish[i] = st[i];
+    }
+  }
+  return QT_OK;
+}
+
+qt_status qt_debug_step_forced(qt_ctx* ctx, const int32_t* forced, float* talker_logits, float* pred_logits,
+                               int32_t* chosen) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!forced) { set_err(ctx->err, "forced must not be NULL"); return QT_E_INVALID; }
+  if (!ctx->prefilled || ctx->failed) { set_err(ctx->err, "qt_debug_step_forced needs a successful qt_prefill first"); return QT_E_STATE; }
+  if (ctx->frames_done >= ctx->max_frames) { set_err(ctx->err, "max_frames reached"); return QT_E_STATE; }
+  const qt_config& c = ctx->cfg;
+  const int B = ctx->B, MB = c.max_batch;
+  for (int r = 0; r < B; ++r)
+    for (int g = 0; g < kGroups; ++g) {
+      const int v = forced[r * kGroups + g];
+      const int hi = g == 0 ? c.talker_vocab : c.codebook;
+      if (v < 0 || v >= hi) { set_err(ctx->err, "forced[%d][%d]=%d out of range", r, g, v); return QT_E_RANGE; }
+    }
+  hipStream_t s = ctx->stream;
+  HIPCK(hipMemcpyAsync(ctx->forced, forced, (size_t)B * kGroups * sizeof(int), hipMemcpyHostToDevice, s));
+  qt_status r = frame_common(ctx, ctx->forced);
+  if (r != QT_OK) return r;
+  if (talker_logits)
+    HIPCK(hipMemcpy(talker_logits, ctx->logits_t, (size_t)B * c.talker_vocab * 4, hipMemcpyDeviceToHost));
+  if (pred_logits) {
+    std::vector<float> tmp((size_t)15 * MB * c.codebook);
+    HIPCK(hipMemcpy(tmp.data(), ctx->logits_p, tmp.size() * 4, hipMemcpyDeviceToHost));
+    for (int st = 0; st < 15; ++st)
+      for (int i = 0; i < B; ++i)
+        memcpy(pred_logits + ((size_t)i * 15 + st) * c.codebook, tmp.data() + ((size_t)st * MB + i) * c.codebook,
+               (size_t)c.codebook * 4);
+  }
+  if (chosen) HIPCK(hipMemcpy(chosen, ctx->own, (size_t)B * kGroups * sizeof(int), hipMemcpyDeviceToHost));
+  ctx->frames_done++;
+  return QT_OK;
+}
+
+qt_status qt_debug_talker_logits(qt_ctx* ctx, float* logits) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!logits) { set_err(ctx->err, "logits must not be NULL"); return QT_E_INVALID; }
+  if (!ctx->prefilled) { set_err(ctx->err, "no prefill yet"); return QT_E_STATE; }
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  HIPCK(hipMemcpy(logits, ctx->logits_t, (size_t)ctx->B * ctx->cfg.talker_vocab * 4, hipMemcpyDeviceToHost));
+  return QT_OK;
+}
+
+qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* logits, const uint32_t* seen,
+                          const float* noise, const float* probs, int32_t processors, int32_t eos,
+                          int32_t suppress_begin, int32_t suppress_end, const qt_sampling* samp, uint64_t seed,
+                          int32_t stream, int32_t sel_index, int32_t* out_code, float* processed, int32_t* status) {
+  if (B < 1 || B > 65535 || V < 2 || V > kMaxVocab) { set_err(g_err, "B or V out of range"); return QT_E_INVALID; }
+  if (!logits || !out_code || !status) { set_err(g_err, "logits, out_code and status must not be NULL"); return QT_E_INVALID; }
+  if (!sampling_ok(samp, g_err, "select")) return QT_E_INVALID;
+  if (processors && (eos < 0 || eos >= V || suppress_begin < 0 || suppress_begin > suppress_end || suppress_end > V)) {
+    set_err(g_err, "eos / suppress range out of range");
+    return QT_E_INVALID;
+  }
+  if (sel_index < 0 || stream < 0) { set_err(g_err, "sel_index and stream must be >= 0"); return QT_E_INVALID; }
+  SelectArgs a{};
+  a.logits = logits; a.ld = V; a.V = V; a.B = B;
+  a.processors = processors;
+  a.seen = const_cast<uint32_t*>(seen); a.seen_words = (V + 31) / 32;
+  a.penalty = seen ? samp->repetition_penalty : 1.0f; a.min_new = samp->min_new_tokens;
+  a.eos = eos; a.sup_b = suppress_begin; a.sup_e = suppress_end;
+  a.do_sample = samp->do_sample; a.temperature = samp->temperature; a.top_k = samp->top_k; a.top_p = samp->top_p;
+  a.seed = seed; a.stream = stream; a.ctr = nullptr; a.ctr_add = sel_index;
+  a.noise_in = noise; a.probs_in = probs;
+  a.used = out_code; a.used_ld = 1; a.used_col = 0;
+  a.processed_out = processed; a.status = status; a.epi = 0;
+  hipError_t e = launch_select(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) { set_err(g_err, "select launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+  return QT_OK;
+}
+
+qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
+                          int32_t M, const float* gain, float eps, int32_t epilogue, float* Y, int32_t reps) {
+  if (wdtype != QT_DTYPE_F32 && wdtype != QT_DTYPE_BF16) { set_err(g_err, "bad wdtype"); return QT_E_INVALID; }
+  if (!W || !X || !Y) { set_err(g_err, "W, X and Y must not be NULL"); return QT_E_INVALID; }
+  if (N < 1 || K < 8 || K % 8 || M < 1 || reps < 1 || epilogue < 0 || epilogue > 2 || (epilogue == 2 && N % 2)) {
+    set_err(g_err, "bad shape: need N >= 1, K a positive multiple of 8, M >= 1, even N for SwiGLU");
+    return QT_E_INVALID;
+  }
+  if (K > 24576) { set_err(g_err, "K too large for the LDS activation tile"); return QT_E_INVALID; }
+  LinearArgs a{};
+  a.W = W; a.wdtype = wdtype; a.N = N; a.K = K; a.X = X; a.ldx = K; a.M = M; a.gain = gain; a.eps = eps;
+  a.Y = Y; a.ldy = epilogue == 2 ? N / 2 : N; a.epi = epilogue;
+  for (int i = 0; i < reps; ++i) {
+    hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
+    if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+  }
+  return QT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Internal interface between the C-ABI layer (qt_api.hip) and the gfx950
+// kernels (qt_kernels.hip). Not installed; the public ABI is include/qt.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace qt {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum Epi { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
+
+// Device status word bits (read at the once-per-frame sync).
+enum StatusBits : int { ST_NONFINITE = 1, ST_RANGE = 2 };
+
+// Y[m, :] (op)= W · norm(X[m, :]) for m < M.  W is [N, K] row-major
+// (nn.Linear layout), f32 or bf16; X, Y fp32.  With EPI_SWIGLU the rows of W
+// come in (gate j, up j) pairs and Y[m, j] = silu(gate) * up.
+struct LinearArgs {
+  const void* W; int wdtype; int N; int K;
+  const float* X; long ldx; int M;
+  const float* gain; float eps;        // RMSNorm prologue when gain != nullptr
+  float* Y; long ldy; int epi;
+  float* norm_out; long ld_norm;       // optional copy of the normalised X
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+
+// One contiguous run of tokens of one batch row: row, first token (row of the
+// activation arrays), token count, first position (before pos_base / row_pos).
+struct Run { int row, tok0, ntok, pos0; };
+
+// Per-head QK-RMSNorm + rope of q and k, K/V write into the cache, then causal
+// GQA attention of every token of the run over cached positions <= its own.
+struct AttnArgs {
+  const float* qkv; long ld_qkv;       // [T, (nq + 2 nkv) d]
+  float* out; long ld_out;             // [T, nq d]
+  const float* q_gain; const float* k_gain; float eps; float scale;
+  const float* cos; const float* sin;  // [max_pos, d/2]
+  void* kc; void* vc; int kvdtype;     // this layer: [rows][nkv][max_pos][d]
+  long row_stride; int max_pos;
+  const Run* runs; int n_runs; const int* row_pos; int pos_base;
+  int nq, nkv, d;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// Per-request settings kept in device memory, so that one captured frame
+// graph serves every request of the same batch size.
+struct SampParams { int do_sample; float temperature; int top_k; float top_p; float penalty; int min_new; };
+struct ReqParams {
+  SampParams samp[2];                  // [0] talker, [1] code predictor
+  uint64_t seed;
+  int max_frames; int has_text;
+  const float* text; const float* pad; // trailing text rows / tts_pad (device)
+};
+
+// Logits processing + selection for one batch of rows (one block per row).
+// With req != nullptr the sampling settings, seed, max_frames and text / pad
+// pointers are read from req (samp[which]) instead of the fields below.
+struct SelectArgs {
+  const ReqParams* req; int which;
+  const float* logits; long ld; int V; int B;
+  // talker processors
+  int processors;
+  uint32_t* seen; int seen_words;
+  float penalty; int min_new; int eos; int sup_b; int sup_e;
+  // warpers
+  int do_sample; float temperature; int top_k; float top_p;
+  uint64_t seed; int stream; const int* ctr; int ctr_add;
+  // debug inputs (nullable): explicit Exp(1) noise / probabilities [B, V]
+  const float* noise_in; const float* probs_in;
+  // outputs
+  const int* forced; int forced_ld; int forced_col;   // teacher forcing (nullable)
+  int* used; int used_ld; int used_col;                // code that feeds the model
+  int* own; int own_ld; int own_col;                   // the kernel's own choice (nullable)
+  float* processed_out;                                 // debug: processed logits [B, V]
+  int* status;
+  // epilogue 1: code predictor (next input row, feedback sum)
+  int epi;
+  const void* tab; int tab_dtype; int tab_dim; long tab_off;
+  float* next_in; long next_ld;
+  float* fb; long fb_ld;
+  int add_text; const float* text; const int* text_off; const int* text_len; const float* pad;
+  const int* frame_k;
+  // epilogue 2: talker lookahead, finish state
+  int* finished; int* state; int max_frames;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// Frame start: commit code 0 per row (forced / EOS for finished rows), mark
+// it seen, start the feedback sum, build the 2-token predictor pass-0 input.
+struct FrameStartArgs {
+  int B; int eos; int V;
+  const int* code0_next; const int* finished; const int* forced; int forced_ld;
+  uint32_t* seen; int seen_words;
+  int* codes;                          // [B, 16]
+  const void* temb; int tdtype; int H; // talker codec table [V, H]
+  const float* h;                      // [B, H] talker hidden for pass 0
+  float* pass0; long pass0_ld;         // [2B, H]
+  float* fb; long fb_ld;               // [B, H]
+  int* status;
+};
+hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s);
+
+// Frame end: frame counter and per-row talker positions advance by one.
+hipError_t launch_frame_advance(int* frame_k, int* pos, int B, hipStream_t s);
+
+// Row gather / scatter copies dst[i] = src[idx[i]] (fp32 rows of width n).
+hipError_t launch_copy_rows(const float* src, long ld_src, const int* idx, int count,
+                            float* dst, long ld_dst, int n, hipStream_t s);
+
+// Copy/convert [rows, n] from f32 or bf16 into the packed weight layout.
+hipError_t launch_convert(const void* src, int sdtype, long ld_src, void* dst, int ddtype, long ld_dst,
+                          long rows, int n, hipStream_t s);
+// Fill an int32 buffer.
+hipError_t launch_fill_i32(int* p, int v, long n, hipStream_t s);
+
+}  // namespace qt

@@ -1,0 +1,745 @@
+// gfx950 (CDNA4) kernels of the Qwen3-TTS 12 Hz per-frame generation step.
+//
+// Every step of the frame runs here: the weight-streaming projections with
+// fused RMSNorm prologues and residual / SwiGLU epilogues, the fused
+// QK-RMSNorm + rope + KV write + GQA attention, the logits processors and the
+// single-sample selection (Philox4x64-10 exponential race), the frame-start
+// commit of code 0 and the code-predictor gathers that also build the
+// embedding-sum feedback. Activations are fp32, weights fp32 or bf16, the KV
+// cache fp32 or bf16; accumulation is fp32 throughout.
+#include "qt_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+
+namespace qt {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = 256;  // threads per block for every kernel here
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// Round to nearest even; inputs are finite activations.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float ld_elem(const T* p, long i);
+template <> __device__ __forceinline__ float ld_elem<float>(const float* p, long i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, long i) { return bf16_to_f32(p[i]); }
+template <typename T> __device__ __forceinline__ void st_elem(T* p, long i, float v);
+template <> __device__ __forceinline__ void st_elem<float>(float* p, long i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st_elem<uint16_t>(uint16_t* p, long i, float v) { p[i] = f32_to_bf16(v); }
+
+__device__ __forceinline__ float ld_any(const void* p, int dt, long i) {
+  return dt == DT_BF16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Block-wide reductions for NT threads; `red` is LDS scratch of >= NT/64 floats.
+// All threads of the block must call them.
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += red[i];
+  return t;
+}
+__device__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+__device__ int block_or(int v, int* redi) {
+  __syncthreads();
+  if (threadIdx.x == 0) redi[0] = 0;
+  __syncthreads();
+  if (v) atomicOr(&redi[0], 1);
+  __syncthreads();
+  return redi[0];
+}
+// argmax with the lowest index on ties; (value, index) pairs, -inf allowed.
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+__device__ int block_argmax(float v, int i, float* redf, int* redi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o);
+    int oi = __shfl_xor(i, o);
+    better(v, i, ov, oi);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { redf[threadIdx.x >> 6] = v; redi[threadIdx.x >> 6] = i; }
+  __syncthreads();
+  float bv = redf[0];
+  int bi = redi[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) better(bv, bi, redf[w], redi[w]);
+  return bi;
+}
+
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default 64 KB (static LDS of the kernel still counts against the 160 KB).
+static hipError_t ensure_lds(const void* fn, size_t bytes, size_t* have) {
+  if (bytes <= 64 * 1024 || bytes <= *have) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) *have = bytes;
+  return e;
+}
+
+// ---------------------------------------------------------------- linear
+// Weight-streaming projection. Block = 4 waves; a wave owns R consecutive
+// output rows (KS waves share one row group and split K). Each lane streams
+// 16-byte chunks of its rows with nontemporal loads; the MT activation rows
+// (RMSNorm'd when a gain is given) sit in LDS and are reused by all rows.
+template <typename WT, int R, int MT, int KS>
+__global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
+  extern __shared__ float xs[];  // [MT][K], then reduction scratch
+  const int K = p.K, N = p.N;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m0 = blockIdx.y * MT;
+  const int mt = min(MT, p.M - m0);
+  float* red = xs + (long)MT * K;          // [4]
+  float* part = red + 4;                   // [4][R][MT]
+
+  for (int m = 0; m < mt; ++m) {
+    const float* xr = p.X + (long)(m0 + m) * p.ldx;
+    if (p.gain) {
+      float ss = 0.f;
+      for (int k = tid; k < K; k += NT) { float v = xr[k]; ss += v * v; }
+      ss = block_sum(ss, red);
+      const float den = sqrtf(ss / (float)K + p.eps);
+      for (int k = tid; k < K; k += NT) xs[m * K + k] = xr[k] / den * p.gain[k];
+    } else {
+      for (int k = tid; k < K; k += NT) xs[m * K + k] = xr[k];
+    }
+  }
+  for (int m = mt; m < MT; ++m)
+    for (int k = tid; k < K; k += NT) xs[m * K + k] = 0.f;
+  __syncthreads();
+  if (p.norm_out && blockIdx.x == 0)
+    for (int m = 0; m < mt; ++m)
+      for (int k = tid; k < K; k += NT) p.norm_out[(long)(m0 + m) * p.ld_norm + k] = xs[m * K + k];
+
+  constexpr int EPC = 16 / sizeof(WT);     // weight elements per 16-byte chunk
+  constexpr int RG = 4 / KS;               // row groups per block
+  const int wrow = wave / KS, ks = wave % KS;
+  const int row0 = (blockIdx.x * RG + wrow) * R;
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+
+  const WT* W = (const WT*)p.W;
+  for (int k0 = (ks * 64 + lane) * EPC; k0 < K; k0 += KS * 64 * EPC) {
+    u32x4 wv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      if (row < N) wv[r] = __builtin_nontemporal_load((const u32x4*)(W + (long)row * K + k0));
+      else wv[r] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (EPC == 8) {
+        const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
+        const f32x4 xb = *(const f32x4*)(xs + m * K + k0 + 4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float s = acc[r][m];
+          s = fmaf(bf_lo(wv[r].x), xa.x, s); s = fmaf(bf_hi(wv[r].x), xa.y, s);
+          s = fmaf(bf_lo(wv[r].y), xa.z, s); s = fmaf(bf_hi(wv[r].y), xa.w, s);
+          s = fmaf(bf_lo(wv[r].z), xb.x, s); s = fmaf(bf_hi(wv[r].z), xb.y, s);
+          s = fmaf(bf_lo(wv[r].w), xb.z, s); s = fmaf(bf_hi(wv[r].w), xb.w, s);
+          acc[r][m] = s;
+        }
+      } else {
+        const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float s = acc[r][m];
+          s = fmaf(__uint_as_float(wv[r].x), xa.x, s); s = fmaf(__uint_as_float(wv[r].y), xa.y, s);
+          s = fmaf(__uint_as_float(wv[r].z), xa.z, s); s = fmaf(__uint_as_float(wv[r].w), xa.w, s);
+          acc[r][m] = s;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  if constexpr (KS > 1) {
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) part[(wave * R + r) * MT + m] = acc[r][m];
+    __syncthreads();
+    if (ks == 0 && lane == 0)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float s = 0.f;
+          for (int j = 0; j < KS; ++j) s += part[((wave + j) * R + r) * MT + m];
+          acc[r][m] = s;
+        }
+  }
+  if (ks != 0 || lane != 0) return;
+  for (int m = 0; m < mt; ++m) {
+    float* y = p.Y + (long)(m0 + m) * p.ldy;
+    if (p.epi == EPI_SWIGLU) {
+#pragma unroll
+      for (int r = 0; r + 1 < R; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 < N) {
+          const float g = acc[r][m], u = acc[r + 1][m];
+          y[row >> 1] = g / (1.f + expf(-g)) * u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row < N) y[row] = (p.epi == EPI_RESIDUAL) ? y[row] + acc[r][m] : acc[r][m];
+      }
+    }
+  }
+}
+
+template <typename WT, int R, int MT, int KS>
+static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
+  constexpr int RG = 4 / KS;
+  dim3 grid((a.N + RG * R - 1) / (RG * R), (a.M + MT - 1) / MT);
+  const size_t lds = ((size_t)MT * a.K + 4 + 4 * R * MT) * sizeof(float);
+  static size_t have = 0;
+  hipError_t e = ensure_lds((const void*)linear_kernel<WT, R, MT, KS>, lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((linear_kernel<WT, R, MT, KS>), grid, dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename WT, int R, int KS>
+static hipError_t launch_linear_mt(const LinearArgs& a, int mt, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_linear_t<WT, R, 1, KS>(a, s);
+    case 2: return launch_linear_t<WT, R, 2, KS>(a, s);
+    case 4: return launch_linear_t<WT, R, 4, KS>(a, s);
+    default: return launch_linear_t<WT, R, 8, KS>(a, s);
+  }
+}
+
+template <typename WT>
+static hipError_t launch_linear_w(const LinearArgs& a, int mt, int R, int KS, hipStream_t s) {
+  if (R == 2) return KS == 4 ? launch_linear_mt<WT, 2, 4>(a, mt, s) : launch_linear_mt<WT, 2, 1>(a, mt, s);
+  return KS == 4 ? launch_linear_mt<WT, 1, 4>(a, mt, s) : launch_linear_mt<WT, 1, 1>(a, mt, s);
+}
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  // activation tile: as many rows as fit in 96 KB of LDS, up to 8
+  int mtmax = 8;
+  while (mtmax > 1 && (size_t)mtmax * a.K * 4 > 96 * 1024) mtmax >>= 1;
+  int mt = 1;
+  while (mt < a.M && mt < mtmax) mt <<= 1;
+  const int R = (a.epi == EPI_SWIGLU || a.N >= 4096) ? 2 : 1;
+  const int KS = (a.N / (4 * R) < 512 && a.K >= 1024) ? 4 : 1;
+  if (a.wdtype == DT_BF16) return launch_linear_w<uint16_t>(a, mt, R, KS, s);
+  return launch_linear_w<float>(a, mt, R, KS, s);
+}
+
+// ---------------------------------------------------------------- attention
+constexpr int ATT_CH = 256;   // keys per online-softmax chunk
+constexpr int MAXG = 8;       // max q heads per kv head
+
+template <typename KVT>
+__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs p) {
+  const int g = blockIdx.x;
+  const Run rn = p.runs[blockIdx.y];
+  const int tid = threadIdx.x;
+  const int d = p.d, half = d >> 1, G = p.nq / p.nkv;
+  const int pos0 = rn.pos0 + p.pos_base + (p.row_pos ? p.row_pos[rn.row] : 0);
+  extern __shared__ float sm[];
+  float* qs = sm;                      // [G][d]
+  float* sc = qs + G * d;              // [G][ATT_CH]
+  float* vec = sc + G * ATT_CH;        // [d]
+  float* part = vec + d;               // [NT/d slices][G][d]
+  float* red = part + NT * G;          // [8]
+  KVT* kc = (KVT*)p.kc + (long)rn.row * p.row_stride + (long)g * p.max_pos * d;
+  KVT* vc = (KVT*)p.vc + (long)rn.row * p.row_stride + (long)g * p.max_pos * d;
+
+  // 1) K (normalised + rotated) and V of every token of the run into the cache
+  for (int i = 0; i < rn.ntok; ++i) {
+    const float* src = p.qkv + (long)(rn.tok0 + i) * p.ld_qkv;
+    const float* kr = src + (long)p.nq * d + g * d;
+    const float* vr = src + (long)(p.nq + p.nkv) * d + g * d;
+    const int pos = pos0 + i;
+    const float kv = tid < d ? kr[tid] : 0.f;
+    const float ss = block_sum(kv * kv, red);
+    const float den = sqrtf(ss / (float)d + p.eps);
+    if (tid < d) vec[tid] = kv / den * p.k_gain[tid];
+    __syncthreads();
+    if (tid < half) {
+      const float c = p.cos[(long)pos * half + tid], s = p.sin[(long)pos * half + tid];
+      const float x1 = vec[tid], x2 = vec[tid + half];
+      st_elem<KVT>(kc, (long)pos * d + tid, x1 * c - x2 * s);
+      st_elem<KVT>(kc, (long)pos * d + tid + half, x2 * c + x1 * s);
+    }
+    if (tid < d) st_elem<KVT>(vc, (long)pos * d + tid, vr[tid]);
+    __syncthreads();
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  const int nsl = NT / d;              // key slices of the P·V product
+  const int dim = tid % d, sl = tid / d;
+  for (int i = 0; i < rn.ntok; ++i) {
+    const long t = rn.tok0 + i;
+    const float* src = p.qkv + t * p.ld_qkv;
+    const int pos = pos0 + i, L = pos + 1;
+    // q heads of this group: RMSNorm over d, then rope
+    for (int hh = 0; hh < G; ++hh) {
+      const float qv = tid < d ? src[(long)(g * G + hh) * d + tid] : 0.f;
+      const float ss = block_sum(qv * qv, red);
+      const float den = sqrtf(ss / (float)d + p.eps);
+      if (tid < d) vec[tid] = qv / den * p.q_gain[tid];
+      __syncthreads();
+      if (tid < half) {
+        const float c = p.cos[(long)pos * half + tid], s = p.sin[(long)pos * half + tid];
+        const float x1 = vec[tid], x2 = vec[tid + half];
+        qs[hh * d + tid] = x1 * c - x2 * s;
+        qs[hh * d + tid + half] = x2 * c + x1 * s;
+      }
+      __syncthreads();
+    }
+    float mrun[MAXG], lrun[MAXG], acc[MAXG];
+    for (int hh = 0; hh < G; ++hh) { mrun[hh] = -INFINITY; lrun[hh] = 0.f; acc[hh] = 0.f; }
+    for (int c0 = 0; c0 < L; c0 += ATT_CH) {
+      const int cn = min(ATT_CH, L - c0);
+      for (int j = tid; j < cn; j += NT) {
+        const KVT* kr = kc + (long)(c0 + j) * d;
+        float dots[MAXG];
+        for (int hh = 0; hh < G; ++hh) dots[hh] = 0.f;
+        for (int e = 0; e < d; ++e) {
+          const float kvv = ld_elem<KVT>(kr, e);
+          for (int hh = 0; hh < G; ++hh) dots[hh] = fmaf(qs[hh * d + e], kvv, dots[hh]);
+        }
+        for (int hh = 0; hh < G; ++hh) sc[hh * ATT_CH + j] = dots[hh] * p.scale;
+      }
+      __syncthreads();
+      for (int hh = 0; hh < G; ++hh) {
+        float mx = -INFINITY;
+        for (int j = tid; j < cn; j += NT) mx = fmaxf(mx, sc[hh * ATT_CH + j]);
+        mx = block_max(mx, red);
+        const float mnew = fmaxf(mrun[hh], mx);
+        const float corr = expf(mrun[hh] - mnew);
+        float sum = 0.f;
+        for (int j = tid; j < cn; j += NT) {
+          const float e = expf(sc[hh * ATT_CH + j] - mnew);
+          sc[hh * ATT_CH + j] = e;
+          sum += e;
+        }
+        sum = block_sum(sum, red);   // its barriers also publish sc
+        lrun[hh] = lrun[hh] * corr + sum;
+        acc[hh] *= corr;
+        mrun[hh] = mnew;
+      }
+      for (int j = sl; j < cn; j += nsl) {
+        const float vv = ld_elem<KVT>(vc, (long)(c0 + j) * d + dim);
+        for (int hh = 0; hh < G; ++hh) acc[hh] = fmaf(sc[hh * ATT_CH + j], vv, acc[hh]);
+      }
+      __syncthreads();
+    }
+    for (int hh = 0; hh < G; ++hh) part[(sl * G + hh) * d + dim] = acc[hh];
+    __syncthreads();
+    if (tid < d) {
+      for (int hh = 0; hh < G; ++hh) {
+        float s = 0.f;
+        for (int q = 0; q < nsl; ++q) s += part[(q * G + hh) * d + tid];
+        p.out[t * p.ld_out + (long)(g * G + hh) * d + tid] = s / lrun[hh];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n_runs <= 0) return hipSuccess;
+  const int G = a.nq / a.nkv;
+  const size_t lds = ((size_t)G * a.d + (size_t)G * ATT_CH + a.d + (size_t)NT * G + 8) * sizeof(float);
+  dim3 grid(a.nkv, a.n_runs);
+  if (a.kvdtype == DT_BF16) hipLaunchKernelGGL(attn_kernel<uint16_t>, grid, dim3(NT), lds, s, a);
+  else hipLaunchKernelGGL(attn_kernel<float>, grid, dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x64-10 (Salmon et al., SC'11): 10 rounds of two 64x64->128-bit
+// multiplies of counter words 0 and 2, halves mixed with words 1 and 3 and
+// the key; the key is bumped by two Weyl constants between rounds.
+__device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                                 uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return c0;
+}
+// E ~ Exp(1): u = ((x >> 12) + 1/2) 2^-52 in (0,1), E = -ln u in double, rounded to float.
+__device__ __forceinline__ float exp_noise(uint64_t seed, int row, int stream, int index, int id) {
+  const uint64_t x = philox_word0((uint64_t)id, (uint64_t)stream, (uint64_t)(int64_t)index, (uint64_t)row, seed, 0ull);
+  const double u = ((double)(x >> 12) + 0.5) * 0x1p-52;
+  return (float)(-log(u));
+}
+
+// ---------------------------------------------------------------- selection
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
+  const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
+  extern __shared__ float sm[];
+  float* v = sm;                         // [V] logits -> processed -> tempered -> p
+  float* cp = v + V;                     // [V] compacted survivor p
+  int* cid = (int*)(cp + V);             // [V] compacted survivor ids
+  float* sp = (float*)(cid + V);         // [V] survivors in (p desc, id asc) order
+  int* sid = (int*)(sp + V);             // [V]
+  __shared__ float redf[8];
+  __shared__ int redi[8];
+  __shared__ int hist[256];
+  __shared__ int scan[NT];
+  __shared__ int sh_int[4];
+  __shared__ float sh_f[2];
+
+  // settings: from the request block when given
+  int do_sample = a.do_sample, top_k = a.top_k, min_new = a.min_new, max_frames = a.max_frames;
+  float temperature = a.temperature, top_p = a.top_p, penalty = a.penalty;
+  uint64_t seed = a.seed;
+  const float* text = a.text;
+  const float* pad = a.pad;
+  int has_text = a.text_len != nullptr;
+  if (a.req) {
+    const SampParams sp = a.req->samp[a.which];
+    do_sample = sp.do_sample; top_k = sp.top_k; min_new = sp.min_new; temperature = sp.temperature;
+    top_p = sp.top_p; penalty = sp.penalty; seed = a.req->seed; max_frames = a.req->max_frames;
+    text = a.req->text; pad = a.req->pad; has_text = a.req->has_text;
+  }
+  const float* lg = a.logits + (long)r * a.ld;
+  int bad = 0;
+  for (int i = tid; i < V; i += NT) {
+    const float x = lg[i];
+    if (isnan(x) || x == INFINITY) bad = 1;
+    v[i] = x;
+  }
+  bad = block_or(bad, redi);
+  const int jsel = (a.ctr ? *a.ctr : 0) + a.ctr_add;
+  if (a.processors) {
+    const uint32_t* seen = a.seen + (long)r * a.seen_words;
+    const bool pen = penalty != 1.0f;
+    for (int i = tid; i < V; i += NT) {
+      float x = v[i];
+      if (pen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
+      if (i == a.eos && jsel < min_new) x = -INFINITY;
+      if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
+      v[i] = x;
+    }
+  }
+  __syncthreads();
+  if (a.processed_out)
+    for (int i = tid; i < V; i += NT) a.processed_out[(long)r * V + i] = v[i];
+
+  int choice = 0;
+  if (bad) {
+    if (tid == 0) atomicOr(a.status, ST_NONFINITE);
+  } else if (!do_sample) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = tid; i < V; i += NT) better(bv, bi, v[i], i);
+    choice = block_argmax(bv, bi, redf, redi);
+    if (choice >= V) choice = 0;   // every logit -inf (cannot happen: EOS or codes survive)
+  } else {
+    if (a.probs_in) {
+      for (int i = tid; i < V; i += NT) v[i] = a.probs_in[(long)r * V + i];
+      __syncthreads();
+    } else {
+      for (int i = tid; i < V; i += NT) v[i] = v[i] / temperature;
+      __syncthreads();
+      if (top_k > 0 && top_k < V) {
+        // radix select of the k-th largest value, 8 bits at a time from the top
+        uint32_t prefix = 0, mask = 0;
+        int kk = top_k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          hist[tid] = 0;
+          __syncthreads();
+          for (int i = tid; i < V; i += NT) {
+            const uint32_t key = ord_key(v[i]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+          }
+          __syncthreads();
+          if (tid == 0) {
+            int cum = 0, b = 255;
+            for (; b > 0; --b) {
+              if (cum + hist[b] >= kk) break;
+              cum += hist[b];
+            }
+            sh_int[0] = b;
+            sh_int[1] = kk - cum;
+          }
+          __syncthreads();
+          prefix |= ((uint32_t)sh_int[0]) << shift;
+          mask |= 255u << shift;
+          kk = sh_int[1];
+          __syncthreads();
+        }
+        const float tau = key_float(prefix);
+        for (int i = tid; i < V; i += NT)
+          if (v[i] < tau) v[i] = -INFINITY;
+        __syncthreads();
+      }
+      float mx = -INFINITY;
+      for (int i = tid; i < V; i += NT) mx = fmaxf(mx, v[i]);
+      mx = block_max(mx, redf);
+      float sum = 0.f;
+      for (int i = tid; i < V; i += NT) {
+        const float e = expf(v[i] - mx);
+        v[i] = e;
+        sum += e;
+      }
+      sum = block_sum(sum, redf);
+      for (int i = tid; i < V; i += NT) v[i] = v[i] / sum;
+      __syncthreads();
+    }
+    // compact survivors (p > 0) in index order: contiguous chunk per thread + scan
+    const int chunk = (V + NT - 1) / NT;
+    const int b0 = tid * chunk, b1 = min(V, b0 + chunk);
+    int cnt = 0;
+    for (int i = b0; i < b1; ++i) cnt += v[i] > 0.f;
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int ns = scan[NT - 1];
+    int o = scan[tid] - cnt;
+    for (int i = b0; i < b1; ++i)
+      if (v[i] > 0.f) { cp[o] = v[i]; cid[o] = i; ++o; }
+    __syncthreads();
+    // order by (p desc, id asc) via ranks
+    for (int c = tid; c < ns; c += NT) {
+      const float pc = cp[c];
+      const int ic = cid[c];
+      int rank = 0;
+      for (int j = 0; j < ns; ++j) {
+        const float pj = cp[j];
+        rank += (pj > pc) || (pj == pc && cid[j] < ic);
+      }
+      sp[rank] = pc;
+      sid[rank] = ic;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int keep = ns;
+      if (top_p < 1.0f) {
+        float cs = 0.f;
+        for (int j = 0; j < ns; ++j) {
+          cs += sp[j];
+          if (cs >= top_p) { keep = j + 1; break; }
+        }
+      }
+      sh_int[2] = keep;
+    }
+    __syncthreads();
+    const int keep = sh_int[2];
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = tid; j < keep; j += NT) {
+      const int id = sid[j];
+      const float e = a.noise_in ? a.noise_in[(long)r * V + id]
+                                 : exp_noise(seed, r, a.stream, jsel, id);
+      better(bv, bi, sp[j] / e, id);
+    }
+    choice = block_argmax(bv, bi, redf, redi);
+    if (choice >= V) choice = 0;
+  }
+
+  // commit
+  if (tid == 0) {
+    int used = choice;
+    if (a.forced) used = a.forced[(long)r * a.forced_ld + a.forced_col];
+    a.used[(long)r * a.used_ld + a.used_col] = used;
+    if (a.own) a.own[(long)r * a.own_ld + a.own_col] = choice;
+    sh_int[3] = used;
+    if (a.epi == 2) {
+      const int kf = a.frame_k ? *a.frame_k : -1;
+      if (a.finished[r]) {
+        a.state[r] = 3;
+      } else if (used == a.eos) {
+        a.state[r] = 1;
+        a.finished[r] = 1;
+      } else if (kf >= 0 && kf + 1 >= max_frames) {
+        a.state[r] = 2;
+        a.finished[r] = 1;
+      } else {
+        a.state[r] = 0;
+      }
+    }
+  }
+  __syncthreads();
+  if (a.epi == 1) {
+    const int used = sh_int[3];
+    const long base = (a.tab_off + used) * (long)a.tab_dim;
+    const int kf = a.frame_k ? *a.frame_k : 0;
+    const bool txt = a.add_text && has_text && kf < a.text_len[r];
+    for (int k = tid; k < a.tab_dim; k += NT) {
+      const float val = ld_any(a.tab, a.tab_dtype, base + k);
+      if (a.next_in) a.next_in[(long)r * a.next_ld + k] = val;
+      float f = a.fb[(long)r * a.fb_ld + k] + val;
+      if (a.add_text) f = f + (txt ? text[((long)a.text_off[r] + kf) * a.tab_dim + k] : pad[k]);
+      a.fb[(long)r * a.fb_ld + k] = f;
+    }
+  }
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  const size_t lds = (size_t)a.V * 5 * sizeof(float);
+  static size_t have = 0;
+  hipError_t e = ensure_lds((const void*)select_kernel, lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- frame control
+__global__ __launch_bounds__(NT) void frame_start_kernel(FrameStartArgs a) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  __shared__ int sh;
+  if (tid == 0) {
+    int c = a.finished[r] ? a.eos : (a.forced ? a.forced[(long)r * a.forced_ld] : a.code0_next[r]);
+    if (c < 0 || c >= a.V) { atomicOr(a.status, ST_RANGE); c = 0; }
+    if (!a.finished[r]) a.seen[(long)r * a.seen_words + (c >> 5)] |= 1u << (c & 31);
+    a.codes[(long)r * 16] = c;
+    sh = c;
+  }
+  __syncthreads();
+  const int c = sh;
+  const long tb = (long)c * a.H;
+  for (int k = tid; k < a.H; k += NT) {
+    const float t = ld_any(a.temb, a.tdtype, tb + k);
+    a.pass0[(long)(2 * r) * a.pass0_ld + k] = a.h[(long)r * a.H + k];
+    a.pass0[(long)(2 * r + 1) * a.pass0_ld + k] = t;
+    a.fb[(long)r * a.fb_ld + k] = t;
+  }
+}
+
+hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(frame_start_kernel, dim3(a.B), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ void frame_advance_kernel(int* frame_k, int* pos, int B) {
+  const int t = threadIdx.x;
+  for (int r = t; r < B; r += blockDim.x) pos[r] += 1;
+  if (t == 0) *frame_k += 1;
+}
+
+hipError_t launch_frame_advance(int* frame_k, int* pos, int B, hipStream_t s) {
+  hipLaunchKernelGGL(frame_advance_kernel, dim3(1), dim3(NT), 0, s, frame_k, pos, B);
+  return hipGetLastError();
+}
+
+__global__ void copy_rows_kernel(const float* src, long ld_src, const int* idx, float* dst, long ld_dst, int n) {
+  const int i = blockIdx.x;
+  const float* s = src + (long)idx[i] * ld_src;
+  float* d = dst + (long)i * ld_dst;
+  for (int k = threadIdx.x; k < n; k += blockDim.x) d[k] = s[k];
+}
+
+hipError_t launch_copy_rows(const float* src, long ld_src, const int* idx, int count, float* dst, long ld_dst,
+                            int n, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(count), dim3(NT), 0, s, src, ld_src, idx, dst, ld_dst, n);
+  return hipGetLastError();
+}
+
+__global__ void convert_kernel(const void* src, int sdt, long ld_src, void* dst, int ddt, long ld_dst,
+                               long rows, int n) {
+  const long total = rows * n;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    const long rr = i / n, c = i % n;
+    if (sdt == ddt && sdt == DT_BF16) {
+      ((uint16_t*)dst)[rr * ld_dst + c] = ((const uint16_t*)src)[rr * ld_src + c];
+    } else {
+      const float x = ld_any(src, sdt, rr * ld_src + c);
+      if (ddt == DT_BF16) ((uint16_t*)dst)[rr * ld_dst + c] = f32_to_bf16(x);
+      else ((float*)dst)[rr * ld_dst + c] = x;
+    }
+  }
+}
+
+hipError_t launch_convert(const void* src, int sdtype, long ld_src, void* dst, int ddtype, long ld_dst, long rows,
+                          int n, hipStream_t s) {
+  const long total = rows * n;
+  if (total <= 0) return hipSuccess;
+  long blocks = (total + NT - 1) / NT;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(convert_kernel, dim3((unsigned)blocks), dim3(NT), 0, s, src, sdtype, ld_src, dst, ddtype, ld_dst,
+                     rows, n);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int* p, int v, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int* p, int v, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long blocks = (n + NT - 1) / NT;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(NT), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace qt

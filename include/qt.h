@@ -1,0 +1,241 @@
+/*
+ * qt.h - C ABI of the Qwen3-TTS 12 Hz per-frame generation step on MI355X.
+ *
+ * What one frame computes (Mizuoto engine page, "How it works"; ncnn port
+ * discussion 6798, section 1 "structure"):
+ *   - the code predictor, a 5-layer Qwen3-style decoder with 15 embedding
+ *     tables and 15 heads, runs a 2-token prefill [previous talker hidden ;
+ *     talker codec embedding of code 0] and applies head 0 to get code 1, then
+ *     14 autoregressive steps where step s embeds code s with table s-1 and
+ *     applies head s to get code s+1;
+ *   - the 16 codes form one 80 ms frame; the sum of their embeddings plus the
+ *     next trailing text embedding (tts_pad once the text is used up) is the
+ *     next talker input;
+ *   - the 28-layer talker decoder runs one step on that input and its codec
+ *     head picks the next code 0 through the logits processors (repetition
+ *     penalty -> min-new-tokens EOS mask -> suppress [suppress_begin,
+ *     suppress_end) except EOS -> greedy argmax, or temperature -> top-k ->
+ *     top-p -> one exponential-race draw argmax(p / Exp(1))).
+ * N frames therefore take N+1 talker selections and 15 N predictor passes
+ * (ncnn CustomVoice port discussion 6832, section 3.1).
+ *
+ * Conventions for every entry point:
+ *   - All device pointers point to memory the caller owns, allocated on the
+ *     device the context was created on; all work is enqueued on the stream
+ *     given to qt_create. Host pointers are plain host memory.
+ *   - Weight matrices are row-major [out, in] (nn.Linear layout); every
+ *     weight tensor (matrices, norm gains, tables, heads) has element type
+ *     qt_config.weight_dtype (QT_DTYPE_F32: float, QT_DTYPE_BF16: the upper 16
+ *     bits of a float). Activations, prompts and logits are float32.
+ *   - Arguments are validated before any device work (dimensions, sizes,
+ *     capacity, id ranges - ncnn CustomVoice port section 3.6: every length
+ *     and id is checked before an embedding access or copy). On error nothing
+ *     is written, the status code is returned and qt_last_error() describes
+ *     it. No C++ exception crosses this boundary.
+ *   - Non-finite logits (NaN or +inf) seen on the device are reported at the
+ *     once-per-frame synchronisation as QT_E_NAN (Mizuoto "Speed": a NaN
+ *     probability is still an error, read at the one wait per frame); the
+ *     context then needs a new qt_prefill.
+ */
+#ifndef QT_H
+#define QT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qt_status;
+#define QT_OK 0
+#define QT_E_INVALID 1  /* bad argument or dimension                           */
+#define QT_E_RANGE 2    /* id or length out of range                            */
+#define QT_E_CAPACITY 3 /* B > max_batch or P_r + max_frames > max_positions    */
+#define QT_E_NOMEM 4    /* workspace too small / allocation failed              */
+#define QT_E_HIP 5      /* HIP runtime error                                    */
+#define QT_E_NAN 6      /* non-finite logit seen on the device                  */
+#define QT_E_STATE 7    /* call out of order                                    */
+
+#define QT_DTYPE_F32 0
+#define QT_DTYPE_BF16 1
+
+/* Dimensions of one Qwen3-style decoder (talker or code predictor). */
+typedef struct qt_decoder_dims {
+  int32_t layers;
+  int32_t hidden;       /* multiple of 64                                       */
+  int32_t n_heads;      /* q heads; multiple of n_kv_heads, n_heads/n_kv <= 8   */
+  int32_t n_kv_heads;
+  int32_t head_dim;     /* even, 16..256; n_heads*head_dim multiple of 64       */
+  int32_t intermediate; /* SwiGLU width, multiple of 64                         */
+  float rope_theta;
+  float rms_eps;
+} qt_decoder_dims;
+
+typedef struct qt_config {
+  qt_decoder_dims talker;
+  qt_decoder_dims predictor;
+  int32_t talker_vocab;   /* codec vocabulary of the talker head (3072), <= 6144 */
+  int32_t n_groups;       /* codes per frame; must be 16                        */
+  int32_t codebook;       /* predictor vocabulary (2048), <= 6144               */
+  int32_t eos_id;         /* 2150                                               */
+  int32_t suppress_begin; /* 2048: talker ids in [begin, end) except EOS are    */
+  int32_t suppress_end;   /* 3072: never chosen                                 */
+  int32_t pred_in_proj;   /* 1: predictor inputs pass a [Hp, H] projection;     */
+                          /* 0: requires predictor.hidden == talker.hidden      */
+  int32_t weight_dtype;   /* QT_DTYPE_F32 | QT_DTYPE_BF16                       */
+  int32_t kv_dtype;       /* element type of both KV caches                     */
+  int32_t max_batch;      /* rows per prefill                                   */
+  int32_t max_positions;  /* talker cache length per row                        */
+} qt_config;
+
+/* Device pointers of one decoder layer (element type weight_dtype). */
+typedef struct qt_layer_weights {
+  const void* attn_norm; /* [H]               */
+  const void* wq;        /* [n_heads*d, H]    */
+  const void* wk;        /* [n_kv*d, H]       */
+  const void* wv;        /* [n_kv*d, H]       */
+  const void* q_norm;    /* [d]               */
+  const void* k_norm;    /* [d]               */
+  const void* wo;        /* [H, n_heads*d]    */
+  const void* mlp_norm;  /* [H]               */
+  const void* w_gate;    /* [I, H]            */
+  const void* w_up;      /* [I, H]            */
+  const void* w_down;    /* [H, I]            */
+} qt_layer_weights;
+
+typedef struct qt_weights {
+  const qt_layer_weights* talker_layers; /* host array [talker.layers]                  */
+  const void* talker_norm;               /* [H] final norm of the talker                */
+  const void* talker_codec_embed;        /* [talker_vocab, H]                           */
+  const void* talker_codec_head;         /* [talker_vocab, H]                           */
+  const qt_layer_weights* pred_layers;   /* host array [predictor.layers]               */
+  const void* pred_norm;                 /* [Hp]                                        */
+  const void* pred_embeds;               /* [15*codebook, H]: table j at rows j*codebook */
+  const void* pred_heads;                /* [15*codebook, Hp]: head s at rows s*codebook */
+  const void* pred_in_proj;              /* [Hp, H] or NULL when pred_in_proj == 0      */
+} qt_weights;
+
+/* Logits processing of one selector (talker or predictor). */
+typedef struct qt_sampling {
+  int32_t do_sample;        /* 0: greedy argmax, lowest index on ties              */
+  float temperature;        /* > 0                                                 */
+  int32_t top_k;            /* 0 disables                                          */
+  float top_p;              /* (0, 1]; 1 disables                                  */
+  float repetition_penalty; /* talker only: >= 1 (1 disables)                      */
+  int32_t min_new_tokens;   /* talker only: EOS masked while selections < this     */
+} qt_sampling;
+
+typedef struct qt_ctx qt_ctx;
+
+/* Device bytes qt_create needs for this configuration (packed weights, KV
+ * caches, activations, row state). Host-only arithmetic; overflow-checked. */
+qt_status qt_workspace_bytes(const qt_config* cfg, size_t* bytes);
+
+/* Validate a configuration without touching any device. */
+qt_status qt_config_check(const qt_config* cfg);
+
+/* Create a context on the current HIP device. Copies and repacks the weights
+ * (fused q/k/v and gate/up matrices) into `workspace` (device memory of at
+ * least qt_workspace_bytes bytes, owned by the caller and kept alive until
+ * qt_destroy), so the caller may free its weight buffers afterwards. With
+ * workspace == NULL the library allocates the workspace itself and frees it
+ * in qt_destroy. hip_stream: a hipStream_t (NULL = the default stream). */
+qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, size_t ws_bytes,
+                    void* hip_stream, qt_ctx** out);
+
+/* Start generation for B rows (the prompt prefill; ncnn port section 5).
+ *   prompt      device float [sum(prompt_lens), H]: row r's prompt embeddings
+ *               packed after row r-1's, positions 0..P_r-1
+ *   prompt_lens host int32 [B], each >= 1
+ *   text        device float [sum(text_lens), H] or NULL: trailing text
+ *               embeddings; frame k of row r adds text row k while k < n_r
+ *   text_lens   host int32 [B] or NULL (NULL: no trailing text)
+ *   tts_pad     device float [H]: added once the text is used up
+ *   talker, predictor: processor / warper settings
+ *   seed        key of the sampling noise (Philox4x64-10, counter = (vocab
+ *               id, stream, selection index, row))
+ *   max_frames  >= 1; P_r + max_frames <= max_positions
+ * Runs the talker over the prompts, applies the codec head at each row's last
+ * position and performs talker selection 0 (ncnn CustomVoice port section
+ * 3.1: step 0 only selects the first code 0). Synchronises the stream. */
+qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t* prompt_lens,
+                     const float* text, const int32_t* text_lens, const float* tts_pad,
+                     const qt_sampling* talker, const qt_sampling* predictor, uint64_t seed,
+                     int32_t max_frames);
+
+/* One frame for every row: predictor codes 1..15 for the current code 0, the
+ * feedback sum, one talker step and the next talker selection (the
+ * lookahead). One host synchronisation.
+ *   codes  host int32 [B, 16]: the frame (code 0, codes 1..15)
+ *   state  host uint8 [B]: 0 active; 1 finished with this frame (the
+ *          lookahead is EOS: reason stop); 2 finished with this frame
+ *          (max_frames reached: reason length, lookahead discarded); 3 row
+ *          had already finished (codes undefined; the row is fed EOS).
+ * Returns QT_E_STATE when every row has finished or no prefill was done. */
+qt_status qt_step_frame(qt_ctx* ctx, int32_t* codes, uint8_t* state);
+
+/* qt_prefill + qt_step_frame until every row finished.
+ *   codes    host int32 [B, max_frames, 16]; frames past n_frames[r] untouched
+ *   n_frames host int32 [B]
+ *   finish   host uint8 [B]: 1 stop (EOS), 2 length (max_frames) */
+qt_status qt_generate(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t* prompt_lens,
+                      const float* text, const int32_t* text_lens, const float* tts_pad,
+                      const qt_sampling* talker, const qt_sampling* predictor, uint64_t seed,
+                      int32_t max_frames, int32_t* codes, int32_t* n_frames, uint8_t* finish);
+
+/* Release the context and everything it allocated. NULL is a no-op. */
+void qt_destroy(qt_ctx* ctx);
+
+/* Text of the last error of `ctx` (or of the calling thread when ctx is NULL:
+ * errors of qt_create / qt_config_check). Never NULL. */
+const char* qt_last_error(const qt_ctx* ctx);
+
+/* ---- test and measurement entry points (same kernels as the frame) ---- */
+
+/* Teacher-forced frame: like qt_step_frame, but code 0 of this frame is
+ * forced[r][0] and the predictor chain and feedback use forced[r][1..15];
+ * rows never finish. Outputs (host, each may be NULL):
+ *   talker_logits [B, talker_vocab]  raw logits of the lookahead selection
+ *   pred_logits   [B, 15, codebook]  raw logits of predictor heads 0..14
+ *   chosen        [B, 16]            the kernels' own choices: [1..15] the
+ *                                     predictor's, [0] the lookahead code 0
+ * forced ids are range-checked on the host first. */
+qt_status qt_debug_step_forced(qt_ctx* ctx, const int32_t* forced, float* talker_logits,
+                               float* pred_logits, int32_t* chosen);
+
+/* Raw talker logits of the latest talker selection, host float [B, vocab]
+ * (after qt_prefill: selection 0). */
+qt_status qt_debug_talker_logits(qt_ctx* ctx, float* logits);
+
+/* Run the selection kernel once on caller data (no context needed).
+ *   logits    device float [B, V]
+ *   seen      device uint32 [B, ceil(V/32)] or NULL (penalty set)
+ *   noise     device float [B, V] explicit Exp(1) noise, or NULL (Philox)
+ *   probs     device float [B, V] explicit probabilities (skips temperature,
+ *             top-k and softmax; top-p and the race still run), or NULL
+ *   processors 1: apply penalty / min-new / suppress (talker), 0: none
+ *   sel_index selection index (min-new test and noise counter)
+ *   out_code  device int32 [B]; processed device float [B, V] or NULL
+ *   status    device int32 [1], OR-ed with 1 on a non-finite logit */
+qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* logits,
+                          const uint32_t* seen, const float* noise, const float* probs,
+                          int32_t processors, int32_t eos, int32_t suppress_begin, int32_t suppress_end,
+                          const qt_sampling* samp, uint64_t seed, int32_t stream, int32_t sel_index,
+                          int32_t* out_code, float* processed, int32_t* status);
+
+/* Y = op(W · norm(X)) with the projection kernel of the frame (no context).
+ *   W [N, K] device, element type wdtype; X device float [M, K];
+ *   gain device float [K] or NULL (RMSNorm prologue with eps);
+ *   epilogue 0: Y = W x, 1: Y += W x, 2: SwiGLU over (gate, up) row pairs,
+ *   Y [M, N] (or [M, N/2] for SwiGLU) device float.
+ *   reps >= 1 launches (for timing). */
+qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K,
+                          const float* X, int32_t M, const float* gain, float eps, int32_t epilogue,
+                          float* Y, int32_t reps);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QT_H */

@@ -74,15 +74,11 @@ def top2_margin(l):
     return float(f[0] - f[1])
 
 
-def warp(l, samp):
-    """Temperature -> top-k -> softmax -> top-p.
+def tempered_softmax(l, samp):
+    """Temperature -> top-k -> softmax. Returns (z, p), both float32.
 
-    Returns (z, p, keep): z the tempered, top-k-masked logits; p their float32
-    softmax; keep the ids that survive top-p, ordered by (p desc, id asc).
     Top-k keeps every id whose value is >= the k-th largest (ties at the
-    threshold kept). Top-p keeps the shortest prefix of that order whose
-    float32 running sum reaches top_p (the crossing id included, at least one
-    id); top_p >= 1 keeps every id with p > 0.
+    threshold kept); the others get -inf and probability 0.
     """
     z = l / F32(samp["temperature"])
     k = int(samp["top_k"])
@@ -93,17 +89,30 @@ def warp(l, samp):
     e = np.exp(z - m)
     s = np.sum(e, dtype=F32)
     p = (e / s).astype(F32)
+    return z, p
+
+
+def top_p_keep(p, top_p):
+    """Ids that survive top-p, ordered by (p desc, id asc).
+
+    Keeps the shortest prefix of that order whose float32 running sum reaches
+    top_p (the crossing id included, at least one id); top_p >= 1 keeps every
+    id with p > 0.
+    """
     ids = [i for i in range(p.size) if p[i] > 0]
     ids.sort(key=lambda i: (-p[i], i))
-    tp = float(samp["top_p"])
-    if tp >= 1.0:
-        keep = ids
-    else:
-        csum = np.cumsum(p[ids], dtype=F32)
-        hit = np.nonzero(csum >= F32(tp))[0]
-        n = int(hit[0]) + 1 if hit.size else len(ids)
-        keep = ids[:n]
-    return z, p, keep
+    if float(top_p) >= 1.0:
+        return ids
+    csum = np.cumsum(p[ids], dtype=F32)
+    hit = np.nonzero(csum >= F32(top_p))[0]
+    n = int(hit[0]) + 1 if hit.size else len(ids)
+    return ids[:n]
+
+
+def warp(l, samp):
+    """Temperature -> top-k -> softmax -> top-p: returns (z, p, keep)."""
+    z, p = tempered_softmax(l, samp)
+    return z, p, top_p_keep(p, samp["top_p"])
 
 
 def race(p, keep, noise):

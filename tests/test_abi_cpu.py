@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/qt.h declares, and rejects bad arguments before any device work
+(ncnn CustomVoice port section 3.6: fail-closed checks of lengths, ids and
+overflow before any access)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from codec_lm_autoregressive_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qt.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="libqt.so not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qt_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert "qt_create" in names and "qt_step_frame" in names and "qt_generate" in names
+    lib = C.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg06(**kw):
+    c = binding.make_config(synth.dims("qwen06b"), "bf16", max_batch=1, max_positions=160)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_valid_configs_pass():
+    assert binding.config_check(cfg06()) == binding.QT_OK
+    tiny = binding.make_config(synth.dims("tiny"), "f32", max_batch=1, max_positions=64)
+    assert binding.config_check(tiny) == binding.QT_OK
+    big = binding.make_config(synth.dims("qwen17b"), "bf16", max_batch=8, max_positions=320)
+    assert binding.config_check(big) == binding.QT_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_groups", 15), ("talker_vocab", 1), ("codebook", 9000), ("eos_id", 3072), ("eos_id", -1),
+    ("suppress_begin", 3000), ("suppress_end", 4000), ("weight_dtype", 7), ("kv_dtype", -1),
+    ("max_batch", 0), ("max_positions", 1), ("pred_in_proj", 2),
+])
+def test_bad_config_rejected(field, value):
+    c = cfg06(**{field: value})
+    if field == "suppress_begin":
+        c.suppress_end = 2900
+    assert binding.config_check(c) == binding.QT_E_INVALID
+    assert binding.lib().qt_last_error(None)
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("n_kv_heads", 3), ("hidden", 1000), ("layers", 0),
+                                         ("intermediate", 100), ("rope_theta", 0.0), ("rms_eps", -1.0)])
+def test_bad_dims_rejected(field, value):
+    c = cfg06()
+    setattr(c.talker, field, value)
+    assert binding.config_check(c) == binding.QT_E_INVALID
+
+
+def test_predictor_width_needs_projection():
+    dm = synth.dims("qwen17b")
+    c = binding.make_config(dm, "bf16")
+    c.pred_in_proj = 0
+    assert binding.config_check(c) == binding.QT_E_INVALID
+
+
+def test_workspace_bytes():
+    dm = synth.dims("qwen06b")
+    n = binding.workspace_bytes(cfg06())
+    # packed bf16 weights alone: 33 layers of 15.73 M params + tables and heads
+    params = 33 * (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) + 2 * 3072 * 1024 + 2 * 15 * 2048 * 1024
+    assert n >= 2 * params
+    assert n < 2 * params + (1 << 30)
+    # KV grows linearly with max_batch * max_positions
+    n2 = binding.workspace_bytes(cfg06(max_batch=2))
+    kv_row = 28 * 8 * 160 * 128 * 2 * 2
+    assert n2 - n >= kv_row
+    del dm
+
+
+def test_workspace_overflow_reported():
+    c = cfg06(max_batch=4096, max_positions=1 << 20)
+    c.talker.layers = 1024
+    c.talker.hidden = 16384
+    c.talker.intermediate = 65536
+    c.pred_in_proj = 1
+    s = C.c_size_t(0)
+    st = binding.lib().qt_workspace_bytes(C.byref(c), C.byref(s))
+    assert st in (binding.QT_OK, binding.QT_E_CAPACITY)
+    if st == binding.QT_OK:
+        assert s.value > (1 << 40)
+
+
+def test_create_rejects_null_weights_without_device():
+    L = binding.lib()
+    w = binding.Weights()
+    ctx = C.c_void_p()
+    st = L.qt_create(C.byref(cfg06()), C.byref(w), None, 0, None, C.byref(ctx))
+    assert st == binding.QT_E_INVALID
+    assert not ctx.value
+    assert b"NULL" in L.qt_last_error(None)
+
+
+def test_null_ctx_calls_rejected():
+    L = binding.lib()
+    ts = binding.sampling(synth.GREEDY)
+    assert L.qt_prefill(None, 1, None, None, None, None, None, C.byref(ts), C.byref(ts), 0, 1) == binding.QT_E_INVALID
+    assert L.qt_step_frame(None, None, None) == binding.QT_E_INVALID
+    assert L.qt_debug_step_forced(None, None, None, None, None) == binding.QT_E_INVALID
+    L.qt_destroy(None)
+
+
+def test_debug_entry_points_validate_before_launch():
+    L = binding.lib()
+    # bad shapes are rejected before any device pointer is touched
+    assert L.qt_debug_linear(None, 1, None, 10, 7, None, 1, None, 1e-6, 0, None, 1) == binding.QT_E_INVALID
+    assert L.qt_debug_linear(None, 1, C.c_void_p(16), 10, 12, C.c_void_p(16), 1, None, 1e-6, 0,
+                             C.c_void_p(16), 1) == binding.QT_E_INVALID  # K not a multiple of 8
+    sm = binding.sampling(dict(synth.SAMPLING, temperature=0.0))
+    assert L.qt_debug_select(None, 1, 3072, C.c_void_p(16), None, None, None, 1, 2150, 2048, 3072, C.byref(sm), 0,
+                             0, 0, C.c_void_p(16), None, C.c_void_p(16)) == binding.QT_E_INVALID
