@@ -53,7 +53,10 @@ bool dims_ok(const qt_decoder_dims& d, char* err, const char* who) {
   if (d.layers < 1 || d.layers > 1024) { set_err(err, "%s.layers must be in 1..1024", who); return false; }
   if (d.hidden < 64 || d.hidden > 16384 || d.hidden % 64) { set_err(err, "%s.hidden must be a multiple of 64 in 64..16384", who); return false; }
   if (d.n_kv_heads < 1 || d.n_heads < 1 || d.n_heads % d.n_kv_heads) { set_err(err, "%s.n_heads must be a positive multiple of n_kv_heads", who); return false; }
-  if (d.n_heads / d.n_kv_heads > 8) { set_err(err, "%s: at most 8 q heads per kv head", who); return false; }
+  {
+    const int gq = d.n_heads / d.n_kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8) { set_err(err, "%s: n_heads / n_kv_heads must be 1, 2, 4 or 8", who); return false; }
+  }
   if (d.head_dim != 16 && d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) {
     set_err(err, "%s.head_dim must be 16, 32, 64, 128 or 256", who); return false;
   }
@@ -192,7 +195,7 @@ Layout plan_layout(const qt_config& c) {
   L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
   L.seen_words = (int)((V + 31) / 32);
   L.seen = p.take(p.sz.mul({B, (size_t)L.seen_words, 4}));
-  L.max_runs = (int)std::min<size_t>((size_t)1 << 30, 3 * B + (B * MP) / kPrefillChunk + 2 + B);
+  L.max_runs = (int)std::min<size_t>((size_t)1 << 30, 3 * B + B * MP);
   L.runs = p.take(p.sz.mul({(size_t)L.max_runs, sizeof(Run)}));
   L.idx = p.take(B * 4);
   L.frame_out = p.take(p.sz.mul({1 + B + B * kGroups, 4}));
@@ -309,7 +312,7 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 
 // ---- the decoder stack over M tokens
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
-                     int pos_base, hipStream_t s) {
+                     int pos_base, hipStream_t s, bool prefill = false) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -335,7 +338,16 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     t.row_stride = row_stride; t.max_pos = maxpos;
     t.runs = runs; t.n_runs = n_runs; t.row_pos = row_pos; t.pos_base = pos_base;
     t.nq = d.nq; t.nkv = d.nkv; t.d = d.d;
-    HIPCK(launch_attention(t, s));
+    if (prefill) {
+      // every key of the chunk first, then one block per (kv head, query token)
+      t.mode = ATT_WRITE;
+      HIPCK(launch_attention(t, s));
+      t.mode = ATT_ATTEND;
+      HIPCK(launch_attention(t, s));
+    } else {
+      t.mode = ATT_WRITE_ATTEND;
+      HIPCK(launch_attention(t, s));
+    }
     // x += W_o · attn
     a.W = w.wo; a.N = d.H; a.K = d.nqd; a.X = ctx->attn; a.ldx = d.nqd; a.gain = nullptr;
     a.Y = x; a.ldy = d.H; a.epi = EPI_RESIDUAL;
@@ -656,8 +668,9 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
     for (int r = 0; r < B; ++r) {
       const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
       if (a >= b) continue;
-      runs.push_back(Run{r, (int)(a - t0), (int)(b - a), (int)(a - start[r])});
-      ch.nrun++;
+      for (long tk = a; tk < b; ++tk)  // one run per prompt token
+        runs.push_back(Run{r, (int)(tk - t0), 1, (int)(tk - start[r])});
+      ch.nrun += (int)(b - a);
       if (start[r + 1] - 1 >= t0 && start[r + 1] - 1 < t0 + ch.n) {
         if (ch.lastrow0 < 0) ch.lastrow0 = r;
         lastidx.push_back((int)(start[r + 1] - 1 - t0));
@@ -692,7 +705,7 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
 
   for (const Chunk& ch : chunks) {
     HIPCK(hipMemcpyAsync(ctx->x_t, prompt + ch.t0 * T.H, (size_t)ch.n * T.H * 4, hipMemcpyDeviceToDevice, s));
-    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s);
+    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s, true);
     if (r != QT_OK) return r;
     if (ch.nlast > 0)
       HIPCK(launch_copy_rows(ctx->x_t, T.H, ctx->idx + ch.last0, ch.nlast, ctx->xlast + (size_t)ch.lastrow0 * T.H, T.H,

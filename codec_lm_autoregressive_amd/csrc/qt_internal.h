@@ -31,7 +31,9 @@ struct Run { int row, tok0, ntok, pos0; };
 
 // Per-head QK-RMSNorm + rope of q and k, K/V write into the cache, then causal
 // GQA attention of every token of the run over cached positions <= its own.
+enum AttnMode { ATT_WRITE_ATTEND = 0, ATT_WRITE = 1, ATT_ATTEND = 2 };
 struct AttnArgs {
+  int mode;
   const float* qkv; long ld_qkv;       // [T, (nq + 2 nkv) d]
   float* out; long ld_out;             // [T, nq d]
   const float* q_gain; const float* k_gain; float eps; float scale;

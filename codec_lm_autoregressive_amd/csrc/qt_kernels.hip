@@ -118,6 +118,36 @@ static hipError_t ensure_lds(const void* fn, size_t bytes, size_t* have) {
 // output rows (KS waves share one row group and split K). Each lane streams
 // 16-byte chunks of its rows with nontemporal loads; the MT activation rows
 // (RMSNorm'd when a gain is given) sit in LDS and are reused by all rows.
+template <typename WT, int R, int MT>
+__device__ __forceinline__ void linear_fma(float (&acc)[R][MT], const u32x4 (&wv)[R], const float* xs, int K, int k0) {
+  constexpr int EPC = 16 / sizeof(WT);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if constexpr (EPC == 8) {
+      const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
+      const f32x4 xb = *(const f32x4*)(xs + m * K + k0 + 4);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float s = acc[r][m];
+        s = fmaf(bf_lo(wv[r].x), xa.x, s); s = fmaf(bf_hi(wv[r].x), xa.y, s);
+        s = fmaf(bf_lo(wv[r].y), xa.z, s); s = fmaf(bf_hi(wv[r].y), xa.w, s);
+        s = fmaf(bf_lo(wv[r].z), xb.x, s); s = fmaf(bf_hi(wv[r].z), xb.y, s);
+        s = fmaf(bf_lo(wv[r].w), xb.z, s); s = fmaf(bf_hi(wv[r].w), xb.w, s);
+        acc[r][m] = s;
+      }
+    } else {
+      const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float s = acc[r][m];
+        s = fmaf(__uint_as_float(wv[r].x), xa.x, s); s = fmaf(__uint_as_float(wv[r].y), xa.y, s);
+        s = fmaf(__uint_as_float(wv[r].z), xa.z, s); s = fmaf(__uint_as_float(wv[r].w), xa.w, s);
+        acc[r][m] = s;
+      }
+    }
+  }
+}
+
 template <typename WT, int R, int MT, int KS>
 __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
   extern __shared__ float xs[];  // [MT][K], then reduction scratch
@@ -127,6 +157,28 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
   const int mt = min(MT, p.M - m0);
   float* red = xs + (long)MT * K;          // [4]
   float* part = red + 4;                   // [4][R][MT]
+
+  constexpr int EPC = 16 / sizeof(WT);     // weight elements per 16-byte chunk
+  constexpr int RG = 4 / KS;               // row groups per block
+  constexpr int NPRE = R == 1 ? 4 : 2;     // chunks per row fetched before the prologue
+  const int wrow = wave / KS, ks = wave % KS;
+  const int row0 = (blockIdx.x * RG + wrow) * R;
+  const int kbase = (ks * 64 + lane) * EPC;
+  const int kstride = KS * 64 * EPC;
+  const WT* W = (const WT*)p.W;
+  // The weights do not depend on the activations: put this lane's first
+  // chunks in flight before the activation tile is read and normalised.
+  u32x4 wpre[NPRE][R];
+#pragma unroll
+  for (int c = 0; c < NPRE; ++c) {
+    const int k0 = kbase + c * kstride;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      if (row < N && k0 < K) wpre[c][r] = __builtin_nontemporal_load((const u32x4*)(W + (long)row * K + k0));
+      else wpre[c][r] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
 
   for (int m = 0; m < mt; ++m) {
     const float* xr = p.X + (long)(m0 + m) * p.ldx;
@@ -147,18 +199,17 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
     for (int m = 0; m < mt; ++m)
       for (int k = tid; k < K; k += NT) p.norm_out[(long)(m0 + m) * p.ld_norm + k] = xs[m * K + k];
 
-  constexpr int EPC = 16 / sizeof(WT);     // weight elements per 16-byte chunk
-  constexpr int RG = 4 / KS;               // row groups per block
-  const int wrow = wave / KS, ks = wave % KS;
-  const int row0 = (blockIdx.x * RG + wrow) * R;
   float acc[R][MT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
-
-  const WT* W = (const WT*)p.W;
-  for (int k0 = (ks * 64 + lane) * EPC; k0 < K; k0 += KS * 64 * EPC) {
+#pragma unroll
+  for (int c = 0; c < NPRE; ++c) {
+    const int k0 = kbase + c * kstride;
+    if (k0 < K) linear_fma<WT, R, MT>(acc, wpre[c], xs, K, k0);
+  }
+  for (int k0 = kbase + NPRE * kstride; k0 < K; k0 += kstride) {
     u32x4 wv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -166,31 +217,7 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
       if (row < N) wv[r] = __builtin_nontemporal_load((const u32x4*)(W + (long)row * K + k0));
       else wv[r] = (u32x4){0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if constexpr (EPC == 8) {
-        const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
-        const f32x4 xb = *(const f32x4*)(xs + m * K + k0 + 4);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float s = acc[r][m];
-          s = fmaf(bf_lo(wv[r].x), xa.x, s); s = fmaf(bf_hi(wv[r].x), xa.y, s);
-          s = fmaf(bf_lo(wv[r].y), xa.z, s); s = fmaf(bf_hi(wv[r].y), xa.w, s);
-          s = fmaf(bf_lo(wv[r].z), xb.x, s); s = fmaf(bf_hi(wv[r].z), xb.y, s);
-          s = fmaf(bf_lo(wv[r].w), xb.z, s); s = fmaf(bf_hi(wv[r].w), xb.w, s);
-          acc[r][m] = s;
-        }
-      } else {
-        const f32x4 xa = *(const f32x4*)(xs + m * K + k0);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float s = acc[r][m];
-          s = fmaf(__uint_as_float(wv[r].x), xa.x, s); s = fmaf(__uint_as_float(wv[r].y), xa.y, s);
-          s = fmaf(__uint_as_float(wv[r].z), xa.z, s); s = fmaf(__uint_as_float(wv[r].w), xa.w, s);
-          acc[r][m] = s;
-        }
-      }
-    }
+    linear_fma<WT, R, MT>(acc, wv, xs, K, k0);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -277,128 +304,290 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- attention
-constexpr int ATT_CH = 256;   // keys per online-softmax chunk
-constexpr int MAXG = 8;       // max q heads per kv head
+// One block per (kv head g, run of tokens of one row); D = head_dim and
+// G = q heads per kv head are compile-time, so every per-head array lives in
+// registers. For each token: RMSNorm of k and of the G q heads over head_dim,
+// rotate-half rope at the token's position, K/V row write into the cache,
+// then causal attention of the G q heads over positions 0..pos in chunks of NT
+// keys with an online softmax. Scores: one key per thread, its row read with
+// 16-byte loads, q broadcast from LDS. P·V: one wave per 64-key slice, each
+// lane owning D/64 adjacent elements of every V row (one vector load per row),
+// partial outputs combined across the 4 waves in LDS.
+// Modes: ATT_WRITE_ATTEND (decode / predictor: per token write, then attend),
+// ATT_WRITE (prefill pass 1: K/V rows only), ATT_ATTEND (prefill pass 2: the
+// cache already holds every key).
+template <int G>
+__device__ __forceinline__ void block_reduce_g(float (&v)[G], float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) v[hh] = is_max ? wave_max(v[hh]) : wave_sum(v[hh]);
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) red[wave * G + hh] = v[hh];
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float t = red[hh];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) t = is_max ? fmaxf(t, red[w * G + hh]) : t + red[w * G + hh];
+    v[hh] = t;
+  }
+}
 
+// 16-byte chunk of a cache row -> floats
 template <typename KVT>
+__device__ __forceinline__ void unpack_chunk(const u32x4& w, float* x) {
+  if constexpr (sizeof(KVT) == 2) {
+    x[0] = bf_lo(w.x); x[1] = bf_hi(w.x); x[2] = bf_lo(w.y); x[3] = bf_hi(w.y);
+    x[4] = bf_lo(w.z); x[5] = bf_hi(w.z); x[6] = bf_lo(w.w); x[7] = bf_hi(w.w);
+  } else {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+}
+
+template <typename KVT, int D, int G>
 __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs p) {
+  constexpr int HALF = D / 2;
+  constexpr int EPN = (D + 63) / 64;       // elements per lane in the RMSNorm step (strided by 64)
+  constexpr int EPC = 16 / sizeof(KVT);    // cache elements per 16-byte chunk
+  constexpr int CPK = D / EPC;             // chunks per cache row
+  constexpr int TPK = CPK < 4 ? CPK : 4;   // threads per key in the score step
+  constexpr int CPT = CPK / TPK;           // chunks per thread in the score step
+  constexpr int KCH = NT / TPK;            // keys per chunk of the online softmax
+  constexpr int KPP = NT / CPK;            // keys per pass of the P·V product
+  constexpr int NPV = KCH / KPP;           // P·V passes per chunk (V chunks per thread)
+  static_assert(CPK <= 64 && 64 % CPK == 0 && KCH % KPP == 0, "cache row layout");
   const int g = blockIdx.x;
   const Run rn = p.runs[blockIdx.y];
-  const int tid = threadIdx.x;
-  const int d = p.d, half = d >> 1, G = p.nq / p.nkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos0 = rn.pos0 + p.pos_base + (p.row_pos ? p.row_pos[rn.row] : 0);
+  const bool write = p.mode != ATT_ATTEND, attend = p.mode != ATT_WRITE;
   extern __shared__ float sm[];
-  float* qs = sm;                      // [G][d]
-  float* sc = qs + G * d;              // [G][ATT_CH]
-  float* vec = sc + G * ATT_CH;        // [d]
-  float* part = vec + d;               // [NT/d slices][G][d]
-  float* red = part + NT * G;          // [8]
-  KVT* kc = (KVT*)p.kc + (long)rn.row * p.row_stride + (long)g * p.max_pos * d;
-  KVT* vc = (KVT*)p.vc + (long)rn.row * p.row_stride + (long)g * p.max_pos * d;
+  float* raw = sm;                      // [G + 1][D] normalised q heads, then k
+  float* qs = raw + (G + 1) * D;        // [G][D] rotated q heads
+  float* pl = qs + G * D;               // [G][KCH] probabilities of the chunk
+  float* part = pl + G * KCH;           // [4][G][D] per-wave partial outputs
+  float* red = part + 4 * G * D;        // [2][4][G]
+  KVT* kc = (KVT*)p.kc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  const int ksub = tid % TPK, kkey = tid / TPK;       // score role: (key of the chunk, row part)
+  const int vchunk = tid % CPK, vslot = tid / CPK;    // P·V role: (key slot, 16-byte chunk)
 
-  // 1) K (normalised + rotated) and V of every token of the run into the cache
-  for (int i = 0; i < rn.ntok; ++i) {
-    const float* src = p.qkv + (long)(rn.tok0 + i) * p.ld_qkv;
-    const float* kr = src + (long)p.nq * d + g * d;
-    const float* vr = src + (long)(p.nq + p.nkv) * d + g * d;
-    const int pos = pos0 + i;
-    const float kv = tid < d ? kr[tid] : 0.f;
-    const float ss = block_sum(kv * kv, red);
-    const float den = sqrtf(ss / (float)d + p.eps);
-    if (tid < d) vec[tid] = kv / den * p.k_gain[tid];
-    __syncthreads();
-    if (tid < half) {
-      const float c = p.cos[(long)pos * half + tid], s = p.sin[(long)pos * half + tid];
-      const float x1 = vec[tid], x2 = vec[tid + half];
-      st_elem<KVT>(kc, (long)pos * d + tid, x1 * c - x2 * s);
-      st_elem<KVT>(kc, (long)pos * d + tid + half, x2 * c + x1 * s);
-    }
-    if (tid < d) st_elem<KVT>(vc, (long)pos * d + tid, vr[tid]);
-    __syncthreads();
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  const int nsl = NT / d;              // key slices of the P·V product
-  const int dim = tid % d, sl = tid / d;
   for (int i = 0; i < rn.ntok; ++i) {
     const long t = rn.tok0 + i;
+    const int pos = pos0 + i;
     const float* src = p.qkv + t * p.ld_qkv;
-    const int pos = pos0 + i, L = pos + 1;
-    // q heads of this group: RMSNorm over d, then rope
-    for (int hh = 0; hh < G; ++hh) {
-      const float qv = tid < d ? src[(long)(g * G + hh) * d + tid] : 0.f;
-      const float ss = block_sum(qv * qv, red);
-      const float den = sqrtf(ss / (float)d + p.eps);
-      if (tid < d) vec[tid] = qv / den * p.q_gain[tid];
-      __syncthreads();
-      if (tid < half) {
-        const float c = p.cos[(long)pos * half + tid], s = p.sin[(long)pos * half + tid];
-        const float x1 = vec[tid], x2 = vec[tid + half];
-        qs[hh * d + tid] = x1 * c - x2 * s;
-        qs[hh * d + tid + half] = x2 * c + x1 * s;
+    // (a) RMSNorm over head_dim: vector v (< G: q head, == G: k) on wave v % 4
+    for (int v = wave; v <= G; v += NT / 64) {
+      if ((v < G && !attend) || (v == G && !write)) continue;
+      const float* x = src + (v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D);
+      const float* gain = v < G ? p.q_gain : p.k_gain;
+      float vals[EPN], gv[EPN];
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPN; ++c) {
+        const int e = lane + 64 * c;
+        vals[c] = e < D ? x[e] : 0.f;
+        gv[c] = e < D ? gain[e] : 0.f;
+        ss += vals[c] * vals[c];
       }
-      __syncthreads();
+      ss = wave_sum(ss);
+      const float den = sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+      for (int c = 0; c < EPN; ++c) {
+        const int e = lane + 64 * c;
+        if (e < D) raw[v * D + e] = vals[c] / den * gv[c];
+      }
     }
-    float mrun[MAXG], lrun[MAXG], acc[MAXG];
-    for (int hh = 0; hh < G; ++hh) { mrun[hh] = -INFINITY; lrun[hh] = 0.f; acc[hh] = 0.f; }
-    for (int c0 = 0; c0 < L; c0 += ATT_CH) {
-      const int cn = min(ATT_CH, L - c0);
-      for (int j = tid; j < cn; j += NT) {
-        const KVT* kr = kc + (long)(c0 + j) * d;
-        float dots[MAXG];
-        for (int hh = 0; hh < G; ++hh) dots[hh] = 0.f;
-        for (int e = 0; e < d; ++e) {
-          const float kvv = ld_elem<KVT>(kr, e);
-          for (int hh = 0; hh < G; ++hh) dots[hh] = fmaf(qs[hh * d + e], kvv, dots[hh]);
-        }
-        for (int hh = 0; hh < G; ++hh) sc[hh * ATT_CH + j] = dots[hh] * p.scale;
-      }
-      __syncthreads();
-      for (int hh = 0; hh < G; ++hh) {
-        float mx = -INFINITY;
-        for (int j = tid; j < cn; j += NT) mx = fmaxf(mx, sc[hh * ATT_CH + j]);
-        mx = block_max(mx, red);
-        const float mnew = fmaxf(mrun[hh], mx);
-        const float corr = expf(mrun[hh] - mnew);
-        float sum = 0.f;
-        for (int j = tid; j < cn; j += NT) {
-          const float e = expf(sc[hh * ATT_CH + j] - mnew);
-          sc[hh * ATT_CH + j] = e;
-          sum += e;
-        }
-        sum = block_sum(sum, red);   // its barriers also publish sc
-        lrun[hh] = lrun[hh] * corr + sum;
-        acc[hh] *= corr;
-        mrun[hh] = mnew;
-      }
-      for (int j = sl; j < cn; j += nsl) {
-        const float vv = ld_elem<KVT>(vc, (long)(c0 + j) * d + dim);
-        for (int hh = 0; hh < G; ++hh) acc[hh] = fmaf(sc[hh * ATT_CH + j], vv, acc[hh]);
-      }
-      __syncthreads();
-    }
-    for (int hh = 0; hh < G; ++hh) part[(sl * G + hh) * d + dim] = acc[hh];
+    if (write)
+      for (int e = tid; e < D; e += NT)
+        st_elem<KVT>(vc, (long)pos * D + e, src[(long)(p.nq + p.nkv) * D + (long)g * D + e]);
     __syncthreads();
-    if (tid < d) {
-      for (int hh = 0; hh < G; ++hh) {
-        float s = 0.f;
-        for (int q = 0; q < nsl; ++q) s += part[(q * G + hh) * d + tid];
-        p.out[t * p.ld_out + (long)(g * G + hh) * d + tid] = s / lrun[hh];
+    // (b) rope of the q heads and of k; the k row goes to the cache
+    for (int e = tid; e < (G + 1) * HALF; e += NT) {
+      const int v = e / HALF, j = e % HALF;
+      if ((v < G && !attend) || (v == G && !write)) continue;
+      const float c = p.cos[(long)pos * HALF + j], s = p.sin[(long)pos * HALF + j];
+      const float x1 = raw[v * D + j], x2 = raw[v * D + j + HALF];
+      const float o1 = x1 * c - x2 * s, o2 = x2 * c + x1 * s;
+      if (v < G) {
+        qs[v * D + j] = o1;
+        qs[v * D + j + HALF] = o2;
+      } else {
+        st_elem<KVT>(kc, (long)pos * D + j, o1);
+        st_elem<KVT>(kc, (long)pos * D + j + HALF, o2);
       }
+    }
+    // Rows written above are read back below by other threads of this block.
+    // Their cache lines were not read earlier in this kernel, except by the
+    // earlier tokens of a multi-token run, which the fence covers.
+    if (write && attend && rn.ntok > 1) __threadfence();
+    __syncthreads();
+    if (!attend) continue;
+
+    // (c) attention over positions 0..pos in chunks of KCH keys. Loads are
+    // unconditional (rows past the end are clamped to the last valid one and
+    // weighted 0) so each thread's K and V chunks go out in one batch.
+    const int L = pos + 1;
+    float m[G], l[G], acc[G][EPC];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPC; ++c) acc[hh][c] = 0.f;
+    }
+    u32x4 kv[CPT], vv[NPV];
+    auto load_chunk = [&](int c0, u32x4 (&kd)[CPT], u32x4 (&vd)[NPV]) {
+      const int cn = min(KCH, L - c0);
+      const int jk = c0 + min(kkey, cn - 1);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) kd[c] = *(const u32x4*)(kc + (long)jk * D + (ksub * CPT + c) * EPC);
+#pragma unroll
+      for (int b = 0; b < NPV; ++b) {
+        const int jv = c0 + min(vslot + b * KPP, cn - 1);
+        vd[b] = *(const u32x4*)(vc + (long)jv * D + vchunk * EPC);
+      }
+    };
+    load_chunk(0, kv, vv);
+    for (int c0 = 0; c0 < L; c0 += KCH) {
+      const int cn = min(KCH, L - c0);
+      float sc[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        float x[EPC];
+        unpack_chunk<KVT>(kv[c], x);
+        const int e0 = (ksub * CPT + c) * EPC;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const f32x4* q4 = (const f32x4*)(qs + hh * D + e0);
+#pragma unroll
+          for (int e = 0; e < EPC; e += 4) {
+            const f32x4 q = q4[e / 4];
+            sc[hh] = fmaf(q.x, x[e], sc[hh]);
+            sc[hh] = fmaf(q.y, x[e + 1], sc[hh]);
+            sc[hh] = fmaf(q.z, x[e + 2], sc[hh]);
+            sc[hh] = fmaf(q.w, x[e + 3], sc[hh]);
+          }
+        }
+      }
+      const bool kvalid = kkey < cn;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+        for (int o = 1; o < TPK; o <<= 1) sc[hh] += __shfl_xor(sc[hh], o);
+        sc[hh] = kvalid ? sc[hh] * p.scale : -INFINITY;
+      }
+      // the next chunk's rows go in flight behind this chunk's softmax and P·V
+      u32x4 vn[NPV];
+      const bool more = c0 + KCH < L;
+      if (more) load_chunk(c0 + KCH, kv, vn);
+      float mx[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) mx[hh] = sc[hh];
+      block_reduce_g<G>(mx, red, true);
+      float ps[G], corr[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float mnew = fmaxf(m[hh], mx[hh]);
+        corr[hh] = expf(m[hh] - mnew);
+        m[hh] = mnew;
+        const float e = kvalid ? expf(sc[hh] - mnew) : 0.f;
+        if (ksub == 0) pl[hh * KCH + kkey] = e;
+        ps[hh] = ksub == 0 ? e : 0.f;
+      }
+      block_reduce_g<G>(ps, red + 4 * G, false);   // its barriers also publish pl
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        l[hh] = l[hh] * corr[hh] + ps[hh];
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) acc[hh][c] *= corr[hh];
+      }
+#pragma unroll
+      for (int b = 0; b < NPV; ++b) {
+        const int jl = vslot + b * KPP;          // pl is 0 for jl >= cn
+        float x[EPC];
+        unpack_chunk<KVT>(vv[b], x);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pw = pl[hh * KCH + jl];
+#pragma unroll
+          for (int c = 0; c < EPC; ++c) acc[hh][c] = fmaf(pw, x[c], acc[hh][c]);
+        }
+      }
+      if (more)
+#pragma unroll
+        for (int b = 0; b < NPV; ++b) vv[b] = vn[b];
+      __syncthreads();   // pl is rewritten by the next chunk
+    }
+    // sum the key slots: lanes CPK apart inside a wave, then the 4 waves in LDS
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int c = 0; c < EPC; ++c) {
+        float s = acc[hh][c];
+        for (int o = CPK; o < 64; o <<= 1) s += __shfl_xor(s, o);
+        acc[hh][c] = s;
+      }
+    if (lane < CPK)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) part[(wave * G + hh) * D + vchunk * EPC + c] = acc[hh][c];
+    __syncthreads();
+    for (int e = tid; e < G * D; e += NT) {
+      const int hh = e / D, dim = e % D;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) s += part[(w * G + hh) * D + dim];
+      p.out[t * p.ld_out + (long)(g * G + hh) * D + dim] = s / l[hh];
     }
     __syncthreads();
   }
 }
 
+template <typename KVT, int D, int G>
+static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
+  constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
+  const size_t lds = ((size_t)(2 * G + 1) * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  static size_t have = 0;
+  hipError_t e = ensure_lds((const void*)attn_kernel<KVT, D, G>, lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_kernel<KVT, D, G>), dim3(a.nkv, a.n_runs), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename KVT, int D>
+static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.nq / a.nkv) {
+    case 1: return launch_attention_dg<KVT, D, 1>(a, s);
+    case 2: return launch_attention_dg<KVT, D, 2>(a, s);
+    case 4: return launch_attention_dg<KVT, D, 4>(a, s);
+    case 8: return launch_attention_dg<KVT, D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename KVT>
+static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 16: return launch_attention_d<KVT, 16>(a, s);
+    case 32: return launch_attention_d<KVT, 32>(a, s);
+    case 64: return launch_attention_d<KVT, 64>(a, s);
+    case 128: return launch_attention_d<KVT, 128>(a, s);
+    case 256: return launch_attention_d<KVT, 256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_runs <= 0) return hipSuccess;
-  const int G = a.nq / a.nkv;
-  const size_t lds = ((size_t)G * a.d + (size_t)G * ATT_CH + a.d + (size_t)NT * G + 8) * sizeof(float);
-  dim3 grid(a.nkv, a.n_runs);
-  if (a.kvdtype == DT_BF16) hipLaunchKernelGGL(attn_kernel<uint16_t>, grid, dim3(NT), lds, s, a);
-  else hipLaunchKernelGGL(attn_kernel<float>, grid, dim3(NT), lds, s, a);
-  return hipGetLastError();
+  if (a.kvdtype == DT_BF16) return launch_attention_t<uint16_t>(a, s);
+  return launch_attention_t<float>(a, s);
 }
 
 // ---------------------------------------------------------------- Philox

@@ -64,7 +64,7 @@ typedef int32_t qt_status;
 typedef struct qt_decoder_dims {
   int32_t layers;
   int32_t hidden;       /* multiple of 64                                       */
-  int32_t n_heads;      /* q heads; multiple of n_kv_heads, n_heads/n_kv <= 8   */
+  int32_t n_heads;      /* q heads; n_heads / n_kv_heads is 1, 2, 4 or 8         */
   int32_t n_kv_heads;
   int32_t head_dim;     /* even, 16..256; n_heads*head_dim multiple of 64       */
   int32_t intermediate; /* SwiGLU width, multiple of 64                         */
