@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--workload", default="qwen06b_bf16_b1")
     ap.add_argument("--frames", type=int, default=None, help="override the frame cap of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=12, help="frames of the oracle's timed sample")
+    ap.add_argument("--cpu-frames", type=int, default=None,
+                    help="frames of the oracle's timed sample (default: the whole workload)")
     ap.add_argument("--kernel-reps", type=int, default=200)
     return ap.parse_args()
 
@@ -156,7 +157,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, args.cpu_frames)
+        cpu = cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, args.cpu_frames or frames)
 
     out = {
         "metric": "16-code frames/sec (0.6B-shaped talker + code predictor)",
@@ -206,8 +207,8 @@ def cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, n_frames):
     r = oracle.generate(w, dm, rows, pad_np, wl["talker"], wl["predictor"], 0, n_frames, record=False)[0]
     dt = time.perf_counter() - t0
     return {"value": round(r["n_frames"] / dt, 4), "unit": "frames/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"row 0 only: prefill of {int(lens[0])} tokens + {r['n_frames']} frames "
-                      f"(of {wl['frames']}), numpy fp32, {dt:.1f}s"}
+            "sample": f"row 0: prefill of {int(lens[0])} tokens + {r['n_frames']} frames "
+                      f"(workload: {len(lens)} row(s), {wl['frames']} frames), numpy fp32, {dt:.1f}s"}
 
 
 if __name__ == "__main__":

@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqt.so")
+# QT_LIB points at another build of the same library (developer A/B runs).
+LIB_PATH = os.environ.get("QT_LIB") or os.path.join(_PKG, "libqt.so")
 
 QT_OK, QT_E_INVALID, QT_E_RANGE, QT_E_CAPACITY, QT_E_NOMEM, QT_E_HIP, QT_E_NAN, QT_E_STATE = range(8)
 QT_DTYPE_F32, QT_DTYPE_BF16 = 0, 1

@@ -20,6 +20,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads per block for every kernel here
 
+// Weight rows are streamed once per pass. QT_WEIGHT_NT selects nontemporal
+// loads (1) or ordinary cached loads (0).
+#ifndef QT_WEIGHT_NT
+#define QT_WEIGHT_NT 1
+#endif
+__device__ __forceinline__ u32x4 ld_weight(const void* p) {
+#if QT_WEIGHT_NT
+  return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
+}
+
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = row0 + r;
-      if (row < N && k0 < K) wpre[c][r] = __builtin_nontemporal_load((const u32x4*)(W + (long)row * K + k0));
+      if (row < N && k0 < K) wpre[c][r] = ld_weight(W + (long)row * K + k0);
       else wpre[c][r] = (u32x4){0u, 0u, 0u, 0u};
     }
   }
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = row0 + r;
-      if (row < N) wv[r] = __builtin_nontemporal_load((const u32x4*)(W + (long)row * K + k0));
+      if (row < N) wv[r] = ld_weight(W + (long)row * K + k0);
       else wv[r] = (u32x4){0u, 0u, 0u, 0u};
     }
     linear_fma<WT, R, MT>(acc, wv, xs, K, k0);
@@ -241,7 +254,9 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
         }
   }
   if (ks != 0 || lane != 0) return;
-  for (int m = 0; m < mt; ++m) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= mt) break;
     float* y = p.Y + (long)(m0 + m) * p.ldy;
     if (p.epi == EPI_SWIGLU) {
 #pragma unroll
@@ -260,6 +275,217 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
       }
     }
   }
+}
+
+// Register-only projection for a few activation rows (decode batches). A wave
+// owns R output rows and 1/KS of K: its weight chunks and the matching
+// activation chunks go out in one batch (addresses clamped, no divergent
+// loads), the RMSNorm sum of squares comes from a wave reduction (plus one
+// LDS exchange between the KS waves of a row group), and no activation tile
+// is staged in LDS.
+template <typename WT, int R, int MT, int KS, int NC>
+__global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
+  constexpr int EPC = 16 / sizeof(WT);
+  constexpr int RG = 4 / KS;
+  __shared__ float red[4][MT];
+  __shared__ float part[4][R][MT];
+  const int K = p.K, N = p.N;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wrow = wave / KS, ks = wave % KS;
+  const int row0 = (blockIdx.x * RG + wrow) * R;
+  const int m0 = blockIdx.y * MT;
+  const int mt = min(MT, p.M - m0);
+  const WT* W = (const WT*)p.W;
+  u32x4 w[NC][R];
+  float x[NC][MT][EPC];
+  bool kin[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
+    kin[c] = k0 < K;
+    const int kc = kin[c] ? k0 : K - EPC;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      w[c][r] = ld_weight(W + (long)row * K + kc);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float* xr = p.X + (long)(m0 + min(m, mt - 1)) * p.ldx + kc;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const f32x4 v = *(const f32x4*)(xr + e);
+        x[c][m][e] = v.x; x[c][m][e + 1] = v.y; x[c][m][e + 2] = v.z; x[c][m][e + 3] = v.w;
+      }
+    }
+  }
+  if (p.gain) {
+    float g[NC][EPC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
+      const float* gp = p.gain + (kin[c] ? k0 : K - EPC);
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const f32x4 v = *(const f32x4*)(gp + e);
+        g[c][e] = v.x; g[c][e + 1] = v.y; g[c][e + 2] = v.z; g[c][e + 3] = v.w;
+      }
+    }
+    float ss[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (kin[c])
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) s += x[c][m][e] * x[c][m][e];
+      ss[m] = wave_sum(s);
+    }
+    if constexpr (KS > 1) {
+      if (lane == 0)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) red[wave][m] = ss[m];
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float s = 0.f;
+        for (int j = 0; j < KS; ++j) s += red[wrow * KS + j][m];
+        ss[m] = s;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float den = sqrtf(ss[m] / (float)K + p.eps);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) x[c][m][e] = x[c][m][e] / den * g[c][e];
+    }
+  }
+  if (p.norm_out && blockIdx.x == 0 && wrow == 0)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
+      if (kin[c])
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < mt)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p.norm_out[(long)(m0 + m) * p.ld_norm + k0 + e] = x[c][m][e];
+    }
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (!kin[c]) continue;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float wf[8];
+      if constexpr (EPC == 8) {
+        wf[0] = bf_lo(w[c][r].x); wf[1] = bf_hi(w[c][r].x); wf[2] = bf_lo(w[c][r].y); wf[3] = bf_hi(w[c][r].y);
+        wf[4] = bf_lo(w[c][r].z); wf[5] = bf_hi(w[c][r].z); wf[6] = bf_lo(w[c][r].w); wf[7] = bf_hi(w[c][r].w);
+      } else {
+        wf[0] = __uint_as_float(w[c][r].x); wf[1] = __uint_as_float(w[c][r].y);
+        wf[2] = __uint_as_float(w[c][r].z); wf[3] = __uint_as_float(w[c][r].w);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float s = acc[r][m];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s = fmaf(wf[e], x[c][m][e], s);
+        acc[r][m] = s;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  if constexpr (KS > 1) {
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) part[wave][r][m] = acc[r][m];
+    __syncthreads();
+    if (ks == 0 && lane == 0)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float s = 0.f;
+          for (int j = 0; j < KS; ++j) s += part[wave + j][r][m];
+          acc[r][m] = s;
+        }
+  }
+  if (ks != 0 || lane != 0) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= mt) break;
+    float* y = p.Y + (long)(m0 + m) * p.ldy;
+    if (p.epi == EPI_SWIGLU) {
+#pragma unroll
+      for (int r = 0; r + 1 < R; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 < N) {
+          const float g = acc[r][m], u = acc[r + 1][m];
+          y[row >> 1] = g / (1.f + expf(-g)) * u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row < N) y[row] = (p.epi == EPI_RESIDUAL) ? y[row] + acc[r][m] : acc[r][m];
+      }
+    }
+  }
+}
+
+template <typename WT, int R, int MT, int KS, int NC>
+static hipError_t launch_gemv_t(const LinearArgs& a, hipStream_t s) {
+  constexpr int RG = 4 / KS;
+  dim3 grid((a.N + RG * R - 1) / (RG * R), (a.M + MT - 1) / MT);
+  hipLaunchKernelGGL((gemv_kernel<WT, R, MT, KS, NC>), grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename WT, int R, int MT, int KS>
+static hipError_t launch_gemv_nc(const LinearArgs& a, int nc, hipStream_t s) {
+  switch (nc) {
+    case 1: return launch_gemv_t<WT, R, MT, KS, 1>(a, s);
+    case 2: return launch_gemv_t<WT, R, MT, KS, 2>(a, s);
+    case 3: return launch_gemv_t<WT, R, MT, KS, 3>(a, s);
+    default: return launch_gemv_t<WT, R, MT, KS, 4>(a, s);
+  }
+}
+
+template <typename WT, int R, int MT>
+static hipError_t launch_gemv_ks(const LinearArgs& a, int ks, int nc, hipStream_t s) {
+  if (ks == 4) return launch_gemv_nc<WT, R, MT, 4>(a, nc, s);
+  if (ks == 2) return launch_gemv_nc<WT, R, MT, 2>(a, nc, s);
+  return launch_gemv_nc<WT, R, MT, 1>(a, nc, s);
+}
+
+// Register path when the batch is small and K fits in <= 4 chunks per lane.
+template <typename WT>
+static bool try_gemv(const LinearArgs& a, hipStream_t s, hipError_t* err) {
+  constexpr int EPC = 16 / sizeof(WT);
+  if (a.M > 2 || a.K % EPC) return false;
+  const int R = (a.epi == EPI_SWIGLU || a.N >= 4096) ? 2 : 1;
+  int ks = 1;
+  while (ks < 4 && a.N / (4 / ks * R) < 768) ks *= 2;   // enough blocks to cover the chip
+  const int per = ks * 64 * EPC;
+  const int nc = (a.K + per - 1) / per;
+  if (nc > 4) return false;
+  const int mt = a.M <= 1 ? 1 : 2;
+  if (R == 2) *err = mt == 1 ? launch_gemv_ks<WT, 2, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 2, 2>(a, ks, nc, s);
+  else *err = mt == 1 ? launch_gemv_ks<WT, 1, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 2>(a, ks, nc, s);
+  return true;
 }
 
 template <typename WT, int R, int MT, int KS>
@@ -292,6 +518,10 @@ static hipError_t launch_linear_w(const LinearArgs& a, int mt, int R, int KS, hi
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
+  {
+    hipError_t e = hipSuccess;
+    if (a.wdtype == DT_BF16 ? try_gemv<uint16_t>(a, s, &e) : try_gemv<float>(a, s, &e)) return e;
+  }
   // activation tile: as many rows as fit in 96 KB of LDS, up to 8
   int mtmax = 8;
   while (mtmax > 1 && (size_t)mtmax * a.K * 4 > 96 * 1024) mtmax >>= 1;
