@@ -132,7 +132,7 @@ struct Layout {
   std::vector<LayerBuf> tl, pl;
   size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj;
   size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
-  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p;
+  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den;
   size_t rowstate, seen, runs, idx, frame_out, req;
   size_t total;
   int tmax, seen_words, max_runs;
@@ -190,6 +190,8 @@ Layout plan_layout(const qt_config& c) {
   L.xlast = p.take(p.sz.mul({B, (size_t)t.H, 4}));
   L.logits_t = p.take(p.sz.mul({B, V, 4}));
   L.logits_p = p.take(p.sz.mul({15, B, C, 4}));
+  L.rope_rows = p.take(p.sz.mul({B, (size_t)t.d, 4}));
+  L.row_den = p.take(p.sz.mul({T, 4}));
   (void)Hm;
   // row state: code0_next, finished, pos, text_off, text_len [B]; frame_k; own/forced [B,16]
   L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
@@ -228,7 +230,7 @@ struct qt_ctx {
   void *temb, *thead, *pemb, *phead, *pproj;
   float *cos_t, *sin_t, *cos_p, *sin_p;
   void *kc_t, *vc_t, *kc_p, *vc_p;
-  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p;
+  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den;
   int *code0_next, *finished, *pos, *text_off, *text_len, *frame_k, *own, *forced;
   uint32_t* seen;
   Run* runs;
@@ -312,7 +314,7 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 
 // ---- the decoder stack over M tokens
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
-                     int pos_base, hipStream_t s, bool prefill = false) {
+                     int pos_base, hipStream_t s, bool prefill = false, bool single_token = false) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -326,6 +328,7 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     LinearArgs a{};
     a.wdtype = ctx->cfg.weight_dtype;
     a.eps = d.eps;
+    a.row_den = ctx->row_den;
     // q/k/v = W_qkv · RMSNorm(x)
     a.W = w.wqkv; a.N = d.qkv; a.K = d.H; a.X = x; a.ldx = d.H; a.M = M; a.gain = w.attn_norm;
     a.Y = ctx->qkv; a.ldy = d.qkv; a.epi = EPI_STORE;
@@ -346,6 +349,8 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
       HIPCK(launch_attention(t, s));
     } else {
       t.mode = ATT_WRITE_ATTEND;
+      t.single_token = single_token;
+      t.rope_rows = (single_token && talker) ? ctx->rope_rows : nullptr;
       HIPCK(launch_attention(t, s));
     }
     // x += W_o · attn
@@ -399,9 +404,11 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   fs.temb = ctx->temb; fs.tdtype = wd; fs.H = T.H; fs.h = ctx->h;
   fs.pass0 = proj ? ctx->xin_w : ctx->x_p; fs.pass0_ld = T.H;
   fs.fb = ctx->x_t; fs.fb_ld = T.H; fs.status = ctx->frame_out;
+  fs.cos = ctx->cos_t; fs.sin = ctx->sin_t; fs.pos = ctx->pos; fs.half = T.d / 2; fs.rope_rows = ctx->rope_rows;
   HIPCK(launch_frame_start(fs, s));
 
   LinearArgs pa{};
+  pa.row_den = ctx->row_den;
   pa.wdtype = wd; pa.W = ctx->pproj; pa.N = P.H; pa.K = T.H; pa.X = ctx->xin_w; pa.ldx = T.H;
   pa.Y = ctx->x_p; pa.ldy = P.H; pa.epi = EPI_STORE;
 
@@ -409,9 +416,10 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     const int M = st == 0 ? 2 * B : B;
     if (proj) { pa.M = M; HIPCK(launch_linear(pa, s)); }
     if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s)); }
-    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s)); }
+    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true)); }
     // head st on the last token of each row
     LinearArgs ha{};
+    ha.row_den = ctx->row_den;
     ha.wdtype = wd; ha.W = (const char*)ctx->phead + (size_t)st * C * P.H * esize(wd); ha.N = C; ha.K = P.H;
     ha.X = st == 0 ? ctx->x_p + P.H : ctx->x_p; ha.ldx = st == 0 ? 2L * P.H : P.H; ha.M = B;
     ha.gain = ctx->pred_norm; ha.eps = P.eps;
@@ -432,8 +440,9 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     HIPCK(launch_select(sa, s));
   }
   // talker step at position P_r + k
-  QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s));
+  QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s, false, true));
   LinearArgs ta{};
+  ta.row_den = ctx->row_den;
   ta.wdtype = wd; ta.W = ctx->thead; ta.N = ctx->cfg.talker_vocab; ta.K = T.H; ta.X = ctx->x_t; ta.ldx = T.H; ta.M = B;
   ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = ctx->cfg.talker_vocab; ta.epi = EPI_STORE;
   ta.norm_out = ctx->h; ta.ld_norm = T.H;
@@ -557,6 +566,8 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
   ctx->xin_w = cfg->pred_in_proj ? at<float>(ctx, L.xin_w) : nullptr;
   ctx->h = at<float>(ctx, L.h); ctx->xlast = at<float>(ctx, L.xlast);
   ctx->logits_t = at<float>(ctx, L.logits_t); ctx->logits_p = at<float>(ctx, L.logits_p);
+  ctx->rope_rows = at<float>(ctx, L.rope_rows);
+  ctx->row_den = at<float>(ctx, L.row_den);
   int* rs = at<int>(ctx, L.rowstate);
   const int MB = cfg->max_batch;
   ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->text_off = rs + 3 * MB;
@@ -712,6 +723,7 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
                              T.H, s));
   }
   LinearArgs ta{};
+  ta.row_den = ctx->row_den;
   ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H; ta.X = ctx->xlast; ta.ldx = T.H;
   ta.M = B; ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = c.talker_vocab;
   ta.epi = EPI_STORE; ta.norm_out = ctx->h; ta.ld_norm = T.H;
@@ -890,7 +902,8 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
 }
 
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
-                          int32_t M, const float* gain, float eps, int32_t epilogue, float* Y, int32_t reps) {
+                          int32_t M, const float* gain, float eps, int32_t epilogue, float* Y, float* scratch,
+                          int32_t reps) {
   if (wdtype != QT_DTYPE_F32 && wdtype != QT_DTYPE_BF16) { set_err(g_err, "bad wdtype"); return QT_E_INVALID; }
   if (!W || !X || !Y) { set_err(g_err, "W, X and Y must not be NULL"); return QT_E_INVALID; }
   if (N < 1 || K < 8 || K % 8 || M < 1 || reps < 1 || epilogue < 0 || epilogue > 2 || (epilogue == 2 && N % 2)) {
@@ -901,6 +914,7 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
   LinearArgs a{};
   a.W = W; a.wdtype = wdtype; a.N = N; a.K = K; a.X = X; a.ldx = K; a.M = M; a.gain = gain; a.eps = eps;
   a.Y = Y; a.ldy = epilogue == 2 ? N / 2 : N; a.epi = epilogue;
+  a.row_den = scratch;
   for (int i = 0; i < reps; ++i) {
     hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
     if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }

@@ -22,6 +22,7 @@ struct LinearArgs {
   const float* gain; float eps;        // RMSNorm prologue when gain != nullptr
   float* Y; long ldy; int epi;
   float* norm_out; long ld_norm;       // optional copy of the normalised X
+  float* row_den;                      // [M] scratch for the matrix-core path (nullptr: not used)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
@@ -34,6 +35,8 @@ struct Run { int row, tok0, ntok, pos0; };
 enum AttnMode { ATT_WRITE_ATTEND = 0, ATT_WRITE = 1, ATT_ATTEND = 2 };
 struct AttnArgs {
   int mode;
+  int single_token;                    // run i is token i of row i, at position pos_base + row_pos[i]
+  const float* rope_rows;              // [rows][d]: cos | sin at each row's position, or nullptr
   const float* qkv; long ld_qkv;       // [T, (nq + 2 nkv) d]
   float* out; long ld_out;             // [T, nq d]
   const float* q_gain; const float* k_gain; float eps; float scale;
@@ -100,6 +103,8 @@ struct FrameStartArgs {
   float* pass0; long pass0_ld;         // [2B, H]
   float* fb; long fb_ld;               // [B, H]
   int* status;
+  // cos | sin rows of the talker's position this frame, for its attention
+  const float* cos; const float* sin; const int* pos; int half; float* rope_rows;
 };
 hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s);
 

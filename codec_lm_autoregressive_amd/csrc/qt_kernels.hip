@@ -19,6 +19,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads per block for every kernel here
+constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use the matrix cores
 
 // Weight rows are streamed once per pass. QT_WEIGHT_NT selects nontemporal
 // loads (1) or ordinary cached loads (0).
@@ -516,8 +517,165 @@ static hipError_t launch_linear_w(const LinearArgs& a, int mt, int R, int KS, hi
   return KS == 4 ? launch_linear_mt<WT, 1, 4>(a, mt, s) : launch_linear_mt<WT, 1, 1>(a, mt, s);
 }
 
+// ---------------------------------------------------------------- MFMA GEMM
+// Y[M, N] (op)= norm(X)[M, K] · W[N, K]^T for many activation rows (prompt
+// prefill, large batches) on the bf16 matrix cores. The fp32 activations are
+// split into bf16 hi + lo parts (hi = rne(x), lo = rne(x - hi)); W is exactly
+// bf16, so each product is exact and two v_mfma_f32_32x32x16_bf16 per step
+// with fp32 accumulation keep the result within ~2^-17 of an fp32 GEMM.
+// Block: 4 waves in a 2x2 grid, tile BM x BN, K staged 32 at a time in LDS
+// (rows padded to 40 elements). RMSNorm uses per-row denominators from
+// row_norm_kernel and is applied while the activation tile is staged.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int GK = 32;        // K per LDS stage
+constexpr int GLD = GK + 8;   // padded LDS row (bf16 elements)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+template <int BM, int BN>
+__global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float* __restrict__ den) {
+  constexpr int TM = BM / 64, TN = BN / 64;      // 32x32 MFMA tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sah[BM * GLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sal[BM * GLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[BN * GLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const uint16_t* W = (const uint16_t*)p.W;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  constexpr int AV = BM * GK / 4 / NT;   // float4 of X per thread per stage
+  constexpr int BV = BN * GK / 8 / NT;   // 16-byte W chunks per thread per stage
+  for (int k0 = 0; k0 < K; k0 += GK) {
+    f32x4 xa[AV];
+    u32x4 wb[BV];
+#pragma unroll
+    for (int q = 0; q < AV; ++q) {
+      const int idx = tid + q * NT, r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+      const int row = m0 + r;
+      xa[q] = row < M ? *(const f32x4*)(p.X + (long)row * p.ldx + k0 + c) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < BV; ++q) {
+      const int idx = tid + q * NT, r = idx / (GK / 8), c = (idx % (GK / 8)) * 8;
+      const int n = n0 + r;
+      wb[q] = n < N ? ld_weight(W + (long)n * K + k0 + c) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    __syncthreads();   // the previous stage's MFMAs are done with the LDS tiles
+#pragma unroll
+    for (int q = 0; q < AV; ++q) {
+      const int idx = tid + q * NT, r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+      const int row = m0 + r;
+      float x[4] = {xa[q].x, xa[q].y, xa[q].z, xa[q].w};
+      if (p.gain && row < M) {
+        const float d = den[row];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = x[e] / d * p.gain[k0 + c + e];
+      }
+      uint16_t h[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(x[e]);
+        lo[e] = f32_to_bf16(x[e] - bf16_to_f32(h[e]));
+      }
+      *(uint2*)&sah[r * GLD + c] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      *(uint2*)&sal[r * GLD + c] = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+    }
+#pragma unroll
+    for (int q = 0; q < BV; ++q) {
+      const int idx = tid + q * NT, r = idx / (GK / 8), c = (idx % (GK / 8)) * 8;
+      *(u32x4*)&sb[r * GLD + c] = wb[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < GK; ks += 16) {
+      bf16x8 ah[TM], al[TM], bv[TN];
+      const int kk = ks + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+        ah[i] = *(const bf16x8*)&sah[r * GLD + kk];
+        al[i] = *(const bf16x8*)&sal[r * GLD + kk];
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * (BN / 2) + j * 32 + (lane & 31);
+        bv[j] = *(const bf16x8*)&sb[r * GLD + kk];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+#pragma unroll
+  for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < TN; ++tj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = m0 + wm * (BM / 2) + ti * 32 + i;
+        const int col = n0 + wn * (BN / 2) + tj * 32 + (lane & 31);
+        const float v = acc[ti][tj][r];
+        if (p.epi == EPI_SWIGLU) {
+          const float u = __shfl_xor(v, 1);   // the (gate, up) pair sits in lanes 2c, 2c+1
+          if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * u;
+        } else if (row < M && col < N) {
+          float* y = p.Y + (long)row * p.ldy + col;
+          *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+        }
+      }
+}
+
+// den[m] = sqrt(mean(X[m]^2) + eps); optionally the normalised rows.
+__global__ __launch_bounds__(NT) void row_norm_kernel(LinearArgs p, float* den) {
+  __shared__ float red[8];
+  const int m = blockIdx.x;
+  const float* x = p.X + (long)m * p.ldx;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < p.K; k += NT) ss += x[k] * x[k];
+  ss = block_sum(ss, red);
+  const float d = sqrtf(ss / (float)p.K + p.eps);
+  if (threadIdx.x == 0) den[m] = d;
+  if (p.norm_out)
+    for (int k = threadIdx.x; k < p.K; k += NT) p.norm_out[(long)m * p.ld_norm + k] = x[k] / d * p.gain[k];
+}
+
+static hipError_t launch_mfma(const LinearArgs& a, float* den, hipStream_t s) {
+  if (a.gain) {
+    hipLaunchKernelGGL(row_norm_kernel, dim3(a.M), dim3(NT), 0, s, a, den);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.M > 64) {
+    dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
+    hipLaunchKernelGGL((mfma_gemm_kernel<128, 128>), grid, dim3(NT), 0, s, a, den);
+  } else {
+    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+    hipLaunchKernelGGL((mfma_gemm_kernel<64, 64>), grid, dim3(NT), 0, s, a, den);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
+  // many rows of bf16 weights: matrix cores (needs K % 32 == 0 and row scratch)
+  if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)
+    return launch_mfma(a, a.row_den, s);
   {
     hipError_t e = hipSuccess;
     if (a.wdtype == DT_BF16 ? try_gemv<uint16_t>(a, s, &e) : try_gemv<float>(a, s, &e)) return e;
@@ -564,6 +722,11 @@ __device__ __forceinline__ void block_reduce_g(float (&v)[G], float* red, bool i
     v[hh] = t;
   }
 }
+
+// the value a cache element holds after being stored
+template <typename KVT> __device__ __forceinline__ float kv_round(float x);
+template <> __device__ __forceinline__ float kv_round<float>(float x) { return x; }
+template <> __device__ __forceinline__ float kv_round<uint16_t>(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
 // 16-byte chunk of a cache row -> floats
 template <typename KVT>
@@ -780,10 +943,250 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs p) {
   }
 }
 
+// Single-token decode (the talker step and predictor steps 1..14): every
+// load is issued at kernel start (this token's q/k/v, gains, cos/sin, and the
+// first chunk of older K/V rows), and this token's own K/V stay in LDS instead
+// of being read back from the cache. Older rows come only from positions
+// < pos, which earlier kernels wrote.
+template <typename KVT, int D, int G>
+__global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
+  constexpr int HALF = D / 2;
+  constexpr int EPN = (D + 63) / 64;
+  constexpr int EPC = 16 / sizeof(KVT);
+  constexpr int CPK = D / EPC;
+  constexpr int TPK = CPK < 4 ? CPK : 4;
+  constexpr int CPT = CPK / TPK;
+  constexpr int KCH = NT / TPK;
+  constexpr int KPP = NT / CPK;
+  constexpr int NPV = KCH / KPP;
+  static_assert(CPK <= 64 && 64 % CPK == 0 && KCH % KPP == 0, "cache row layout");
+  const int g = blockIdx.x;
+  const int row = blockIdx.y;          // one token per row, token index = row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pos = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
+  const int L = pos + 1;
+  extern __shared__ float sm[];
+  float* raw = sm;                      // [G + 1][D]
+  float* qs = raw + (G + 1) * D;        // [G][D]
+  float* kcur = qs + G * D;             // [D] this token's key, as stored
+  float* vcur = kcur + D;               // [D] this token's value, as stored
+  float* pl = vcur + D;                 // [G][KCH]
+  float* part = pl + G * KCH;           // [4][G][D]
+  float* red = part + 4 * G * D;        // [2][4][G]
+  KVT* kc = (KVT*)p.kc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  const int ksub = tid % TPK, kkey = tid / TPK;
+  const int vchunk = tid % CPK, vslot = tid / CPK;
+  const float* src = p.qkv + (long)row * p.ld_qkv;
+  const int lastrow = p.max_pos - 1;
+
+  // Row addresses do not depend on pos (only clamped to the cache), so these
+  // loads leave together with this token's loads; rows >= pos may hold
+  // anything and are kept out of the sums by the key guards below.
+  u32x4 kv[CPT], vv[NPV];
+  auto load_chunk = [&](int c0, u32x4 (&kd)[CPT], u32x4 (&vd)[NPV]) {
+    const int jk = min(c0 + kkey, lastrow);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) kd[c] = *(const u32x4*)(kc + (long)jk * D + (ksub * CPT + c) * EPC);
+#pragma unroll
+    for (int b = 0; b < NPV; ++b) {
+      const int jv = min(c0 + vslot + b * KPP, lastrow);
+      vd[b] = *(const u32x4*)(vc + (long)jv * D + vchunk * EPC);
+    }
+  };
+  load_chunk(0, kv, vv);
+  // cos/sin of this thread's rope pairs: from the per-row rows prepared for
+  // this step (no dependence on pos) or from the table
+  constexpr int RPT = ((G + 1) * HALF + NT - 1) / NT;
+  float cs_t[RPT], sn_t[RPT];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int e = tid + q * NT;
+    const int j = e % HALF;
+    if (p.rope_rows) {
+      cs_t[q] = p.rope_rows[(long)row * D + j];
+      sn_t[q] = p.rope_rows[(long)row * D + HALF + j];
+    } else {
+      cs_t[q] = p.cos[(long)pos * HALF + j];
+      sn_t[q] = p.sin[(long)pos * HALF + j];
+    }
+  }
+
+  // this token: RMSNorm of the q heads and k (vector v on wave v % 4), v as stored
+  for (int v = wave; v <= G; v += NT / 64) {
+    const float* x = src + (v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D);
+    const float* gain = v < G ? p.q_gain : p.k_gain;
+    float vals[EPN], gv[EPN];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPN; ++c) {
+      const int e = lane + 64 * c;
+      vals[c] = e < D ? x[e] : 0.f;
+      gv[c] = e < D ? gain[e] : 0.f;
+      ss += vals[c] * vals[c];
+    }
+    ss = wave_sum(ss);
+    const float den = sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+    for (int c = 0; c < EPN; ++c) {
+      const int e = lane + 64 * c;
+      if (e < D) raw[v * D + e] = vals[c] / den * gv[c];
+    }
+  }
+  for (int e = tid; e < D; e += NT) {
+    const float vvv = src[(long)(p.nq + p.nkv) * D + (long)g * D + e];
+    st_elem<KVT>(vc, (long)pos * D + e, vvv);
+    vcur[e] = kv_round<KVT>(vvv);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int e = tid + q * NT;
+    if (e >= (G + 1) * HALF) break;
+    const int v = e / HALF, j = e % HALF;
+    const float c = cs_t[q], s = sn_t[q];
+    const float x1 = raw[v * D + j], x2 = raw[v * D + j + HALF];
+    const float o1 = x1 * c - x2 * s, o2 = x2 * c + x1 * s;
+    if (v < G) {
+      qs[v * D + j] = o1;
+      qs[v * D + j + HALF] = o2;
+    } else {
+      st_elem<KVT>(kc, (long)pos * D + j, o1);
+      st_elem<KVT>(kc, (long)pos * D + j + HALF, o2);
+      kcur[j] = kv_round<KVT>(o1);
+      kcur[j + HALF] = kv_round<KVT>(o2);
+    }
+  }
+  __syncthreads();
+
+  float m[G], l[G], acc[G][EPC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPC; ++c) acc[hh][c] = 0.f;
+  }
+  for (int c0 = 0; c0 < L; c0 += KCH) {
+    const int cn = min(KCH, L - c0);
+    const int j = c0 + kkey;
+    float sc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      float x[EPC];
+      const int e0 = (ksub * CPT + c) * EPC;
+      if (j == pos) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) x[e] = kcur[e0 + e];
+      } else {
+        unpack_chunk<KVT>(kv[c], x);
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const f32x4* q4 = (const f32x4*)(qs + hh * D + e0);
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          const f32x4 q = q4[e / 4];
+          sc[hh] = fmaf(q.x, x[e], sc[hh]);
+          sc[hh] = fmaf(q.y, x[e + 1], sc[hh]);
+          sc[hh] = fmaf(q.z, x[e + 2], sc[hh]);
+          sc[hh] = fmaf(q.w, x[e + 3], sc[hh]);
+        }
+      }
+    }
+    const bool kvalid = kkey < cn;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int o = 1; o < TPK; o <<= 1) sc[hh] += __shfl_xor(sc[hh], o);
+      sc[hh] = kvalid ? sc[hh] * p.scale : -INFINITY;
+    }
+    u32x4 vn[NPV];
+    const bool more = c0 + KCH < L;
+    if (more) load_chunk(c0 + KCH, kv, vn);
+    float mx[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) mx[hh] = sc[hh];
+    block_reduce_g<G>(mx, red, true);
+    float ps[G], corr[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mnew = fmaxf(m[hh], mx[hh]);
+      corr[hh] = expf(m[hh] - mnew);
+      m[hh] = mnew;
+      const float e = kvalid ? expf(sc[hh] - mnew) : 0.f;
+      if (ksub == 0) pl[hh * KCH + kkey] = e;
+      ps[hh] = ksub == 0 ? e : 0.f;
+    }
+    block_reduce_g<G>(ps, red + 4 * G, false);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      l[hh] = l[hh] * corr[hh] + ps[hh];
+#pragma unroll
+      for (int c = 0; c < EPC; ++c) acc[hh][c] *= corr[hh];
+    }
+#pragma unroll
+    for (int b = 0; b < NPV; ++b) {
+      const int jl = vslot + b * KPP;
+      if (jl < cn) {                 // rows past pos are never multiplied in
+        float x[EPC];
+        if (c0 + jl == pos) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[e] = vcur[vchunk * EPC + e];
+        } else {
+          unpack_chunk<KVT>(vv[b], x);
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pw = pl[hh * KCH + jl];
+#pragma unroll
+          for (int c = 0; c < EPC; ++c) acc[hh][c] = fmaf(pw, x[c], acc[hh][c]);
+        }
+      }
+    }
+    if (more)
+#pragma unroll
+      for (int b = 0; b < NPV; ++b) vv[b] = vn[b];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int c = 0; c < EPC; ++c) {
+      float s = acc[hh][c];
+      for (int o = CPK; o < 64; o <<= 1) s += __shfl_xor(s, o);
+      acc[hh][c] = s;
+    }
+  if (lane < CPK)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int c = 0; c < EPC; ++c) part[(wave * G + hh) * D + vchunk * EPC + c] = acc[hh][c];
+  __syncthreads();
+  for (int e = tid; e < G * D; e += NT) {
+    const int hh = e / D, dim = e % D;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) s += part[(w * G + hh) * D + dim];
+    p.out[(long)row * p.ld_out + (long)(g * G + hh) * D + dim] = s / l[hh];
+  }
+}
+
 template <typename KVT, int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
   constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
-  const size_t lds = ((size_t)(2 * G + 1) * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  const size_t lds = ((size_t)(2 * G + 1) * D + 2 * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  if constexpr (D <= 128) {   // wider heads use the general kernel (register budget)
+    if (a.single_token && a.mode == ATT_WRITE_ATTEND) {
+      static size_t have1 = 0;
+      hipError_t e = ensure_lds((const void*)attn_decode_kernel<KVT, D, G>, lds, &have1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_decode_kernel<KVT, D, G>), dim3(a.nkv, a.n_runs), dim3(NT), lds, s, a);
+      return hipGetLastError();
+    }
+  }
   static size_t have = 0;
   hipError_t e = ensure_lds((const void*)attn_kernel<KVT, D, G>, lds, &have);
   if (e != hipSuccess) return e;
@@ -1084,6 +1487,13 @@ __global__ __launch_bounds__(NT) void frame_start_kernel(FrameStartArgs a) {
   }
   __syncthreads();
   const int c = sh;
+  if (a.rope_rows) {
+    const long pr = (long)a.pos[r] * a.half;
+    for (int j = tid; j < a.half; j += NT) {
+      a.rope_rows[(long)r * 2 * a.half + j] = a.cos[pr + j];
+      a.rope_rows[(long)r * 2 * a.half + a.half + j] = a.sin[pr + j];
+    }
+  }
   const long tb = (long)c * a.H;
   for (int k = tid; k < a.H; k += NT) {
     const float t = ld_any(a.temb, a.tdtype, tb + k);

@@ -224,15 +224,17 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
                           const qt_sampling* samp, uint64_t seed, int32_t stream, int32_t sel_index,
                           int32_t* out_code, float* processed, int32_t* status);
 
-/* Y = op(W · norm(X)) with the projection kernel of the frame (no context).
+/* Y = op(W · norm(X)) with the projection kernels of the frame (no context).
  *   W [N, K] device, element type wdtype; X device float [M, K];
  *   gain device float [K] or NULL (RMSNorm prologue with eps);
  *   epilogue 0: Y = W x, 1: Y += W x, 2: SwiGLU over (gate, up) row pairs,
  *   Y [M, N] (or [M, N/2] for SwiGLU) device float.
+ *   scratch device float [M] or NULL: with bf16 weights, M >= 16 and
+ *   K % 32 == 0 it enables the matrix-core (MFMA) kernel, as in the frame.
  *   reps >= 1 launches (for timing). */
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K,
                           const float* X, int32_t M, const float* gain, float eps, int32_t epilogue,
-                          float* Y, int32_t reps);
+                          float* Y, float* scratch, int32_t reps);
 
 #ifdef __cplusplus
 }

@@ -37,11 +37,18 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
     return y
 
 
+@pytest.mark.parametrize("mc", [True, False])
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("N,K,M", [(4096, 1024, 1), (1024, 2048, 3), (6144, 1024, 8), (1024, 3072, 5),
-                                   (3072, 512, 17), (200, 64, 2), (2048, 1024, 64), (96, 6144, 9)])
+                                   (3072, 512, 17), (200, 64, 2), (2048, 1024, 64), (96, 6144, 9),
+                                   (1024, 3072, 16), (200, 96, 130), (6144, 1024, 257), (2048, 2048, 1024)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
-def test_linear_matches_oracle(wdt, N, K, M, epi, norm):
+def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
+    """mc: hand the library its row scratch, which routes bf16 weights with
+    M >= 16 and K % 32 == 0 to the MFMA kernel; without it they take the
+    LDS-tile kernel."""
+    if not mc and (wdt != "bf16" or M < 16):
+        pytest.skip("same kernel as the mc=True case")
     torch = _torch()
     g = np.random.default_rng(N * 7 + K + M)
     W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -54,7 +61,7 @@ def test_linear_matches_oracle(wdt, N, K, M, epi, norm):
     Xd = torch.from_numpy(X).cuda()
     Gd = torch.from_numpy(gain).cuda() if gain is not None else None
     Yd = torch.from_numpy(Y0.copy()).cuda()
-    binding.debug_linear(Wd, Xd, Gd, 1e-6, epi, Yd, wdtype=wdt)
+    binding.debug_linear(Wd, Xd, Gd, 1e-6, epi, Yd, wdtype=wdt, matrix_cores=mc)
     torch.cuda.synchronize()
     got = Yd.cpu().numpy().astype(np.float64)
     ref = _ref_linear(W, X, gain, 1e-6, epi, Y0)

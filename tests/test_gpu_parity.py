@@ -95,6 +95,19 @@ def test_tiny_fp32_greedy_parity():
     eng.close()
 
 
+def test_tiny_bf16_parity():
+    """head_dim 64 with a bf16 KV cache (the one-wave decode attention path)."""
+    wl = synth.workload("tiny_fp32_b1")
+    dm = synth.dims(wl["model"])
+    w = weights(wl["model"], "bf16")
+    lens = np.array([8, 3, 13], dtype=np.int32)
+    prompts = synth.split_rows(synth.make_prompts(lens, dm["talker"]["hidden"], seed=21), lens)
+    pad = synth.make_tts_pad(dm["talker"]["hidden"], seed=22)
+    eng = binding.Engine(dm, w, "bf16", max_batch=3, max_positions=96)
+    teacher_forced_check(eng, w, dm, prompts, lens, pad, synth.SAMPLING, synth.PRED_SAMPLING, 5, 70, 5e-2)
+    eng.close()
+
+
 def test_tiny_trailing_text_parity():
     wl = synth.workload("tiny_fp32_b1")
     dm = synth.dims(wl["model"])
