@@ -56,15 +56,32 @@ __device__ __forceinline__ float ld_any(const void* p, int dt, long i) {
   return dt == DT_BF16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
+// Wave-wide reductions with DPP lane moves (no LDS round trips): within each
+// row of 16 lanes via quad permutes and mirrors, then row 0 -> 1, 2 -> 3
+// (row_bcast:15) and row 1 -> 2, 3 (row_bcast:31); lane 63 then holds the
+// result, which readlane broadcasts. Every lane of the wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float v, float id) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWS, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<0xb1, 0xf>(v, 0.f);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e, 0xf>(v, 0.f);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141, 0xf>(v, 0.f);   // row_half_mirror
+  v += dpp_f<0x140, 0xf>(v, 0.f);   // row_mirror
+  v += dpp_f<0x142, 0xa>(v, 0.f);   // row_bcast:15 into rows 1, 3
+  v += dpp_f<0x143, 0xc>(v, 0.f);   // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<0xb1, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x4e, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x141, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x140, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x142, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(v, -INFINITY));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Block-wide reductions for NT threads; `red` is LDS scratch of >= NT/64 floats.
@@ -464,7 +481,6 @@ static hipError_t launch_gemv_nc(const LinearArgs& a, int nc, hipStream_t s) {
     default: return launch_gemv_t<WT, R, MT, KS, 4>(a, s);
   }
 }
-
 template <typename WT, int R, int MT>
 static hipError_t launch_gemv_ks(const LinearArgs& a, int ks, int nc, hipStream_t s) {
   if (ks == 4) return launch_gemv_nc<WT, R, MT, 4>(a, nc, s);
@@ -483,9 +499,9 @@ static bool try_gemv(const LinearArgs& a, hipStream_t s, hipError_t* err) {
   const int per = ks * 64 * EPC;
   const int nc = (a.K + per - 1) / per;
   if (nc > 4) return false;
-  const int mt = a.M <= 1 ? 1 : 2;
-  if (R == 2) *err = mt == 1 ? launch_gemv_ks<WT, 2, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 2, 2>(a, ks, nc, s);
-  else *err = mt == 1 ? launch_gemv_ks<WT, 1, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 2>(a, ks, nc, s);
+  // both activation rows in one block: the weights stream once
+  if (a.M == 1) *err = R == 2 ? launch_gemv_ks<WT, 2, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 1>(a, ks, nc, s);
+  else *err = R == 2 ? launch_gemv_ks<WT, 2, 2>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 2>(a, ks, nc, s);
   return true;
 }
 
@@ -534,6 +550,18 @@ constexpr int GLD = GK + 8;   // padded LDS row (bf16 elements)
 
 __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+// Two fp32 -> two bf16 (round to nearest even) with one v_cvt_pk_bf16_f32; a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// Split (a, b) into bf16 hi = rne(x) and lo = rne(x - hi), packed in pairs.
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_pk_bf16(a, b);
+  lo = cvt_pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 template <int BM, int BN>
 __global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float* __restrict__ den) {
   constexpr int TM = BM / 64, TN = BN / 64;      // 32x32 MFMA tiles per wave
@@ -577,18 +605,15 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float
       const int row = m0 + r;
       float x[4] = {xa[q].x, xa[q].y, xa[q].z, xa[q].w};
       if (p.gain && row < M) {
-        const float d = den[row];
+        const float rd = 1.f / den[row];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = x[e] / d * p.gain[k0 + c + e];
+        for (int e = 0; e < 4; ++e) x[e] = x[e] * rd * p.gain[k0 + c + e];
       }
-      uint16_t h[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = f32_to_bf16(x[e]);
-        lo[e] = f32_to_bf16(x[e] - bf16_to_f32(h[e]));
-      }
-      *(uint2*)&sah[r * GLD + c] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-      *(uint2*)&sal[r * GLD + c] = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+      uint32_t h0, l0, h1, l1;
+      split_pk(x[0], x[1], h0, l0);
+      split_pk(x[2], x[3], h1, l1);
+      *(uint2*)&sah[r * GLD + c] = make_uint2(h0, h1);
+      *(uint2*)&sal[r * GLD + c] = make_uint2(l0, l1);
     }
 #pragma unroll
     for (int q = 0; q < BV; ++q) {
@@ -671,15 +696,196 @@ static hipError_t launch_mfma(const LinearArgs& a, float* den, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- skinny MFMA
+// Projection for 3..16 activation rows with bf16 weights: the weights stream
+// once, with coalesced loads, and the products run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16).
+// Block = 4 waves on one tile of 16 weight rows; K is cut into slices of 256
+// and wave w takes slices w, w + 4, ... (S per wave). Per slice a wave loads
+// its 16 x 256 weight tile (each half-wave reads 512 contiguous bytes of one
+// row) and the M activation rows (a full wave per row), writes them to its own
+// LDS region (activations RMSNorm'd and split into bf16 hi + lo on the way)
+// and reads back MFMA fragments: step u contracts k in [32u, 32u + 32).
+// The hi and lo parts both multiply the exact bf16 weights with fp32
+// accumulation; the four waves' 16 x 16 tiles are summed in LDS in a fixed
+// order. Weight loads run PF slices ahead, activation loads two.
+constexpr int SK_SLICE = 256;
+constexpr int SK_LD = SK_SLICE + 8;      // LDS row stride (bf16 elements): 528 bytes
+constexpr int SK_NW = 4;                 // waves per block
+constexpr int SK_MAXM = 16;
+
+static size_t skinny_lds_bytes(int M) {
+  return (size_t)SK_NW * (16 * SK_LD * 2 + 2 * M * SK_LD * 2) + SK_NW * 4 * 64 * 4 + SK_NW * 16 * 4;
+}
+
+template <int S, bool NORM>
+__global__ __launch_bounds__(SK_NW * 64) void skinny_kernel(LinearArgs p) {
+  static_assert(!NORM || S <= 2, "the norm prologue keeps every slice of a row in registers");
+  constexpr int PF = S < 3 ? S : 3;      // weight slices in flight
+  constexpr int XB = S < 2 ? S : 2;      // activation slices in flight
+  extern __shared__ __attribute__((aligned(16))) unsigned char sk_smem[];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int K = p.K, N = p.N, M = p.M;
+  uint16_t* Wl = (uint16_t*)sk_smem + w * 16 * SK_LD;
+  uint16_t* Xh = (uint16_t*)sk_smem + SK_NW * 16 * SK_LD + w * 2 * M * SK_LD;
+  uint16_t* Xl = Xh + M * SK_LD;
+  float* red = (float*)(sk_smem + SK_NW * (16 * SK_LD * 2 + 2 * M * SK_LD * 2));
+  float* rss = red + SK_NW * 4 * 64;
+  const uint16_t* W = (const uint16_t*)p.W;
+  // weight tile load: instruction q reads row 2q + lane / 32, elements 8 (lane % 32) .. + 8
+  const uint16_t* wrow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) wrow[q] = W + (long)min(n0 + 2 * q + (lane >> 5), N - 1) * K + 8 * (lane & 31);
+  u32x4 wv[PF][8];
+  f32x4 xv[XB][SK_MAXM];
+  auto load_w = [&](int si, int slot) __attribute__((always_inline)) {
+    const int k0 = (si * SK_NW + w) * SK_SLICE;
+    if (k0 < K)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[slot][q] = ld_weight(wrow[q] + k0);
+  };
+  auto load_x = [&](int si, int slot) __attribute__((always_inline)) {
+    const int k0 = (si * SK_NW + w) * SK_SLICE;
+    if (k0 < K)
+#pragma unroll
+      for (int m = 0; m < SK_MAXM; ++m)
+        if (m < M) xv[slot][m] = *(const f32x4*)(p.X + (long)m * p.ldx + k0 + 4 * lane);
+  };
+#pragma unroll
+  for (int si = 0; si < PF; ++si) load_w(si, si);
+#pragma unroll
+  for (int si = 0; si < XB; ++si) load_x(si, si);
+  float inv[SK_MAXM];   // per row 1 / sqrt(mean(x^2) + eps)
+  const float rk = 1.f / (float)K;
+  if constexpr (NORM) {
+    // row sums of squares over all of K: lanes, then the waves
+#pragma unroll
+    for (int m = 0; m < SK_MAXM; ++m) {
+      float ss = 0.f;
+#pragma unroll
+      for (int si = 0; si < S; ++si)
+        if ((si * SK_NW + w) * SK_SLICE < K && m < M) {
+          const f32x4 v = xv[si][m];
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      ss = wave_sum(ss);
+      if (lane == 0 && m < M) rss[w * 16 + m] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < SK_MAXM; ++m) {
+      float tot = 0.f;
+      if (m < M)
+#pragma unroll
+        for (int q = 0; q < SK_NW; ++q) tot += rss[q * 16 + m];
+      inv[m] = 1.f / sqrtf(tot * rk + p.eps);   // reciprocal of the row's RMS denominator
+    }
+  }
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int jr = min(j, M - 1);   // padding rows of the tile repeat the last row; their results are dropped
+#pragma unroll
+  for (int si = 0; si < S; ++si) {
+    const int k0 = (si * SK_NW + w) * SK_SLICE;
+    const bool live = k0 < K;
+    if (live) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) *(u32x4*)&Wl[(2 * q + (lane >> 5)) * SK_LD + 8 * (lane & 31)] = wv[si % PF][q];
+      f32x4 gv = (f32x4){1.f, 1.f, 1.f, 1.f};
+      if constexpr (NORM) gv = *(const f32x4*)(p.gain + k0 + 4 * lane);
+#pragma unroll
+      for (int m = 0; m < SK_MAXM; ++m) {
+        if (m < M) {
+        float x[4] = {xv[si % 2][m].x, xv[si % 2][m].y, xv[si % 2][m].z, xv[si % 2][m].w};
+        if constexpr (NORM) {
+          x[0] = x[0] * inv[m] * gv.x; x[1] = x[1] * inv[m] * gv.y;
+          x[2] = x[2] * inv[m] * gv.z; x[3] = x[3] * inv[m] * gv.w;
+          if (p.norm_out && blockIdx.x == 0)
+            *(f32x4*)(p.norm_out + (long)m * p.ld_norm + k0 + 4 * lane) = (f32x4){x[0], x[1], x[2], x[3]};
+        }
+        uint32_t h0, l0, h1, l1;
+        split_pk(x[0], x[1], h0, l0);
+        split_pk(x[2], x[3], h1, l1);
+        *(uint2*)&Xh[m * SK_LD + 4 * lane] = make_uint2(h0, h1);
+        *(uint2*)&Xl[m * SK_LD + 4 * lane] = make_uint2(l0, l1);
+        }
+      }
+    }
+    // refill the register slots just drained
+    if (si + PF < S) load_w(si + PF, si % PF);
+    if (si + 2 < S) load_x(si + 2, si % 2);
+    __syncthreads();
+    if (live)
+#pragma unroll
+      for (int u = 0; u < SK_SLICE / 32; ++u) {
+        const int kk = 32 * u + 8 * g;
+        const bf16x8 bw = *(const bf16x8*)&Wl[j * SK_LD + kk];
+        const bf16x8 ah = *(const bf16x8*)&Xh[jr * SK_LD + kk];
+        const bf16x8 al = *(const bf16x8*)&Xl[jr * SK_LD + kk];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+      }
+    __syncthreads();
+  }
+  // D(i, j) of the 16x16 tile: lane j + 16 * (i / 4), register i % 4; wave r sums register r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(w * 4 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  const int r = w;
+  float v = 0.f;
+#pragma unroll
+  for (int q = 0; q < SK_NW; ++q) v += red[(q * 4 + r) * 64 + lane];
+  const int row = 4 * g + r, col = n0 + j;
+  if (p.epi == EPI_SWIGLU) {
+    const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes j, j ^ 1
+    if (!(j & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
+  } else if (row < M && col < N) {
+    float* y = p.Y + (long)row * p.ldy + col;
+    *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+  }
+}
+
+template <int S, bool NORM>
+static hipError_t launch_skinny_k(const LinearArgs& a, hipStream_t s) {
+  static size_t have = 0;
+  hipError_t e = ensure_lds((const void*)skinny_kernel<S, NORM>, skinny_lds_bytes(SK_MAXM), &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((skinny_kernel<S, NORM>), dim3((a.N + 15) / 16), dim3(SK_NW * 64), skinny_lds_bytes(a.M), s, a);
+  return hipGetLastError();
+}
+
+static bool skinny_fits(const LinearArgs& a) {
+  if (a.wdtype != DT_BF16 || a.M < 3 || a.M > SK_MAXM || a.K % SK_SLICE != 0) return false;
+  const int S = (a.K / SK_SLICE + SK_NW - 1) / SK_NW;
+  return a.gain ? S <= 2 : S <= 6;
+}
+
+static hipError_t launch_skinny(const LinearArgs& a, hipStream_t s) {
+  const int S = (a.K / SK_SLICE + SK_NW - 1) / SK_NW;
+  if (a.gain) return S == 1 ? launch_skinny_k<1, true>(a, s) : launch_skinny_k<2, true>(a, s);
+  switch (S) {
+    case 1: return launch_skinny_k<1, false>(a, s);
+    case 2: return launch_skinny_k<2, false>(a, s);
+    case 3: return launch_skinny_k<3, false>(a, s);
+    case 4: return launch_skinny_k<4, false>(a, s);
+    case 5: return launch_skinny_k<5, false>(a, s);
+    default: return launch_skinny_k<6, false>(a, s);
+  }
+}
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  // many rows of bf16 weights: matrix cores (needs K % 32 == 0 and row scratch)
-  if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)
-    return launch_mfma(a, a.row_den, s);
+  // one or two rows: register GEMV, the weights streamed once with fp32 FMA
   {
     hipError_t e = hipSuccess;
     if (a.wdtype == DT_BF16 ? try_gemv<uint16_t>(a, s, &e) : try_gemv<float>(a, s, &e)) return e;
   }
+  // a few more rows of bf16 weights: weight-streaming MFMA kernel
+  if (skinny_fits(a)) return launch_skinny(a, s);
+  // many rows of bf16 weights: matrix-core GEMM (needs K % 32 == 0 and row scratch)
+  if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)
+    return launch_mfma(a, a.row_den, s);
   // activation tile: as many rows as fit in 96 KB of LDS, up to 8
   int mtmax = 8;
   while (mtmax > 1 && (size_t)mtmax * a.K * 4 > 96 * 1024) mtmax >>= 1;
@@ -1267,7 +1473,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   int* sid = (int*)(sp + V);             // [V]
   __shared__ float redf[8];
   __shared__ int redi[8];
-  __shared__ int hist[256];
+  __shared__ int hist[NT / 64 * 256];
   __shared__ int scan[NT];
   __shared__ int sh_int[4];
   __shared__ float sh_f[2];
@@ -1326,25 +1532,36 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       for (int i = tid; i < V; i += NT) v[i] = v[i] / temperature;
       __syncthreads();
       if (top_k > 0 && top_k < V) {
-        // radix select of the k-th largest value, 8 bits at a time from the top
+        // radix select of the k-th largest value, 8 bits at a time from the top;
+        // per-wave histograms, then a parallel suffix count finds the digit
         uint32_t prefix = 0, mask = 0;
         int kk = top_k;
+        const int lane = tid & 63, wv = tid >> 6;
         for (int shift = 24; shift >= 0; shift -= 8) {
-          hist[tid] = 0;
+#pragma unroll
+          for (int q = 0; q < NT / 64; ++q) hist[q * 256 + tid] = 0;
           __syncthreads();
           for (int i = tid; i < V; i += NT) {
             const uint32_t key = ord_key(v[i]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+            if ((key & mask) == prefix) atomicAdd(&hist[wv * 256 + ((key >> shift) & 255u)], 1);
           }
           __syncthreads();
-          if (tid == 0) {
-            int cum = 0, b = 255;
-            for (; b > 0; --b) {
-              if (cum + hist[b] >= kk) break;
-              cum += hist[b];
-            }
-            sh_int[0] = b;
-            sh_int[1] = kk - cum;
+          int h = 0;   // count of digit tid
+#pragma unroll
+          for (int q = 0; q < NT / 64; ++q) h += hist[q * 256 + tid];
+          int sfx = h;   // inclusive suffix count over digits >= tid, within the wave
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_down(sfx, o);
+            if (lane + o < 64) sfx += t;
+          }
+          if (lane == 0) scan[wv] = sfx;
+          __syncthreads();
+          for (int q = wv + 1; q < NT / 64; ++q) sfx += scan[q];
+          const int above = sfx - h;   // count of digits > tid
+          if (sfx >= kk && above < kk) {   // exactly one digit: the k-th largest lies in it
+            sh_int[0] = tid;
+            sh_int[1] = kk - above;
           }
           __syncthreads();
           prefix |= ((uint32_t)sh_int[0]) << shift;
@@ -1402,12 +1619,20 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
+      // sequential fp32 cumulative sum in (p desc, id asc) order; reads batched by 8
       int keep = ns;
       if (top_p < 1.0f) {
         float cs = 0.f;
-        for (int j = 0; j < ns; ++j) {
-          cs += sp[j];
-          if (cs >= top_p) { keep = j + 1; break; }
+        for (int j0 = 0; j0 < ns && keep == ns; j0 += 8) {
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = j0 + e < ns ? sp[j0 + e] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (keep == ns && j0 + e < ns) {
+              cs += t[e];
+              if (cs >= top_p) keep = j0 + e + 1;
+            }
         }
       }
       sh_int[2] = keep;

@@ -41,7 +41,8 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("N,K,M", [(4096, 1024, 1), (1024, 2048, 3), (6144, 1024, 8), (1024, 3072, 5),
                                    (3072, 512, 17), (200, 64, 2), (2048, 1024, 64), (96, 6144, 9),
-                                   (1024, 3072, 16), (200, 96, 130), (6144, 1024, 257), (2048, 2048, 1024)])
+                                   (1024, 3072, 16), (200, 96, 130), (6144, 1024, 257), (2048, 2048, 1024),
+                                   (200, 1024, 12), (1000, 768, 30), (4096, 2048, 24)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row scratch, which routes bf16 weights with
