@@ -132,7 +132,8 @@ struct Layout {
   std::vector<LayerBuf> tl, pl;
   size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj;
   size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
-  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den;
+  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den, part;
+  long part_floats;
   size_t rowstate, seen, runs, idx, frame_out, req;
   size_t total;
   int tmax, seen_words, max_runs;
@@ -192,6 +193,20 @@ Layout plan_layout(const qt_config& c) {
   L.logits_p = p.take(p.sz.mul({15, B, C, 4}));
   L.rope_rows = p.take(p.sz.mul({B, (size_t)t.d, 4}));
   L.row_den = p.take(p.sz.mul({T, 4}));
+  // split-K partial sums: (K / 256) x rows x N for the largest projection at up to 128 rows
+  {
+    const size_t rows = std::min<size_t>(128, T);
+    size_t need = 0;
+    auto lin = [&](size_t n, size_t k) { need = std::max(need, (k / 256) * rows * n); };
+    for (const Dec* d : {&t, &q}) {
+      lin(d->qkv, d->H); lin(d->H, d->nqd); lin(2 * (size_t)d->I, d->H); lin(d->H, d->I);
+    }
+    lin(V, t.H); lin(C, q.H);
+    if (c.pred_in_proj) lin(q.H, t.H);
+    need = std::min<size_t>(need, (size_t)16 << 20);
+    L.part_floats = (long)need;
+    L.part = p.take(p.sz.mul({need, 4}));
+  }
   (void)Hm;
   // row state: code0_next, finished, pos, text_off, text_len [B]; frame_k; own/forced [B,16]
   L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
@@ -230,7 +245,8 @@ struct qt_ctx {
   void *temb, *thead, *pemb, *phead, *pproj;
   float *cos_t, *sin_t, *cos_p, *sin_p;
   void *kc_t, *vc_t, *kc_p, *vc_p;
-  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den;
+  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den, *part;
+  long part_floats;
   int *code0_next, *finished, *pos, *text_off, *text_len, *frame_k, *own, *forced;
   uint32_t* seen;
   Run* runs;
@@ -329,6 +345,7 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     a.wdtype = ctx->cfg.weight_dtype;
     a.eps = d.eps;
     a.row_den = ctx->row_den;
+    a.part = ctx->part; a.part_floats = ctx->part_floats;
     // q/k/v = W_qkv · RMSNorm(x)
     a.W = w.wqkv; a.N = d.qkv; a.K = d.H; a.X = x; a.ldx = d.H; a.M = M; a.gain = w.attn_norm;
     a.Y = ctx->qkv; a.ldy = d.qkv; a.epi = EPI_STORE;
@@ -409,6 +426,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
 
   LinearArgs pa{};
   pa.row_den = ctx->row_den;
+  pa.part = ctx->part; pa.part_floats = ctx->part_floats;
   pa.wdtype = wd; pa.W = ctx->pproj; pa.N = P.H; pa.K = T.H; pa.X = ctx->xin_w; pa.ldx = T.H;
   pa.Y = ctx->x_p; pa.ldy = P.H; pa.epi = EPI_STORE;
 
@@ -420,6 +438,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     // head st on the last token of each row
     LinearArgs ha{};
     ha.row_den = ctx->row_den;
+    ha.part = ctx->part; ha.part_floats = ctx->part_floats;
     ha.wdtype = wd; ha.W = (const char*)ctx->phead + (size_t)st * C * P.H * esize(wd); ha.N = C; ha.K = P.H;
     ha.X = st == 0 ? ctx->x_p + P.H : ctx->x_p; ha.ldx = st == 0 ? 2L * P.H : P.H; ha.M = B;
     ha.gain = ctx->pred_norm; ha.eps = P.eps;
@@ -443,6 +462,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s, false, true));
   LinearArgs ta{};
   ta.row_den = ctx->row_den;
+  ta.part = ctx->part; ta.part_floats = ctx->part_floats;
   ta.wdtype = wd; ta.W = ctx->thead; ta.N = ctx->cfg.talker_vocab; ta.K = T.H; ta.X = ctx->x_t; ta.ldx = T.H; ta.M = B;
   ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = ctx->cfg.talker_vocab; ta.epi = EPI_STORE;
   ta.norm_out = ctx->h; ta.ld_norm = T.H;
@@ -568,6 +588,8 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
   ctx->logits_t = at<float>(ctx, L.logits_t); ctx->logits_p = at<float>(ctx, L.logits_p);
   ctx->rope_rows = at<float>(ctx, L.rope_rows);
   ctx->row_den = at<float>(ctx, L.row_den);
+  ctx->part = at<float>(ctx, L.part);
+  ctx->part_floats = L.part_floats;
   int* rs = at<int>(ctx, L.rowstate);
   const int MB = cfg->max_batch;
   ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->text_off = rs + 3 * MB;
@@ -724,6 +746,7 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
   }
   LinearArgs ta{};
   ta.row_den = ctx->row_den;
+  ta.part = ctx->part; ta.part_floats = ctx->part_floats;
   ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H; ta.X = ctx->xlast; ta.ldx = T.H;
   ta.M = B; ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = c.talker_vocab;
   ta.epi = EPI_STORE; ta.norm_out = ctx->h; ta.ld_norm = T.H;
@@ -903,7 +926,7 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
 
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
                           int32_t M, const float* gain, float eps, int32_t epilogue, float* Y, float* scratch,
-                          int32_t reps) {
+                          int64_t scratch_floats, int32_t reps) {
   if (wdtype != QT_DTYPE_F32 && wdtype != QT_DTYPE_BF16) { set_err(g_err, "bad wdtype"); return QT_E_INVALID; }
   if (!W || !X || !Y) { set_err(g_err, "W, X and Y must not be NULL"); return QT_E_INVALID; }
   if (N < 1 || K < 8 || K % 8 || M < 1 || reps < 1 || epilogue < 0 || epilogue > 2 || (epilogue == 2 && N % 2)) {
@@ -914,7 +937,11 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
   LinearArgs a{};
   a.W = W; a.wdtype = wdtype; a.N = N; a.K = K; a.X = X; a.ldx = K; a.M = M; a.gain = gain; a.eps = eps;
   a.Y = Y; a.ldy = epilogue == 2 ? N / 2 : N; a.epi = epilogue;
-  a.row_den = scratch;
+  if (scratch && scratch_floats >= M) {
+    const long den = ((long)M + 63) / 64 * 64;   // partial sums start 256-byte aligned
+    a.row_den = scratch;
+    if (scratch_floats > den) { a.part = scratch + den; a.part_floats = scratch_floats - den; }
+  }
   for (int i = 0; i < reps; ++i) {
     hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
     if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }

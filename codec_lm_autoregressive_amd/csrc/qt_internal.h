@@ -23,6 +23,7 @@ struct LinearArgs {
   float* Y; long ldy; int epi;
   float* norm_out; long ld_norm;       // optional copy of the normalised X
   float* row_den;                      // [M] scratch for the matrix-core path (nullptr: not used)
+  float* part; long part_floats;       // split-K partial sums for 17..128 rows (nullptr: not used)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 

@@ -874,6 +874,160 @@ static hipError_t launch_skinny(const LinearArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------- split-K MFMA GEMM
+// Projection for 17..128 activation rows (batched decode, short prompts).
+// Block = 4 waves (2 x 2) on a 64 x 64 output tile and one K range of KZ
+// (256 or 512): every load of that range is issued up front with coalesced
+// reads, then staged 64 k at a time through LDS (activations RMSNorm'd with
+// the row denominators of row_norm_kernel and split into bf16 hi + lo) and
+// contracted with v_mfma_f32_32x32x16_bf16, each wave owning a 32 x 32 tile.
+// With one K range the epilogue is applied directly; otherwise each block
+// writes its partial tile and splitk_reduce_kernel sums the ranges in a fixed
+// order and applies the epilogue, so results do not depend on timing.
+constexpr int SG_T = 64;          // output tile edge (rows and columns)
+constexpr int SG_GK = 64;         // k per LDS stage
+constexpr int SG_LD = SG_GK + 8;  // LDS row stride (bf16): 144 bytes
+
+template <int KZ, bool NORM>
+__global__ __launch_bounds__(NT) void splitk_kernel(LinearArgs p, const float* __restrict__ den) {
+  constexpr int ST = KZ / SG_GK;          // stages
+  constexpr int XV = SG_T * SG_GK / 4 / NT;   // float4 of X per thread per stage (4)
+  constexpr int WV = SG_T * SG_GK / 8 / NT;   // 16-byte W chunks per thread per stage (2)
+  __shared__ __attribute__((aligned(16))) uint16_t xh[SG_T * SG_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[SG_T * SG_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t wl[SG_T * SG_LD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * SG_T, m0 = blockIdx.y * SG_T, kb = blockIdx.z * KZ;
+  const int M = p.M, N = p.N, K = p.K;
+  const uint16_t* W = (const uint16_t*)p.W;
+  f32x4 xv[ST][XV];
+  u32x4 wv[ST][WV];
+#pragma unroll
+  for (int st = 0; st < ST; ++st) {
+#pragma unroll
+    for (int q = 0; q < WV; ++q) {
+      const int idx = tid + q * NT, r = idx >> 3, c = (idx & 7) * 8;
+      wv[st][q] = ld_weight(W + (long)min(n0 + r, N - 1) * K + kb + st * SG_GK + c);
+    }
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int idx = tid + q * NT, r = idx >> 4, c = (idx & 15) * 4;
+      xv[st][q] = *(const f32x4*)(p.X + (long)min(m0 + r, M - 1) * p.ldx + kb + st * SG_GK + c);
+    }
+  }
+  float rden[XV];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) rden[q] = 1.f / den[min(m0 + ((tid + q * NT) >> 4), M - 1)];
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < ST; ++st) {
+    if (st > 0) __syncthreads();   // the previous stage's fragments have been read
+#pragma unroll
+    for (int q = 0; q < WV; ++q) {
+      const int idx = tid + q * NT, r = idx >> 3, c = (idx & 7) * 8;
+      *(u32x4*)&wl[r * SG_LD + c] = wv[st][q];
+    }
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int idx = tid + q * NT, r = idx >> 4, c = (idx & 15) * 4;
+      float x[4] = {xv[st][q].x, xv[st][q].y, xv[st][q].z, xv[st][q].w};
+      if constexpr (NORM) {
+        const f32x4 g = *(const f32x4*)(p.gain + kb + st * SG_GK + c);
+        x[0] = x[0] * rden[q] * g.x; x[1] = x[1] * rden[q] * g.y;
+        x[2] = x[2] * rden[q] * g.z; x[3] = x[3] * rden[q] * g.w;
+      }
+      uint32_t h0, l0, h1, l1;
+      split_pk(x[0], x[1], h0, l0);
+      split_pk(x[2], x[3], h1, l1);
+      *(uint2*)&xh[r * SG_LD + c] = make_uint2(h0, h1);
+      *(uint2*)&xl[r * SG_LD + c] = make_uint2(l0, l1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < SG_GK; kk += 16) {
+      const int k = kk + 8 * (lane >> 5);
+      const bf16x8 ah = *(const bf16x8*)&xh[(wm * 32 + (lane & 31)) * SG_LD + k];
+      const bf16x8 al = *(const bf16x8*)&xl[(wm * 32 + (lane & 31)) * SG_LD + k];
+      const bf16x8 bw = *(const bf16x8*)&wl[(wn * 32 + (lane & 31)) * SG_LD + k];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bw, acc, 0, 0, 0);
+    }
+  }
+  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  const int col = n0 + wn * 32 + (lane & 31);
+  const bool direct = gridDim.z == 1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    const float v = acc[r];
+    if (!direct) {
+      if (row < M && col < N) p.part[((long)blockIdx.z * M + row) * N + col] = v;
+    } else if (p.epi == EPI_SWIGLU) {
+      const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
+      if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
+    } else if (row < M && col < N) {
+      float* y = p.Y + (long)row * p.ldy + col;
+      *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+    }
+  }
+}
+
+// Sums the Z partial tiles of each output in order z = 0..Z-1 and applies the
+// epilogue; one thread per 4 consecutive columns (N % 4 == 0).
+__global__ __launch_bounds__(NT) void splitk_reduce_kernel(LinearArgs p, int Z) {
+  const int n4 = p.N / 4;
+  const long t = (long)blockIdx.x * NT + threadIdx.x;
+  if (t >= (long)p.M * n4) return;
+  const int row = (int)(t / n4), c = (int)(t % n4) * 4;
+  f32x4 s = *(const f32x4*)(p.part + (long)row * p.N + c);
+  for (int z = 1; z < Z; ++z) s += *(const f32x4*)(p.part + ((long)z * p.M + row) * p.N + c);
+  float* y = p.Y + (long)row * p.ldy;
+  if (p.epi == EPI_SWIGLU) {
+    y[c / 2] = s.x / (1.f + expf(-s.x)) * s.y;
+    y[c / 2 + 1] = s.z / (1.f + expf(-s.z)) * s.w;
+  } else if (p.epi == EPI_RESIDUAL) {
+    y[c] += s.x; y[c + 1] += s.y; y[c + 2] += s.z; y[c + 3] += s.w;
+  } else {
+    y[c] = s.x; y[c + 1] = s.y; y[c + 2] = s.z; y[c + 3] = s.w;
+  }
+}
+
+static bool splitk_plan(const LinearArgs& a, int* kz, int* Z) {
+  if (a.wdtype != DT_BF16 || a.M < 17 || a.M > 128 || a.K % 256 || a.N % 4 || !a.row_den) return false;
+  for (int k = 256; k <= 512; k *= 2) {
+    if (a.K % k) break;
+    const int z = a.K / k;
+    if (z == 1 || (a.part && (long)z * a.M * a.N <= a.part_floats)) { *kz = k; *Z = z; return true; }
+  }
+  return false;
+}
+
+template <int KZ>
+static hipError_t launch_splitk_k(const LinearArgs& a, int Z, hipStream_t s) {
+  dim3 grid((a.N + SG_T - 1) / SG_T, (a.M + SG_T - 1) / SG_T, Z);
+  if (a.gain) hipLaunchKernelGGL((splitk_kernel<KZ, true>), grid, dim3(NT), 0, s, a, a.row_den);
+  else hipLaunchKernelGGL((splitk_kernel<KZ, false>), grid, dim3(NT), 0, s, a, a.row_den);
+  return hipGetLastError();
+}
+
+static hipError_t launch_splitk(const LinearArgs& a, int kz, int Z, hipStream_t s) {
+  if (a.gain) {
+    hipLaunchKernelGGL(row_norm_kernel, dim3(a.M), dim3(NT), 0, s, a, a.row_den);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = kz == 256 ? launch_splitk_k<256>(a, Z, s) : launch_splitk_k<512>(a, Z, s);
+  if (e != hipSuccess || Z == 1) return e;
+  const long threads = (long)a.M * (a.N / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, s, a, Z);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
@@ -883,6 +1037,11 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   }
   // a few more rows of bf16 weights: weight-streaming MFMA kernel
   if (skinny_fits(a)) return launch_skinny(a, s);
+  // up to 128 rows: split-K MFMA GEMM
+  {
+    int kz, Z;
+    if (splitk_plan(a, &kz, &Z)) return launch_splitk(a, kz, Z, s);
+  }
   // many rows of bf16 weights: matrix-core GEMM (needs K % 32 == 0 and row scratch)
   if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)
     return launch_mfma(a, a.row_den, s);

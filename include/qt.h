@@ -229,12 +229,15 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
  *   gain device float [K] or NULL (RMSNorm prologue with eps);
  *   epilogue 0: Y = W x, 1: Y += W x, 2: SwiGLU over (gate, up) row pairs,
  *   Y [M, N] (or [M, N/2] for SwiGLU) device float.
- *   scratch device float [M] or NULL: with bf16 weights, M >= 16 and
- *   K % 32 == 0 it enables the matrix-core (MFMA) kernel, as in the frame.
+ *   scratch device float [scratch_floats] or NULL: with bf16 weights it lets
+ *   the frame's matrix-core kernels run: at least M floats (row RMS
+ *   denominators) enable the tiled MFMA GEMM; beyond the first M rounded up
+ *   to 64 floats, space for the split-K partial sums ((K / 256) * M * N
+ *   floats, or half of that) enables the split-K GEMM for 17..128 rows.
  *   reps >= 1 launches (for timing). */
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K,
                           const float* X, int32_t M, const float* gain, float eps, int32_t epilogue,
-                          float* Y, float* scratch, int32_t reps);
+                          float* Y, float* scratch, int64_t scratch_floats, int32_t reps);
 
 #ifdef __cplusplus
 }
