@@ -7,10 +7,14 @@ step and the lookahead selection) until every row stops or reaches the frame
 cap. `value` is 16-code frames per second over the timed steps, inputs already
 resident in device memory.
 
-Default workload: the 0.6B-shaped talker + predictor, bf16 weights (fp32
-accumulate), bf16 KV cache, batch 1, greedy, 32-token prompt, 100 frames.
+Default workload (`value`): the 0.6B-shaped talker + predictor, bf16 weights
+(fp32 accumulate), fp16 KV cache, batch 1, greedy, 32-token prompt, 100
+frames. The same line reports, under `batches`, one timed request each of the
+batch-8 (sampling, prompts 32..256, 200 frames) and batch-64 (sampling,
+prompts 128..512, 1024 frames) workloads, and the oracle timed on the host
+cores on a bounded sample (row 0 of the batch-1 workload, up to 100 frames).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--batches A,B]
 """
 from __future__ import annotations
 
@@ -71,13 +75,97 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen06b_bf16_b1")
     ap.add_argument("--frames", type=int, default=None, help="override the frame cap of the workload")
+    ap.add_argument("--batches", default="qwen06b_bf16_b8_sampling,qwen06b_bf16_b64_sampling",
+                    help="further workloads reported under 'batches' (one timed request each; '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=None,
-                    help="frames of the oracle's timed sample (default: the whole workload)")
+    ap.add_argument("--cpu-frames", type=int, default=100,
+                    help="frames of the oracle's timed sample (row 0 of the workload)")
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop and a 64 MiB copy (for counter runs)")
     return ap.parse_args()
+
+
+class Workload:
+    """Seeded inputs of one workload, resident on the device, and its engine."""
+
+    def __init__(self, torch, binding, synth, name, frames=None):
+        self.name = name
+        self.wl = wl = synth.workload(name)
+        self.dm = dm = synth.dims(wl["model"])
+        self.frames = frames or wl["frames"]
+        self.B = wl["B"]
+        H = dm["talker"]["hidden"]
+        t0 = time.time()
+        self.w = synth.make_weights(dm, seed=0, dtype=wl["dtype"])
+        self.lens = synth.prompt_lengths(self.B, *wl["prompt"], seed=2)
+        self.prompt_np = synth.make_prompts(self.lens, H, seed=1)
+        self.pad_np = synth.make_tts_pad(H, seed=3)
+        print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        self.eng = binding.Engine(dm, self.w, wl["dtype"], max_batch=self.B,
+                                  max_positions=max(wl["max_positions"], int(self.lens.max()) + self.frames))
+        self.kv = "f16" if wl["dtype"] == "bf16" else "f32"   # the engine's default cache type
+        with torch.cuda.stream(self.eng.stream):
+            self.prompt = torch.from_numpy(self.prompt_np).cuda()
+            self.pad = torch.from_numpy(self.pad_np).cuda()
+        torch.cuda.synchronize()
+
+    def request(self, frames=None):
+        wl = self.wl
+        return self.eng.generate(self.prompt, self.lens, self.pad, wl["talker"], wl["predictor"], 0,
+                                 frames or self.frames)
+
+    def run(self, torch, binding, steps, warmup):
+        """Whole requests (prefill + frame loop): row-frames per second; then
+        the decode-only frame time with HIP events on the engine's stream."""
+        for _ in range(warmup):
+            self.request()
+        torch.cuda.synchronize()
+        total_frames = row_frames = 0
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            codes, n, fin = self.request()
+            total_frames += int(n.max())
+            row_frames += int(n.sum())
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        wl, eng, stream = self.wl, self.eng, self.eng.stream
+        eng.prefill(self.prompt, self.lens, self.pad, wl["talker"], wl["predictor"], 0, self.frames)
+        eng.step_frame()  # the first frame after a prefill runs eagerly; later ones replay the graph
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nf = 0
+        ev0.record(stream)
+        try:
+            for _ in range(self.frames - 1):
+                _, st = eng.step_frame()
+                nf += 1
+                if np.all(st != 0):
+                    break
+        except binding.QtError:
+            pass
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        frame_ms = ev0.elapsed_time(ev1) / max(nf, 1)
+        mean_ctx = float(np.mean(self.lens)) + (self.frames - 1) / 2.0 + 1
+        wbytes = 2 if wl["dtype"] == "bf16" else 4
+        fb = frame_bytes(self.dm, self.B, mean_ctx, wbytes, 2 if self.kv != "f32" else 4)
+        value = row_frames / dt
+        return dict(value=value, dt=dt, steps=steps, total_frames=total_frames, frame_ms=frame_ms, fb=fb,
+                    ms_per_step=dt * 1000 / steps)
+
+    def config(self, total_frames, steps):
+        wl, dm = self.wl, self.dm
+        return {"workload": self.name, "batch": self.B, "prompt_lens": [int(x) for x in self.lens][:8],
+                "frames_cap": self.frames, "frames_per_step": total_frames // max(steps, 1),
+                "talker_layers": dm["talker"]["layers"], "predictor_layers": dm["predictor"]["layers"],
+                "hidden": dm["talker"]["hidden"], "kv_cache": self.kv,
+                "sampling": "sampled" if wl["talker"]["do_sample"] else "greedy"}
+
+
+def roof(fb, frame_ms):
+    gbs = fb / (frame_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "bytes_per_frame": int(fb), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -90,19 +178,11 @@ def main():
     from codec_lm_autoregressive_amd import binding, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = synth.workload(args.workload)
-    dm = synth.dims(wl["model"])
-    frames = args.frames or wl["frames"]
-    B = wl["B"]
-    H = dm["talker"]["hidden"]
-    t0 = time.time()
-    w = synth.make_weights(dm, seed=0, dtype=wl["dtype"])
-    lens = synth.prompt_lengths(B, *wl["prompt"], seed=2)
-    prompt_np = synth.make_prompts(lens, H, seed=1)
-    pad_np = synth.make_tts_pad(H, seed=3)
-    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     if args.kernel_only:
-        us, nbytes = kernel_timing(torch, binding, w, dm, wl, B, args.kernel_reps)
+        wl = synth.workload(args.workload)
+        dm = synth.dims(wl["model"])
+        w = synth.make_weights(dm, seed=0, dtype=wl["dtype"])
+        us, nbytes = kernel_timing(torch, binding, w, dm, wl, wl["B"], args.kernel_reps)
         # a plain copy of known size, to scale the byte counters
         a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -111,94 +191,63 @@ def main():
         print(json.dumps({"kernel_avg_us": round(us, 3), "kernel_bytes": nbytes,
                           "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "copy_bytes": 64 << 20}))
         return
-    eng = binding.Engine(dm, w, wl["dtype"], max_batch=B, max_positions=max(wl["max_positions"],
-                                                                            int(lens.max()) + frames))
-    stream = eng.stream
-    with torch.cuda.stream(stream):
-        prompt = torch.from_numpy(prompt_np).cuda()
-        pad = torch.from_numpy(pad_np).cuda()
-    torch.cuda.synchronize()
 
-    def one_request():
-        return eng.generate(prompt, lens, pad, wl["talker"], wl["predictor"], 0, frames)
-
-
-    for _ in range(args.warmup):
-        one_request()
-    torch.cuda.synchronize()
-    total_frames = 0
-    row_frames = 0
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        codes, n, fin = one_request()
-        total_frames += int(n.max())
-        row_frames += int(n.sum())
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt * 1000 / args.steps
-    value = row_frames / dt
-
-    # decode-only frame time with HIP events on the engine's stream
-    eng.prefill(prompt, lens, pad, wl["talker"], wl["predictor"], 0, frames)
-    eng.step_frame()  # first frame of a request runs eagerly when no graph exists yet
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    nf = 0
-    ev0.record(stream)
-    try:
-        for _ in range(frames - 1):
-            _, st = eng.step_frame()
-            nf += 1
-            if np.all(st != 0):
-                break
-    except binding.QtError:
-        pass
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    frame_ms = ev0.elapsed_time(ev1) / max(nf, 1)
-
-    mean_ctx = float(np.mean(lens)) + (frames - 1) / 2.0 + 1
-    wbytes = 2 if wl["dtype"] == "bf16" else 4
+    main_wl = Workload(torch, binding, synth, args.workload, args.frames)
+    r = main_wl.run(torch, binding, args.steps, args.warmup)
+    B, wl, dm, w = main_wl.B, main_wl.wl, main_wl.dm, main_wl.w
     kern_us, kern_bytes = kernel_timing(torch, binding, w, dm, wl, B, args.kernel_reps)
     kern_gbs = kern_bytes / (kern_us * 1e-6) / 1e9
-    I = dm["talker"]["intermediate"]
-    fb = frame_bytes(dm, B, mean_ctx, wbytes, wbytes)
+    H, I = dm["talker"]["hidden"], dm["talker"]["intermediate"]
+    main_wl.eng.close()
+
+    batches = []
+    for name in [x for x in args.batches.split(",") if x]:
+        x = Workload(torch, binding, synth, name)
+        # warm-up: a short request captures the frame graph
+        x.request(min(x.frames, 4))
+        q = x.run(torch, binding, 1, 0)
+        batches.append({"workload": name, "batch": x.B, "value": round(q["value"], 3), "unit": "frames/s",
+                        "ms_per_request": round(q["ms_per_step"], 3),
+                        "decode_ms_per_frame": round(q["frame_ms"], 4),
+                        "decode_frames_per_s": round(x.B * 1000.0 / q["frame_ms"], 1),
+                        "rtf": round(FRAMES_PER_AUDIO_SECOND * x.B / q["value"], 6) if q["value"] else None,
+                        "frame_roofline": roof(q["fb"], q["frame_ms"]),
+                        "config": x.config(q["total_frames"], 1)})
+        x.eng.close()
+        del x
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, args.cpu_frames or frames)
+        cpu = cpu_baseline(w, dm, wl, main_wl.lens, main_wl.prompt_np, main_wl.pad_np,
+                           min(args.cpu_frames, main_wl.frames))
 
     out = {
         "metric": "16-code frames/sec (0.6B-shaped talker + code predictor)",
-        "value": round(value, 3),
+        "value": round(r["value"], 3),
         "unit": "frames/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": round(r["ms_per_step"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 weights, fp32 accumulate" if wl["dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded random weights and prompt embeddings)",
-        "config": {"workload": args.workload, "batch": B, "prompt_lens": [int(x) for x in lens][:8],
-                   "frames_cap": frames, "frames_per_step": total_frames // args.steps,
-                   "talker_layers": dm["talker"]["layers"], "predictor_layers": dm["predictor"]["layers"],
-                   "hidden": H, "sampling": "sampled" if wl["talker"]["do_sample"] else "greedy"},
+        "config": main_wl.config(r["total_frames"], args.steps),
         # per-row real-time factor: wall time / audio time (audio = frames / 12.5 Hz)
-        "rtf": round(FRAMES_PER_AUDIO_SECOND * B / value, 6) if value else None,
-        "decode_ms_per_frame": round(frame_ms, 4),
-        "frame_roofline": {"bound": "hbm", "bytes_per_frame": int(fb),
-                           "achieved": round(fb / (frame_ms * 1e-3) / 1e9, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(fb / (frame_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "linear_kernel (gate/up SwiGLU projection, N=%d K=%d M=%d)" % (2 * I, H, B),
+        "rtf": round(FRAMES_PER_AUDIO_SECOND * B / r["value"], 6) if r["value"] else None,
+        "decode_ms_per_frame": round(r["frame_ms"], 4),
+        "frame_roofline": roof(r["fb"], r["frame_ms"]),
+        "roofline": {"kernel": "gemv_kernel (gate/up SwiGLU projection, N=%d K=%d M=%d)" % (2 * I, H, B),
                      "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "avg_launch_us": round(kern_us, 3), "bytes_per_launch": int(kern_bytes)},
+        "batches": batches,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    eng.close()
 
 
 def kernel_timing(torch, binding, w, dm, wl, B, reps):

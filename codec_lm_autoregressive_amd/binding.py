@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("QT_LIB") or os.path.join(_PKG, "libqt.so")
 
 QT_OK, QT_E_INVALID, QT_E_RANGE, QT_E_CAPACITY, QT_E_NOMEM, QT_E_HIP, QT_E_NAN, QT_E_STATE = range(8)
-QT_DTYPE_F32, QT_DTYPE_BF16 = 0, 1
+QT_DTYPE_F32, QT_DTYPE_BF16, QT_DTYPE_F16 = 0, 1, 2
+_DTYPES = {"f32": QT_DTYPE_F32, "bf16": QT_DTYPE_BF16, "f16": QT_DTYPE_F16}
 STATUS_NAMES = {0: "QT_OK", 1: "QT_E_INVALID", 2: "QT_E_RANGE", 3: "QT_E_CAPACITY", 4: "QT_E_NOMEM",
                 5: "QT_E_HIP", 6: "QT_E_NAN", 7: "QT_E_STATE"}
 
@@ -107,7 +108,11 @@ def _dec(d):
 
 def make_config(dm, weight_dtype="bf16", kv_dtype=None, max_batch=1, max_positions=256):
     wd = QT_DTYPE_BF16 if weight_dtype == "bf16" else QT_DTYPE_F32
-    kd = wd if kv_dtype is None else (QT_DTYPE_BF16 if kv_dtype == "bf16" else QT_DTYPE_F32)
+    # default cache: fp16 next to bf16 weights (same bytes as bf16, three more
+    # mantissa bits: K is RMS-normalised and V small, far inside fp16 range)
+    if kv_dtype is None:
+        kv_dtype = "f16" if weight_dtype == "bf16" else "f32"
+    kd = _DTYPES[kv_dtype]
     return Config(_dec(dm["talker"]), _dec(dm["predictor"]), dm["talker_vocab"], dm["n_groups"], dm["codebook"],
                   dm["eos_id"], dm["suppress_begin"], dm["suppress_end"], int(bool(dm["pred_in_proj"])),
                   wd, kd, max_batch, max_positions)

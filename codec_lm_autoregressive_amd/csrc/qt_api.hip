@@ -32,7 +32,7 @@ void set_err(char* buf, const char* fmt, ...) {
   va_end(ap);
 }
 
-size_t esize(int dt) { return dt == QT_DTYPE_BF16 ? 2 : 4; }
+size_t esize(int dt) { return dt == QT_DTYPE_F32 ? 4 : 2; }
 
 // overflow-checked size arithmetic
 struct Sz {
@@ -83,8 +83,9 @@ qt_status check_config(const qt_config* c, char* err) {
     set_err(err, "predictor.hidden must equal talker.hidden without pred_in_proj"); return QT_E_INVALID;
   }
   if ((c->weight_dtype != QT_DTYPE_F32 && c->weight_dtype != QT_DTYPE_BF16) ||
-      (c->kv_dtype != QT_DTYPE_F32 && c->kv_dtype != QT_DTYPE_BF16)) {
-    set_err(err, "weight_dtype / kv_dtype must be QT_DTYPE_F32 or QT_DTYPE_BF16"); return QT_E_INVALID;
+      (c->kv_dtype != QT_DTYPE_F32 && c->kv_dtype != QT_DTYPE_BF16 && c->kv_dtype != QT_DTYPE_F16)) {
+    set_err(err, "weight_dtype must be QT_DTYPE_F32 or QT_DTYPE_BF16; kv_dtype also QT_DTYPE_F16");
+    return QT_E_INVALID;
   }
   if (c->max_batch < 1 || c->max_batch > 4096) { set_err(err, "max_batch must be in 1..4096"); return QT_E_INVALID; }
   if (c->max_positions < 2 || c->max_positions > (1 << 20)) { set_err(err, "max_positions must be in 2..2^20"); return QT_E_INVALID; }

@@ -7,7 +7,7 @@
 
 namespace qt {
 
-enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };   // DT_F16: KV cache only
 enum Epi { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 
 // Device status word bits (read at the once-per-frame sync).

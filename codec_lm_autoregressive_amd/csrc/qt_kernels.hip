@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 namespace qt {
 
@@ -51,6 +52,7 @@ template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p
 template <typename T> __device__ __forceinline__ void st_elem(T* p, long i, float v);
 template <> __device__ __forceinline__ void st_elem<float>(float* p, long i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void st_elem<uint16_t>(uint16_t* p, long i, float v) { p[i] = f32_to_bf16(v); }
+template <> __device__ __forceinline__ void st_elem<_Float16>(_Float16* p, long i, float v) { p[i] = (_Float16)v; }
 
 __device__ __forceinline__ float ld_any(const void* p, int dt, long i) {
   return dt == DT_BF16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
@@ -1092,11 +1094,17 @@ __device__ __forceinline__ void block_reduce_g(float (&v)[G], float* red, bool i
 template <typename KVT> __device__ __forceinline__ float kv_round(float x);
 template <> __device__ __forceinline__ float kv_round<float>(float x) { return x; }
 template <> __device__ __forceinline__ float kv_round<uint16_t>(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+template <> __device__ __forceinline__ float kv_round<_Float16>(float x) { return (float)(_Float16)x; }
 
 // 16-byte chunk of a cache row -> floats
 template <typename KVT>
 __device__ __forceinline__ void unpack_chunk(const u32x4& w, float* x) {
-  if constexpr (sizeof(KVT) == 2) {
+  if constexpr (std::is_same<KVT, _Float16>::value) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = __builtin_bit_cast(h8, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+  } else if constexpr (sizeof(KVT) == 2) {
     x[0] = bf_lo(w.x); x[1] = bf_hi(w.x); x[2] = bf_lo(w.y); x[3] = bf_hi(w.y);
     x[4] = bf_lo(w.z); x[5] = bf_hi(w.z); x[6] = bf_lo(w.w); x[7] = bf_hi(w.w);
   } else {
@@ -1585,6 +1593,7 @@ static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_runs <= 0) return hipSuccess;
   if (a.kvdtype == DT_BF16) return launch_attention_t<uint16_t>(a, s);
+  if (a.kvdtype == DT_F16) return launch_attention_t<_Float16>(a, s);
   return launch_attention_t<float>(a, s);
 }
 

@@ -22,7 +22,9 @@ the tensor's name, so one tensor never depends on the order others are drawn.
 """
 from __future__ import annotations
 
+import os
 import zlib
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -91,11 +93,16 @@ def _stream(seed: int, name: str) -> np.random.Generator:
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
+    return _bf16_round_inplace(np.array(a, dtype=np.float32, copy=True, order="C"))
+
+
+def _bf16_round_inplace(a: np.ndarray) -> np.ndarray:
     u = a.view(np.uint32)
     lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = ((u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)).astype(np.uint32)
-    return r.view(np.float32)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -104,34 +111,44 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+class _Normal:
+    """A weight tensor still to be drawn: N(mean, std^2) from its own stream."""
+
+    def __init__(self, name, shape, std, mean=0.0):
+        self.name, self.shape, self.std, self.mean = name, shape, std, mean
+
+    def draw(self, seed, bf16):
+        g = _stream(seed, self.name)
+        x = g.standard_normal(size=self.shape, dtype=np.float32)
+        if self.std != 1.0:
+            x *= np.float32(self.std)
+        if self.mean != 0.0:
+            x += np.float32(self.mean)
+        return _bf16_round_inplace(x) if bf16 else x
+
+
 def _normal(seed, name, shape, std, mean=0.0):
-    g = _stream(seed, name)
-    x = g.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    if mean != 0.0:
-        x += np.float32(mean)
-    return x
+    return _Normal(name, shape, std, mean).draw(seed, False)
 
 
-def _decoder_weights(seed, prefix, d, in_hidden=None):
+def _decoder_weights(prefix, d, in_hidden=None):
     H = d["hidden"]
     nq, nkv, hd, inter = d["n_heads"], d["n_kv_heads"], d["head_dim"], d["intermediate"]
     layers = []
     for i in range(d["layers"]):
         p = f"{prefix}.{i}."
         layers.append(dict(
-            attn_norm=_normal(seed, p + "attn_norm", (H,), 0.02, 1.0),
-            wq=_normal(seed, p + "wq", (nq * hd, H), 0.02),
-            wk=_normal(seed, p + "wk", (nkv * hd, H), 0.02),
-            wv=_normal(seed, p + "wv", (nkv * hd, H), 0.02),
-            q_norm=_normal(seed, p + "q_norm", (hd,), 0.02, 1.0),
-            k_norm=_normal(seed, p + "k_norm", (hd,), 0.02, 1.0),
-            wo=_normal(seed, p + "wo", (H, nq * hd), 0.02),
-            mlp_norm=_normal(seed, p + "mlp_norm", (H,), 0.02, 1.0),
-            w_gate=_normal(seed, p + "w_gate", (inter, H), 0.02),
-            w_up=_normal(seed, p + "w_up", (inter, H), 0.02),
-            w_down=_normal(seed, p + "w_down", (H, inter), 0.02),
+            attn_norm=_Normal(p + "attn_norm", (H,), 0.02, 1.0),
+            wq=_Normal(p + "wq", (nq * hd, H), 0.02),
+            wk=_Normal(p + "wk", (nkv * hd, H), 0.02),
+            wv=_Normal(p + "wv", (nkv * hd, H), 0.02),
+            q_norm=_Normal(p + "q_norm", (hd,), 0.02, 1.0),
+            k_norm=_Normal(p + "k_norm", (hd,), 0.02, 1.0),
+            wo=_Normal(p + "wo", (H, nq * hd), 0.02),
+            mlp_norm=_Normal(p + "mlp_norm", (H,), 0.02, 1.0),
+            w_gate=_Normal(p + "w_gate", (inter, H), 0.02),
+            w_up=_Normal(p + "w_up", (inter, H), 0.02),
+            w_down=_Normal(p + "w_down", (H, inter), 0.02),
         ))
     return layers
 
@@ -147,22 +164,27 @@ def make_weights(dm: dict, seed: int = 0, dtype: str = "bf16") -> dict:
     H, Hp = t["hidden"], p["hidden"]
     V, C, G = dm["talker_vocab"], dm["codebook"], dm["n_groups"]
     w = dict(
-        talker_layers=_decoder_weights(seed, "talker", t),
-        talker_norm=_normal(seed, "talker.norm", (H,), 0.02, 1.0),
-        talker_codec_embed=_normal(seed, "talker.codec_embed", (V, H), 0.02),
-        talker_codec_head=_normal(seed, "talker.codec_head", (V, H), 0.02),
-        pred_layers=_decoder_weights(seed, "pred", p),
-        pred_norm=_normal(seed, "pred.norm", (Hp,), 0.02, 1.0),
-        pred_embeds=_normal(seed, "pred.embeds", ((G - 1) * C, H), 0.02),
-        pred_heads=_normal(seed, "pred.heads", ((G - 1) * C, Hp), 0.02),
-        pred_in_proj=(_normal(seed, "pred.in_proj", (Hp, H), 0.02)
+        talker_layers=_decoder_weights("talker", t),
+        talker_norm=_Normal("talker.norm", (H,), 0.02, 1.0),
+        talker_codec_embed=_Normal("talker.codec_embed", (V, H), 0.02),
+        talker_codec_head=_Normal("talker.codec_head", (V, H), 0.02),
+        pred_layers=_decoder_weights("pred", p),
+        pred_norm=_Normal("pred.norm", (Hp,), 0.02, 1.0),
+        pred_embeds=_Normal("pred.embeds", ((G - 1) * C, H), 0.02),
+        pred_heads=_Normal("pred.heads", ((G - 1) * C, Hp), 0.02),
+        pred_in_proj=(_Normal("pred.in_proj", (Hp, H), 0.02)
                       if dm["pred_in_proj"] else None),
     )
-    if dtype == "bf16":
-        w = map_arrays(w, bf16_round)
-    elif dtype != "f32":
+    if dtype not in ("bf16", "f32"):
         raise ValueError(dtype)
-    return w
+    # every tensor has its own stream, so drawing them in parallel threads
+    # gives the same values as drawing them one after another
+    leaves = []
+    map_arrays(w, lambda x: leaves.append(x) or x)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        drawn = dict(zip(map(id, leaves), ex.map(lambda x: x.draw(seed, dtype == "bf16"), leaves)))
+    return map_arrays(w, lambda x: drawn[id(x)])
 
 
 def map_arrays(w, fn):

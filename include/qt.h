@@ -59,6 +59,7 @@ typedef int32_t qt_status;
 
 #define QT_DTYPE_F32 0
 #define QT_DTYPE_BF16 1
+#define QT_DTYPE_F16 2   /* IEEE half: KV caches only */
 
 /* Dimensions of one Qwen3-style decoder (talker or code predictor). */
 typedef struct qt_decoder_dims {
@@ -84,7 +85,7 @@ typedef struct qt_config {
   int32_t pred_in_proj;   /* 1: predictor inputs pass a [Hp, H] projection;     */
                           /* 0: requires predictor.hidden == talker.hidden      */
   int32_t weight_dtype;   /* QT_DTYPE_F32 | QT_DTYPE_BF16                       */
-  int32_t kv_dtype;       /* element type of both KV caches                     */
+  int32_t kv_dtype;       /* element type of both KV caches: F32 | BF16 | F16   */
   int32_t max_batch;      /* rows per prefill                                   */
   int32_t max_positions;  /* talker cache length per row                        */
 } qt_config;

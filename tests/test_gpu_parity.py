@@ -95,15 +95,16 @@ def test_tiny_fp32_greedy_parity():
     eng.close()
 
 
-def test_tiny_bf16_parity():
-    """head_dim 64 with a bf16 KV cache (the one-wave decode attention path)."""
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_tiny_bf16_parity(kv):
+    """head_dim 64, bf16 weights, a bf16 or fp16 KV cache."""
     wl = synth.workload("tiny_fp32_b1")
     dm = synth.dims(wl["model"])
     w = weights(wl["model"], "bf16")
     lens = np.array([8, 3, 13], dtype=np.int32)
     prompts = synth.split_rows(synth.make_prompts(lens, dm["talker"]["hidden"], seed=21), lens)
     pad = synth.make_tts_pad(dm["talker"]["hidden"], seed=22)
-    eng = binding.Engine(dm, w, "bf16", max_batch=3, max_positions=96)
+    eng = binding.Engine(dm, w, "bf16", kv_dtype=kv, max_batch=3, max_positions=96)
     teacher_forced_check(eng, w, dm, prompts, lens, pad, synth.SAMPLING, synth.PRED_SAMPLING, 5, 70, 5e-2)
     eng.close()
 
@@ -165,6 +166,77 @@ def test_qwen06b_bf16_b8_sampling_parity():
     pad = synth.make_tts_pad(1024, seed=3)
     eng = binding.Engine(dm, w, "bf16", max_batch=8, max_positions=wl["max_positions"])
     teacher_forced_check(eng, w, dm, prompts, lens, pad, wl["talker"], wl["predictor"], 0, 4, 5e-2, rows=[0, 5, 7])
+    eng.close()
+
+
+def _full_size(name, rows, frames, seed=0, lens=None):
+    wl = synth.workload(name)
+    dm = synth.dims(wl["model"])
+    H = dm["talker"]["hidden"]
+    log(f"{name}: generating weights")
+    w = weights(wl["model"], "bf16")
+    if lens is None:
+        lens = synth.prompt_lengths(wl["B"], *wl["prompt"], seed=2)
+    prompts = synth.split_rows(synth.make_prompts(lens, H, seed=1), lens)
+    pad = synth.make_tts_pad(H, seed=3)
+    eng = binding.Engine(dm, w, "bf16", max_batch=len(lens), max_positions=wl["max_positions"])
+    log(f"{name}: engine ready, prompt lengths {list(lens)[:8]}..., rows {rows}")
+    teacher_forced_check(eng, w, dm, prompts, lens, pad, wl["talker"], wl["predictor"], seed, frames, 5e-2,
+                         rows=rows)
+    return eng, dm, prompts, lens, pad, wl
+
+
+def test_qwen06b_bf16_b64_sampling_parity():
+    """Batch 64 with prompts of 128..512 tokens: the prefill runs 1024-token
+    chunks through the tiled MFMA GEMM, decode runs 64 / 128 rows through the
+    split-K GEMM; rows 0, 29 and 63 are checked against the oracle."""
+    eng, *_ = _full_size("qwen06b_bf16_b64_sampling", [0, 29, 63], 2)
+    eng.close()
+
+
+def test_qwen06b_b64_graph_replay_equals_forced_eager():
+    """At the full batch-64 shape, free-run codes (frames 2.. from graph
+    replays) equal the eager forced replay bit for bit."""
+    wl = synth.workload("qwen06b_bf16_b64_sampling")
+    dm = synth.dims(wl["model"])
+    w = weights(wl["model"], "bf16")
+    lens = synth.prompt_lengths(64, *wl["prompt"], seed=2)
+    prompt = synth.make_prompts(lens, 1024, seed=1)
+    pad = synth.make_tts_pad(1024, seed=3)
+    eng = binding.Engine(dm, w, "bf16", max_batch=64, max_positions=wl["max_positions"])
+    codes, n, _ = eng.generate(prompt, lens, pad, wl["talker"], wl["predictor"], 11, 4)
+    assert np.all((codes[:, :, 1:] >= 0) & (codes[:, :, 1:] < 2048))
+    eng.prefill(prompt, lens, pad, wl["talker"], wl["predictor"], 11, 4)
+    for k in range(int(n.max())):
+        forced = codes[:, k].copy()
+        forced[n <= k] = 0
+        forced[n <= k, 0] = dm["eos_id"]
+        _, _, ch = eng.step_forced(forced)
+        live = n > k
+        np.testing.assert_array_equal(ch[live, 1:], codes[live, k, 1:])
+        if k + 1 < codes.shape[1]:
+            nxt = n > k + 1
+            np.testing.assert_array_equal(ch[nxt, 0], codes[nxt, k + 1, 0])
+    eng.close()
+
+
+def test_long_context_parity():
+    """Talker attention over the batch-64 workload's full KV extent: a
+    1500-token prompt (prefill attention over up to 1500 keys, decode at
+    positions 1500..1501) next to a 700-token one."""
+    eng, *_ = _full_size("qwen06b_bf16_b64_sampling", [0, 1], 2, lens=np.array([1500, 700], dtype=np.int32))
+    eng.close()
+
+
+def test_qwen17b_bf16_b1_parity():
+    """1.7B-class talker (hidden 2048, I 6144) with the 2048 -> 1024 predictor
+    input projection, batch 1 greedy."""
+    eng, *_ = _full_size("qwen17b_bf16_b1", [0], 3)
+    eng.close()
+
+
+def test_qwen17b_bf16_b8_parity():
+    eng, *_ = _full_size("qwen17b_bf16_b8", [0, 7], 2)
     eng.close()
 
 
