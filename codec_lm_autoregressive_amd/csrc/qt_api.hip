@@ -194,11 +194,12 @@ Layout plan_layout(const qt_config& c) {
   L.logits_p = p.take(p.sz.mul({15, B, C, 4}));
   L.rope_rows = p.take(p.sz.mul({B, (size_t)t.d, 4}));
   L.row_den = p.take(p.sz.mul({T, 4}));
-  // split-K partial sums: (K / 256) x rows x N for the largest projection at up to 128 rows
+  // K-range partial sums (and per-row sums of squares): (K / 256) x rows x (N + 1)
+  // for the largest projection at up to 128 rows
   {
     const size_t rows = std::min<size_t>(128, T);
     size_t need = 0;
-    auto lin = [&](size_t n, size_t k) { need = std::max(need, (k / 256) * rows * n); };
+    auto lin = [&](size_t n, size_t k) { need = std::max(need, (k / 256) * rows * (n + 1)); };
     for (const Dec* d : {&t, &q}) {
       lin(d->qkv, d->H); lin(d->H, d->nqd); lin(2 * (size_t)d->I, d->H); lin(d->H, d->I);
     }

@@ -21,6 +21,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads per block for every kernel here
 constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use the matrix cores
+#ifndef ROWS_DIRECT_TILES
+#define ROWS_DIRECT_TILES 64       // output tiles from which the row-block GEMM runs without K ranges
+#endif
 
 // Weight rows are streamed once per pass. QT_WEIGHT_NT selects nontemporal
 // loads (1) or ordinary cached loads (0).
@@ -876,100 +879,182 @@ static hipError_t launch_skinny(const LinearArgs& a, hipStream_t s) {
   }
 }
 
-// ---------------------------------------------------------------- split-K MFMA GEMM
+// ---------------------------------------------------------------- row-block MFMA GEMM
 // Projection for 17..128 activation rows (batched decode, short prompts).
-// Block = 4 waves (2 x 2) on a 64 x 64 output tile and one K range of KZ
-// (256 or 512): every load of that range is issued up front with coalesced
-// reads, then staged 64 k at a time through LDS (activations RMSNorm'd with
-// the row denominators of row_norm_kernel and split into bf16 hi + lo) and
+// Block = 4 waves (2 x 2) on a 64 x 64 output tile and a K range of kz
+// (gridDim.z ranges split K). The range is read in chunks of 256 with
+// coalesced loads, the next chunk's loads in flight while the current one is
+// staged 64 k at a time through LDS (activations split into bf16 hi + lo) and
 // contracted with v_mfma_f32_32x32x16_bf16, each wave owning a 32 x 32 tile.
-// With one K range the epilogue is applied directly; otherwise each block
-// writes its partial tile and splitk_reduce_kernel sums the ranges in a fixed
-// order and applies the epilogue, so results do not depend on timing.
+// RMSNorm is applied after the contraction: norm(x) W^T = (x * g) W^T / rms(x)
+// row by row, so the blocks contract x * g and accumulate the row sums of
+// squares while staging. With one K range the block finishes the rows itself;
+// otherwise it writes its partial tile (and partial sums of squares) and
+// rows_reduce_kernel adds the ranges in a fixed order, scales and applies the
+// epilogue, so results do not depend on timing.
 constexpr int SG_T = 64;          // output tile edge (rows and columns)
 constexpr int SG_GK = 64;         // k per LDS stage
 constexpr int SG_LD = SG_GK + 8;  // LDS row stride (bf16): 144 bytes
+constexpr int SG_CH = 256;        // k per register chunk
 
-template <int KZ, bool NORM>
-__global__ __launch_bounds__(NT) void splitk_kernel(LinearArgs p, const float* __restrict__ den) {
-  constexpr int ST = KZ / SG_GK;          // stages
+// sum over the 16 lanes of a DPP row; every lane of the row gets the result
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xb1, 0xf>(v, 0.f);
+  v += dpp_f<0x4e, 0xf>(v, 0.f);
+  v += dpp_f<0x141, 0xf>(v, 0.f);
+  v += dpp_f<0x140, 0xf>(v, 0.f);
+  return v;
+}
+
+// KW groups of 4 waves split the block's K range (group w takes NCH chunks
+// from kb + w * NCH * 256); their 64 x 64 tiles and row sums of squares are
+// added through LDS in group order before the block finishes or writes its
+// partial tile.
+template <bool NORM, int NCH, int KW>
+__global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
+  constexpr int kz = NCH * SG_CH * KW;   // k per block; each group's NCH register chunks are straight-line
+                                         // code, so the prefetch of chunk c + 1 stays in flight during chunk c
   constexpr int XV = SG_T * SG_GK / 4 / NT;   // float4 of X per thread per stage (4)
   constexpr int WV = SG_T * SG_GK / 8 / NT;   // 16-byte W chunks per thread per stage (2)
-  __shared__ __attribute__((aligned(16))) uint16_t xh[SG_T * SG_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[SG_T * SG_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t wl[SG_T * SG_LD];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NS = SG_CH / SG_GK;           // stages per chunk (4)
+  constexpr int STAGE = 3 * SG_T * SG_LD;     // bf16 elements of one group's LDS stage
+  static_assert(KW == 1 || (KW - 1) * SG_T * SG_T * 4 <= KW * STAGE * 2, "reduction fits in the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KW * STAGE];
+  __shared__ float rs_lds[SG_T];
+  __shared__ float ss_lds[KW][SG_T];
+  const int gtid = threadIdx.x, grp = gtid >> 8, tid = gtid & (NT - 1), wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * SG_T, m0 = blockIdx.y * SG_T, kb = blockIdx.z * KZ;
+  uint16_t* xh = smem + grp * STAGE;
+  uint16_t* xl = xh + SG_T * SG_LD;
+  uint16_t* wl = xl + SG_T * SG_LD;
+  const int n0 = blockIdx.x * SG_T, m0 = blockIdx.y * SG_T, kb = blockIdx.z * kz + grp * NCH * SG_CH;
   const int M = p.M, N = p.N, K = p.K;
   const uint16_t* W = (const uint16_t*)p.W;
-  f32x4 xv[ST][XV];
-  u32x4 wv[ST][WV];
+  // this thread's staging slots: W rows tid / 8 + 32 q, X rows tid / 16 + 16 q
+  const int wc = (tid & 7) * 8, xc = (tid & 15) * 4;
+  const uint16_t* wrow[WV];
+  const float* xrow[XV];
 #pragma unroll
-  for (int st = 0; st < ST; ++st) {
+  for (int q = 0; q < WV; ++q) wrow[q] = W + (long)min(n0 + (tid >> 3) + 32 * q, N - 1) * K + wc;
 #pragma unroll
-    for (int q = 0; q < WV; ++q) {
-      const int idx = tid + q * NT, r = idx >> 3, c = (idx & 7) * 8;
-      wv[st][q] = ld_weight(W + (long)min(n0 + r, N - 1) * K + kb + st * SG_GK + c);
-    }
+  for (int q = 0; q < XV; ++q) xrow[q] = p.X + (long)min(m0 + (tid >> 4) + 16 * q, M - 1) * p.ldx + xc;
+  u32x4 wa[NS][WV], wb[NS][WV];
+  f32x4 xa[NS][XV], xb[NS][XV];
+  float ss[XV];
 #pragma unroll
-    for (int q = 0; q < XV; ++q) {
-      const int idx = tid + q * NT, r = idx >> 4, c = (idx & 15) * 4;
-      xv[st][q] = *(const f32x4*)(p.X + (long)min(m0 + r, M - 1) * p.ldx + kb + st * SG_GK + c);
-    }
-  }
-  float rden[XV];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int q = 0; q < XV; ++q) rden[q] = 1.f / den[min(m0 + ((tid + q * NT) >> 4), M - 1)];
-  }
+  for (int q = 0; q < XV; ++q) ss[q] = 0.f;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // a group's barrier: the 4 waves of the group (all groups run in lock step)
+  auto load = [&](int k0, u32x4 (&wv)[NS][WV], f32x4 (&xv)[NS][XV]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int st = 0; st < ST; ++st) {
-    if (st > 0) __syncthreads();   // the previous stage's fragments have been read
+    for (int st = 0; st < NS; ++st) {
 #pragma unroll
-    for (int q = 0; q < WV; ++q) {
-      const int idx = tid + q * NT, r = idx >> 3, c = (idx & 7) * 8;
-      *(u32x4*)&wl[r * SG_LD + c] = wv[st][q];
+      for (int q = 0; q < WV; ++q) wv[st][q] = ld_weight(wrow[q] + k0 + st * SG_GK);
+#pragma unroll
+      for (int q = 0; q < XV; ++q) xv[st][q] = *(const f32x4*)(xrow[q] + k0 + st * SG_GK);
     }
+  };
+  auto process = [&](int k0, const u32x4 (&wv)[NS][WV], const f32x4 (&xv)[NS][XV]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < XV; ++q) {
-      const int idx = tid + q * NT, r = idx >> 4, c = (idx & 15) * 4;
-      float x[4] = {xv[st][q].x, xv[st][q].y, xv[st][q].z, xv[st][q].w};
-      if constexpr (NORM) {
-        const f32x4 g = *(const f32x4*)(p.gain + kb + st * SG_GK + c);
-        x[0] = x[0] * rden[q] * g.x; x[1] = x[1] * rden[q] * g.y;
-        x[2] = x[2] * rden[q] * g.z; x[3] = x[3] * rden[q] * g.w;
+    for (int st = 0; st < NS; ++st) {
+      __syncthreads();   // the previous stage's fragments have been read
+#pragma unroll
+      for (int q = 0; q < WV; ++q) *(u32x4*)&wl[((tid >> 3) + 32 * q) * SG_LD + wc] = wv[st][q];
+      f32x4 g = (f32x4){1.f, 1.f, 1.f, 1.f};
+      if constexpr (NORM) g = *(const f32x4*)(p.gain + k0 + st * SG_GK + xc);
+#pragma unroll
+      for (int q = 0; q < XV; ++q) {
+        const f32x4 v = xv[st][q];
+        if constexpr (NORM) ss[q] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        uint32_t h0, l0, h1, l1;
+        split_pk(v.x * g.x, v.y * g.y, h0, l0);
+        split_pk(v.z * g.z, v.w * g.w, h1, l1);
+        const int r = (tid >> 4) + 16 * q;
+        *(uint2*)&xh[r * SG_LD + xc] = make_uint2(h0, h1);
+        *(uint2*)&xl[r * SG_LD + xc] = make_uint2(l0, l1);
       }
-      uint32_t h0, l0, h1, l1;
-      split_pk(x[0], x[1], h0, l0);
-      split_pk(x[2], x[3], h1, l1);
-      *(uint2*)&xh[r * SG_LD + c] = make_uint2(h0, h1);
-      *(uint2*)&xl[r * SG_LD + c] = make_uint2(l0, l1);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < SG_GK; kk += 16) {
+        const int k = kk + 8 * (lane >> 5);
+        const bf16x8 ah = *(const bf16x8*)&xh[(wm * 32 + (lane & 31)) * SG_LD + k];
+        const bf16x8 al = *(const bf16x8*)&xl[(wm * 32 + (lane & 31)) * SG_LD + k];
+        const bf16x8 bw = *(const bf16x8*)&wl[(wn * 32 + (lane & 31)) * SG_LD + k];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bw, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bw, acc, 0, 0, 0);
+      }
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c == 0) load(kb, wa, xa);
+    if (c + 1 < NCH) {
+      if (c % 2 == 0) load(kb + (c + 1) * SG_CH, wb, xb);
+      else load(kb + (c + 1) * SG_CH, wa, xa);
+    }
+    if (c % 2 == 0) process(kb + c * SG_CH, wa, xa);
+    else process(kb + c * SG_CH, wb, xb);
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) ss[q] = row16_sum(ss[q]);   // the 16 lanes of a row hold its k slices
+    if ((tid & 15) == 0)
+#pragma unroll
+      for (int q = 0; q < XV; ++q) ss_lds[grp][(tid >> 4) + 16 * q] = ss[q];
+  }
+  __syncthreads();
+  if constexpr (KW > 1) {
+    // groups 1.. park their tiles in the (now idle) stage buffers; group 0 adds them in order
+    float* red = (float*)smem;
+    if (grp > 0)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((grp - 1) * 16 + r) * NT + tid] = acc[r];
+    __syncthreads();
+    if (grp == 0)
+#pragma unroll
+      for (int g2 = 1; g2 < KW; ++g2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += red[((g2 - 1) * 16 + r) * NT + tid];
+  }
+  const bool direct = gridDim.z == 1;
+  if constexpr (NORM) {
+    if (gtid < SG_T) {
+      float t = ss_lds[0][gtid];
+#pragma unroll
+      for (int g2 = 1; g2 < KW; ++g2) t += ss_lds[g2][gtid];
+      const int row = m0 + gtid;
+      if (direct) rs_lds[gtid] = 1.f / sqrtf(t / (float)K + p.eps);
+      else if (blockIdx.x == 0 && row < M) p.part[(long)gridDim.z * M * N + (long)blockIdx.z * M + row] = t;
     }
     __syncthreads();
+    if (grp == 0 && direct && p.norm_out && blockIdx.x == 0)
+      for (int k = xc; k < K; k += SG_GK)
 #pragma unroll
-    for (int kk = 0; kk < SG_GK; kk += 16) {
-      const int k = kk + 8 * (lane >> 5);
-      const bf16x8 ah = *(const bf16x8*)&xh[(wm * 32 + (lane & 31)) * SG_LD + k];
-      const bf16x8 al = *(const bf16x8*)&xl[(wm * 32 + (lane & 31)) * SG_LD + k];
-      const bf16x8 bw = *(const bf16x8*)&wl[(wn * 32 + (lane & 31)) * SG_LD + k];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bw, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bw, acc, 0, 0, 0);
-    }
+        for (int q = 0; q < XV; ++q) {
+          const int r = (tid >> 4) + 16 * q, row = m0 + r;
+          if (row < M) {
+            const f32x4 v = *(const f32x4*)(p.X + (long)row * p.ldx + k), g = *(const f32x4*)(p.gain + k);
+            const float rs = rs_lds[r];
+            *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) =
+                (f32x4){v.x * g.x * rs, v.y * g.y * rs, v.z * g.z * rs, v.w * g.w * rs};
+          }
+        }
   }
+  if (grp > 0) return;   // no barrier follows
   // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
   const int col = n0 + wn * 32 + (lane & 31);
-  const bool direct = gridDim.z == 1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-    const float v = acc[r];
+    const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), row = m0 + lr;
+    float v = acc[r];
     if (!direct) {
       if (row < M && col < N) p.part[((long)blockIdx.z * M + row) * N + col] = v;
-    } else if (p.epi == EPI_SWIGLU) {
+      continue;
+    }
+    if constexpr (NORM) v *= rs_lds[lr];
+    if (p.epi == EPI_SWIGLU) {
       const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
       if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
     } else if (row < M && col < N) {
@@ -979,15 +1064,29 @@ __global__ __launch_bounds__(NT) void splitk_kernel(LinearArgs p, const float* _
   }
 }
 
-// Sums the Z partial tiles of each output in order z = 0..Z-1 and applies the
-// epilogue; one thread per 4 consecutive columns (N % 4 == 0).
-__global__ __launch_bounds__(NT) void splitk_reduce_kernel(LinearArgs p, int Z) {
+// Adds the Z partial tiles of each output in order z = 0..Z-1, applies the
+// row's RMS scale (sums of squares added in the same order) and the epilogue;
+// one thread per 4 consecutive columns (N % 4 == 0). Also writes norm_out.
+__global__ __launch_bounds__(NT) void rows_reduce_kernel(LinearArgs p, int Z) {
   const int n4 = p.N / 4;
   const long t = (long)blockIdx.x * NT + threadIdx.x;
   if (t >= (long)p.M * n4) return;
   const int row = (int)(t / n4), c = (int)(t % n4) * 4;
   f32x4 s = *(const f32x4*)(p.part + (long)row * p.N + c);
   for (int z = 1; z < Z; ++z) s += *(const f32x4*)(p.part + ((long)z * p.M + row) * p.N + c);
+  if (p.gain) {
+    const float* pss = p.part + (long)Z * p.M * p.N;
+    float ssum = pss[row];
+    for (int z = 1; z < Z; ++z) ssum += pss[(long)z * p.M + row];
+    const float rs = 1.f / sqrtf(ssum / (float)p.K + p.eps);
+    s *= rs;
+    if (p.norm_out)
+      for (int k = c; k < p.K; k += p.N) {
+        const f32x4 v = *(const f32x4*)(p.X + (long)row * p.ldx + k), g = *(const f32x4*)(p.gain + k);
+        *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) =
+            (f32x4){v.x * g.x * rs, v.y * g.y * rs, v.z * g.z * rs, v.w * g.w * rs};
+      }
+  }
   float* y = p.Y + (long)row * p.ldy;
   if (p.epi == EPI_SWIGLU) {
     y[c / 2] = s.x / (1.f + expf(-s.x)) * s.y;
@@ -999,34 +1098,79 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(LinearArgs p, int Z) 
   }
 }
 
-static bool splitk_plan(const LinearArgs& a, int* kz, int* Z) {
-  if (a.wdtype != DT_BF16 || a.M < 17 || a.M > 128 || a.K % 256 || a.N % 4 || !a.row_den) return false;
-  for (int k = 256; k <= 512; k *= 2) {
-    if (a.K % k) break;
-    const int z = a.K / k;
-    if (z == 1 || (a.part && (long)z * a.M * a.N <= a.part_floats)) { *kz = k; *Z = z; return true; }
-  }
-  return false;
+// Shapes of the row-block GEMM: Z K ranges (blocks along z), KW 4-wave groups
+// per block and NCH 256-wide register chunks per group, Z * KW * NCH * 256 = K.
+struct RowsPlan { int Z, KW, NCH; };
+
+// (KW, NCH) pairs with an instantiation of rows_gemm_kernel: four groups hold
+// one chunk each (128 registers per lane at 16 waves per CU), two groups up
+// to 4, one group up to 12.
+static bool rows_inst(int kw, int nch) {
+  if (kw == 4) return nch == 1;
+  if (kw == 2) return nch == 1 || nch == 2 || nch == 3 || nch == 4;
+  return kw == 1 && (nch == 1 || nch == 2 || nch == 3 || nch == 4 || nch == 6 || nch == 8 || nch == 12);
 }
 
-template <int KZ>
-static hipError_t launch_splitk_k(const LinearArgs& a, int Z, hipStream_t s) {
-  dim3 grid((a.N + SG_T - 1) / SG_T, (a.M + SG_T - 1) / SG_T, Z);
-  if (a.gain) hipLaunchKernelGGL((splitk_kernel<KZ, true>), grid, dim3(NT), 0, s, a, a.row_den);
-  else hipLaunchKernelGGL((splitk_kernel<KZ, false>), grid, dim3(NT), 0, s, a, a.row_den);
+// One K range (no reduce launch, the K groups of a block share the work) when
+// the output tiles alone give ROWS_DIRECT_TILES blocks; else single-group
+// blocks over the fewest K ranges that give about 256 blocks, limited by the
+// partial-sum space.
+static bool rows_plan(const LinearArgs& a, RowsPlan* pl) {
+  if (a.wdtype != DT_BF16 || a.M < 17 || a.M > 128 || a.K % SG_CH || a.N % 4 || a.ldx % 4) return false;
+  const long tiles = (long)((a.N + SG_T - 1) / SG_T) * ((a.M + SG_T - 1) / SG_T);
+  const int chunks = a.K / SG_CH;
+  if (tiles >= ROWS_DIRECT_TILES)
+    for (int kw = 4; kw >= 1; kw /= 2)
+      if (chunks % kw == 0 && rows_inst(kw, chunks / kw)) { *pl = {1, kw, chunks / kw}; return true; }
+  auto fits = [&](int z) {
+    return chunks % z == 0 && rows_inst(1, chunks / z) &&
+           (z == 1 || (a.part && (long)z * a.M * a.N + (long)z * a.M <= a.part_floats));
+  };
+  int z = 0;
+  for (int c = 1; !z && c <= chunks; ++c)
+    if (fits(c) && (tiles * c >= 256 || c == chunks)) z = c;
+  for (int c = chunks; !z && c >= 1; --c)
+    if (fits(c)) z = c;
+  if (!z) return false;
+  *pl = {z, 1, chunks / z};
+  return true;
+}
+
+template <bool NORM, int KW>
+static hipError_t launch_rows_n(const LinearArgs& a, int nch, dim3 grid, hipStream_t s) {
+  const dim3 block(NT * KW);
+  switch (nch) {
+    case 1: hipLaunchKernelGGL((rows_gemm_kernel<NORM, 1, KW>), grid, block, 0, s, a); break;
+    case 2: if constexpr (KW <= 2) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 2, KW>), grid, block, 0, s, a); break; }
+            return hipErrorInvalidValue;
+    case 3: if constexpr (KW <= 2) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 3, KW>), grid, block, 0, s, a); break; }
+            return hipErrorInvalidValue;
+    case 4: if constexpr (KW <= 2) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 4, KW>), grid, block, 0, s, a); break; }
+            return hipErrorInvalidValue;
+    case 6: if constexpr (KW == 1) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 6, KW>), grid, block, 0, s, a); break; }
+            return hipErrorInvalidValue;
+    case 8: if constexpr (KW == 1) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 8, KW>), grid, block, 0, s, a); break; }
+            return hipErrorInvalidValue;
+    case 12: if constexpr (KW == 1) { hipLaunchKernelGGL((rows_gemm_kernel<NORM, 12, KW>), grid, block, 0, s, a); break; }
+             return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-static hipError_t launch_splitk(const LinearArgs& a, int kz, int Z, hipStream_t s) {
-  if (a.gain) {
-    hipLaunchKernelGGL(row_norm_kernel, dim3(a.M), dim3(NT), 0, s, a, a.row_den);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = kz == 256 ? launch_splitk_k<256>(a, Z, s) : launch_splitk_k<512>(a, Z, s);
-  if (e != hipSuccess || Z == 1) return e;
+template <bool NORM>
+static hipError_t launch_rows_g(const LinearArgs& a, const RowsPlan& pl, dim3 grid, hipStream_t s) {
+  if (pl.KW == 4) return launch_rows_n<NORM, 4>(a, pl.NCH, grid, s);
+  if (pl.KW == 2) return launch_rows_n<NORM, 2>(a, pl.NCH, grid, s);
+  return launch_rows_n<NORM, 1>(a, pl.NCH, grid, s);
+}
+
+static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream_t s) {
+  dim3 grid((a.N + SG_T - 1) / SG_T, (a.M + SG_T - 1) / SG_T, pl.Z);
+  hipError_t e = a.gain ? launch_rows_g<true>(a, pl, grid, s) : launch_rows_g<false>(a, pl, grid, s);
+  if (e != hipSuccess || pl.Z == 1) return e;
   const long threads = (long)a.M * (a.N / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, s, a, Z);
+  hipLaunchKernelGGL(rows_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, s, a, pl.Z);
   return hipGetLastError();
 }
 
@@ -1039,10 +1183,10 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   }
   // a few more rows of bf16 weights: weight-streaming MFMA kernel
   if (skinny_fits(a)) return launch_skinny(a, s);
-  // up to 128 rows: split-K MFMA GEMM
+  // up to 128 rows: row-block MFMA GEMM
   {
-    int kz, Z;
-    if (splitk_plan(a, &kz, &Z)) return launch_splitk(a, kz, Z, s);
+    RowsPlan pl;
+    if (rows_plan(a, &pl)) return launch_rows(a, pl, s);
   }
   // many rows of bf16 weights: matrix-core GEMM (needs K % 32 == 0 and row scratch)
   if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)

@@ -233,8 +233,8 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
  *   scratch device float [scratch_floats] or NULL: with bf16 weights it lets
  *   the frame's matrix-core kernels run: at least M floats (row RMS
  *   denominators) enable the tiled MFMA GEMM; beyond the first M rounded up
- *   to 64 floats, space for the split-K partial sums ((K / 256) * M * N
- *   floats, or half of that) enables the split-K GEMM for 17..128 rows.
+ *   to 64 floats, space for K-range partial sums (up to (K / 256) * M * (N + 1)
+ *   floats) lets the row-block MFMA GEMM for 17..128 rows split K.
  *   reps >= 1 launches (for timing). */
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K,
                           const float* X, int32_t M, const float* gain, float eps, int32_t epilogue,
