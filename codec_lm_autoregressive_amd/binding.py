@@ -86,7 +86,8 @@ def lib():
             "qt_debug_talker_logits": ([vp, vp], i32),
             "qt_debug_select": ([vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, C.POINTER(Sampling), u64, i32,
                                  i32, vp, vp, vp], i32),
-            "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32], i32),
+            "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
+                                 C.c_int64], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -273,13 +274,19 @@ class Engine:
 
 
 def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", reps=1, stream=None,
-                 matrix_cores=True):
+                 matrix_cores=True, copies=1):
     """Y = op(W · norm(X)) on the device (torch tensors: W int16 bf16 bits or float32).
 
     matrix_cores: give the library its row and split-K scratch, so bf16
-    weights with many rows take the MFMA kernels as in the frame."""
+    weights with many rows take the MFMA kernels as in the frame.
+    copies: W may hold [copies, N, K] stacked weight copies; launch i of the
+    reps uses copy i % copies (timing from HBM instead of a cache)."""
     import torch
-    N, K = W.shape
+    if W.dim() == 3:
+        copies, N, K = W.shape
+    else:
+        N, K = W.shape
+        copies = 1
     M = X.shape[0]
     if Y is None:
         Y = torch.zeros((M, N // 2 if epilogue == 2 else N), dtype=torch.float32, device=X.device)
@@ -288,7 +295,7 @@ def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", r
     s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
     _check(lib().qt_debug_linear(C.c_void_p(s), QT_DTYPE_BF16 if wdtype == "bf16" else QT_DTYPE_F32,
                                  _ptr(W), N, K, _ptr(X), M, _ptr(gain), eps, epilogue, _ptr(Y), _ptr(scratch),
-                                 n_scratch if matrix_cores else 0, reps))
+                                 n_scratch if matrix_cores else 0, reps, copies, N * K * W.element_size()))
     return Y
 
 

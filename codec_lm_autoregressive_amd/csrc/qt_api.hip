@@ -928,7 +928,7 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
 
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
                           int32_t M, const float* gain, float eps, int32_t epilogue, float* Y, float* scratch,
-                          int64_t scratch_floats, int32_t reps) {
+                          int64_t scratch_floats, int32_t reps, int32_t w_copies, int64_t w_copy_stride) {
   if (wdtype != QT_DTYPE_F32 && wdtype != QT_DTYPE_BF16) { set_err(g_err, "bad wdtype"); return QT_E_INVALID; }
   if (!W || !X || !Y) { set_err(g_err, "W, X and Y must not be NULL"); return QT_E_INVALID; }
   if (N < 1 || K < 8 || K % 8 || M < 1 || reps < 1 || epilogue < 0 || epilogue > 2 || (epilogue == 2 && N % 2)) {
@@ -944,7 +944,12 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
     a.row_den = scratch;
     if (scratch_floats > den) { a.part = scratch + den; a.part_floats = scratch_floats - den; }
   }
+  if (w_copies < 1 || (w_copies > 1 && w_copy_stride < (int64_t)N * K * (wdtype == QT_DTYPE_BF16 ? 2 : 4))) {
+    set_err(g_err, "w_copies must be >= 1 and copies must not overlap");
+    return QT_E_INVALID;
+  }
   for (int i = 0; i < reps; ++i) {
+    a.W = (const char*)W + (long)(i % w_copies) * w_copy_stride;
     hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
     if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   }

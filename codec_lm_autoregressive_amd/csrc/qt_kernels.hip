@@ -22,7 +22,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int NT = 256;  // threads per block for every kernel here
 constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use the matrix cores
 #ifndef ROWS_DIRECT_TILES
-#define ROWS_DIRECT_TILES 64       // output tiles from which the row-block GEMM runs without K ranges
+#define ROWS_DIRECT_TILES 192      // output tiles from which the row-block GEMM runs without K ranges
 #endif
 
 // Weight rows are streamed once per pass. QT_WEIGHT_NT selects nontemporal
@@ -498,9 +498,13 @@ template <typename WT>
 static bool try_gemv(const LinearArgs& a, hipStream_t s, hipError_t* err) {
   constexpr int EPC = 16 / sizeof(WT);
   if (a.M > 2 || a.K % EPC) return false;
-  const int R = (a.epi == EPI_SWIGLU || a.N >= 4096) ? 2 : 1;
+  // Wide outputs: two rows per wave and at least 256 blocks; narrow ones
+  // (1024 rows): one row per wave and at least 768 blocks (measured with the
+  // weights streamed from HBM).
+  const bool wide = a.epi == EPI_SWIGLU || a.N >= 2048;
+  const int R = wide ? 2 : 1, min_blocks = wide ? 256 : 768;
   int ks = 1;
-  while (ks < 4 && a.N / (4 / ks * R) < 768) ks *= 2;   // enough blocks to cover the chip
+  while (ks < 4 && a.N / (4 / ks * R) < min_blocks) ks *= 2;
   const int per = ks * 64 * EPC;
   const int nc = (a.K + per - 1) / per;
   if (nc > 4) return false;

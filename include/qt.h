@@ -235,10 +235,14 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
  *   denominators) enable the tiled MFMA GEMM; beyond the first M rounded up
  *   to 64 floats, space for K-range partial sums (up to (K / 256) * M * (N + 1)
  *   floats) lets the row-block MFMA GEMM for 17..128 rows split K.
- *   reps >= 1 launches (for timing). */
+ *   reps >= 1 launches (for timing); launch i uses the weight copy
+ *   W + (i % w_copies) * w_copy_stride bytes (w_copies >= 1; copies of at
+ *   least N * K elements each, so timed launches can stream from HBM rather
+ *   than from a cache that holds one copy). */
 qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K,
                           const float* X, int32_t M, const float* gain, float eps, int32_t epilogue,
-                          float* Y, float* scratch, int64_t scratch_floats, int32_t reps);
+                          float* Y, float* scratch, int64_t scratch_floats, int32_t reps,
+                          int32_t w_copies, int64_t w_copy_stride);
 
 #ifdef __cplusplus
 }

@@ -122,9 +122,9 @@ def test_null_ctx_calls_rejected():
 def test_debug_entry_points_validate_before_launch():
     L = binding.lib()
     # bad shapes are rejected before any device pointer is touched
-    assert L.qt_debug_linear(None, 1, None, 10, 7, None, 1, None, 1e-6, 0, None, None, 0, 1) == binding.QT_E_INVALID
+    assert L.qt_debug_linear(None, 1, None, 10, 7, None, 1, None, 1e-6, 0, None, None, 0, 1, 1, 0) == binding.QT_E_INVALID
     assert L.qt_debug_linear(None, 1, C.c_void_p(16), 10, 12, C.c_void_p(16), 1, None, 1e-6, 0,
-                             C.c_void_p(16), None, 0, 1) == binding.QT_E_INVALID  # K not a multiple of 8
+                             C.c_void_p(16), None, 0, 1, 1, 0) == binding.QT_E_INVALID  # K not a multiple of 8
     sm = binding.sampling(dict(synth.SAMPLING, temperature=0.0))
     assert L.qt_debug_select(None, 1, 3072, C.c_void_p(16), None, None, None, 1, 2150, 2048, 3072, C.byref(sm), 0,
                              0, 0, C.c_void_p(16), None, C.c_void_p(16)) == binding.QT_E_INVALID

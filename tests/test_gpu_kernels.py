@@ -72,6 +72,22 @@ def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     assert np.max(np.abs(got - ref)) / scale < 2e-5, (np.max(np.abs(got - ref)), scale)
 
 
+def test_linear_weight_copies_rotate():
+    """qt_debug_linear's timing mode: launch i reads weight copy i % copies."""
+    torch = _torch()
+    g = np.random.default_rng(3)
+    N, K, M = 512, 1024, 1
+    W = [synth.bf16_round((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in range(2)]
+    X = g.standard_normal((M, K)).astype(np.float32)
+    Ws = torch.stack([binding.to_device_weight(w, "bf16") for w in W]).contiguous()
+    Xd = torch.from_numpy(X).cuda()
+    for reps, last in [(3, 0), (4, 1)]:
+        Yd = binding.debug_linear(Ws, Xd, None, 1e-6, 0, reps=reps)
+        torch.cuda.synchronize()
+        ref = X.astype(np.float64) @ W[last].astype(np.float64).T
+        assert np.max(np.abs(Yd.cpu().numpy() - ref)) < 1e-4 * np.max(np.abs(ref))
+
+
 CFG = dict(eos_id=2150, suppress_begin=2048, suppress_end=3072)
 
 
