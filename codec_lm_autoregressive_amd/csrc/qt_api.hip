@@ -331,8 +331,10 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 }
 
 // ---- the decoder stack over M tokens
+// pass0: the code predictor's 2-token pass (row r's tokens are activation rows
+// 2r and 2r + 1 at positions 0 and 1).
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
-                     int pos_base, hipStream_t s, bool prefill = false, bool single_token = false) {
+                     int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -366,6 +368,18 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
       HIPCK(launch_attention(t, s));
       t.mode = ATT_ATTEND;
       HIPCK(launch_attention(t, s));
+    } else if (pass0 && d.d <= 128) {
+      // token 0 of every row (position 0), then token 1 (position 1), which
+      // attends to the key and value the first launch wrote
+      t.mode = ATT_WRITE_ATTEND;
+      t.single_token = 1;
+      t.tok_stride = 2;
+      t.row_pos = nullptr;
+      for (int tok = 0; tok < 2; ++tok) {
+        t.tok_off = tok;
+        t.pos_base = tok;
+        HIPCK(launch_attention(t, s));
+      }
     } else {
       t.mode = ATT_WRITE_ATTEND;
       t.single_token = single_token;
@@ -435,7 +449,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   for (int st = 0; st < 15; ++st) {
     const int M = st == 0 ? 2 * B : B;
     if (proj) { pa.M = M; HIPCK(launch_linear(pa, s)); }
-    if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s)); }
+    if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s, false, false, true)); }
     else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true)); }
     // head st on the last token of each row
     LinearArgs ha{};

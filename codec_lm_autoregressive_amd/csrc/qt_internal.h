@@ -37,6 +37,8 @@ enum AttnMode { ATT_WRITE_ATTEND = 0, ATT_WRITE = 1, ATT_ATTEND = 2 };
 struct AttnArgs {
   int mode;
   int single_token;                    // run i is token i of row i, at position pos_base + row_pos[i]
+  int tok_stride, tok_off;             // single_token with tok_stride > 0: row i's token is activation
+                                       // row i * tok_stride + tok_off (q/k/v in, attention out)
   const float* rope_rows;              // [rows][d]: cos | sin at each row's position, or nullptr
   const float* qkv; long ld_qkv;       // [T, (nq + 2 nkv) d]
   float* out; long ld_out;             // [T, nq d]

@@ -1482,7 +1482,9 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
   constexpr int NPV = KCH / KPP;
   static_assert(CPK <= 64 && 64 % CPK == 0 && KCH % KPP == 0, "cache row layout");
   const int g = blockIdx.x;
-  const int row = blockIdx.y;          // one token per row, token index = row
+  const int row = blockIdx.y;          // batch row (cache row)
+  // activation row of its token: the row itself, or row * tok_stride + tok_off
+  const long arow = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
   const int L = pos + 1;
@@ -1498,7 +1500,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
   KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
   const int ksub = tid % TPK, kkey = tid / TPK;
   const int vchunk = tid % CPK, vslot = tid / CPK;
-  const float* src = p.qkv + (long)row * p.ld_qkv;
+  const float* src = p.qkv + arow * p.ld_qkv;
   const int lastrow = p.max_pos - 1;
 
   // Row addresses do not depend on pos (only clamped to the cache), so these
@@ -1691,7 +1693,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) s += part[(w * G + hh) * D + dim];
-    p.out[(long)row * p.ld_out + (long)(g * G + hh) * D + dim] = s / l[hh];
+    p.out[arow * p.ld_out + (long)(g * G + hh) * D + dim] = s / l[hh];
   }
 }
 
@@ -1808,6 +1810,41 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     text = a.req->text; pad = a.req->pad; has_text = a.req->has_text;
   }
   const float* lg = a.logits + (long)r * a.ld;
+  const int jsel = (a.ctr ? *a.ctr : 0) + a.ctr_add;
+  int choice = 0;
+  if (!do_sample && !a.processed_out) {
+    // greedy: the non-finite check, the processors and the argmax (lowest
+    // id on ties) in one pass over the logits, one exchange between waves
+    const uint32_t* seen = a.seen + (long)r * a.seen_words;
+    const bool pen = a.processors && penalty != 1.0f;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff, badl = 0;
+    for (int i = tid; i < V; i += NT) {
+      float x = lg[i];
+      badl |= isnan(x) || x == INFINITY;
+      if (a.processors) {
+        if (pen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
+        if (i == a.eos && jsel < min_new) x = -INFINITY;
+        if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
+      }
+      better(bv, bi, x, i);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) better(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+    const int wbad = __any(badl);
+    const int lane = tid & 63, wv = tid >> 6;
+    if (lane == 0) { redf[wv] = bv; redi[wv] = bi; redi[4 + wv] = wbad; }
+    __syncthreads();
+    bv = redf[0]; bi = redi[0];
+    int bad = redi[4];
+#pragma unroll
+    for (int q = 1; q < NT / 64; ++q) { better(bv, bi, redf[q], redi[q]); bad |= redi[4 + q]; }
+    if (bad) {
+      if (tid == 0) atomicOr(a.status, ST_NONFINITE);
+    } else {
+      choice = bi < V ? bi : 0;   // every logit -inf cannot happen: EOS or codes survive
+    }
+  } else {
   int bad = 0;
   for (int i = tid; i < V; i += NT) {
     const float x = lg[i];
@@ -1815,7 +1852,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     v[i] = x;
   }
   bad = block_or(bad, redi);
-  const int jsel = (a.ctr ? *a.ctr : 0) + a.ctr_add;
   if (a.processors) {
     const uint32_t* seen = a.seen + (long)r * a.seen_words;
     const bool pen = penalty != 1.0f;
@@ -1831,7 +1867,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (a.processed_out)
     for (int i = tid; i < V; i += NT) a.processed_out[(long)r * V + i] = v[i];
 
-  int choice = 0;
   if (bad) {
     if (tid == 0) atomicOr(a.status, ST_NONFINITE);
   } else if (!do_sample) {
@@ -1908,16 +1943,23 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const int b0 = tid * chunk, b1 = min(V, b0 + chunk);
     int cnt = 0;
     for (int i = b0; i < b1; ++i) cnt += v[i] > 0.f;
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-      const int add = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+    // exclusive prefix of the counts in thread order: within the wave, then
+    // across the waves' totals
+    const int lane = tid & 63, wv = tid >> 6;
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
     }
-    const int ns = scan[NT - 1];
-    int o = scan[tid] - cnt;
+    if (lane == 63) scan[wv] = incl;
+    __syncthreads();
+    int ns = 0, o = incl - cnt;
+#pragma unroll
+    for (int q = 0; q < NT / 64; ++q) {
+      if (q < wv) o += scan[q];
+      ns += scan[q];
+    }
     for (int i = b0; i < b1; ++i)
       if (v[i] > 0.f) { cp[o] = v[i]; cid[o] = i; ++o; }
     __syncthreads();
@@ -1965,6 +2007,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     choice = block_argmax(bv, bi, redf, redi);
     if (choice >= V) choice = 0;
+  }
   }
 
   // commit
