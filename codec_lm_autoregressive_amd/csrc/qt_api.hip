@@ -353,8 +353,15 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     // q/k/v = W_qkv · RMSNorm(x)
     a.W = w.wqkv; a.N = d.qkv; a.K = d.H; a.X = x; a.ldx = d.H; a.M = M; a.gain = w.attn_norm;
     a.Y = ctx->qkv; a.ldy = d.qkv; a.epi = EPI_STORE;
+    // single-token decode attention adds split-K partial sums itself, so a
+    // split projection needs no reduce launch
+    const bool decode_attn = !prefill && (single_token || pass0) && d.d <= 128;
+    const int zq = decode_attn ? linear_split_ranges(a) : 1;
+    a.defer = zq > 1;
     HIPCK(launch_linear(a, s));
+    a.defer = 0;
     AttnArgs t{};
+    if (zq > 1) { t.part = ctx->part; t.part_z = zq; t.part_rows = M; t.part_k = d.H; t.part_eps = d.eps; }
     t.qkv = ctx->qkv; t.ld_qkv = d.qkv; t.out = ctx->attn; t.ld_out = d.nqd;
     t.q_gain = w.q_norm; t.k_gain = w.k_norm; t.eps = d.eps; t.scale = (float)(1.0 / std::sqrt((double)d.d));
     t.cos = talker ? ctx->cos_t : ctx->cos_p; t.sin = talker ? ctx->sin_t : ctx->sin_p;

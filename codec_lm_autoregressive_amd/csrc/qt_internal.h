@@ -24,8 +24,13 @@ struct LinearArgs {
   float* norm_out; long ld_norm;       // optional copy of the normalised X
   float* row_den;                      // [M] scratch for the matrix-core path (nullptr: not used)
   float* part; long part_floats;       // split-K partial sums for 17..128 rows (nullptr: not used)
+  int defer;                           // split K: leave the partial sums for the consumer (no reduce)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+// K ranges the launch of a would split into (partial sums in a.part: range z,
+// row m, column n at part[(z * M + m) * N + n]; with a gain the row sums of
+// squares follow at part[Z * M * N + z * M + m]); 1 when it writes Y directly.
+int linear_split_ranges(const LinearArgs& a);
 
 // One contiguous run of tokens of one batch row: row, first token (row of the
 // activation arrays), token count, first position (before pos_base / row_pos).
@@ -48,6 +53,11 @@ struct AttnArgs {
   long row_stride; int max_pos;
   const Run* runs; int n_runs; const int* row_pos; int pos_base;
   int nq, nkv, d;
+  // single-token decode: q/k/v as split-K partial sums of the RMSNorm'd
+  // projection instead of qkv (part_z > 0): value = (sum over z of
+  // part[(z * part_rows + row) * ld_qkv + col]) / rms(row), the rms from the
+  // partial row sums of squares of part_k inputs and part_eps
+  const float* part; int part_z; int part_rows; int part_k; float part_eps;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

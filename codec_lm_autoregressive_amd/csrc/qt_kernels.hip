@@ -494,6 +494,16 @@ static hipError_t launch_gemv_ks(const LinearArgs& a, int ks, int nc, hipStream_
 }
 
 // Register path when the batch is small and K fits in <= 4 chunks per lane.
+static bool gemv_fits(const LinearArgs& a) {
+  const int epc = a.wdtype == DT_BF16 ? 8 : 4;
+  if (a.M > 2 || a.K % epc) return false;
+  const bool wide = a.epi == EPI_SWIGLU || a.N >= 2048;
+  const int R = wide ? 2 : 1, min_blocks = wide ? 256 : 768;
+  int ks = 1;
+  while (ks < 4 && a.N / (4 / ks * R) < min_blocks) ks *= 2;
+  return (a.K + ks * 64 * epc - 1) / (ks * 64 * epc) <= 4;
+}
+
 template <typename WT>
 static bool try_gemv(const LinearArgs& a, hipStream_t s, hipError_t* err) {
   constexpr int EPC = 16 / sizeof(WT);
@@ -1172,10 +1182,16 @@ static hipError_t launch_rows_g(const LinearArgs& a, const RowsPlan& pl, dim3 gr
 static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream_t s) {
   dim3 grid((a.N + SG_T - 1) / SG_T, (a.M + SG_T - 1) / SG_T, pl.Z);
   hipError_t e = a.gain ? launch_rows_g<true>(a, pl, grid, s) : launch_rows_g<false>(a, pl, grid, s);
-  if (e != hipSuccess || pl.Z == 1) return e;
+  if (e != hipSuccess || pl.Z == 1 || a.defer) return e;
   const long threads = (long)a.M * (a.N / 4);
   hipLaunchKernelGGL(rows_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, s, a, pl.Z);
   return hipGetLastError();
+}
+
+int linear_split_ranges(const LinearArgs& a) {
+  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a)) return 1;
+  RowsPlan pl;
+  return rows_plan(a, &pl) ? pl.Z : 1;
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
@@ -1502,6 +1518,21 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
   const int vchunk = tid % CPK, vslot = tid / CPK;
   const float* src = p.qkv + arow * p.ld_qkv;
   const int lastrow = p.max_pos - 1;
+  // q/k/v value at column col of this token's projection row: the stored row,
+  // or the sum of the split-K partials (ranges in order) times 1 / rms
+  float prs = 1.f;
+  if (p.part_z > 0) {
+    const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
+    float ssum = pss[arow];
+    for (int z = 1; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow];
+    prs = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
+  }
+  auto qkv_at = [&](long col) -> float {
+    if (p.part_z <= 0) return src[col];
+    float v = p.part[arow * p.ld_qkv + col];
+    for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + arow) * p.ld_qkv + col];
+    return v * prs;
+  };
 
   // Row addresses do not depend on pos (only clamped to the cache), so these
   // loads leave together with this token's loads; rows >= pos may hold
@@ -1544,7 +1575,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
 #pragma unroll
     for (int c = 0; c < EPN; ++c) {
       const int e = lane + 64 * c;
-      vals[c] = e < D ? x[e] : 0.f;
+      vals[c] = e < D ? qkv_at((x - src) + e) : 0.f;
       gv[c] = e < D ? gain[e] : 0.f;
       ss += vals[c] * vals[c];
     }
@@ -1557,7 +1588,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
     }
   }
   for (int e = tid; e < D; e += NT) {
-    const float vvv = src[(long)(p.nq + p.nkv) * D + (long)g * D + e];
+    const float vvv = qkv_at((long)(p.nq + p.nkv) * D + (long)g * D + e);
     st_elem<KVT>(vc, (long)pos * D + e, vvv);
     vcur[e] = kv_round<KVT>(vvv);
   }
