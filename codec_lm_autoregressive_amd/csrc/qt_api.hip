@@ -369,6 +369,11 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     t.row_stride = row_stride; t.max_pos = maxpos;
     t.runs = runs; t.n_runs = n_runs; t.row_pos = row_pos; t.pos_base = pos_base;
     t.nq = d.nq; t.nkv = d.nkv; t.d = d.d;
+    // x += W_o · attn
+    LinearArgs ao = a;
+    ao.W = w.wo; ao.N = d.H; ao.K = d.nqd; ao.X = ctx->attn; ao.ldx = d.nqd; ao.gain = nullptr;
+    ao.Y = x; ao.ldy = d.H; ao.epi = EPI_RESIDUAL;
+    bool fused = false;
     if (prefill) {
       // every key of the chunk first, then one block per (kv head, query token)
       t.mode = ATT_WRITE;
@@ -376,27 +381,29 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
       t.mode = ATT_ATTEND;
       HIPCK(launch_attention(t, s));
     } else if (pass0 && d.d <= 128) {
-      // token 0 of every row (position 0), then token 1 (position 1), which
-      // attends to the key and value the first launch wrote
+      // tokens 0 and 1 of every row (positions 0 and 1); token 1 attends to
+      // token 0's key and value
       t.mode = ATT_WRITE_ATTEND;
       t.single_token = 1;
+      t.ntok = 2;
       t.tok_stride = 2;
+      t.tok_off = 0;
       t.row_pos = nullptr;
-      for (int tok = 0; tok < 2; ++tok) {
-        t.tok_off = tok;
-        t.pos_base = tok;
-        HIPCK(launch_attention(t, s));
-      }
+      t.pos_base = 0;
     } else {
       t.mode = ATT_WRITE_ATTEND;
       t.single_token = single_token;
       t.rope_rows = (single_token && talker) ? ctx->rope_rows : nullptr;
-      HIPCK(launch_attention(t, s));
     }
-    // x += W_o · attn
-    a.W = w.wo; a.N = d.H; a.K = d.nqd; a.X = ctx->attn; a.ldx = d.nqd; a.gain = nullptr;
-    a.Y = x; a.ldy = d.H; a.epi = EPI_RESIDUAL;
-    HIPCK(launch_linear(a, s));
+    if (!prefill) {
+      // the code predictor at one row: attention and o-projection in one launch
+      if (!talker) {
+        const hipError_t e = launch_attention_oproj(t, ao, s);
+        if (e != hipErrorNotSupported) { HIPCK(e); fused = true; }
+      }
+      if (!fused) HIPCK(launch_attention(t, s));
+    }
+    if (!fused) HIPCK(launch_linear(ao, s));
     // act = silu(W_g · RMSNorm(x)) * (W_u · RMSNorm(x))
     a.W = w.wgu; a.N = 2 * d.I; a.K = d.H; a.X = x; a.ldx = d.H; a.gain = w.mlp_norm;
     a.Y = ctx->act; a.ldy = d.I; a.epi = EPI_SWIGLU;

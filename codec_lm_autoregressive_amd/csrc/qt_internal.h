@@ -44,6 +44,8 @@ struct AttnArgs {
   int single_token;                    // run i is token i of row i, at position pos_base + row_pos[i]
   int tok_stride, tok_off;             // single_token with tok_stride > 0: row i's token is activation
                                        // row i * tok_stride + tok_off (q/k/v in, attention out)
+  int ntok;                            // single_token: new tokens per row (1, or 2 with tok_stride 2 and
+                                       // tok_off 0: activation rows 2 i, 2 i + 1 at pos_base, pos_base + 1)
   const float* rope_rows;              // [rows][d]: cos | sin at each row's position, or nullptr
   const float* qkv; long ld_qkv;       // [T, (nq + 2 nkv) d]
   float* out; long ld_out;             // [T, nq d]
@@ -60,6 +62,11 @@ struct AttnArgs {
   const float* part; int part_z; int part_rows; int part_k; float part_eps;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Single-token code-predictor attention (one batch row, <= 16 positions)
+// fused with the o-projection o (x += W_o . attention, o.X == a.out, bf16
+// weights, 16-bit cache). Returns hipErrorNotSupported, doing nothing, for
+// other shapes.
+hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStream_t s);
 
 // Per-request settings kept in device memory, so that one captured frame
 // graph serves every request of the same batch size.

@@ -1728,11 +1728,303 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
   }
 }
 
+// Decode attention for head_dim 128, one kernel launch for the NTOK new
+// tokens of every row (NTOK = 1: a talker or predictor step; NTOK = 2: the
+// predictor's two-token pass at positions 0 and 1). Block = (kv head, row).
+// Keys older than the first new token come from the cache in chunks of KCH
+// rows (large chunks when the grid is a single wave of blocks, small ones,
+// with fewer registers, when several blocks share a compute unit) whose
+// loads all leave at once (4 threads per key for the scores,
+// (16-byte column, key slot) threads for P·V); the new tokens' own keys and
+// values stay in LDS. Each thread keeps its own running softmax sums, so a
+// chunk costs one block-wide max exchange; slots, waves and the sums are
+// combined once at the end.
+template <typename KVT, int G, int NTOK, int KCH>
+__global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
+  constexpr int D = 128, HALF = 64;
+  constexpr int EPC = 16 / sizeof(KVT);      // cache elements per 16-byte chunk
+  constexpr int CPK = D / EPC;               // chunks per cache row
+  constexpr int TPK = 4;                     // threads per key (scores)
+  constexpr int CPT = CPK / TPK;             // chunks per thread (scores)
+  constexpr int KPR = NT / TPK;              // keys per score row
+  constexpr int SR = KCH / KPR;              // keys per thread (scores)
+  constexpr int VS = NT / CPK;               // key slots (P·V)
+  constexpr int NV = KCH / VS;               // keys per thread (P·V)
+  static_assert(KCH % KPR == 0 && KCH % VS == 0 && CPK <= 64, "layout");
+  const int g = blockIdx.x;
+  const int row = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ksub = tid % TPK, kkey = tid / TPK;
+  const int vchunk = tid % CPK, vslot = tid / CPK;
+  __shared__ __align__(16) float qs[NTOK][G][D];   // normalised, rotated q heads
+  __shared__ float knew[NTOK][D], vnew[NTOK][D];   // the new rows, as stored
+  __shared__ float pl[G][KCH];               // probabilities of the chunk
+  __shared__ float part[NT / 64][G][D];
+  __shared__ float red[2][NT / 64][G];
+  KVT* kc = (KVT*)p.kc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+
+  // Only keys older than the new tokens come from the cache (rows < pos0);
+  // groups of keys past them are neither loaded nor computed (the group
+  // tests are uniform across the block).
+  const int pos0 = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
+  u32x4 kr[SR][CPT], vr[NV];
+  auto load_k = [&](int c0) {
+#pragma unroll
+    for (int r = 0; r < SR; ++r) {
+      if (c0 + r * KPR >= pos0) break;
+      const int j = min(c0 + kkey + r * KPR, pos0 - 1);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) kr[r][c] = *(const u32x4*)(kc + (long)j * D + (ksub * CPT + c) * EPC);
+    }
+  };
+  auto load_v = [&](int c0) {
+#pragma unroll
+    for (int b = 0; b < NV; ++b) {
+      if (c0 + b * VS >= pos0) break;
+      const int j = min(c0 + vslot + b * VS, pos0 - 1);
+      vr[b] = *(const u32x4*)(vc + (long)j * D + vchunk * EPC);
+    }
+  };
+  load_k(0);
+  load_v(0);
+
+  // the new tokens: QK-RMSNorm + rope of q heads and k (one wave per vector;
+  // lane owns the rope pair (lane, lane + 64)), K/V rows to the cache and LDS
+  float prs[NTOK];
+  const long arow0 = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    prs[t] = 1.f;
+    if (p.part_z > 0) {
+      const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
+      float ssum = 0.f;
+      for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow0 + t];
+      prs[t] = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
+    }
+  }
+  auto qkv_at = [&](int t, long col) -> float {
+    const long ar = arow0 + t;
+    if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
+    float v = p.part[ar * p.ld_qkv + col];
+    for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
+    return v * prs[t];
+  };
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int pos = pos0 + t;
+    float cs, sn;
+    if (p.rope_rows) {
+      cs = p.rope_rows[(long)row * D + lane];
+      sn = p.rope_rows[(long)row * D + HALF + lane];
+    } else {
+      cs = p.cos[(long)pos * HALF + lane];
+      sn = p.sin[(long)pos * HALF + lane];
+    }
+    for (int v = wave; v <= G + 1; v += NT / 64) {
+      if (v == G + 1) {                       // value row, stored as is
+        const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
+        const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
+        st_elem<KVT>(vc, (long)pos * D + lane, x1);
+        st_elem<KVT>(vc, (long)pos * D + lane + HALF, x2);
+        vnew[t][lane] = kv_round<KVT>(x1);
+        vnew[t][lane + HALF] = kv_round<KVT>(x2);
+        continue;
+      }
+      const long col = v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D;
+      const float* gain = v < G ? p.q_gain : p.k_gain;
+      const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
+      const float g1 = gain[lane], g2 = gain[lane + HALF];
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float den = sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 / den * g1, y2 = x2 / den * g2;
+      const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
+      if (v < G) {
+        qs[t][v][lane] = o1;
+        qs[t][v][lane + HALF] = o2;
+      } else {
+        st_elem<KVT>(kc, (long)pos * D + lane, o1);
+        st_elem<KVT>(kc, (long)pos * D + lane + HALF, o2);
+        knew[t][lane] = kv_round<KVT>(o1);
+        knew[t][lane + HALF] = kv_round<KVT>(o2);
+      }
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int L = pos0 + t + 1;               // keys 0 .. pos0 + t
+    float m[G], l[G], acc[G][EPC];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+    }
+    if (t > 0 && pos0 > KCH) { load_k(0); load_v(0); }   // the registers hold the previous token's last chunk
+    for (int c0 = 0; c0 < L; c0 += KCH) {
+      float s[SR][G];
+#pragma unroll
+      for (int r = 0; r < SR; ++r) {
+        const int j = c0 + kkey + r * KPR;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s[r][hh] = -INFINITY;
+        if (c0 + r * KPR >= L) continue;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s[r][hh] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int e0 = (ksub * CPT + c) * EPC;
+          float x[EPC];
+          if (j >= pos0) {
+            const int jn = min(j - pos0, NTOK - 1);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) x[e] = knew[jn][e0 + e];
+          } else {
+            unpack_chunk<KVT>(kr[r][c], x);
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            const f32x4* q4 = (const f32x4*)(&qs[t][hh][e0]);
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4) {
+              const f32x4 q = q4[e / 4];
+              s[r][hh] = fmaf(q.x, x[e], s[r][hh]);
+              s[r][hh] = fmaf(q.y, x[e + 1], s[r][hh]);
+              s[r][hh] = fmaf(q.z, x[e + 2], s[r][hh]);
+              s[r][hh] = fmaf(q.w, x[e + 3], s[r][hh]);
+            }
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          s[r][hh] += __shfl_xor(s[r][hh], 1);
+          s[r][hh] += __shfl_xor(s[r][hh], 2);
+          s[r][hh] = j < L ? s[r][hh] * p.scale : -INFINITY;
+        }
+      }
+      const bool more = c0 + KCH < L;
+      if (more) load_k(c0 + KCH);              // next chunk's keys, behind this chunk's softmax
+      float mx[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float v = s[0][hh];
+#pragma unroll
+        for (int r = 1; r < SR; ++r) v = fmaxf(v, s[r][hh]);
+        mx[hh] = wave_max(v);
+      }
+      if (lane == 0)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) red[0][wave][hh] = mx[hh];
+      __syncthreads();
+      float corr[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float v = red[0][0][hh];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) v = fmaxf(v, red[0][w][hh]);
+        const float mnew = fmaxf(m[hh], v);
+        corr[hh] = expf(m[hh] - mnew);
+        m[hh] = mnew;
+        float lsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < SR; ++r) {
+          const float e = expf(s[r][hh] - mnew);
+          if (ksub == 0) pl[hh][kkey + r * KPR] = e;
+          lsum += e;
+        }
+        l[hh] = l[hh] * corr[hh] + (ksub == 0 ? lsum : 0.f);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[hh][e] *= corr[hh];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < NV; ++b) {
+        const int jl = vslot + b * VS, j = c0 + jl;
+        if (c0 + b * VS >= L) break;
+        float x[EPC];
+        if (j >= pos0) {
+          const int jn = min(j - pos0, NTOK - 1);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[e] = vnew[jn][vchunk * EPC + e];
+        } else {
+          unpack_chunk<KVT>(vr[b], x);
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pw = pl[hh][jl];         // 0 past the last key
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pw, x[e], acc[hh][e]);
+        }
+      }
+      if (more) load_v(c0 + KCH);
+      __syncthreads();                         // pl and red are rewritten next
+    }
+    // combine: key slots (lanes CPK apart), then waves; the softmax sums too
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        float v = acc[hh][e];
+#pragma unroll
+        for (int o = CPK; o < 64; o <<= 1) v += __shfl_xor(v, o);
+        acc[hh][e] = v;
+      }
+      l[hh] = wave_sum(l[hh]);
+    }
+    if (lane < CPK)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) part[wave][hh][vchunk * EPC + e] = acc[hh][e];
+    if (lane == 0)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) red[1][wave][hh] = l[hh];
+    __syncthreads();
+    for (int e = tid; e < G * D; e += NT) {
+      const int hh = e / D, dim = e % D;
+      float v = 0.f, ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) { v += part[w][hh][dim]; ls += red[1][w][hh]; }
+      p.out[(arow0 + t) * p.ld_out + (long)(g * G + hh) * D + dim] = v / ls;
+    }
+    if (t + 1 < NTOK) __syncthreads();
+  }
+}
+
 template <typename KVT, int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
   constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
   const size_t lds = ((size_t)(2 * G + 1) * D + 2 * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  if constexpr (D == 128 && G <= 4) {
+    const int nt = a.ntok > 0 ? a.ntok : 1;
+    if (a.single_token && a.mode == ATT_WRITE_ATTEND && (nt == 1 || (nt == 2 && a.tok_stride == 2 && a.tok_off == 0))) {
+      constexpr int big = 512 / sizeof(KVT), small = 64;
+      const dim3 grid(a.nkv, a.n_runs);
+      const bool one_wave = (long)a.nkv * a.n_runs <= 256;   // at most one block per compute unit
+      if (nt == 2) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 2, small>), grid, dim3(NT), 0, s, a);
+      else if (one_wave) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, big>), grid, dim3(NT), 0, s, a);
+      else hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small>), grid, dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (D <= 128) {   // wider heads use the general kernel (register budget)
+    if (a.single_token && a.mode == ATT_WRITE_ATTEND && a.ntok == 2) {
+      // two tokens per row (activation rows 2 r and 2 r + 1): token 0, then
+      // token 1, which attends to the key and value the first launch wrote
+      AttnArgs b = a;
+      b.ntok = 1;
+      b.tok_stride = 2;
+      for (int t = 0; t < 2; ++t) {
+        b.tok_off = t;
+        b.pos_base = a.pos_base + t;
+        hipError_t e = launch_attention_dg<KVT, D, G>(b, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
     if (a.single_token && a.mode == ATT_WRITE_ATTEND) {
       static size_t have1 = 0;
       hipError_t e = ensure_lds((const void*)attn_decode_kernel<KVT, D, G>, lds, &have1);
@@ -1776,6 +2068,232 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.kvdtype == DT_BF16) return launch_attention_t<uint16_t>(a, s);
   if (a.kvdtype == DT_F16) return launch_attention_t<_Float16>(a, s);
   return launch_attention_t<float>(a, s);
+}
+
+// ---------------------------------------------------------------- predictor attention + o-projection
+// The code predictor at batch 1 attends over at most 16 positions, so every
+// block of the o-projection recomputes the whole attention (one wave per kv
+// head) while its rows of W_o are in flight, then applies them: one launch
+// instead of two. NTOK new tokens (1: a step, 2: the two-token pass at
+// positions 0 and 1) sit in activation rows 0 .. NTOK-1. Block b owns output
+// rows [b RO, (b + 1) RO); block 0 also writes the new K/V rows.
+// Scores: lane = (key j, quarter of the head dims); P·V: lane = (8-dim
+// column chunk, key slot j mod 4).
+template <typename KVT, int NKV, int G, int RO, int NTOK>
+__global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, LinearArgs o) {
+  constexpr int D = 128, HALF = 64, NQ = NKV * G, KO = NQ * D;
+  constexpr int EPC = 8;                       // 16-bit cache elements per 16-byte chunk
+  constexpr int RW = RO / NKV;                 // o rows per wave
+  constexpr int KC = KO / 512;                 // 16-byte weight chunks per lane and row
+  static_assert(sizeof(KVT) == 2 && RO % NKV == 0 && KO % 512 == 0, "layout");
+  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * RO + g * RW;
+  __shared__ __align__(16) float qs[NKV][NTOK][G][D];
+  __shared__ __align__(16) float knew[NKV][NTOK][D];
+  __shared__ __align__(16) float vnew[NKV][NTOK][D];
+  __shared__ __align__(16) float att[NTOK][KO];
+
+  // Loads leave in the order they are needed (the vector-memory counter
+  // drains in issue order): this wave's q/k/v values, gains and rope rows,
+  // then the cached K/V rows (unconditional, clamped rows; rows past the
+  // context are never used), then this wave's rows of W_o, which stream in
+  // behind the attention.
+  const int pos0 = p.pos_base;                 // keys 0 .. pos0 - 1 are cached
+  KVT* kc = (KVT*)p.kc + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)g * p.max_pos * D;
+  const int sj = lane >> 2, sq = lane & 3;     // score role: key, quarter
+  const int vch = lane & 15, vsl = lane >> 4;  // P·V role: column chunk, key slot
+  float xin[NTOK][G + 2][2], cs[NTOK], sn[NTOK];
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const float* src = p.qkv + (long)t * p.ld_qkv;
+#pragma unroll
+    for (int v = 0; v < G + 2; ++v) {
+      const float* x = src + (v < G ? (long)(g * G + v) * D : (long)(NQ + (v - G) * NKV) * D + (long)g * D);
+      xin[t][v][0] = x[lane];
+      xin[t][v][1] = x[lane + HALF];
+    }
+    cs[t] = p.cos[(long)(pos0 + t) * HALF + lane];
+    sn[t] = p.sin[(long)(pos0 + t) * HALF + lane];
+  }
+  const float gq1 = p.q_gain[lane], gq2 = p.q_gain[lane + HALF];
+  const float gk1 = p.k_gain[lane], gk2 = p.k_gain[lane + HALF];
+  const int jmax = max(pos0 - 1, 0);
+  u32x4 kr[4], vr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kr[c] = *(const u32x4*)(kc + (long)min(sj, jmax) * D + sq * 32 + c * EPC);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vr[i] = *(const u32x4*)(vc + (long)min(vsl + 4 * i, jmax) * D + vch * EPC);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* W = (const uint16_t*)o.W;
+  u32x4 w[RW][KC];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) w[r][c] = ld_weight(W + (long)(n0 + r) * KO + c * 512 + lane * 8);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // new tokens: QK-RMSNorm and rope (lane owns the pair (lane, lane + 64))
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int pos = pos0 + t;
+#pragma unroll
+    for (int v = 0; v <= G; ++v) {
+      const float x1 = xin[t][v][0], x2 = xin[t][v][1];
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float den = sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 / den * (v < G ? gq1 : gk1), y2 = x2 / den * (v < G ? gq2 : gk2);
+      const float o1 = y1 * cs[t] - y2 * sn[t], o2 = y2 * cs[t] + y1 * sn[t];
+      if (v < G) {
+        qs[g][t][v][lane] = o1;
+        qs[g][t][v][lane + HALF] = o2;
+      } else {
+        knew[g][t][lane] = kv_round<KVT>(o1);
+        knew[g][t][lane + HALF] = kv_round<KVT>(o2);
+        if (blockIdx.x == 0) {
+          st_elem<KVT>(kc, (long)pos * D + lane, o1);
+          st_elem<KVT>(kc, (long)pos * D + lane + HALF, o2);
+        }
+      }
+    }
+    const float v1 = xin[t][G + 1][0], v2 = xin[t][G + 1][1];
+    vnew[g][t][lane] = kv_round<KVT>(v1);
+    vnew[g][t][lane + HALF] = kv_round<KVT>(v2);
+    if (blockIdx.x == 0) {
+      st_elem<KVT>(vc, (long)pos * D + lane, v1);
+      st_elem<KVT>(vc, (long)pos * D + lane + HALF, v2);
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int L = pos0 + t + 1;
+    float s[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
+    if (sj < L) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e0 = sq * 32 + c * EPC;
+        float x[EPC];
+        if (sj >= pos0) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[e] = knew[g][sj - pos0][e0 + e];
+        } else {
+          unpack_chunk<KVT>(kr[c], x);
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const f32x4* q4 = (const f32x4*)(&qs[g][t][hh][e0]);
+#pragma unroll
+          for (int e = 0; e < EPC; e += 4) {
+            const f32x4 q = q4[e / 4];
+            s[hh] = fmaf(q.x, x[e], s[hh]);
+            s[hh] = fmaf(q.y, x[e + 1], s[hh]);
+            s[hh] = fmaf(q.z, x[e + 2], s[hh]);
+            s[hh] = fmaf(q.w, x[e + 3], s[hh]);
+          }
+        }
+      }
+    }
+    float pr[G], l[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      s[hh] += dpp_f<0xb1, 0xf>(s[hh], 0.f);   // quad_perm [1,0,3,2]
+      s[hh] += dpp_f<0x4e, 0xf>(s[hh], 0.f);   // quad_perm [2,3,0,1]
+      s[hh] = sj < L ? s[hh] * p.scale : -INFINITY;
+      const float mx = wave_max(s[hh]);
+      pr[hh] = expf(s[hh] - mx);
+      l[hh] = wave_sum(sq == 0 ? pr[hh] : 0.f);
+    }
+    float acc[G][EPC];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = vsl + 4 * i;
+      float pw[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) pw[hh] = __shfl(pr[hh], (j & 15) * 4);
+      if (j < L) {
+        float x[EPC];
+        if (j >= pos0) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[e] = vnew[g][j - pos0][vch * EPC + e];
+        } else {
+          unpack_chunk<KVT>(vr[i], x);
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pw[hh], x[e], acc[hh][e]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        float v = acc[hh][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[hh][e] = v;
+      }
+    if (vsl == 0)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) att[t][(g * G + hh) * D + vch * EPC + e] = acc[hh][e] / l[hh];
+  }
+  __syncthreads();
+
+  // o-projection rows of this wave, residual added in place
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const f32x4* x4 = (const f32x4*)(&att[t][c * 512 + lane * 8]);
+        const f32x4 xa = x4[0], xb = x4[1];
+        const u32x4 q = w[r][c];
+        a = fmaf(bf_lo(q.x), xa.x, a); a = fmaf(bf_hi(q.x), xa.y, a);
+        a = fmaf(bf_lo(q.y), xa.z, a); a = fmaf(bf_hi(q.y), xa.w, a);
+        a = fmaf(bf_lo(q.z), xb.x, a); a = fmaf(bf_hi(q.z), xb.y, a);
+        a = fmaf(bf_lo(q.w), xb.z, a); a = fmaf(bf_hi(q.w), xb.w, a);
+      }
+      a = wave_sum(a);
+      if (lane == 0) {
+        float* y = o.Y + (long)t * o.ldy + n0 + r;
+        *y = *y + a;
+      }
+    }
+  }
+}
+
+template <typename KVT>
+static hipError_t launch_pred_attn_o_t(const AttnArgs& a, const LinearArgs& o, hipStream_t s) {
+  constexpr int RO = 16;
+  hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStream_t s) {
+  // one new token per launch: for the two-token pass the separate kernels are as fast
+  const int nt = a.ntok > 0 ? a.ntok : 1;
+  const bool ok = nt == 1 && a.single_token && a.mode == ATT_WRITE_ATTEND && a.n_runs == 1 && a.d == 128 && a.nkv == 8 &&
+                  a.nq == 16 && a.ld_qkv >= (long)(a.nq + 2 * a.nkv) * a.d && a.part_z <= 0 && !a.row_pos && !a.rope_rows && a.max_pos <= 16 &&
+                  a.pos_base >= 0 && a.pos_base + nt <= a.max_pos &&
+                  (nt == 1 || (nt == 2 && a.tok_stride == 2 && a.tok_off == 0)) && (nt == 2 || a.tok_stride == 0) &&
+                  (a.kvdtype == DT_F16 || a.kvdtype == DT_BF16) &&
+                  o.wdtype == DT_BF16 && o.K == a.nq * a.d && o.N % 16 == 0 && o.M == nt && o.epi == EPI_RESIDUAL &&
+                  !o.gain && o.ldx == o.K && o.X == a.out && a.ld_out == o.K;
+  if (!ok) return hipErrorNotSupported;
+  if (a.kvdtype == DT_F16) return launch_pred_attn_o_t<_Float16>(a, o, s);
+  return launch_pred_attn_o_t<uint16_t>(a, o, s);
 }
 
 // ---------------------------------------------------------------- Philox
