@@ -321,17 +321,16 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
   const WT* W = (const WT*)p.W;
   u32x4 w[NC][R];
   float x[NC][MT][EPC];
+  float g[NC][EPC];
   bool kin[NC];
+  // Activations and gains first, weights last: the vector-memory counter
+  // drains in issue order, so the RMSNorm below waits only for the small
+  // activation loads while the weight rows are still in flight.
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
     kin[c] = k0 < K;
     const int kc = kin[c] ? k0 : K - EPC;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(row0 + r, N - 1);
-      w[c][r] = ld_weight(W + (long)row * K + kc);
-    }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const float* xr = p.X + (long)(m0 + min(m, mt - 1)) * p.ldx + kc;
@@ -341,19 +340,35 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
         x[c][m][e] = v.x; x[c][m][e + 1] = v.y; x[c][m][e + 2] = v.z; x[c][m][e + 3] = v.w;
       }
     }
-  }
-  if (p.gain) {
-    float g[NC][EPC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
-      const float* gp = p.gain + (kin[c] ? k0 : K - EPC);
+    if (p.gain) {
+      const float* gp = p.gain + kc;
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
         const f32x4 v = *(const f32x4*)(gp + e);
         g[c][e] = v.x; g[c][e + 1] = v.y; g[c][e + 2] = v.z; g[c][e + 3] = v.w;
       }
     }
+  }
+  // residual epilogue: the old output values, loaded now (only this wave writes them)
+  float yold[R][MT];
+  if (p.epi == EPI_RESIDUAL)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) yold[r][m] = p.Y[(long)(m0 + min(m, mt - 1)) * p.ldy + min(row0 + r, N - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
+    const int kc = k0 < K ? k0 : K - EPC;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      w[c][r] = ld_weight(W + (long)row * K + kc);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (p.gain) {
     float ss[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -463,7 +478,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = row0 + r;
-        if (row < N) y[row] = (p.epi == EPI_RESIDUAL) ? y[row] + acc[r][m] : acc[r][m];
+        if (row < N) y[row] = (p.epi == EPI_RESIDUAL) ? yold[r][m] + acc[r][m] : acc[r][m];
       }
     }
   }
@@ -2330,6 +2345,11 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// MPT logits per thread (V <= MPT * NT). Every global load of a phase is
+// issued before its first use (the row's logits and seen bits, the feedback
+// row; then the chosen table row), so a selection costs two memory round
+// trips whatever V is.
+template <int MPT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
   extern __shared__ float sm[];
@@ -2345,6 +2365,30 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ int sh_int[4];
   __shared__ float sh_f[2];
 
+  // this row's logits (element tid + q NT), the seen bits they need and, for
+  // the code-predictor epilogue, the feedback row: one batch of loads
+  const float* lg = a.logits + (long)r * a.ld;
+  float lv[MPT];
+  uint32_t sw[MPT];
+#pragma unroll
+  for (int q = 0; q < MPT; ++q) lv[q] = lg[min(tid + q * NT, V - 1)];
+  // (no seen bits without a seen array: the penalty is then off)
+  const bool has_seen = a.processors && a.seen != nullptr;
+  if (has_seen) {
+    const uint32_t* seen = a.seen + (long)r * a.seen_words;
+#pragma unroll
+    for (int q = 0; q < MPT; ++q) sw[q] = seen[min((tid + q * NT) >> 5, a.seen_words - 1)];
+  }
+  constexpr int EPT = 8;                 // feedback elements per thread (tab_dim <= EPT * NT)
+  float fbv[EPT];
+  const bool epi_fast = a.epi == 1 && a.tab_dim <= EPT * NT;
+  if (epi_fast)
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) fbv[q] = a.fb[(long)r * a.fb_ld + min(tid + q * NT, a.tab_dim - 1)];
+  const int kf0 = a.frame_k ? *a.frame_k : 0, kf = kf0;
+  const int forced_v = a.forced ? a.forced[(long)r * a.forced_ld + a.forced_col] : 0;
+  const int fin = a.epi == 2 ? a.finished[r] : 0;
+
   // settings: from the request block when given
   int do_sample = a.do_sample, top_k = a.top_k, min_new = a.min_new, max_frames = a.max_frames;
   float temperature = a.temperature, top_p = a.top_p, penalty = a.penalty;
@@ -2358,21 +2402,26 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     top_p = sp.top_p; penalty = sp.penalty; seed = a.req->seed; max_frames = a.req->max_frames;
     text = a.req->text; pad = a.req->pad; has_text = a.req->has_text;
   }
-  const float* lg = a.logits + (long)r * a.ld;
   const int jsel = (a.ctr ? *a.ctr : 0) + a.ctr_add;
+  float padv[EPT] = {};
+  if (epi_fast && a.add_text)
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) padv[q] = pad[min(tid + q * NT, a.tab_dim - 1)];
   int choice = 0;
   if (!do_sample && !a.processed_out) {
     // greedy: the non-finite check, the processors and the argmax (lowest
     // id on ties) in one pass over the logits, one exchange between waves
-    const uint32_t* seen = a.seen + (long)r * a.seen_words;
-    const bool pen = a.processors && penalty != 1.0f;
+    const bool pen = has_seen && penalty != 1.0f;
     float bv = -INFINITY;
     int bi = 0x7fffffff, badl = 0;
-    for (int i = tid; i < V; i += NT) {
-      float x = lg[i];
+#pragma unroll
+    for (int q = 0; q < MPT; ++q) {
+      const int i = tid + q * NT;
+      if (i >= V) break;
+      float x = lv[q];
       badl |= isnan(x) || x == INFINITY;
       if (a.processors) {
-        if (pen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
+        if (pen && ((sw[q] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
         if (i == a.eos && jsel < min_new) x = -INFINITY;
         if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
       }
@@ -2395,24 +2444,21 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   } else {
   int bad = 0;
-  for (int i = tid; i < V; i += NT) {
-    const float x = lg[i];
+  const bool pen = has_seen && penalty != 1.0f;
+#pragma unroll
+  for (int q = 0; q < MPT; ++q) {
+    const int i = tid + q * NT;
+    if (i >= V) break;
+    float x = lv[q];
     if (isnan(x) || x == INFINITY) bad = 1;
+    if (a.processors) {
+      if (pen && ((sw[q] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
+      if (i == a.eos && jsel < min_new) x = -INFINITY;
+      if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
+    }
     v[i] = x;
   }
   bad = block_or(bad, redi);
-  if (a.processors) {
-    const uint32_t* seen = a.seen + (long)r * a.seen_words;
-    const bool pen = penalty != 1.0f;
-    for (int i = tid; i < V; i += NT) {
-      float x = v[i];
-      if (pen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x < 0.f ? x * penalty : x / penalty;
-      if (i == a.eos && jsel < min_new) x = -INFINITY;
-      if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
-      v[i] = x;
-    }
-  }
-  __syncthreads();
   if (a.processed_out)
     for (int i = tid; i < V; i += NT) a.processed_out[(long)r * V + i] = v[i];
 
@@ -2562,13 +2608,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // commit
   if (tid == 0) {
     int used = choice;
-    if (a.forced) used = a.forced[(long)r * a.forced_ld + a.forced_col];
+    if (a.forced) used = forced_v;
     a.used[(long)r * a.used_ld + a.used_col] = used;
     if (a.own) a.own[(long)r * a.own_ld + a.own_col] = choice;
     sh_int[3] = used;
     if (a.epi == 2) {
-      const int kf = a.frame_k ? *a.frame_k : -1;
-      if (a.finished[r]) {
+      const int kf = a.frame_k ? kf0 : -1;
+      if (fin) {
         a.state[r] = 3;
       } else if (used == a.eos) {
         a.state[r] = 1;
@@ -2582,10 +2628,29 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  if (a.epi == 1) {
+  if (epi_fast) {
     const int used = sh_int[3];
     const long base = (a.tab_off + used) * (long)a.tab_dim;
-    const int kf = a.frame_k ? *a.frame_k : 0;
+    const bool txt = a.add_text && has_text && kf < a.text_len[r];
+    float tv[EPT], xt[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int k = min(tid + q * NT, a.tab_dim - 1);
+      tv[q] = ld_any(a.tab, a.tab_dtype, base + k);
+      xt[q] = txt ? text[((long)a.text_off[r] + kf) * a.tab_dim + k] : padv[q];
+    }
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int k = tid + q * NT;
+      if (k >= a.tab_dim) break;
+      if (a.next_in) a.next_in[(long)r * a.next_ld + k] = tv[q];
+      float f = fbv[q] + tv[q];
+      if (a.add_text) f = f + xt[q];
+      a.fb[(long)r * a.fb_ld + k] = f;
+    }
+  } else if (a.epi == 1) {
+    const int used = sh_int[3];
+    const long base = (a.tab_off + used) * (long)a.tab_dim;
     const bool txt = a.add_text && has_text && kf < a.text_len[r];
     for (int k = tid; k < a.tab_dim; k += NT) {
       const float val = ld_any(a.tab, a.tab_dtype, base + k);
@@ -2597,14 +2662,24 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  if (a.B <= 0) return hipSuccess;
+template <int MPT>
+static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.V * 5 * sizeof(float);
   static size_t have = 0;
-  hipError_t e = ensure_lds((const void*)select_kernel, lds, &have);
+  hipError_t e = ensure_lds((const void*)select_kernel<MPT>, lds, &have);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(NT), lds, s, a);
+  hipLaunchKernelGGL(select_kernel<MPT>, dim3(a.B), dim3(NT), lds, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  if (a.V < 1 || a.V > 24 * NT) return hipErrorInvalidValue;
+  if (a.V <= 4 * NT) return launch_select_t<4>(a, s);
+  if (a.V <= 8 * NT) return launch_select_t<8>(a, s);
+  if (a.V <= 12 * NT) return launch_select_t<12>(a, s);
+  if (a.V <= 16 * NT) return launch_select_t<16>(a, s);
+  return launch_select_t<24>(a, s);
 }
 
 // ---------------------------------------------------------------- frame control
