@@ -787,10 +787,22 @@ __global__ __launch_bounds__(SK_NW * 64) void skinny_kernel(LinearArgs p) {
       for (int m = 0; m < SK_MAXM; ++m)
         if (m < M) xv[slot][m] = *(const f32x4*)(p.X + (long)m * p.ldx + k0 + 4 * lane);
   };
-#pragma unroll
-  for (int si = 0; si < PF; ++si) load_w(si, si);
+  // activations, gains and the residual inputs first, weights last: the
+  // vector-memory counter drains in issue order, so the norm below waits
+  // only for the activations while the weight slices are in flight
 #pragma unroll
   for (int si = 0; si < XB; ++si) load_x(si, si);
+  f32x4 gvs[NORM ? S : 1];
+  if constexpr (NORM)
+#pragma unroll
+    for (int si = 0; si < S; ++si) gvs[si] = *(const f32x4*)(p.gain + min((si * SK_NW + w) * SK_SLICE, K - SK_SLICE) + 4 * lane);
+  const int orow = 4 * g + w, ocol = n0 + j;   // this lane's output element
+  float yold = 0.f;
+  if (p.epi == EPI_RESIDUAL) yold = p.Y[(long)min(orow, M - 1) * p.ldy + min(ocol, N - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int si = 0; si < PF; ++si) load_w(si, si);
+  __builtin_amdgcn_sched_barrier(0);
   float inv[SK_MAXM];   // per row 1 / sqrt(mean(x^2) + eps)
   const float rk = 1.f / (float)K;
   if constexpr (NORM) {
@@ -827,7 +839,7 @@ __global__ __launch_bounds__(SK_NW * 64) void skinny_kernel(LinearArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) *(u32x4*)&Wl[(2 * q + (lane >> 5)) * SK_LD + 8 * (lane & 31)] = wv[si % PF][q];
       f32x4 gv = (f32x4){1.f, 1.f, 1.f, 1.f};
-      if constexpr (NORM) gv = *(const f32x4*)(p.gain + k0 + 4 * lane);
+      if constexpr (NORM) gv = gvs[si];
 #pragma unroll
       for (int m = 0; m < SK_MAXM; ++m) {
         if (m < M) {
@@ -875,8 +887,7 @@ __global__ __launch_bounds__(SK_NW * 64) void skinny_kernel(LinearArgs p) {
     const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes j, j ^ 1
     if (!(j & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
   } else if (row < M && col < N) {
-    float* y = p.Y + (long)row * p.ldy + col;
-    *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+    p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold + v : v;
   }
 }
 
