@@ -1107,17 +1107,48 @@ __global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
 // Adds the Z partial tiles of each output in order z = 0..Z-1, applies the
 // row's RMS scale (sums of squares added in the same order) and the epilogue;
 // one thread per 4 consecutive columns (N % 4 == 0). Also writes norm_out.
+// ZT > 0: exactly ZT ranges, every partial load issued before the first add
+// (a loop would wait for each load in turn); ZT == 0: any Z.
+template <int ZT>
 __global__ __launch_bounds__(NT) void rows_reduce_kernel(LinearArgs p, int Z) {
   const int n4 = p.N / 4;
   const long t = (long)blockIdx.x * NT + threadIdx.x;
   if (t >= (long)p.M * n4) return;
   const int row = (int)(t / n4), c = (int)(t % n4) * 4;
-  f32x4 s = *(const f32x4*)(p.part + (long)row * p.N + c);
-  for (int z = 1; z < Z; ++z) s += *(const f32x4*)(p.part + ((long)z * p.M + row) * p.N + c);
+  const float* pss = p.part + (long)Z * p.M * p.N;
+  // the residual's old values go out with the partial loads
+  f32x4 yold = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (p.epi == EPI_RESIDUAL) {
+    const float* yr = p.Y + (long)row * p.ldy + c;
+    yold = (f32x4){yr[0], yr[1], yr[2], yr[3]};
+  }
+  f32x4 s;
+  float ssum = 0.f;
+  if constexpr (ZT > 0) {
+    f32x4 v[ZT];
+    float q[ZT];
+#pragma unroll
+    for (int z = 0; z < ZT; ++z) v[z] = *(const f32x4*)(p.part + ((long)z * p.M + row) * p.N + c);
+    if (p.gain)
+#pragma unroll
+      for (int z = 0; z < ZT; ++z) q[z] = pss[(long)z * p.M + row];
+    s = v[0];
+#pragma unroll
+    for (int z = 1; z < ZT; ++z) s += v[z];
+    if (p.gain) {
+      ssum = q[0];
+#pragma unroll
+      for (int z = 1; z < ZT; ++z) ssum += q[z];
+    }
+  } else {
+    s = *(const f32x4*)(p.part + (long)row * p.N + c);
+    for (int z = 1; z < Z; ++z) s += *(const f32x4*)(p.part + ((long)z * p.M + row) * p.N + c);
+    if (p.gain) {
+      ssum = pss[row];
+      for (int z = 1; z < Z; ++z) ssum += pss[(long)z * p.M + row];
+    }
+  }
   if (p.gain) {
-    const float* pss = p.part + (long)Z * p.M * p.N;
-    float ssum = pss[row];
-    for (int z = 1; z < Z; ++z) ssum += pss[(long)z * p.M + row];
     const float rs = 1.f / sqrtf(ssum / (float)p.K + p.eps);
     s *= rs;
     if (p.norm_out)
@@ -1132,7 +1163,7 @@ __global__ __launch_bounds__(NT) void rows_reduce_kernel(LinearArgs p, int Z) {
     y[c / 2] = s.x / (1.f + expf(-s.x)) * s.y;
     y[c / 2 + 1] = s.z / (1.f + expf(-s.z)) * s.w;
   } else if (p.epi == EPI_RESIDUAL) {
-    y[c] += s.x; y[c + 1] += s.y; y[c + 2] += s.z; y[c + 3] += s.w;
+    y[c] = yold.x + s.x; y[c + 1] = yold.y + s.y; y[c + 2] = yold.z + s.z; y[c + 3] = yold.w + s.w;
   } else {
     y[c] = s.x; y[c + 1] = s.y; y[c + 2] = s.z; y[c + 3] = s.w;
   }
@@ -1210,7 +1241,17 @@ static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream
   hipError_t e = a.gain ? launch_rows_g<true>(a, pl, grid, s) : launch_rows_g<false>(a, pl, grid, s);
   if (e != hipSuccess || pl.Z == 1 || a.defer) return e;
   const long threads = (long)a.M * (a.N / 4);
-  hipLaunchKernelGGL(rows_reduce_kernel, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, s, a, pl.Z);
+  const dim3 grid_r((unsigned)((threads + NT - 1) / NT));
+  switch (pl.Z) {
+    case 2: hipLaunchKernelGGL(rows_reduce_kernel<2>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 3: hipLaunchKernelGGL(rows_reduce_kernel<3>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 4: hipLaunchKernelGGL(rows_reduce_kernel<4>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 6: hipLaunchKernelGGL(rows_reduce_kernel<6>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 8: hipLaunchKernelGGL(rows_reduce_kernel<8>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 12: hipLaunchKernelGGL(rows_reduce_kernel<12>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    case 16: hipLaunchKernelGGL(rows_reduce_kernel<16>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+    default: hipLaunchKernelGGL(rows_reduce_kernel<0>, grid_r, dim3(NT), 0, s, a, pl.Z); break;
+  }
   return hipGetLastError();
 }
 
@@ -1819,21 +1860,43 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
   // lane owns the rope pair (lane, lane + 64)), K/V rows to the cache and LDS
   float prs[NTOK];
   const long arow0 = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  // split-K partial sums: up to PZ ranges with every load issued before the
+  // first add (clamped ranges past part_z are loaded but not added)
+  constexpr int PZ = 8;
+  const bool pz_fast = p.part_z <= PZ;
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
     prs[t] = 1.f;
     if (p.part_z > 0) {
       const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
       float ssum = 0.f;
-      for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow0 + t];
+      if (pz_fast) {
+        float q[PZ];
+#pragma unroll
+        for (int z = 0; z < PZ; ++z) q[z] = pss[(long)min(z, p.part_z - 1) * p.part_rows + arow0 + t];
+#pragma unroll
+        for (int z = 0; z < PZ; ++z) if (z < p.part_z) ssum += q[z];
+      } else {
+        for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow0 + t];
+      }
       prs[t] = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
     }
   }
   auto qkv_at = [&](int t, long col) -> float {
     const long ar = arow0 + t;
     if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
-    float v = p.part[ar * p.ld_qkv + col];
-    for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
+    float v;
+    if (pz_fast) {
+      float q[PZ];
+#pragma unroll
+      for (int z = 0; z < PZ; ++z) q[z] = p.part[((long)min(z, p.part_z - 1) * p.part_rows + ar) * p.ld_qkv + col];
+      v = q[0];
+#pragma unroll
+      for (int z = 1; z < PZ; ++z) if (z < p.part_z) v += q[z];
+    } else {
+      v = p.part[ar * p.ld_qkv + col];
+      for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
+    }
     return v * prs[t];
   };
 #pragma unroll
