@@ -1261,6 +1261,175 @@ int linear_split_ranges(const LinearArgs& a) {
   return rows_plan(a, &pl) ? pl.Z : 1;
 }
 
+// ---------------------------------------------------------------- matrix-core GEMV
+// Projection of up to 16 activation rows on the matrix cores with no LDS
+// staging of either operand: v_mfma_f32_16x16x32_bf16 takes B = W^T straight
+// from a 16-byte load of a weight row (lane l: row n0 + l % 16, k offset
+// 8 (l / 16)), and A = the activations, which each lane loads as fp32 for its
+// row l % 16 (rows past M repeat row M - 1 and are dropped), scales by the
+// RMSNorm gain and splits into bf16 hi + lo (two MFMAs, fp32-accurate).
+// Block = KSW waves, one 16-row output tile; wave w covers K range w with NG
+// groups of 8 k-steps (256 k), the next group's loads in flight while a group
+// is processed. The waves' tiles and the row sums of squares are added in
+// LDS in wave order; RMSNorm is applied after the contraction as a per-row
+// scale.
+template <int KSW, int NG, bool NORM>
+__global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
+  constexpr int GS = 8;                        // k-steps of 32 per group
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lk = lane >> 4;    // operand row, k sub-block
+  const int n0 = blockIdx.x * 16;
+  const int M = p.M, N = p.N, K = p.K;
+  const int kw0 = w * (K / KSW);               // this wave's K range
+  __shared__ __align__(16) float red[KSW][64][4];
+  __shared__ float ssr[KSW][16];
+  __shared__ float inv_s[16];
+  const uint16_t* wrow = (const uint16_t*)p.W + (long)min(n0 + li, N - 1) * K + kw0 + 8 * lk;
+  const float* xrow = p.X + (long)min(li, M - 1) * p.ldx + kw0 + 8 * lk;
+  const float* grow = NORM ? p.gain + kw0 + 8 * lk : nullptr;
+  // the residual's old values of this lane's outputs (rows 4 lk + r, column n0 + li)
+  float yold[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.epi == EPI_RESIDUAL)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yold[r] = p.Y[(long)min(4 * lk + r, M - 1) * p.ldy + min(n0 + li, N - 1)];
+  u32x4 wa[GS], wb[GS];
+  f32x4 xa[GS][2], xb[GS][2], ga[GS][2], gb[GS][2];
+  auto load_x = [&](int gi, f32x4 (&xv)[GS][2], f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < GS; ++st) {
+      const int k = (gi * GS + st) * 32;
+      xv[st][0] = *(const f32x4*)(xrow + k);
+      xv[st][1] = *(const f32x4*)(xrow + k + 4);
+      if constexpr (NORM) {
+        gv[st][0] = *(const f32x4*)(grow + k);
+        gv[st][1] = *(const f32x4*)(grow + k + 4);
+      }
+    }
+  };
+  auto load_w = [&](int gi, u32x4 (&wv)[GS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < GS; ++st) wv[st] = ld_weight(wrow + (gi * GS + st) * 32);
+  };
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  auto process = [&](const u32x4 (&wv)[GS], const f32x4 (&xv)[GS][2], const f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < GS; ++st) {
+      float x[8] = {xv[st][0].x, xv[st][0].y, xv[st][0].z, xv[st][0].w, xv[st][1].x, xv[st][1].y, xv[st][1].z, xv[st][1].w};
+      if constexpr (NORM) {
+        const float g[8] = {gv[st][0].x, gv[st][0].y, gv[st][0].z, gv[st][0].w, gv[st][1].x, gv[st][1].y, gv[st][1].z, gv[st][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { ss = fmaf(x[e], x[e], ss); x[e] *= g[e]; }
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+      const bf16x8 al = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[st]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+    }
+  };
+  // activations (and gains) first, weights last: the norm sums below wait
+  // only for the activations
+  load_x(0, xa, ga);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(0, wa);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + 1 < NG) {
+      if (gi % 2 == 0) { load_x(gi + 1, xb, gb); load_w(gi + 1, wb); }
+      else { load_x(gi + 1, xa, ga); load_w(gi + 1, wa); }
+    }
+    if (gi % 2 == 0) process(wa, xa, ga);
+    else process(wb, xb, gb);
+  }
+  // D(i, j) of the tile: lane j + 16 (i / 4), register i % 4
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[w][lane][r] = acc[r];
+  if constexpr (NORM) {
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (lk == 0) ssr[w][li] = ss;
+  }
+  __syncthreads();
+  if constexpr (NORM) {
+    if (threadIdx.x < 16) {
+      float t = ssr[0][threadIdx.x];
+#pragma unroll
+      for (int q = 1; q < KSW; ++q) t += ssr[q][threadIdx.x];
+      inv_s[threadIdx.x] = 1.f / sqrtf(t / (float)K + p.eps);
+    }
+    __syncthreads();
+  }
+  if (w != 0) return;
+  f32x4 v = *(const f32x4*)red[0][lane];
+#pragma unroll
+  for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][lane];
+  float rs[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (NORM) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rs[r] = inv_s[4 * lk + r];
+    if (p.norm_out && blockIdx.x == 0)
+      for (int e = lane; e < 16 * (K / 4); e += 64) {
+        const int row = e / (K / 4), k = (e % (K / 4)) * 4;
+        if (row < M) {
+          const f32x4 xv = *(const f32x4*)(p.X + (long)row * p.ldx + k), gv = *(const f32x4*)(p.gain + k);
+          const float s = inv_s[row];
+          *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) = (f32x4){xv.x * gv.x * s, xv.y * gv.y * s, xv.z * gv.z * s, xv.w * gv.w * s};
+        }
+      }
+  }
+  const int col = n0 + li;
+  const float vv[4] = {v.x * rs[0], v.y * rs[1], v.z * rs[2], v.w * rs[3]};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * lk + r;
+    if (p.epi == EPI_SWIGLU) {
+      const float up = __shfl_xor(vv[r], 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes li, li ^ 1
+      if (!(li & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = vv[r] / (1.f + expf(-vv[r])) * up;
+    } else if (row < M && col < N) {
+      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[r] + vv[r] : vv[r];
+    }
+  }
+}
+
+template <int KSW, bool NORM>
+static hipError_t launch_mfma_gemv_k(const LinearArgs& a, int ng, hipStream_t s) {
+  const dim3 grid((a.N + 15) / 16), block(KSW * 64);
+  switch (ng) {
+    case 1: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 1, NORM>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 2, NORM>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 3, NORM>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 4, NORM>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 6, NORM>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// 3..16 activation rows of bf16 weights with K a multiple of 256 and at
+// least 128 output tiles (narrower outputs stream better through the
+// row-block kernel): 4 waves (2 or 1 for short K), NG groups of 256 k each.
+static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng) {
+  if (a.wdtype != DT_BF16 || a.M < 3 || a.M > 16 || a.N < 2048 || a.K % 256 || a.ldx % 4 || a.defer) return false;
+  const int groups = a.K / 256;
+  for (int k = 4; k >= 1; k /= 2)
+    if (groups % k == 0) {
+      const int g = groups / k;
+      if (g == 1 || g == 2 || g == 3 || g == 4 || g == 6) { *ksw = k; *ng = g; return true; }
+    }
+  return false;
+}
+
+static hipError_t launch_mfma_gemv(const LinearArgs& a, int ksw, int ng, hipStream_t s) {
+  if (ksw == 4) return a.gain ? launch_mfma_gemv_k<4, true>(a, ng, s) : launch_mfma_gemv_k<4, false>(a, ng, s);
+  if (ksw == 2) return a.gain ? launch_mfma_gemv_k<2, true>(a, ng, s) : launch_mfma_gemv_k<2, false>(a, ng, s);
+  return a.gain ? launch_mfma_gemv_k<1, true>(a, ng, s) : launch_mfma_gemv_k<1, false>(a, ng, s);
+}
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
@@ -1268,7 +1437,12 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
     hipError_t e = hipSuccess;
     if (a.wdtype == DT_BF16 ? try_gemv<uint16_t>(a, s, &e) : try_gemv<float>(a, s, &e)) return e;
   }
-  // a few more rows of bf16 weights: weight-streaming MFMA kernel
+  // a few more rows of bf16 weights: matrix-core GEMV (wide outputs), else
+  // the row-block weight-streaming MFMA kernel
+  {
+    int ksw, ng;
+    if (mfma_gemv_plan(a, &ksw, &ng)) return launch_mfma_gemv(a, ksw, ng, s);
+  }
   if (skinny_fits(a)) return launch_skinny(a, s);
   // up to 128 rows: row-block MFMA GEMM
   {
