@@ -1255,51 +1255,60 @@ static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream
   return hipGetLastError();
 }
 
+static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng);
 int linear_split_ranges(const LinearArgs& a) {
-  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a)) return 1;
+  int ksw, ng;
+  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a) || mfma_gemv_plan(a, &ksw, &ng)) return 1;
   RowsPlan pl;
   return rows_plan(a, &pl) ? pl.Z : 1;
 }
 
 // ---------------------------------------------------------------- matrix-core GEMV
-// Projection of up to 16 activation rows on the matrix cores with no LDS
-// staging of either operand: v_mfma_f32_16x16x32_bf16 takes B = W^T straight
+// Projection of up to 16 MT activation rows (MT 16-row tiles) on the matrix
+// cores with no LDS staging of either operand: v_mfma_f32_16x16x32_bf16 takes B = W^T straight
 // from a 16-byte load of a weight row (lane l: row n0 + l % 16, k offset
 // 8 (l / 16)), and A = the activations, which each lane loads as fp32 for its
 // row l % 16 (rows past M repeat row M - 1 and are dropped), scales by the
 // RMSNorm gain and splits into bf16 hi + lo (two MFMAs, fp32-accurate).
-// Block = KSW waves, one 16-row output tile; wave w covers K range w with NG
-// groups of 8 k-steps (256 k), the next group's loads in flight while a group
-// is processed. The waves' tiles and the row sums of squares are added in
-// LDS in wave order; RMSNorm is applied after the contraction as a per-row
-// scale.
-template <int KSW, int NG, bool NORM>
+// Block = KSW waves (KSW >= MT), one 16-row output tile; wave w covers K
+// range w with NG groups of 8 / MT k-steps of 32, the next group's loads in
+// flight while a group is processed. The waves' tiles and the row sums of
+// squares are added in LDS in wave order (wave t finishes m-tile t); RMSNorm
+// is applied after the contraction as a per-row scale.
+template <int KSW, int NG, bool NORM, int MT>
 __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
-  constexpr int GS = 8;                        // k-steps of 32 per group
+  constexpr int GS = 8 / MT;                   // k-steps of 32 per group
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lk = lane >> 4;    // operand row, k sub-block
   const int n0 = blockIdx.x * 16;
   const int M = p.M, N = p.N, K = p.K;
   const int kw0 = w * (K / KSW);               // this wave's K range
-  __shared__ __align__(16) float red[KSW][64][4];
-  __shared__ float ssr[KSW][16];
-  __shared__ float inv_s[16];
+  __shared__ __align__(16) float red[KSW][MT][64][4];
+  __shared__ float ssr[KSW][16 * MT];
+  __shared__ float inv_s[16 * MT];
   const uint16_t* wrow = (const uint16_t*)p.W + (long)min(n0 + li, N - 1) * K + kw0 + 8 * lk;
-  const float* xrow = p.X + (long)min(li, M - 1) * p.ldx + kw0 + 8 * lk;
+  const float* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xrow[t] = p.X + (long)min(16 * t + li, M - 1) * p.ldx + kw0 + 8 * lk;
   const float* grow = NORM ? p.gain + kw0 + 8 * lk : nullptr;
   // the residual's old values of this lane's outputs (rows 4 lk + r, column n0 + li)
-  float yold[4] = {0.f, 0.f, 0.f, 0.f};
+  float yold[MT][4] = {};
   if (p.epi == EPI_RESIDUAL)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) yold[r] = p.Y[(long)min(4 * lk + r, M - 1) * p.ldy + min(n0 + li, N - 1)];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yold[t][r] = p.Y[(long)min(16 * t + 4 * lk + r, M - 1) * p.ldy + min(n0 + li, N - 1)];
   u32x4 wa[GS], wb[GS];
-  f32x4 xa[GS][2], xb[GS][2], ga[GS][2], gb[GS][2];
-  auto load_x = [&](int gi, f32x4 (&xv)[GS][2], f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
+  f32x4 xa[GS][MT][2], xb[GS][MT][2], ga[GS][2], gb[GS][2];
+  auto load_x = [&](int gi, f32x4 (&xv)[GS][MT][2], f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < GS; ++st) {
       const int k = (gi * GS + st) * 32;
-      xv[st][0] = *(const f32x4*)(xrow + k);
-      xv[st][1] = *(const f32x4*)(xrow + k + 4);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        xv[st][t][0] = *(const f32x4*)(xrow[t] + k);
+        xv[st][t][1] = *(const f32x4*)(xrow[t] + k + 4);
+      }
       if constexpr (NORM) {
         gv[st][0] = *(const f32x4*)(grow + k);
         gv[st][1] = *(const f32x4*)(grow + k + 4);
@@ -1310,25 +1319,31 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
 #pragma unroll
     for (int st = 0; st < GS; ++st) wv[st] = ld_weight(wrow + (gi * GS + st) * 32);
   };
-  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float ss = 0.f;
-  auto process = [&](const u32x4 (&wv)[GS], const f32x4 (&xv)[GS][2], const f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
+  f32x4 acc[MT];
+  float ss[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) { acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f}; ss[t] = 0.f; }
+  auto process = [&](const u32x4 (&wv)[GS], const f32x4 (&xv)[GS][MT][2], const f32x4 (&gv)[GS][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < GS; ++st) {
-      float x[8] = {xv[st][0].x, xv[st][0].y, xv[st][0].z, xv[st][0].w, xv[st][1].x, xv[st][1].y, xv[st][1].z, xv[st][1].w};
-      if constexpr (NORM) {
-        const float g[8] = {gv[st][0].x, gv[st][0].y, gv[st][0].z, gv[st][0].w, gv[st][1].x, gv[st][1].y, gv[st][1].z, gv[st][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { ss = fmaf(x[e], x[e], ss); x[e] *= g[e]; }
-      }
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
-      const bf16x8 al = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
       const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[st]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        float x[8] = {xv[st][t][0].x, xv[st][t][0].y, xv[st][t][0].z, xv[st][t][0].w,
+                      xv[st][t][1].x, xv[st][t][1].y, xv[st][t][1].z, xv[st][t][1].w};
+        if constexpr (NORM) {
+          const float g[8] = {gv[st][0].x, gv[st][0].y, gv[st][0].z, gv[st][0].w, gv[st][1].x, gv[st][1].y, gv[st][1].z, gv[st][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { ss[t] = fmaf(x[e], x[e], ss[t]); x[e] *= g[e]; }
+        }
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+        const bf16x8 al = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[t], 0, 0, 0);
+      }
     }
   };
   // activations (and gains) first, weights last: the norm sums below wait
@@ -1346,17 +1361,20 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
     if (gi % 2 == 0) process(wa, xa, ga);
     else process(wb, xb, gb);
   }
-  // D(i, j) of the tile: lane j + 16 (i / 4), register i % 4
+  // D(i, j) of a tile: lane j + 16 (i / 4), register i % 4
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[w][lane][r] = acc[r];
-  if constexpr (NORM) {
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    if (lk == 0) ssr[w][li] = ss;
+  for (int t = 0; t < MT; ++t) {
+    *(f32x4*)red[w][t][lane] = acc[t];
+    if constexpr (NORM) {
+      float q = ss[t];
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+      if (lk == 0) ssr[w][16 * t + li] = q;
+    }
   }
   __syncthreads();
   if constexpr (NORM) {
-    if (threadIdx.x < 16) {
+    if (threadIdx.x < 16 * MT) {
       float t = ssr[0][threadIdx.x];
 #pragma unroll
       for (int q = 1; q < KSW; ++q) t += ssr[q][threadIdx.x];
@@ -1364,16 +1382,18 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
     }
     __syncthreads();
   }
-  if (w != 0) return;
-  f32x4 v = *(const f32x4*)red[0][lane];
+  // wave w < MT finishes m-tile w
+  if (w >= MT) return;
+  const int t = w;
+  f32x4 v = *(const f32x4*)red[0][t][lane];
 #pragma unroll
-  for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][lane];
+  for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][t][lane];
   float rs[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (NORM) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rs[r] = inv_s[4 * lk + r];
-    if (p.norm_out && blockIdx.x == 0)
-      for (int e = lane; e < 16 * (K / 4); e += 64) {
+    for (int r = 0; r < 4; ++r) rs[r] = inv_s[16 * t + 4 * lk + r];
+    if (p.norm_out && blockIdx.x == 0 && t == 0)
+      for (int e = lane; e < M * (K / 4); e += 64) {
         const int row = e / (K / 4), k = (e % (K / 4)) * 4;
         if (row < M) {
           const f32x4 xv = *(const f32x4*)(p.X + (long)row * p.ldx + k), gv = *(const f32x4*)(p.gain + k);
@@ -1386,37 +1406,39 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
   const float vv[4] = {v.x * rs[0], v.y * rs[1], v.z * rs[2], v.w * rs[3]};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = 4 * lk + r;
+    const int row = 16 * t + 4 * lk + r;
     if (p.epi == EPI_SWIGLU) {
       const float up = __shfl_xor(vv[r], 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes li, li ^ 1
       if (!(li & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = vv[r] / (1.f + expf(-vv[r])) * up;
     } else if (row < M && col < N) {
-      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[r] + vv[r] : vv[r];
+      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[t][r] + vv[r] : vv[r];
     }
   }
 }
 
-template <int KSW, bool NORM>
+template <int KSW, bool NORM, int MT>
 static hipError_t launch_mfma_gemv_k(const LinearArgs& a, int ng, hipStream_t s) {
   const dim3 grid((a.N + 15) / 16), block(KSW * 64);
   switch (ng) {
-    case 1: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 1, NORM>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 2, NORM>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 3, NORM>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 4, NORM>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 6, NORM>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 1, NORM, MT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 2, NORM, MT>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 3, NORM, MT>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 4, NORM, MT>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((mfma_gemv_kernel<KSW, 6, NORM, MT>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// 3..16 activation rows of bf16 weights with K a multiple of 256 and at
+// 3..32 activation rows of bf16 weights with K a multiple of 256 and at
 // least 128 output tiles (narrower outputs stream better through the
-// row-block kernel): 4 waves (2 or 1 for short K), NG groups of 256 k each.
+// row-block kernel): 4 waves (2 or 1 for short K; at least MT).
 static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng) {
-  if (a.wdtype != DT_BF16 || a.M < 3 || a.M > 16 || a.N < 2048 || a.K % 256 || a.ldx % 4 || a.defer) return false;
-  const int groups = a.K / 256;
-  for (int k = 4; k >= 1; k /= 2)
+  if (a.wdtype != DT_BF16 || a.M < 3 || a.M > 32 || a.N < 2048 || a.K % 256 || a.ldx % 4 || a.defer)
+    return false;
+  const int mt = a.M <= 16 ? 1 : 2;
+  const int groups = a.K / (256 / mt);          // groups of 8 / mt k-steps
+  for (int k = 4; k >= mt; k /= 2)
     if (groups % k == 0) {
       const int g = groups / k;
       if (g == 1 || g == 2 || g == 3 || g == 4 || g == 6) { *ksw = k; *ng = g; return true; }
@@ -1424,10 +1446,19 @@ static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng) {
   return false;
 }
 
+template <int MT>
+static hipError_t launch_mfma_gemv_mt(const LinearArgs& a, int ksw, int ng, hipStream_t s) {
+  if (ksw == 4) return a.gain ? launch_mfma_gemv_k<4, true, MT>(a, ng, s) : launch_mfma_gemv_k<4, false, MT>(a, ng, s);
+  if constexpr (MT <= 2)
+    if (ksw == 2) return a.gain ? launch_mfma_gemv_k<2, true, MT>(a, ng, s) : launch_mfma_gemv_k<2, false, MT>(a, ng, s);
+  if constexpr (MT == 1) return a.gain ? launch_mfma_gemv_k<1, true, MT>(a, ng, s) : launch_mfma_gemv_k<1, false, MT>(a, ng, s);
+  return hipErrorInvalidValue;
+}
+
 static hipError_t launch_mfma_gemv(const LinearArgs& a, int ksw, int ng, hipStream_t s) {
-  if (ksw == 4) return a.gain ? launch_mfma_gemv_k<4, true>(a, ng, s) : launch_mfma_gemv_k<4, false>(a, ng, s);
-  if (ksw == 2) return a.gain ? launch_mfma_gemv_k<2, true>(a, ng, s) : launch_mfma_gemv_k<2, false>(a, ng, s);
-  return a.gain ? launch_mfma_gemv_k<1, true>(a, ng, s) : launch_mfma_gemv_k<1, false>(a, ng, s);
+  if (a.M <= 16) return launch_mfma_gemv_mt<1>(a, ksw, ng, s);
+  if (a.M <= 32) return launch_mfma_gemv_mt<2>(a, ksw, ng, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {

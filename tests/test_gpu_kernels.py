@@ -44,14 +44,14 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
                                    (1024, 3072, 16), (200, 96, 130), (6144, 1024, 257), (2048, 2048, 1024),
                                    (200, 1024, 12), (1000, 768, 30), (4096, 2048, 24), (1024, 3072, 128),
                                    (2052, 512, 100), (2048, 1024, 3), (3072, 2048, 16), (4096, 512, 7),
-                                   (2048, 256, 4), (2056, 1536, 11)])
+                                   (2048, 256, 4), (2056, 1536, 11), (6144, 1024, 32), (2048, 3072, 20)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row and split-K scratch, which routes bf16
     weights with 17..128 rows to the split-K MFMA GEMM and more rows to the
     tiled MFMA GEMM; without it they take the LDS-tile FMA kernel. 3..16 rows
-    use the register-operand matrix-core GEMV when N >= 2048 and the skinny
-    MFMA kernel otherwise, either way."""
+    use the register-operand matrix-core GEMV when N >= 2048 (also up to 32
+    rows) and the skinny MFMA kernel otherwise, either way."""
     if not mc and (wdt != "bf16" or M < 16):
         pytest.skip("same kernel as the mc=True case")
     torch = _torch()
