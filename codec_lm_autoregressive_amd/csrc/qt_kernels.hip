@@ -394,11 +394,11 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const float den = sqrtf(ss[m] / (float)K + p.eps);
+      const float rden = 1.f / sqrtf(ss[m] / (float)K + p.eps);   // one division, then products
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) x[c][m][e] = x[c][m][e] / den * g[c][e];
+        for (int e = 0; e < EPC; ++e) x[c][m][e] = x[c][m][e] * rden * g[c][e];
     }
   }
   if (p.norm_out && blockIdx.x == 0 && wrow == 0)
@@ -2130,8 +2130,8 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
       const float g1 = gain[lane], g2 = gain[lane + HALF];
       const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float den = sqrtf(ss / (float)D + p.eps);
-      const float y1 = x1 / den * g1, y2 = x2 / den * g2;
+      const float rden = 1.f / sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 * rden * g1, y2 = x2 * rden * g2;
       const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
       if (v < G) {
         qs[t][v][lane] = o1;
@@ -2435,8 +2435,8 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
     for (int v = 0; v <= G; ++v) {
       const float x1 = xin[t][v][0], x2 = xin[t][v][1];
       const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float den = sqrtf(ss / (float)D + p.eps);
-      const float y1 = x1 / den * (v < G ? gq1 : gk1), y2 = x2 / den * (v < G ? gq2 : gk2);
+      const float rden = 1.f / sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 * rden * (v < G ? gq1 : gk1), y2 = x2 * rden * (v < G ? gq2 : gk2);
       const float o1 = y1 * cs[t] - y2 * sn[t], o2 = y2 * cs[t] + y1 * sn[t];
       if (v < G) {
         qs[g][t][v][lane] = o1;
@@ -2537,9 +2537,11 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
       }
     if (vsl == 0)
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
+      for (int hh = 0; hh < G; ++hh) {
+        const float rl = 1.f / l[hh];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) att[t][(g * G + hh) * D + vch * EPC + e] = acc[hh][e] / l[hh];
+        for (int e = 0; e < EPC; ++e) att[t][(g * G + hh) * D + vch * EPC + e] = acc[hh][e] * rl;
+      }
   }
   __syncthreads();
 
