@@ -2458,7 +2458,10 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
       st_elem<KVT>(vc, (long)pos * D + lane + HALF, v2);
     }
   }
-  __syncthreads();
+  // the attention below reads only this wave's own LDS rows
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
@@ -2467,6 +2470,7 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
     if (sj < L) {
+      float sp[G][4];                          // one partial sum per chunk: short dependence chains
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e0 = sq * 32 + c * EPC;
@@ -2480,16 +2484,20 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const f32x4* q4 = (const f32x4*)(&qs[g][t][hh][e0]);
+          float a = 0.f;
 #pragma unroll
           for (int e = 0; e < EPC; e += 4) {
             const f32x4 q = q4[e / 4];
-            s[hh] = fmaf(q.x, x[e], s[hh]);
-            s[hh] = fmaf(q.y, x[e + 1], s[hh]);
-            s[hh] = fmaf(q.z, x[e + 2], s[hh]);
-            s[hh] = fmaf(q.w, x[e + 3], s[hh]);
+            a = fmaf(q.x, x[e], a);
+            a = fmaf(q.y, x[e + 1], a);
+            a = fmaf(q.z, x[e + 2], a);
+            a = fmaf(q.w, x[e + 3], a);
           }
+          sp[hh][c] = a;
         }
       }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) s[hh] = (sp[hh][0] + sp[hh][1]) + (sp[hh][2] + sp[hh][3]);
     }
     float pr[G], l[G];
 #pragma unroll
@@ -2550,17 +2558,22 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
   for (int t = 0; t < NTOK; ++t) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      float a = 0.f;
+      float ap[KC];                            // one partial sum per chunk: short dependence chains
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const f32x4* x4 = (const f32x4*)(&att[t][c * 512 + lane * 8]);
         const f32x4 xa = x4[0], xb = x4[1];
         const u32x4 q = w[r][c];
-        a = fmaf(bf_lo(q.x), xa.x, a); a = fmaf(bf_hi(q.x), xa.y, a);
-        a = fmaf(bf_lo(q.y), xa.z, a); a = fmaf(bf_hi(q.y), xa.w, a);
-        a = fmaf(bf_lo(q.z), xb.x, a); a = fmaf(bf_hi(q.z), xb.y, a);
-        a = fmaf(bf_lo(q.w), xb.z, a); a = fmaf(bf_hi(q.w), xb.w, a);
+        float b = bf_lo(q.x) * xa.x;
+        b = fmaf(bf_hi(q.x), xa.y, b);
+        b = fmaf(bf_lo(q.y), xa.z, b); b = fmaf(bf_hi(q.y), xa.w, b);
+        b = fmaf(bf_lo(q.z), xb.x, b); b = fmaf(bf_hi(q.z), xb.y, b);
+        b = fmaf(bf_lo(q.w), xb.z, b); b = fmaf(bf_hi(q.w), xb.w, b);
+        ap[c] = b;
       }
+      float a = ap[0];
+#pragma unroll
+      for (int c = 1; c < KC; ++c) a += ap[c];
       a = wave_sum(a);
       if (lane == 0) {
         float* y = o.Y + (long)t * o.ldy + n0 + r;
