@@ -2647,14 +2647,16 @@ template <int MPT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
   extern __shared__ float sm[];
+  int P2 = 1;                            // V rounded up to a power of two
+  while (P2 < V) P2 <<= 1;
   float* v = sm;                         // [V] logits -> processed -> tempered -> p
-  float* cp = v + V;                     // [V] compacted survivor p
-  int* cid = (int*)(cp + V);             // [V] compacted survivor ids
-  float* sp = (float*)(cid + V);         // [V] survivors in (p desc, id asc) order
+  float* cp = v + V;                     // [P2] compacted survivor p (top-k candidates before that)
+  int* cid = (int*)(cp + P2);            // [P2] compacted survivor ids
+  float* sp = (float*)(cid + P2);        // [V] survivors in (p desc, id asc) order
   int* sid = (int*)(sp + V);             // [V]
   __shared__ float redf[8];
   __shared__ int redi[8];
-  __shared__ int hist[NT / 64 * 256];
+  __shared__ __align__(16) int hist[NT / 64 * 256];
   __shared__ int scan[NT];
   __shared__ int sh_int[4];
   __shared__ float sh_f[2];
@@ -2750,6 +2752,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       if (i == a.eos && jsel < min_new) x = -INFINITY;
       if (i >= a.sup_b && i < a.sup_e && i != a.eos) x = -INFINITY;
     }
+    lv[q] = x;
     v[i] = x;
   }
   bad = block_or(bad, redi);
@@ -2765,12 +2768,17 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     choice = block_argmax(bv, bi, redf, redi);
     if (choice >= V) choice = 0;   // every logit -inf (cannot happen: EOS or codes survive)
   } else {
+    // probabilities in registers, element tid + q NT (every pass over the row
+    // is register arithmetic plus a block reduction; no LDS round trips)
+    float pv[MPT];
     if (a.probs_in) {
-      for (int i = tid; i < V; i += NT) v[i] = a.probs_in[(long)r * V + i];
-      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) pv[q] = a.probs_in[(long)r * V + min(tid + q * NT, V - 1)];
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) if (tid + q * NT >= V) pv[q] = 0.f;
     } else {
-      for (int i = tid; i < V; i += NT) v[i] = v[i] / temperature;
-      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) pv[q] = tid + q * NT < V ? lv[q] / temperature : -INFINITY;
       if (top_k > 0 && top_k < V) {
         // radix select of the k-th largest value, 8 bits at a time from the top;
         // per-wave histograms, then a parallel suffix count finds the digit
@@ -2781,9 +2789,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 #pragma unroll
           for (int q = 0; q < NT / 64; ++q) hist[q * 256 + tid] = 0;
           __syncthreads();
-          for (int i = tid; i < V; i += NT) {
-            const uint32_t key = ord_key(v[i]);
-            if ((key & mask) == prefix) atomicAdd(&hist[wv * 256 + ((key >> shift) & 255u)], 1);
+#pragma unroll
+          for (int q = 0; q < MPT; ++q) {
+            const uint32_t key = ord_key(pv[q]);
+            if (tid + q * NT < V && (key & mask) == prefix) atomicAdd(&hist[wv * 256 + ((key >> shift) & 255u)], 1);
           }
           __syncthreads();
           int h = 0;   // count of digit tid
@@ -2810,23 +2819,87 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           __syncthreads();
         }
         const float tau = key_float(prefix);
-        for (int i = tid; i < V; i += NT)
-          if (v[i] < tau) v[i] = -INFINITY;
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < MPT; ++q) if (pv[q] < tau) pv[q] = -INFINITY;
       }
       float mx = -INFINITY;
-      for (int i = tid; i < V; i += NT) mx = fmaxf(mx, v[i]);
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) mx = fmaxf(mx, pv[q]);
       mx = block_max(mx, redf);
       float sum = 0.f;
-      for (int i = tid; i < V; i += NT) {
-        const float e = expf(v[i] - mx);
-        v[i] = e;
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) {
+        const float e = expf(pv[q] - mx);
+        pv[q] = e;
         sum += e;
       }
       sum = block_sum(sum, redf);
-      for (int i = tid; i < V; i += NT) v[i] = v[i] / sum;
-      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < MPT; ++q) pv[q] = pv[q] / sum;
     }
+    // Few survivors (p > 0): one wave gathers them (in any order: the sort
+    // below makes the result independent of it), sorts them by (p desc, id
+    // asc) in registers, runs the sequential top-p sum and the race.
+    if (tid == 0) sh_int[2] = 0;
+    __syncthreads();
+    int* tid_list = (int*)cid;
+    float* tp_list = cp;
+#pragma unroll
+    for (int q = 0; q < MPT; ++q) {
+      const int i = tid + q * NT;
+      if (i < V && pv[q] > 0.f) {
+        const int slot = atomicAdd(&sh_int[2], 1);
+        tp_list[slot] = pv[q];
+        tid_list[slot] = i;
+      }
+    }
+    __syncthreads();
+    const int nsv = sh_int[2];
+    if (nsv <= 64) {
+      if (tid < 64) {
+        const int lane = tid;
+        float pp = lane < nsv ? tp_list[lane] : -1.f;
+        int id = lane < nsv ? tid_list[lane] : 0x7fffffff;
+        // bitonic sort of 64 (p, id) pairs, lane order = (p desc, id asc)
+#pragma unroll
+        for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+          for (int j = k >> 1; j > 0; j >>= 1) {
+            const float po = __shfl_xor(pp, j);
+            const int io = __shfl_xor(id, j);
+            const bool o_first = po > pp || (po == pp && io < id);
+            const bool lower = (lane & j) == 0, up = (lane & k) == 0;
+            // the lower lane of a pair keeps the element that comes first in an up block
+            const bool take = (lower == up) ? o_first : !o_first;
+            if (take) { pp = po; id = io; }
+          }
+        // sequential fp32 running sum in that order (lane 0 of the wave)
+        int keep = nsv;
+        if (top_p < 1.0f) {
+          float cs = 0.f;
+          keep = nsv;
+          for (int j = 0; j < nsv; ++j) {
+            cs += __shfl(pp, j);
+            if (cs >= top_p) { keep = j + 1; break; }
+          }
+        }
+        float sc = -INFINITY;
+        int bi = 0x7fffffff;
+        if (lane < keep) {
+          const float e = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, r, a.stream, jsel, id);
+          sc = pp / e;
+          bi = id;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) better(sc, bi, __shfl_xor(sc, o), __shfl_xor(bi, o));
+        if (lane == 0) sh_int[2] = bi < V ? bi : 0;
+      }
+      __syncthreads();
+      choice = sh_int[2];
+    } else {
+#pragma unroll
+    for (int q = 0; q < MPT; ++q) if (tid + q * NT < V) v[tid + q * NT] = pv[q];
+    __syncthreads();
     // compact survivors (p > 0) in index order: contiguous chunk per thread + scan
     const int chunk = (V + NT - 1) / NT;
     const int b0 = tid * chunk, b1 = min(V, b0 + chunk);
@@ -2852,19 +2925,49 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int i = b0; i < b1; ++i)
       if (v[i] > 0.f) { cp[o] = v[i]; cid[o] = i; ++o; }
     __syncthreads();
-    // order by (p desc, id asc) via ranks
-    for (int c = tid; c < ns; c += NT) {
-      const float pc = cp[c];
-      const int ic = cid[c];
-      int rank = 0;
-      for (int j = 0; j < ns; ++j) {
-        const float pj = cp[j];
-        rank += (pj > pc) || (pj == pc && cid[j] < ic);
+    // Order by (p desc, id asc), which only top-p needs (the race is order
+    // free): ranks for a few survivors, a bitonic sort of the padded list in
+    // place for many.
+    const float* spo = sp;
+    const int* sido = sid;
+    if (top_p >= 1.0f) {
+      spo = cp;
+      sido = cid;
+    } else if (ns <= 2 * NT) {
+      for (int c = tid; c < ns; c += NT) {
+        const float pc = cp[c];
+        const int ic = cid[c];
+        int rank = 0;
+        for (int j = 0; j < ns; ++j) {
+          const float pj = cp[j];
+          rank += (pj > pc) || (pj == pc && cid[j] < ic);
+        }
+        sp[rank] = pc;
+        sid[rank] = ic;
       }
-      sp[rank] = pc;
-      sid[rank] = ic;
+      __syncthreads();
+    } else {
+      for (int i = ns + tid; i < P2; i += NT) { cp[i] = -1.f; cid[i] = 0x7fffffff; }   // padding sorts last
+      __syncthreads();
+      for (int k = 2; k <= P2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < P2; i += NT) {
+            const int l = i ^ j;
+            if (l > i) {
+              const float pa = cp[i], pb = cp[l];
+              const int ia = cid[i], ib = cid[l];
+              const bool b_first = pb > pa || (pb == pa && ib < ia);
+              const bool a_first = pa > pb || (pa == pb && ia < ib);
+              if ((i & k) == 0 ? b_first : a_first) {
+                cp[i] = pb; cp[l] = pa; cid[i] = ib; cid[l] = ia;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      spo = cp;
+      sido = cid;
     }
-    __syncthreads();
     if (tid == 0) {
       // sequential fp32 cumulative sum in (p desc, id asc) order; reads batched by 8
       int keep = ns;
@@ -2873,7 +2976,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int j0 = 0; j0 < ns && keep == ns; j0 += 8) {
           float t[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) t[e] = j0 + e < ns ? sp[j0 + e] : 0.f;
+          for (int e = 0; e < 8; ++e) t[e] = j0 + e < ns ? spo[j0 + e] : 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             if (keep == ns && j0 + e < ns) {
@@ -2889,13 +2992,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int j = tid; j < keep; j += NT) {
-      const int id = sid[j];
+      const int id = sido[j];
       const float e = a.noise_in ? a.noise_in[(long)r * V + id]
                                  : exp_noise(seed, r, a.stream, jsel, id);
-      better(bv, bi, sp[j] / e, id);
+      better(bv, bi, spo[j] / e, id);
     }
     choice = block_argmax(bv, bi, redf, redi);
     if (choice >= V) choice = 0;
+    }
   }
   }
 
@@ -2958,7 +3062,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 
 template <int MPT>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.V * 5 * sizeof(float);
+  size_t p2 = 1;
+  while (p2 < (size_t)a.V) p2 <<= 1;
+  const size_t lds = ((size_t)a.V * 3 + 2 * p2) * sizeof(float);
   static size_t have = 0;
   hipError_t e = ensure_lds((const void*)select_kernel<MPT>, lds, &have);
   if (e != hipSuccess) return e;
