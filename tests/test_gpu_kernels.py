@@ -146,6 +146,29 @@ def test_select_probs_and_noise_bit_exact():
             assert int(out[r]) == ref, (r, tp)
 
 
+@pytest.mark.parametrize("n_nonzero", [100, 600, 2048])
+def test_select_many_survivors_bit_exact(n_nonzero):
+    """More survivors than one wave holds: the block-wide orderings (ranks up to
+    512 survivors, a bitonic sort beyond) feed the same top-p sum and race."""
+    torch = _torch()
+    B, V = 4, 2048
+    g = np.random.default_rng(50 + n_nonzero)
+    P = np.zeros((B, V), dtype=np.float32)
+    for r in range(B):
+        ids = g.choice(V, size=n_nonzero, replace=False)
+        w = g.integers(1, 9, size=ids.size).astype(np.float64)   # many equal p: id order breaks the ties
+        P[r, ids] = (w / w.sum()).astype(np.float32)
+    E = g.exponential(size=(B, V)).astype(np.float32) + np.float32(1e-3)
+    for tp in (0.8, 1.0, 0.3):
+        samp = dict(synth.PRED_SAMPLING, top_p=tp, top_k=0)
+        out, _, _ = binding.debug_select(torch.from_numpy(P).cuda(), samp, noise=torch.from_numpy(E).cuda(),
+                                         probs=torch.from_numpy(P).cuda())
+        for r in range(B):
+            keep = sampling.top_p_keep(P[r], tp)
+            ref, _ = sampling.race(P[r], keep, lambda i, r=r: E[r, i])
+            assert int(out[r]) == ref, (n_nonzero, r, tp)
+
+
 def test_device_philox_matches_oracle():
     """Same probabilities, noise drawn on the device vs the oracle's Philox."""
     torch = _torch()
