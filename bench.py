@@ -35,7 +35,7 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 # HBM bytes per launch of the gate/up projection from two rocprofv3 --pmc runs
 # of `bench.py --kernel-only` (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000, scaled by
 # a 64 MiB copy), valid for the kernel source with this SHA-256 prefix only.
-COUNTED_TRAFFIC = {"kernel_src_sha256_16": "b36eda5f0752f15e", "bytes": 12740644}
+COUNTED_TRAFFIC = {"kernel_src_sha256_16": "458f2c1fdca84126", "bytes": 12726234}
 
 
 def counted_traffic():
