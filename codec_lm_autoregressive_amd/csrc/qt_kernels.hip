@@ -1104,6 +1104,135 @@ __global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
   }
 }
 
+// One 256-wide K range per block (the plan with one 4-wave group and one
+// register chunk): every load of the range (activations, then weights, then
+// the gains) leaves before the first use, and each 64-k stage is staged into
+// its own LDS buffer (NB buffers, stage st in buffer st % NB), so one barrier
+// per stage suffices: a wave that writes stage st has passed barrier st - 1,
+// which every wave reaches only after its MFMAs on stage st - 2. With four
+// buffers the stores of a stage never wait on another wave's MFMAs; two
+// buffers halve the LDS so two blocks share a compute unit when the grid has
+// more blocks than there are units. Partial tiles go out with nontemporal
+// stores (the reduce or the attention kernel reads them once).
+template <bool NORM, int NB>
+__global__ __launch_bounds__(NT) void rows_gemm1_kernel(LinearArgs p) {
+  constexpr int XV = SG_T * SG_GK / 4 / NT;   // float4 of X per thread per stage (4)
+  constexpr int WV = SG_T * SG_GK / 8 / NT;   // 16-byte W chunks per thread per stage (2)
+  constexpr int NS = SG_CH / SG_GK;           // stages (4)
+  constexpr int STAGE = 3 * SG_T * SG_LD;     // bf16 elements of one stage: X hi, X lo, W
+  extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
+  __shared__ float rs_lds[SG_T];
+  __shared__ float ss_lds[SG_T];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * SG_T, m0 = blockIdx.y * SG_T, kb = blockIdx.z * SG_CH;
+  const int M = p.M, N = p.N, K = p.K;
+  const int wc = (tid & 7) * 8, xc = (tid & 15) * 4;
+  f32x4 xv[NS][XV];
+  u32x4 wv[NS][WV];
+  f32x4 gv[NS];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const float* xr = p.X + (long)min(m0 + (tid >> 4) + 16 * q, M - 1) * p.ldx + kb + xc;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) xv[st][q] = *(const f32x4*)(xr + st * SG_GK);
+  }
+#pragma unroll
+  for (int q = 0; q < WV; ++q) {
+    const uint16_t* wr = (const uint16_t*)p.W + (long)min(n0 + (tid >> 3) + 32 * q, N - 1) * K + kb + wc;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) wv[st][q] = ld_weight(wr + st * SG_GK);
+  }
+  if constexpr (NORM)
+#pragma unroll
+    for (int st = 0; st < NS; ++st) gv[st] = *(const f32x4*)(p.gain + kb + st * SG_GK + xc);
+  float ss[XV];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) ss[q] = 0.f;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    uint16_t* xh = dsm + (st % NB) * STAGE;
+    uint16_t* xl = xh + SG_T * SG_LD;
+    uint16_t* wl = xl + SG_T * SG_LD;
+#pragma unroll
+    for (int q = 0; q < WV; ++q) *(u32x4*)&wl[((tid >> 3) + 32 * q) * SG_LD + wc] = wv[st][q];
+    f32x4 g = (f32x4){1.f, 1.f, 1.f, 1.f};
+    if constexpr (NORM) g = gv[st];
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const f32x4 v = xv[st][q];
+      if constexpr (NORM) ss[q] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      uint32_t h0, l0, h1, l1;
+      split_pk(v.x * g.x, v.y * g.y, h0, l0);
+      split_pk(v.z * g.z, v.w * g.w, h1, l1);
+      const int r = (tid >> 4) + 16 * q;
+      *(uint2*)&xh[r * SG_LD + xc] = make_uint2(h0, h1);
+      *(uint2*)&xl[r * SG_LD + xc] = make_uint2(l0, l1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < SG_GK; kk += 16) {
+      const int k = kk + 8 * (lane >> 5);
+      const bf16x8 ah = *(const bf16x8*)&xh[(wm * 32 + (lane & 31)) * SG_LD + k];
+      const bf16x8 al = *(const bf16x8*)&xl[(wm * 32 + (lane & 31)) * SG_LD + k];
+      const bf16x8 bw = *(const bf16x8*)&wl[(wn * 32 + (lane & 31)) * SG_LD + k];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bw, acc, 0, 0, 0);
+    }
+  }
+  const bool direct = gridDim.z == 1;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) ss[q] = row16_sum(ss[q]);   // the 16 lanes of a row hold its k slices
+    if ((tid & 15) == 0)
+#pragma unroll
+      for (int q = 0; q < XV; ++q) ss_lds[(tid >> 4) + 16 * q] = ss[q];
+    __syncthreads();
+    if (tid < SG_T) {
+      const int row = m0 + tid;
+      if (direct) rs_lds[tid] = 1.f / sqrtf(ss_lds[tid] / (float)K + p.eps);
+      else if (blockIdx.x == 0 && row < M) p.part[(long)gridDim.z * M * N + (long)blockIdx.z * M + row] = ss_lds[tid];
+    }
+    if (direct) {
+      __syncthreads();
+      if (p.norm_out && blockIdx.x == 0)
+        for (int k = xc; k < K; k += SG_GK)
+#pragma unroll
+          for (int q = 0; q < XV; ++q) {
+            const int r = (tid >> 4) + 16 * q, row = m0 + r;
+            if (row < M) {
+              const f32x4 v = *(const f32x4*)(p.X + (long)row * p.ldx + k), g = *(const f32x4*)(p.gain + k);
+              const float rs = rs_lds[r];
+              *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) =
+                  (f32x4){v.x * g.x * rs, v.y * g.y * rs, v.z * g.z * rs, v.w * g.w * rs};
+            }
+          }
+    }
+  }
+  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  const int col = n0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), row = m0 + lr;
+    float v = acc[r];
+    if (!direct) {
+      if (row < M && col < N) __builtin_nontemporal_store(v, p.part + ((long)blockIdx.z * M + row) * N + col);
+      continue;
+    }
+    if constexpr (NORM) v *= rs_lds[lr];
+    if (p.epi == EPI_SWIGLU) {
+      const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
+      if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
+    } else if (row < M && col < N) {
+      float* y = p.Y + (long)row * p.ldy + col;
+      *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+    }
+  }
+}
+
 // Adds the Z partial tiles of each output in order z = 0..Z-1, applies the
 // row's RMS scale (sums of squares added in the same order) and the epilogue;
 // one thread per 4 consecutive columns (N % 4 == 0). Also writes norm_out.
@@ -1236,9 +1365,28 @@ static hipError_t launch_rows_g(const LinearArgs& a, const RowsPlan& pl, dim3 gr
   return launch_rows_n<NORM, 1>(a, pl.NCH, grid, s);
 }
 
+template <bool NORM, int NB>
+static hipError_t launch_rows1(const LinearArgs& a, dim3 grid, hipStream_t s) {
+  static size_t have = 0;
+  const size_t lds = (size_t)NB * 3 * SG_T * SG_LD * sizeof(uint16_t);
+  hipError_t e = ensure_lds((const void*)rows_gemm1_kernel<NORM, NB>, lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rows_gemm1_kernel<NORM, NB>), grid, dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
 static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream_t s) {
   dim3 grid((a.N + SG_T - 1) / SG_T, (a.M + SG_T - 1) / SG_T, pl.Z);
-  hipError_t e = a.gain ? launch_rows_g<true>(a, pl, grid, s) : launch_rows_g<false>(a, pl, grid, s);
+  hipError_t e;
+  if (pl.KW == 1 && pl.NCH == 1) {
+    // four stage buffers (110 KB of LDS, one block per compute unit) while the grid fits the
+    // 256 units, else two (55 KB, two blocks per unit)
+    const bool wide = (long)grid.x * grid.y * grid.z > 256;
+    e = a.gain ? (wide ? launch_rows1<true, 2>(a, grid, s) : launch_rows1<true, 4>(a, grid, s))
+               : (wide ? launch_rows1<false, 2>(a, grid, s) : launch_rows1<false, 4>(a, grid, s));
+  } else {
+    e = a.gain ? launch_rows_g<true>(a, pl, grid, s) : launch_rows_g<false>(a, pl, grid, s);
+  }
   if (e != hipSuccess || pl.Z == 1 || a.defer) return e;
   const long threads = (long)a.M * (a.N / 4);
   const dim3 grid_r((unsigned)((threads + NT - 1) / NT));

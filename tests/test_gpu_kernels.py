@@ -44,7 +44,8 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
                                    (1024, 3072, 16), (200, 96, 130), (6144, 1024, 257), (2048, 2048, 1024),
                                    (200, 1024, 12), (1000, 768, 30), (4096, 2048, 24), (1024, 3072, 128),
                                    (2052, 512, 100), (2048, 1024, 3), (3072, 2048, 16), (4096, 512, 7),
-                                   (2048, 256, 4), (2056, 1536, 11), (6144, 1024, 32), (2048, 3072, 20)])
+                                   (2048, 256, 4), (2056, 1536, 11), (6144, 1024, 32), (2048, 3072, 20),
+                                   (6144, 1024, 64), (1024, 256, 40), (4096, 1024, 48)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row and split-K scratch, which routes bf16
