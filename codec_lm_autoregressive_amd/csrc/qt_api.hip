@@ -133,8 +133,8 @@ struct Layout {
   std::vector<LayerBuf> tl, pl;
   size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj;
   size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
-  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den, part;
-  long part_floats;
+  size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den, part, xsplit;
+  long part_floats, xsplit_floats;
   size_t rowstate, seen, runs, idx, frame_out, req;
   size_t total;
   int tmax, seen_words, max_runs;
@@ -209,6 +209,12 @@ Layout plan_layout(const qt_config& c) {
     L.part_floats = (long)need;
     L.part = p.take(p.sz.mul({need, 4}));
   }
+  // bf16 hi/lo split of the activations of one prefill chunk (projections of more than 128 rows)
+  {
+    const size_t kmax = std::max({(size_t)t.H, (size_t)q.H, (size_t)t.nqd, (size_t)q.nqd, Im});
+    L.xsplit_floats = T > 128 ? (long)(T * kmax) : 0;
+    L.xsplit = T > 128 ? p.take(p.sz.mul({T, kmax, 4})) : 0;
+  }
   (void)Hm;
   // row state: code0_next, finished, pos, text_off, text_len [B]; frame_k; own/forced [B,16]
   L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
@@ -247,8 +253,8 @@ struct qt_ctx {
   void *temb, *thead, *pemb, *phead, *pproj;
   float *cos_t, *sin_t, *cos_p, *sin_p;
   void *kc_t, *vc_t, *kc_p, *vc_p;
-  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den, *part;
-  long part_floats;
+  float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den, *part, *xsplit;
+  long part_floats, xsplit_floats;
   int *code0_next, *finished, *pos, *text_off, *text_len, *frame_k, *own, *forced;
   uint32_t* seen;
   Run* runs;
@@ -348,7 +354,7 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     LinearArgs a{};
     a.wdtype = ctx->cfg.weight_dtype;
     a.eps = d.eps;
-    a.row_den = ctx->row_den;
+    a.row_den = ctx->row_den; a.xs = ctx->xsplit; a.xs_floats = ctx->xsplit_floats;
     a.part = ctx->part; a.part_floats = ctx->part_floats;
     // q/k/v = W_qkv · RMSNorm(x)
     a.W = w.wqkv; a.N = d.qkv; a.K = d.H; a.X = x; a.ldx = d.H; a.M = M; a.gain = w.attn_norm;
@@ -455,7 +461,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   HIPCK(launch_frame_start(fs, s));
 
   LinearArgs pa{};
-  pa.row_den = ctx->row_den;
+  pa.row_den = ctx->row_den; pa.xs = ctx->xsplit; pa.xs_floats = ctx->xsplit_floats;
   pa.part = ctx->part; pa.part_floats = ctx->part_floats;
   pa.wdtype = wd; pa.W = ctx->pproj; pa.N = P.H; pa.K = T.H; pa.X = ctx->xin_w; pa.ldx = T.H;
   pa.Y = ctx->x_p; pa.ldy = P.H; pa.epi = EPI_STORE;
@@ -467,7 +473,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true)); }
     // head st on the last token of each row
     LinearArgs ha{};
-    ha.row_den = ctx->row_den;
+    ha.row_den = ctx->row_den; ha.xs = ctx->xsplit; ha.xs_floats = ctx->xsplit_floats;
     ha.part = ctx->part; ha.part_floats = ctx->part_floats;
     ha.wdtype = wd; ha.W = (const char*)ctx->phead + (size_t)st * C * P.H * esize(wd); ha.N = C; ha.K = P.H;
     ha.X = st == 0 ? ctx->x_p + P.H : ctx->x_p; ha.ldx = st == 0 ? 2L * P.H : P.H; ha.M = B;
@@ -491,7 +497,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   // talker step at position P_r + k
   QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s, false, true));
   LinearArgs ta{};
-  ta.row_den = ctx->row_den;
+  ta.row_den = ctx->row_den; ta.xs = ctx->xsplit; ta.xs_floats = ctx->xsplit_floats;
   ta.part = ctx->part; ta.part_floats = ctx->part_floats;
   ta.wdtype = wd; ta.W = ctx->thead; ta.N = ctx->cfg.talker_vocab; ta.K = T.H; ta.X = ctx->x_t; ta.ldx = T.H; ta.M = B;
   ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = ctx->cfg.talker_vocab; ta.epi = EPI_STORE;
@@ -620,6 +626,8 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
   ctx->row_den = at<float>(ctx, L.row_den);
   ctx->part = at<float>(ctx, L.part);
   ctx->part_floats = L.part_floats;
+  ctx->xsplit = L.xsplit_floats > 0 ? at<float>(ctx, L.xsplit) : nullptr;
+  ctx->xsplit_floats = L.xsplit_floats;
   int* rs = at<int>(ctx, L.rowstate);
   const int MB = cfg->max_batch;
   ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->text_off = rs + 3 * MB;
@@ -775,7 +783,7 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
                              T.H, s));
   }
   LinearArgs ta{};
-  ta.row_den = ctx->row_den;
+  ta.row_den = ctx->row_den; ta.xs = ctx->xsplit; ta.xs_floats = ctx->xsplit_floats;
   ta.part = ctx->part; ta.part_floats = ctx->part_floats;
   ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H; ta.X = ctx->xlast; ta.ldx = T.H;
   ta.M = B; ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = c.talker_vocab;
@@ -970,7 +978,10 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
   if (scratch && scratch_floats >= M) {
     const long den = ((long)M + 63) / 64 * 64;   // partial sums start 256-byte aligned
     a.row_den = scratch;
-    if (scratch_floats > den) { a.part = scratch + den; a.part_floats = scratch_floats - den; }
+    if (scratch_floats > den) {
+      a.part = scratch + den; a.part_floats = scratch_floats - den;
+      a.xs = a.part; a.xs_floats = a.part_floats;   // the split of > 128 rows needs no partial sums
+    }
   }
   if (w_copies < 1 || (w_copies > 1 && w_copy_stride < (int64_t)N * K * (wdtype == QT_DTYPE_BF16 ? 2 : 4))) {
     set_err(g_err, "w_copies must be >= 1 and copies must not overlap");

@@ -25,6 +25,8 @@ struct LinearArgs {
   float* row_den;                      // [M] scratch for the matrix-core path (nullptr: not used)
   float* part; long part_floats;       // split-K partial sums for 17..128 rows (nullptr: not used)
   int defer;                           // split K: leave the partial sums for the consumer (no reduce)
+  void* xs; long xs_floats;            // > 128 rows: scratch for the bf16 hi/lo split of the
+                                       // (normalised) activations, M * K floats (nullptr: not used)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 // K ranges the launch of a would split into (partial sums in a.part: range z,

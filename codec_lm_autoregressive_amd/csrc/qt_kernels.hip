@@ -714,6 +714,179 @@ __global__ __launch_bounds__(NT) void row_norm_kernel(LinearArgs p, float* den) 
     for (int k = threadIdx.x; k < p.K; k += NT) p.norm_out[(long)m * p.ld_norm + k] = x[k] / d * p.gain[k];
 }
 
+// ---------------------------------------------------------------- prefill GEMM
+// Projection of many activation rows (prompt prefill chunks). A prologue
+// kernel normalises each row once (RMSNorm and gain when a gain is given) and
+// splits it into bf16 hi + lo planes, xs = [2][M][K]; the GEMM then reads
+// plain bf16 tiles of both planes and of W. Block = 4 waves in a 2 x 2 grid on
+// a (64 TM) x (64 TN) tile, each wave a TM x TN grid of 32 x 32
+// v_mfma_f32_32x32x16_bf16 tiles (hi and lo products into one accumulator).
+// K runs in stages of 32 through two LDS buffers: the global loads of stage
+// s + 1 are in flight while stage s is contracted, then stored to the other
+// buffer, so one barrier per stage keeps every buffer's readers and writers
+// apart (a buffer is rewritten only after the barrier that ends its reads).
+__global__ __launch_bounds__(NT) void split_rows_kernel(LinearArgs p, uint16_t* __restrict__ xs) {
+  __shared__ float red[8];
+  const int m = blockIdx.x, K = p.K;
+  const float* x = p.X + (long)m * p.ldx;
+  float rs = 1.f;
+  if (p.gain) {
+    float ss = 0.f;
+    for (int k = 4 * threadIdx.x; k < K; k += 4 * NT) {
+      const f32x4 v = *(const f32x4*)(x + k);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum(ss, red);
+    rs = 1.f / sqrtf(ss / (float)K + p.eps);
+  }
+  uint16_t* hi = xs + (long)m * K;
+  uint16_t* lo = xs + ((long)p.M + m) * K;
+  for (int k = 4 * threadIdx.x; k < K; k += 4 * NT) {
+    f32x4 v = *(const f32x4*)(x + k);
+    if (p.gain) {
+      const f32x4 g = *(const f32x4*)(p.gain + k);
+      v = (f32x4){v.x * rs * g.x, v.y * rs * g.y, v.z * rs * g.z, v.w * rs * g.w};
+      if (p.norm_out) *(f32x4*)(p.norm_out + (long)m * p.ld_norm + k) = v;
+    }
+    uint32_t h0, l0, h1, l1;
+    split_pk(v.x, v.y, h0, l0);
+    split_pk(v.z, v.w, h1, l1);
+    *(uint2*)(hi + k) = make_uint2(h0, h1);
+    *(uint2*)(lo + k) = make_uint2(l0, l1);
+  }
+}
+
+template <int TM, int TN>
+__global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  constexpr int AV = BM * GK / 8 / NT;            // 16-byte chunks per thread per stage, each A plane
+  constexpr int BV = BN * GK / 8 / NT;            // and of W
+  constexpr int BUF = (2 * BM + BN) * GLD;        // bf16 elements of one stage: A hi, A lo, W
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * BUF];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  // staging slots: A rows idx / 4 (4 chunks of 8 per 32-k row), W rows likewise
+  const uint16_t* ah_src[AV];
+  const uint16_t* al_src[AV];
+  const uint16_t* w_src[BV];
+  int a_off[AV], w_off[BV];
+#pragma unroll
+  for (int q = 0; q < AV; ++q) {
+    const int idx = tid + q * NT, r = idx >> 2, c = (idx & 3) * 8;
+    const long row = min(m0 + r, M - 1);
+    ah_src[q] = xs + row * K + c;
+    al_src[q] = xs + ((long)M + row) * K + c;
+    a_off[q] = r * GLD + c;
+  }
+#pragma unroll
+  for (int q = 0; q < BV; ++q) {
+    const int idx = tid + q * NT, r = idx >> 2, c = (idx & 3) * 8;
+    w_src[q] = (const uint16_t*)p.W + (long)min(n0 + r, N - 1) * K + c;
+    w_off[q] = r * GLD + c;
+  }
+  u32x4 ra_h[AV], ra_l[AV], rw[BV];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < AV; ++q) { ra_h[q] = *(const u32x4*)(ah_src[q] + k0); ra_l[q] = *(const u32x4*)(al_src[q] + k0); }
+#pragma unroll
+    for (int q = 0; q < BV; ++q) rw[q] = *(const u32x4*)(w_src[q] + k0);
+  };
+  auto store = [&](int b) __attribute__((always_inline)) {
+    uint16_t* base = sm + b * BUF;
+#pragma unroll
+    for (int q = 0; q < AV; ++q) {
+      *(u32x4*)&base[a_off[q]] = ra_h[q];
+      *(u32x4*)&base[BM * GLD + a_off[q]] = ra_l[q];
+    }
+#pragma unroll
+    for (int q = 0; q < BV; ++q) *(u32x4*)&base[2 * BM * GLD + w_off[q]] = rw[q];
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int S = K / GK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < S; ++st) {
+    if (st + 1 < S) load((st + 1) * GK);
+    const uint16_t* base = sm + (st & 1) * BUF;
+#pragma unroll
+    for (int ks = 0; ks < GK; ks += 16) {
+      const int kk = ks + (lane >> 5) * 8;
+      bf16x8 ah[TM], al[TM], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+        ah[i] = *(const bf16x8*)&base[r * GLD + kk];
+        al[i] = *(const bf16x8*)&base[BM * GLD + r * GLD + kk];
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * (BN / 2) + j * 32 + (lane & 31);
+        bv[j] = *(const bf16x8*)&base[2 * BM * GLD + r * GLD + kk];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    if (st + 1 < S) store((st + 1) & 1);
+    __syncthreads();
+  }
+  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+#pragma unroll
+  for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < TN; ++tj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = m0 + wm * (BM / 2) + ti * 32 + i;
+        const int col = n0 + wn * (BN / 2) + tj * 32 + (lane & 31);
+        const float v = acc[ti][tj][r];
+        if (p.epi == EPI_SWIGLU) {
+          const float u = __shfl_xor(v, 1);   // the (gate, up) pair sits in lanes 2c, 2c+1
+          if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * u;
+        } else if (row < M && col < N) {
+          float* y = p.Y + (long)row * p.ldy + col;
+          *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+        }
+      }
+}
+
+// The split GEMM needs K % 32 == 0, rows of 16-byte aligned activations and
+// the split scratch; 128 x 128 tiles while they give at least 256 blocks,
+// else 64 x 128.
+static bool gemm_split_fits(const LinearArgs& a) {
+  return a.wdtype == DT_BF16 && a.K % GK == 0 && a.ldx % 4 == 0 && a.xs && a.xs_floats >= (long)a.M * a.K;
+}
+
+static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
+  uint16_t* xs = (uint16_t*)a.xs;
+  hipLaunchKernelGGL(split_rows_kernel, dim3(a.M), dim3(NT), 0, s, a, xs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (big >= 256) {
+    dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
+    hipLaunchKernelGGL((gemm_split_kernel<2, 2>), grid, dim3(NT), 0, s, a, xs);
+  } else {
+    dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
+    hipLaunchKernelGGL((gemm_split_kernel<1, 2>), grid, dim3(NT), 0, s, a, xs);
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_mfma(const LinearArgs& a, float* den, hipStream_t s) {
   if (a.gain) {
     hipLaunchKernelGGL(row_norm_kernel, dim3(a.M), dim3(NT), 0, s, a, den);
@@ -1629,6 +1802,7 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
     if (rows_plan(a, &pl)) return launch_rows(a, pl, s);
   }
   // many rows of bf16 weights: matrix-core GEMM (needs K % 32 == 0 and row scratch)
+  if (a.M >= MFMA_MIN_ROWS && gemm_split_fits(a)) return launch_gemm_split(a, s);
   if (a.wdtype == DT_BF16 && a.M >= MFMA_MIN_ROWS && a.K % GK == 0 && a.row_den)
     return launch_mfma(a, a.row_den, s);
   // activation tile: as many rows as fit in 96 KB of LDS, up to 8

@@ -234,7 +234,9 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
  *   the frame's matrix-core kernels run: at least M floats (row RMS
  *   denominators) enable the tiled MFMA GEMM; beyond the first M rounded up
  *   to 64 floats, space for K-range partial sums (up to (K / 256) * M * (N + 1)
- *   floats) lets the row-block MFMA GEMM for 17..128 rows split K.
+ *   floats) lets the row-block MFMA GEMM for 17..128 rows split K, and
+ *   M * K floats there let more than 128 rows take the split-activation GEMM
+ *   (the rows normalised once and held as bf16 hi + lo planes).
  *   reps >= 1 launches (for timing); launch i uses the weight copy
  *   W + (i % w_copies) * w_copy_stride bytes (w_copies >= 1; copies of at
  *   least N * K elements each, so timed launches can stream from HBM rather
