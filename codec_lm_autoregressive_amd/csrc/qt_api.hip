@@ -22,7 +22,7 @@ thread_local char g_err[512] = "";
 
 constexpr int kGroups = 16;       // codes per frame
 constexpr int kPredPositions = 16;
-constexpr int kPrefillChunk = 1024;
+constexpr int kPrefillChunk = 4096;
 constexpr int kMaxVocab = 6144;
 
 void set_err(char* buf, const char* fmt, ...) {
