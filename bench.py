@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, vendor figure
 FRAMES_PER_AUDIO_SECOND = 12.5
 
 # HBM bytes per launch of the gate/up projection from two rocprofv3 --pmc runs
@@ -130,7 +131,10 @@ class Workload:
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         wl, eng, stream = self.wl, self.eng, self.eng.stream
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
         eng.prefill(self.prompt, self.lens, self.pad, wl["talker"], wl["predictor"], 0, self.frames)
+        prefill_ms = (time.perf_counter() - tp) * 1000   # qt_prefill ends with its stream synchronised
         eng.step_frame()  # the first frame after a prefill runs eagerly; later ones replay the graph
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nf = 0
@@ -151,7 +155,8 @@ class Workload:
         fb = frame_bytes(self.dm, self.B, mean_ctx, wbytes, 2 if self.kv != "f32" else 4)
         value = row_frames / dt
         return dict(value=value, dt=dt, steps=steps, total_frames=total_frames, frame_ms=frame_ms, fb=fb,
-                    ms_per_step=dt * 1000 / steps)
+                    ms_per_step=dt * 1000 / steps, prefill_ms=prefill_ms,
+                    prefill_flops=prefill_linear_flops(self.dm, int(np.sum(self.lens))))
 
     def config(self, total_frames, steps):
         wl, dm = self.wl, self.dm
@@ -160,6 +165,22 @@ class Workload:
                 "talker_layers": dm["talker"]["layers"], "predictor_layers": dm["predictor"]["layers"],
                 "hidden": dm["talker"]["hidden"], "kv_cache": self.kv,
                 "sampling": "sampled" if wl["talker"]["do_sample"] else "greedy"}
+
+
+def prefill_linear_flops(dm, tokens):
+    """Useful flops of the prompt prefill's projections: 2 per weight per
+    prompt token over the talker's layers (the hi/lo split of the activations
+    doubles the matrix-core work; that is not counted)."""
+    t = dm["talker"]
+    H, d, I = t["hidden"], t["head_dim"], t["intermediate"]
+    per_layer = H * (t["n_heads"] + 2 * t["n_kv_heads"]) * d + t["n_heads"] * d * H + 3 * I * H
+    return 2.0 * tokens * per_layer * t["layers"]
+
+
+def prefill_roof(q):
+    tf = q["prefill_flops"] / (q["prefill_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "flops": q["prefill_flops"], "ms": round(q["prefill_ms"], 3)}
 
 
 def roof(fb, frame_ms):
@@ -212,6 +233,8 @@ def main():
                         "decode_frames_per_s": round(x.B * 1000.0 / q["frame_ms"], 1),
                         "rtf": round(FRAMES_PER_AUDIO_SECOND * x.B / q["value"], 6) if q["value"] else None,
                         "frame_roofline": roof(q["fb"], q["frame_ms"]),
+                        "prefill_tokens": int(np.sum(x.lens)),
+                        "prefill_roofline": prefill_roof(q),
                         "config": x.config(q["total_frames"], 1)})
         x.eng.close()
         del x

@@ -1577,9 +1577,10 @@ static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream
 }
 
 static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng);
+static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns);
 int linear_split_ranges(const LinearArgs& a) {
   int ksw, ng;
-  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a) || mfma_gemv_plan(a, &ksw, &ng)) return 1;
+  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a) || mfma_gemv_plan(a, &ksw, &ng) || mfma_gemv8_plan(a, &ksw, &ng)) return 1;
   RowsPlan pl;
   return rows_plan(a, &pl) ? pl.Z : 1;
 }
@@ -1782,6 +1783,160 @@ static hipError_t launch_mfma_gemv(const LinearArgs& a, int ksw, int ng, hipStre
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------- 8-row matrix-core GEMV
+// Projection of 3..8 activation rows on tiles of 8 weight rows. One
+// v_mfma_f32_16x16x32_bf16 covers 64 k of the tile: A rows 0-7 are the
+// activation rows on the first 32 k, rows 8-15 the same activation rows on the
+// next 32 k, and B columns 0-7 / 8-15 the 8 weight rows on the same two k
+// halves, so the two diagonal 8 x 8 blocks of the product are the tile's
+// partial sums over the two halves (the off-diagonal blocks are discarded)
+// and lane l's 16-byte weight load is row l % 8 at k offset 32 ((l / 8) % 2)
+// + 8 (l / 16): eight lanes read 128 contiguous bytes of a row. Half-height
+// tiles give twice the blocks of the 16-row GEMV, so wide outputs fill every
+// compute unit evenly. Block = KSW waves over K, NS steps of 64 k per wave,
+// every load issued before the first use (activations and gains, then
+// weights); the waves' tiles and row sums of squares are added in LDS in wave
+// order and RMSNorm is applied as a per-row scale after the contraction.
+template <int KSW, int NS, bool NORM>
+__global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r8 = lane & 7, koff = 32 * ((lane >> 3) & 1) + 8 * (lane >> 4);
+  const int n0 = blockIdx.x * 8;
+  const int M = p.M, N = p.N, K = p.K;
+  const int kw0 = w * NS * 64 + koff;
+  __shared__ __align__(16) float red[KSW][64][4];
+  __shared__ float ssr[KSW][8];
+  __shared__ float inv_s[8];
+  const float* xr = p.X + (long)min(r8, M - 1) * p.ldx + kw0;
+  const uint16_t* wr = (const uint16_t*)p.W + (long)min(n0 + r8, N - 1) * K + kw0;
+  f32x4 xv[NS][2], gv[NS][2];
+  u32x4 wv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    xv[s][0] = *(const f32x4*)(xr + 64 * s);
+    xv[s][1] = *(const f32x4*)(xr + 64 * s + 4);
+  }
+  if constexpr (NORM)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      gv[s][0] = *(const f32x4*)(p.gain + kw0 + 64 * s);
+      gv[s][1] = *(const f32x4*)(p.gain + kw0 + 64 * s + 4);
+    }
+  // output (i, j) of this lane after the half combine: activation row 4 (lane / 16) + r, weight row lane % 16
+  const bool owner = (lane & 15) < 8 && lane < 32;
+  float yold[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.epi == EPI_RESIDUAL && owner && w == 0)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yold[r] = p.Y[(long)min(4 * (lane >> 4) + r, M - 1) * p.ldy + min(n0 + (lane & 15), N - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) wv[s] = ld_weight(wr + 64 * s);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float x[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w, xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
+    if constexpr (NORM) {
+      const float g[8] = {gv[s][0].x, gv[s][0].y, gv[s][0].z, gv[s][0].w, gv[s][1].x, gv[s][1].y, gv[s][1].z, gv[s][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { ss = fmaf(x[e], x[e], ss); x[e] *= g[e]; }
+    }
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
+    const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[s]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]}), bw, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]}), bw, acc, 0, 0, 0);
+  }
+  // D(i, j): lane j + 16 (i / 4), register i % 4; block (i + 8, j + 8) sits 40 lanes up
+  f32x4 hi;
+  hi.x = __shfl(acc.x, (lane + 40) & 63); hi.y = __shfl(acc.y, (lane + 40) & 63);
+  hi.z = __shfl(acc.z, (lane + 40) & 63); hi.w = __shfl(acc.w, (lane + 40) & 63);
+  *(f32x4*)red[w][lane] = acc + hi;
+  if constexpr (NORM) {
+    ss += __shfl_xor(ss, 8);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (lane < 8) ssr[w][lane] = ss;
+  }
+  __syncthreads();
+  if constexpr (NORM) {
+    if (threadIdx.x < 8) {
+      float t = ssr[0][threadIdx.x];
+#pragma unroll
+      for (int q = 1; q < KSW; ++q) t += ssr[q][threadIdx.x];
+      inv_s[threadIdx.x] = 1.f / sqrtf(t / (float)K + p.eps);
+    }
+    __syncthreads();
+  }
+  if (w != 0) return;
+  if constexpr (NORM)
+    if (p.norm_out && blockIdx.x == 0)
+      for (int e = lane; e < M * (K / 4); e += 64) {
+        const int row = e / (K / 4), k = (e % (K / 4)) * 4;
+        const f32x4 xx = *(const f32x4*)(p.X + (long)row * p.ldx + k), gg = *(const f32x4*)(p.gain + k);
+        const float sc = inv_s[row];
+        *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) = (f32x4){xx.x * gg.x * sc, xx.y * gg.y * sc, xx.z * gg.z * sc, xx.w * gg.w * sc};
+      }
+  f32x4 v = *(const f32x4*)red[0][lane];
+#pragma unroll
+  for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][lane];
+  const int col = n0 + (lane & 15);
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    float o = vv[r];
+    if constexpr (NORM) o *= inv_s[row & 7];
+    if (p.epi == EPI_SWIGLU) {
+      const float up = __shfl_xor(o, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
+      if (owner && !(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = o / (1.f + expf(-o)) * up;
+    } else if (owner && row < M && col < N) {
+      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[r] + o : o;
+    }
+  }
+}
+
+// 3..8 rows of bf16 weights, K a multiple of 64 KSW with at most 6 steps per
+// wave: 4 waves per block, 8 when the grid has fewer than 256 blocks or K is
+// long.
+static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns) {
+  if (a.wdtype != DT_BF16 || a.M < 3 || a.M > 8 || a.ldx % 4 || a.defer) return false;
+  // a 16-row GEMV grid that is already a multiple of the 256 compute units stays (measured equal or better)
+  {
+    int k16, g16;
+    if (mfma_gemv_plan(a, &k16, &g16) && ((a.N + 15) / 16) % 256 == 0) return false;
+  }
+  for (int k : {4, 8}) {
+    if (k == 4 && (a.N + 7) / 8 < 256) continue;
+    if (a.K % (64 * k)) continue;
+    const int n = a.K / (64 * k);
+    if (n >= 1 && n <= 6) { *ksw = k; *ns = n; return true; }
+  }
+  return false;
+}
+
+template <int KSW, bool NORM>
+static hipError_t launch_mfma_gemv8_k(const LinearArgs& a, int ns, hipStream_t s) {
+  const dim3 grid((a.N + 7) / 8), block(KSW * 64);
+  switch (ns) {
+    case 1: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 1, NORM>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 2, NORM>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 3, NORM>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 4, NORM>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 5, NORM>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 6, NORM>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_mfma_gemv8(const LinearArgs& a, int ksw, int ns, hipStream_t s) {
+  if (ksw == 4) return a.gain ? launch_mfma_gemv8_k<4, true>(a, ns, s) : launch_mfma_gemv8_k<4, false>(a, ns, s);
+  return a.gain ? launch_mfma_gemv8_k<8, true>(a, ns, s) : launch_mfma_gemv8_k<8, false>(a, ns, s);
+}
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
@@ -1793,6 +1948,7 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   // the row-block weight-streaming MFMA kernel
   {
     int ksw, ng;
+    if (mfma_gemv8_plan(a, &ksw, &ng)) return launch_mfma_gemv8(a, ksw, ng, s);
     if (mfma_gemv_plan(a, &ksw, &ng)) return launch_mfma_gemv(a, ksw, ng, s);
   }
   if (skinny_fits(a)) return launch_skinny(a, s);

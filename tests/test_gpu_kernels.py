@@ -45,14 +45,17 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
                                    (200, 1024, 12), (1000, 768, 30), (4096, 2048, 24), (1024, 3072, 128),
                                    (2052, 512, 100), (2048, 1024, 3), (3072, 2048, 16), (4096, 512, 7),
                                    (2048, 256, 4), (2056, 1536, 11), (6144, 1024, 32), (2048, 3072, 20),
-                                   (6144, 1024, 64), (1024, 256, 40), (4096, 1024, 48)])
+                                   (6144, 1024, 64), (1024, 256, 40), (4096, 1024, 48),
+                                   (3072, 1024, 8), (2048, 1024, 6), (1000, 2048, 4)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row and split-K scratch, which routes bf16
     weights with 17..128 rows to the split-K MFMA GEMM and more rows to the
-    tiled MFMA GEMM; without it they take the LDS-tile FMA kernel. 3..16 rows
-    use the register-operand matrix-core GEMV when N >= 2048 (also up to 32
-    rows) and the skinny MFMA kernel otherwise, either way."""
+    split-activation MFMA GEMM; without it they take the LDS-tile FMA kernel.
+    3..8 rows use the 8-row matrix-core GEMV (the 16-row one when its grid is
+    a multiple of 256 blocks), 9..16 rows the register-operand matrix-core
+    GEMV when N >= 2048 (also up to 32 rows) and the skinny MFMA kernel
+    otherwise, either way."""
     if not mc and (wdt != "bf16" or M < 16):
         pytest.skip("same kernel as the mc=True case")
     torch = _torch()
