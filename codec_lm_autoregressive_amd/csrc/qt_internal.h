@@ -62,6 +62,12 @@ struct AttnArgs {
   // part[(z * part_rows + row) * ld_qkv + col]) / rms(row), the rms from the
   // partial row sums of squares of part_k inputs and part_eps
   const float* part; int part_z; int part_rows; int part_k; float part_eps;
+  // single-token decode over kv_split > 1 key ranges (one block each; the
+  // range that holds the new key writes it to the cache): each block leaves
+  // its running max, softmax sum and unnormalised output in
+  // split_buf[row][kv head][range][head of the group][d + 2], and a second
+  // launch combines the ranges in order
+  int kv_split; float* split_buf;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Single-token code-predictor attention (one batch row, <= 16 positions)

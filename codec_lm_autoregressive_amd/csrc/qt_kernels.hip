@@ -2489,7 +2489,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
 // values stay in LDS. Each thread keeps its own running softmax sums, so a
 // chunk costs one block-wide max exchange; slots, waves and the sums are
 // combined once at the end.
-template <typename KVT, int G, int NTOK, int KCH>
+template <typename KVT, int G, int NTOK, int KCH, bool SPLIT = false>
 __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
   constexpr int D = 128, HALF = 64;
   constexpr int EPC = 16 / sizeof(KVT);      // cache elements per 16-byte chunk
@@ -2518,11 +2518,24 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
   // groups of keys past them are neither loaded nor computed (the group
   // tests are uniform across the block).
   const int pos0 = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
+  // SPLIT: this block's keys are [kb, ke) of the cached keys, the last range
+  // also the new ones (a range is a whole number of chunks; ranges past the
+  // cached keys are empty)
+  int kb = 0, ke_cached = pos0;
+  bool owns_new = true;
+  if constexpr (SPLIT) {
+    static_assert(NTOK == 1, "split ranges serve single-token decode");
+    const int S = gridDim.z, sp = blockIdx.z;
+    const int per = ((pos0 + S - 1) / S + KCH - 1) / KCH * KCH;
+    kb = min(sp * per, pos0);
+    ke_cached = min(kb + per, pos0);
+    owns_new = sp == S - 1;
+  }
   u32x4 kr[SR][CPT], vr[NV];
   auto load_k = [&](int c0) {
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
-      if (c0 + r * KPR >= pos0) break;
+      if (c0 + r * KPR >= ke_cached) break;
       const int j = min(c0 + kkey + r * KPR, pos0 - 1);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) kr[r][c] = *(const u32x4*)(kc + (long)j * D + (ksub * CPT + c) * EPC);
@@ -2531,13 +2544,13 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int b = 0; b < NV; ++b) {
-      if (c0 + b * VS >= pos0) break;
+      if (c0 + b * VS >= ke_cached) break;
       const int j = min(c0 + vslot + b * VS, pos0 - 1);
       vr[b] = *(const u32x4*)(vc + (long)j * D + vchunk * EPC);
     }
   };
-  load_k(0);
-  load_v(0);
+  load_k(kb);
+  load_v(kb);
 
   // the new tokens: QK-RMSNorm + rope of q heads and k (one wave per vector;
   // lane owns the rope pair (lane, lane + 64)), K/V rows to the cache and LDS
@@ -2593,7 +2606,7 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       cs = p.cos[(long)pos * HALF + lane];
       sn = p.sin[(long)pos * HALF + lane];
     }
-    for (int v = wave; v <= G + 1; v += NT / 64) {
+    for (int v = wave; v <= (owns_new ? G + 1 : G - 1); v += NT / 64) {
       if (v == G + 1) {                       // value row, stored as is
         const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
         const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
@@ -2626,7 +2639,7 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
 
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
-    const int L = pos0 + t + 1;               // keys 0 .. pos0 + t
+    const int L = owns_new ? pos0 + t + 1 : ke_cached;   // keys kb .. L - 1 (0 .. pos0 + t unsplit)
     float m[G], l[G], acc[G][EPC];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -2636,7 +2649,7 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
     }
     if (t > 0 && pos0 > KCH) { load_k(0); load_v(0); }   // the registers hold the previous token's last chunk
-    for (int c0 = 0; c0 < L; c0 += KCH) {
+    for (int c0 = kb; c0 < L; c0 += KCH) {
       float s[SR][G];
 #pragma unroll
       for (int r = 0; r < SR; ++r) {
@@ -2760,10 +2773,64 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       float v = 0.f, ls = 0.f;
 #pragma unroll
       for (int w = 0; w < NT / 64; ++w) { v += part[w][hh][dim]; ls += red[1][w][hh]; }
-      p.out[(arow0 + t) * p.ld_out + (long)(g * G + hh) * D + dim] = v / ls;
+      if constexpr (SPLIT) {
+        float* sb = p.split_buf + ((((long)row * p.nkv + g) * gridDim.z + blockIdx.z) * G + hh) * (D + 2);
+        sb[dim] = v;
+        if (dim == 0) { sb[D] = m[hh]; sb[D + 1] = ls; }
+      } else {
+        p.out[(arow0 + t) * p.ld_out + (long)(g * G + hh) * D + dim] = v / ls;
+      }
     }
     if (t + 1 < NTOK) __syncthreads();
   }
+}
+
+// Adds the key ranges of a split decode step in range order: with M the
+// largest running max, out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Thread = (row, q head, dim); every partial load of the S ranges is issued
+// before the first use. Empty ranges hold m = -inf, l = 0.
+template <int G, int S>
+__global__ __launch_bounds__(NT) void attn_split_combine_kernel(AttnArgs p) {
+  constexpr int D = 128;
+  const long e = (long)blockIdx.x * NT + threadIdx.x;
+  const int per_row = p.nq * D;
+  if (e >= (long)p.n_runs * per_row) return;
+  const int row = (int)(e / per_row), c = (int)(e % per_row);
+  const int h = c / D, dim = c % D, g = h / G, hh = h % G;
+  const long arow = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  const float* sb = p.split_buf + (((long)row * p.nkv + g) * S * G + hh) * (D + 2);
+  float m[S], o[S], l[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float* q = sb + (long)sp * G * (D + 2);
+    m[sp] = q[D];
+    o[sp] = q[dim];
+    l[sp] = q[D + 1];
+  }
+  float mx = m[0];
+#pragma unroll
+  for (int sp = 1; sp < S; ++sp) mx = fmaxf(mx, m[sp]);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = m[sp] == -INFINITY ? 0.f : expf(m[sp] - mx);
+    num = fmaf(w, o[sp], num);
+    den = fmaf(w, l[sp], den);
+  }
+  p.out[arow * p.ld_out + (long)h * D + dim] = num / den;
+}
+
+template <int G>
+static hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((long)a.n_runs * a.nq * 128 + NT - 1) / NT));
+  switch (a.kv_split) {
+    case 2: hipLaunchKernelGGL((attn_split_combine_kernel<G, 2>), grid, dim3(NT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_split_combine_kernel<G, 4>), grid, dim3(NT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_split_combine_kernel<G, 8>), grid, dim3(NT), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((attn_split_combine_kernel<G, 16>), grid, dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename KVT, int D, int G>
@@ -2776,6 +2843,12 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
       constexpr int big = 512 / sizeof(KVT), small = 64;
       const dim3 grid(a.nkv, a.n_runs);
       const bool one_wave = (long)a.nkv * a.n_runs <= 256;   // at most one block per compute unit
+      if (nt == 1 && a.split_buf && (a.kv_split == 2 || a.kv_split == 4 || a.kv_split == 8 || a.kv_split == 16)) {
+        hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small, true>), dim3(a.nkv, a.n_runs, a.kv_split), dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_split_combine<G>(a, s);
+      }
       if (nt == 2) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 2, small>), grid, dim3(NT), 0, s, a);
       else if (one_wave) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, big>), grid, dim3(NT), 0, s, a);
       else hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small>), grid, dim3(NT), 0, s, a);
