@@ -21,6 +21,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads per block for every kernel here
 constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use the matrix cores
+#ifndef GEMM_SPLIT_SW
+#define GEMM_SPLIT_SW 2        // LDS layout of the prefill GEMM tiles (see SplitLds)
+#endif
 #ifndef ROWS_DIRECT_TILES
 #define ROWS_DIRECT_TILES 192      // output tiles from which the row-block GEMM runs without K ranges
 #endif
@@ -756,12 +759,27 @@ __global__ __launch_bounds__(NT) void split_rows_kernel(LinearArgs p, uint16_t* 
   }
 }
 
-template <int TM, int TN>
+// LDS tile addressing: SW = 0 pads rows to GLD elements; SW = 1 / 2 keep
+// 32-element rows and place 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
+// (1) or c ^ ((r >> 1) & 3) (2), so the lanes of one access fall on distinct
+// banks without padding.
+template <int SW> struct SplitLds {
+  static constexpr int LD = SW == 0 ? GLD : GK;
+  __device__ static int at(int r, int c) {   // c: element offset, a multiple of 8
+    if constexpr (SW == 0) return r * LD + c;
+    else if constexpr (SW == 1) return r * LD + (((c >> 3) ^ ((r >> 2) & 3)) << 3);
+    else return r * LD + (((c >> 3) ^ ((r >> 1) & 3)) << 3);
+  }
+};
+
+template <int TM, int TN, int SW>
 __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
+  using LT = SplitLds<SW>;
+  constexpr int GLD_ = LT::LD;
   constexpr int BM = 64 * TM, BN = 64 * TN;
   constexpr int AV = BM * GK / 8 / NT;            // 16-byte chunks per thread per stage, each A plane
   constexpr int BV = BN * GK / 8 / NT;            // and of W
-  constexpr int BUF = (2 * BM + BN) * GLD;        // bf16 elements of one stage: A hi, A lo, W
+  constexpr int BUF = (2 * BM + BN) * GLD_;        // bf16 elements of one stage: A hi, A lo, W
   __shared__ __attribute__((aligned(16))) uint16_t sm[2 * BUF];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -778,13 +796,13 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
     const long row = min(m0 + r, M - 1);
     ah_src[q] = xs + row * K + c;
     al_src[q] = xs + ((long)M + row) * K + c;
-    a_off[q] = r * GLD + c;
+    a_off[q] = LT::at(r, c);
   }
 #pragma unroll
   for (int q = 0; q < BV; ++q) {
     const int idx = tid + q * NT, r = idx >> 2, c = (idx & 3) * 8;
     w_src[q] = (const uint16_t*)p.W + (long)min(n0 + r, N - 1) * K + c;
-    w_off[q] = r * GLD + c;
+    w_off[q] = LT::at(r, c);
   }
   u32x4 ra_h[AV], ra_l[AV], rw[BV];
   auto load = [&](int k0) __attribute__((always_inline)) {
@@ -798,10 +816,10 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       *(u32x4*)&base[a_off[q]] = ra_h[q];
-      *(u32x4*)&base[BM * GLD + a_off[q]] = ra_l[q];
+      *(u32x4*)&base[BM * GLD_ + a_off[q]] = ra_l[q];
     }
 #pragma unroll
-    for (int q = 0; q < BV; ++q) *(u32x4*)&base[2 * BM * GLD + w_off[q]] = rw[q];
+    for (int q = 0; q < BV; ++q) *(u32x4*)&base[2 * BM * GLD_ + w_off[q]] = rw[q];
   };
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -824,13 +842,13 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * (BM / 2) + i * 32 + (lane & 31);
-        ah[i] = *(const bf16x8*)&base[r * GLD + kk];
-        al[i] = *(const bf16x8*)&base[BM * GLD + r * GLD + kk];
+        ah[i] = *(const bf16x8*)&base[LT::at(r, kk)];
+        al[i] = *(const bf16x8*)&base[BM * GLD_ + LT::at(r, kk)];
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * (BN / 2) + j * 32 + (lane & 31);
-        bv[j] = *(const bf16x8*)&base[2 * BM * GLD + r * GLD + kk];
+        bv[j] = *(const bf16x8*)&base[2 * BM * GLD_ + LT::at(r, kk)];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -865,8 +883,8 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
 }
 
 // The split GEMM needs K % 32 == 0, rows of 16-byte aligned activations and
-// the split scratch; 128 x 128 tiles while they give at least 256 blocks,
-// else 64 x 128.
+// the split scratch; 128 x 128 tiles while they give at least 512 blocks (two
+// per compute unit at a time), else 64 x 128.
 static bool gemm_split_fits(const LinearArgs& a) {
   return a.wdtype == DT_BF16 && a.K % GK == 0 && a.ldx % 4 == 0 && a.xs && a.xs_floats >= (long)a.M * a.K;
 }
@@ -877,12 +895,12 @@ static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (big >= 256) {
+  if (big >= 512) {
     dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-    hipLaunchKernelGGL((gemm_split_kernel<2, 2>), grid, dim3(NT), 0, s, a, xs);
+    hipLaunchKernelGGL((gemm_split_kernel<2, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
   } else {
     dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
-    hipLaunchKernelGGL((gemm_split_kernel<1, 2>), grid, dim3(NT), 0, s, a, xs);
+    hipLaunchKernelGGL((gemm_split_kernel<1, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
   }
   return hipGetLastError();
 }
