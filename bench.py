@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop and a 64 MiB copy (for counter runs)")
+    ap.add_argument("--gemm-kernels", action="store_true",
+                    help="only the batched projections (4096-row prefill chunk, 64-row decode) at the "
+                         "0.6B shapes, timed per launch (for counter runs)")
     return ap.parse_args()
 
 
@@ -199,6 +202,10 @@ def main():
     from codec_lm_autoregressive_amd import binding, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.gemm_kernels:
+        for line in gemm_kernel_timing(torch, binding, synth):
+            print(json.dumps(line), flush=True)
+        return
     if args.kernel_only:
         wl = synth.workload(args.workload)
         dm = synth.dims(wl["model"])
@@ -301,6 +308,38 @@ def kernel_timing(torch, binding, w, dm, wl, B, reps, copies=40):
     wbytes = 2 if wl["dtype"] == "bf16" else 4
     del Ws
     return us, 2 * I * H * wbytes + B * H * 4 + H * 4 + B * I * 4
+
+
+def gemm_kernel_timing(torch, binding, synth, reps=10):
+    """The batched projections of one 0.6B decoder layer through the
+    library's projection entry point: a 4096-row prefill chunk (split
+    activations + matrix-core GEMM) and 64 decode rows (one-range row GEMM +
+    reduce), bf16 weights from a seeded N(0, 0.02) draw. Useful flops count
+    2 per weight per row; the hi/lo split doubles the matrix-core work."""
+    g = np.random.default_rng(7)
+    shapes = [("qkv", 4096, 1024, 0, True), ("o", 1024, 2048, 1, False),
+              ("gate/up", 6144, 1024, 2, True), ("down", 1024, 3072, 1, False)]
+    out = []
+    for M in (4096, 64):
+        for name, N, K, epi, norm in shapes:
+            W = binding.to_device_weight(synth.bf16_round((g.standard_normal((N, K)) * 0.02).astype(np.float32)), "bf16")
+            X = torch.randn(M, K, device="cuda")
+            gain = torch.ones(K, device="cuda") if norm else None
+            Y = torch.zeros(M, N // 2 if epi == 2 else N, device="cuda")
+            binding.debug_linear(W, X, gain, 1e-6, epi, Y, reps=2)
+            cur = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            binding.debug_linear(W, X, gain, 1e-6, epi, Y, reps=reps)
+            e1.record(cur)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000 / reps
+            flops = 2.0 * M * N * K
+            out.append({"rows": M, "proj": name, "N": N, "K": K, "us_per_launch": round(us, 2),
+                        "useful_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                        "matrix_core_TFLOPs": round(2 * flops / (us * 1e-6) / 1e12, 1),
+                        "weight_GBs": round(N * K * 2 / (us * 1e-6) / 1e9, 1)})
+    return out
 
 
 def cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, n_frames):

@@ -290,7 +290,8 @@ def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", r
     M = X.shape[0]
     if Y is None:
         Y = torch.zeros((M, N // 2 if epilogue == 2 else N), dtype=torch.float32, device=X.device)
-    n_scratch = (M + 63) // 64 * 64 + max((K // 256) * M * (N + 1), M * K)
+    # row denominators; split-K partial sums (<= 128 rows) or the hi/lo split of the rows (more rows)
+    n_scratch = (M + 63) // 64 * 64 + ((K // 256) * M * (N + 1) if M <= 128 else M * K)
     scratch = torch.empty(n_scratch, dtype=torch.float32, device=X.device) if matrix_cores else None
     s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
     _check(lib().qt_debug_linear(C.c_void_p(s), QT_DTYPE_BF16 if wdtype == "bf16" else QT_DTYPE_F32,
