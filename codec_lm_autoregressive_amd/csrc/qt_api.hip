@@ -24,7 +24,10 @@ constexpr int kGroups = 16;       // codes per frame
 constexpr int kPredPositions = 16;
 constexpr int kPrefillChunk = 4096;
 constexpr int kMaxVocab = 6144;
-constexpr int kMaxKvSplit = 16;   // key ranges of one decode attention row
+#ifndef QT_MAX_KV_SPLIT
+#define QT_MAX_KV_SPLIT 16
+#endif
+constexpr int kMaxKvSplit = QT_MAX_KV_SPLIT;   // key ranges of one decode attention row
 
 // Key ranges for the talker's single-token decode attention at `rows` batch
 // rows: about 512 blocks (a power of two ranges, at most kMaxKvSplit) when

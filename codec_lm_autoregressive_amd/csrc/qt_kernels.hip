@@ -24,6 +24,9 @@ constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use
 #ifndef GEMM_SPLIT_SW
 #define GEMM_SPLIT_SW 2        // LDS layout of the prefill GEMM tiles (see SplitLds)
 #endif
+#ifndef GEMV8_MAX_TILES
+#define GEMV8_MAX_TILES 3       // 8-row tiles per block of the 8-row matrix-core GEMV (1..3)
+#endif
 #ifndef ROWS_DIRECT_TILES
 #define ROWS_DIRECT_TILES 192      // output tiles from which the row-block GEMM runs without K ranges
 #endif
@@ -1597,10 +1600,10 @@ static hipError_t launch_rows(const LinearArgs& a, const RowsPlan& pl, hipStream
 }
 
 static bool mfma_gemv_plan(const LinearArgs& a, int* ksw, int* ng);
-static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns);
+static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns, int* tiles);
 int linear_split_ranges(const LinearArgs& a) {
-  int ksw, ng;
-  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a) || mfma_gemv_plan(a, &ksw, &ng) || mfma_gemv8_plan(a, &ksw, &ng)) return 1;
+  int ksw, ng, t8;
+  if (a.M <= 0 || gemv_fits(a) || skinny_fits(a) || mfma_gemv_plan(a, &ksw, &ng) || mfma_gemv8_plan(a, &ksw, &ng, &t8)) return 1;
   RowsPlan pl;
   return rows_plan(a, &pl) ? pl.Z : 1;
 }
@@ -1817,20 +1820,22 @@ static hipError_t launch_mfma_gemv(const LinearArgs& a, int ksw, int ng, hipStre
 // every load issued before the first use (activations and gains, then
 // weights); the waves' tiles and row sums of squares are added in LDS in wave
 // order and RMSNorm is applied as a per-row scale after the contraction.
-template <int KSW, int NS, bool NORM>
+template <int KSW, int NS, bool NORM, int T>
 __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r8 = lane & 7, koff = 32 * ((lane >> 3) & 1) + 8 * (lane >> 4);
-  const int n0 = blockIdx.x * 8;
+  const int nb = blockIdx.x * 8 * T;   // T tiles of 8 weight rows share the activation fragments
   const int M = p.M, N = p.N, K = p.K;
   const int kw0 = w * NS * 64 + koff;
-  __shared__ __align__(16) float red[KSW][64][4];
+  __shared__ __align__(16) float red[KSW][T][64][4];
   __shared__ float ssr[KSW][8];
   __shared__ float inv_s[8];
   const float* xr = p.X + (long)min(r8, M - 1) * p.ldx + kw0;
-  const uint16_t* wr = (const uint16_t*)p.W + (long)min(n0 + r8, N - 1) * K + kw0;
+  const uint16_t* wr[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wr[t] = (const uint16_t*)p.W + (long)min(nb + 8 * t + r8, N - 1) * K + kw0;
   f32x4 xv[NS][2], gv[NS][2];
-  u32x4 wv[NS];
+  u32x4 wv[NS][T];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     xv[s][0] = *(const f32x4*)(xr + 64 * s);
@@ -1844,15 +1849,21 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
     }
   // output (i, j) of this lane after the half combine: activation row 4 (lane / 16) + r, weight row lane % 16
   const bool owner = (lane & 15) < 8 && lane < 32;
-  float yold[4] = {0.f, 0.f, 0.f, 0.f};
+  float yold[T][4] = {};
   if (p.epi == EPI_RESIDUAL && owner && w == 0)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) yold[r] = p.Y[(long)min(4 * (lane >> 4) + r, M - 1) * p.ldy + min(n0 + (lane & 15), N - 1)];
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yold[t][r] = p.Y[(long)min(4 * (lane >> 4) + r, M - 1) * p.ldy + min(nb + 8 * t + (lane & 15), N - 1)];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) wv[s] = ld_weight(wr + 64 * s);
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int t = 0; t < T; ++t) wv[s][t] = ld_weight(wr[t] + 64 * s);
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -1865,15 +1876,23 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
-    const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[s]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]}), bw, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]}), bw, acc, 0, 0, 0);
+    const bf16x8 ah = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+    const bf16x8 al = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[s][t]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[t], 0, 0, 0);
+    }
   }
   // D(i, j): lane j + 16 (i / 4), register i % 4; block (i + 8, j + 8) sits 40 lanes up
-  f32x4 hi;
-  hi.x = __shfl(acc.x, (lane + 40) & 63); hi.y = __shfl(acc.y, (lane + 40) & 63);
-  hi.z = __shfl(acc.z, (lane + 40) & 63); hi.w = __shfl(acc.w, (lane + 40) & 63);
-  *(f32x4*)red[w][lane] = acc + hi;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    f32x4 hi;
+    hi.x = __shfl(acc[t].x, (lane + 40) & 63); hi.y = __shfl(acc[t].y, (lane + 40) & 63);
+    hi.z = __shfl(acc[t].z, (lane + 40) & 63); hi.w = __shfl(acc[t].w, (lane + 40) & 63);
+    *(f32x4*)red[w][t][lane] = acc[t] + hi;
+  }
   if constexpr (NORM) {
     ss += __shfl_xor(ss, 8);
     ss += __shfl_xor(ss, 16);
@@ -1899,21 +1918,24 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
         const float sc = inv_s[row];
         *(f32x4*)(p.norm_out + (long)row * p.ld_norm + k) = (f32x4){xx.x * gg.x * sc, xx.y * gg.y * sc, xx.z * gg.z * sc, xx.w * gg.w * sc};
       }
-  f32x4 v = *(const f32x4*)red[0][lane];
 #pragma unroll
-  for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][lane];
-  const int col = n0 + (lane & 15);
-  const float vv[4] = {v.x, v.y, v.z, v.w};
+  for (int t = 0; t < T; ++t) {
+    f32x4 v = *(const f32x4*)red[0][t][lane];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * (lane >> 4) + r;
-    float o = vv[r];
-    if constexpr (NORM) o *= inv_s[row & 7];
-    if (p.epi == EPI_SWIGLU) {
-      const float up = __shfl_xor(o, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
-      if (owner && !(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = o / (1.f + expf(-o)) * up;
-    } else if (owner && row < M && col < N) {
-      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[r] + o : o;
+    for (int q = 1; q < KSW; ++q) v += *(const f32x4*)red[q][t][lane];
+    const int col = nb + 8 * t + (lane & 15);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * (lane >> 4) + r;
+      float o = vv[r];
+      if constexpr (NORM) o *= inv_s[row & 7];
+      if (p.epi == EPI_SWIGLU) {
+        const float up = __shfl_xor(o, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
+        if (owner && !(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = o / (1.f + expf(-o)) * up;
+      } else if (owner && row < M && col < N) {
+        p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yold[t][r] + o : o;
+      }
     }
   }
 }
@@ -1921,40 +1943,51 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
 // 3..8 rows of bf16 weights, K a multiple of 64 KSW with at most 6 steps per
 // wave: 4 waves per block, 8 when the grid has fewer than 256 blocks or K is
 // long.
-static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns) {
+static bool mfma_gemv8_plan(const LinearArgs& a, int* ksw, int* ns, int* tiles) {
   if (a.wdtype != DT_BF16 || a.M < 3 || a.M > 8 || a.ldx % 4 || a.defer) return false;
-  // a 16-row GEMV grid that is already a multiple of the 256 compute units stays (measured equal or better)
-  {
+  // tiles per block: as many as keep at least 256 blocks (1..3), sharing the activation fragments
+  int T = 1;
+  for (int t : {3, 2})
+    if (t <= GEMV8_MAX_TILES && a.N % (8 * t) == 0 && a.N / (8 * t) >= 256) { T = t; break; }
+  if (T == 1) {
+    // a 16-row GEMV grid that is already a multiple of the 256 compute units stays (measured equal or better)
     int k16, g16;
     if (mfma_gemv_plan(a, &k16, &g16) && ((a.N + 15) / 16) % 256 == 0) return false;
   }
   for (int k : {4, 8}) {
-    if (k == 4 && (a.N + 7) / 8 < 256) continue;
+    if (k == 4 && (a.N + 8 * T - 1) / (8 * T) < 256) continue;
     if (a.K % (64 * k)) continue;
     const int n = a.K / (64 * k);
-    if (n >= 1 && n <= 6) { *ksw = k; *ns = n; return true; }
+    if (n >= 1 && n <= 6) { *ksw = k; *ns = n; *tiles = T; return true; }
   }
   return false;
 }
 
-template <int KSW, bool NORM>
+template <int KSW, bool NORM, int T>
 static hipError_t launch_mfma_gemv8_k(const LinearArgs& a, int ns, hipStream_t s) {
-  const dim3 grid((a.N + 7) / 8), block(KSW * 64);
+  const dim3 grid((a.N + 8 * T - 1) / (8 * T)), block(KSW * 64);
   switch (ns) {
-    case 1: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 1, NORM>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 2, NORM>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 3, NORM>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 4, NORM>), grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 5, NORM>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 6, NORM>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 1, NORM, T>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 2, NORM, T>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 3, NORM, T>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 4, NORM, T>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 5, NORM, T>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((mfma_gemv8_kernel<KSW, 6, NORM, T>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-static hipError_t launch_mfma_gemv8(const LinearArgs& a, int ksw, int ns, hipStream_t s) {
-  if (ksw == 4) return a.gain ? launch_mfma_gemv8_k<4, true>(a, ns, s) : launch_mfma_gemv8_k<4, false>(a, ns, s);
-  return a.gain ? launch_mfma_gemv8_k<8, true>(a, ns, s) : launch_mfma_gemv8_k<8, false>(a, ns, s);
+template <int T>
+static hipError_t launch_mfma_gemv8_t(const LinearArgs& a, int ksw, int ns, hipStream_t s) {
+  if (ksw == 4) return a.gain ? launch_mfma_gemv8_k<4, true, T>(a, ns, s) : launch_mfma_gemv8_k<4, false, T>(a, ns, s);
+  return a.gain ? launch_mfma_gemv8_k<8, true, T>(a, ns, s) : launch_mfma_gemv8_k<8, false, T>(a, ns, s);
+}
+
+static hipError_t launch_mfma_gemv8(const LinearArgs& a, int ksw, int ns, int tiles, hipStream_t s) {
+  if (tiles == 3) return launch_mfma_gemv8_t<3>(a, ksw, ns, s);
+  if (tiles == 2) return launch_mfma_gemv8_t<2>(a, ksw, ns, s);
+  return launch_mfma_gemv8_t<1>(a, ksw, ns, s);
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
@@ -1968,7 +2001,8 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   // the row-block weight-streaming MFMA kernel
   {
     int ksw, ng;
-    if (mfma_gemv8_plan(a, &ksw, &ng)) return launch_mfma_gemv8(a, ksw, ng, s);
+    int t8;
+    if (mfma_gemv8_plan(a, &ksw, &ng, &t8)) return launch_mfma_gemv8(a, ksw, ng, t8, s);
     if (mfma_gemv_plan(a, &ksw, &ng)) return launch_mfma_gemv(a, ksw, ng, s);
   }
   if (skinny_fits(a)) return launch_skinny(a, s);
@@ -2626,6 +2660,8 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       cs = p.cos[(long)pos * HALF + lane];
       sn = p.sin[(long)pos * HALF + lane];
     }
+    if (!owns_new)   // masked keys past this range may index the new rows: keep them finite (0 x NaN is NaN)
+      for (int i = tid; i < D; i += NT) { knew[t][i] = 0.f; vnew[t][i] = 0.f; }
     for (int v = wave; v <= (owns_new ? G + 1 : G - 1); v += NT / 64) {
       if (v == G + 1) {                       // value row, stored as is
         const long col = (long)(p.nq + p.nkv) * D + (long)g * D;

@@ -169,6 +169,28 @@ def test_qwen06b_bf16_b8_sampling_parity():
     eng.close()
 
 
+def test_qwen06b_b8_sampling_200_frames_stay_finite():
+    """The whole batch-8 sampling request (200 frames, contexts up to 450
+    keys, the talker attention split over key ranges) completes without a
+    non-finite logit and with codes in range. A split block whose range ends
+    at the new key once read the new-key rows it does not own from stale LDS
+    (0 x NaN in the masked P.V products) at frame 130 of this request."""
+    wl = synth.workload("qwen06b_bf16_b8_sampling")
+    dm = synth.dims(wl["model"])
+    w = weights(wl["model"], "bf16")
+    lens = synth.prompt_lengths(8, *wl["prompt"], seed=2)
+    prompt = synth.make_prompts(lens, 1024, seed=1)
+    pad = synth.make_tts_pad(1024, seed=3)
+    eng = binding.Engine(dm, w, "bf16", max_batch=8, max_positions=wl["max_positions"])
+    codes, n, _ = eng.generate(prompt, lens, pad, wl["talker"], wl["predictor"], 0, wl["frames"])
+    eng.close()
+    assert int(n.max()) > 130
+    for r in range(8):
+        c = codes[r, : int(n[r])]
+        assert np.all((c[:, 1:] >= 0) & (c[:, 1:] < 2048))
+        assert np.all((c[:, 0] >= 0) & ((c[:, 0] < 2048) | (c[:, 0] == dm["eos_id"])))
+
+
 def _full_size(name, rows, frames, seed=0, lens=None):
     wl = synth.workload(name)
     dm = synth.dims(wl["model"])
