@@ -2889,16 +2889,188 @@ static hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Single-token decode attention over at most 16 positions (the code
+// predictor's steps at batch rows > 1), head_dim 128, 16-bit cache.
+// Block = (kv head, row): waves 0..G-1 take the q heads of the group, wave G
+// the new key, wave G + 1 the new value (QK-RMSNorm + rope as in
+// attn_step_kernel, the K/V rows to the cache and LDS); after the one
+// barrier each q-head wave finishes alone. Scores: lane = (key l % 16,
+// quarter l / 16 of the dims), the quarters added with two shuffles; the
+// softmax over the 16 keys stays in 16-lane groups; P.V: lane = 2 dims, the
+// key weights broadcast by shuffles. Every cache load leaves before the
+// prologue (clamped to the cached keys).
+template <typename KVT, int G>
+__global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
+  constexpr int D = 128, HALF = 64;
+  const int g = blockIdx.x, row = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) float qs[G][D];
+  __shared__ __align__(16) float knew[D];
+  __shared__ __align__(16) float vnew[D];
+  KVT* kc = (KVT*)p.kc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  const int pos0 = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
+  const int jk = lane & 15, qd = lane >> 4;
+  const int last = max(pos0 - 1, 0);
+  u32x4 kr[4];
+  uint32_t vr[16];
+  if (wave < G) {
+    const KVT* kp = kc + (long)min(jk, last) * D + 32 * qd;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[c] = *(const u32x4*)(kp + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vr[j] = *(const uint32_t*)(vc + (long)min(j, last) * D + 2 * lane);
+  }
+  // q/k/v of the new token: the projection's rows, or its split-K partial sums
+  const long ar = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  // up to PZ ranges with every load issued before the first add (ranges past
+  // part_z are clamped loads that are not added); more ranges: a loop
+  constexpr int PZ = 8;
+  const bool pz_fast = p.part_z <= PZ;
+  float prs = 1.f;
+  if (p.part_z > 0) {
+    const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
+    float ssum = 0.f;
+    if (pz_fast) {
+      float q[PZ];
+#pragma unroll
+      for (int z = 0; z < PZ; ++z) q[z] = pss[(long)min(z, p.part_z - 1) * p.part_rows + ar];
+#pragma unroll
+      for (int z = 0; z < PZ; ++z) if (z < p.part_z) ssum += q[z];
+    } else {
+      for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + ar];
+    }
+    prs = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
+  }
+  auto qkv_at = [&](long col) -> float {
+    if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
+    float v;
+    if (pz_fast) {
+      float q[PZ];
+#pragma unroll
+      for (int z = 0; z < PZ; ++z) q[z] = p.part[((long)min(z, p.part_z - 1) * p.part_rows + ar) * p.ld_qkv + col];
+      v = q[0];
+#pragma unroll
+      for (int z = 1; z < PZ; ++z) if (z < p.part_z) v += q[z];
+    } else {
+      v = p.part[ar * p.ld_qkv + col];
+      for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
+    }
+    return v * prs;
+  };
+  {
+    float cs, sn;
+    if (p.rope_rows) {
+      cs = p.rope_rows[(long)row * D + lane];
+      sn = p.rope_rows[(long)row * D + HALF + lane];
+    } else {
+      cs = p.cos[(long)pos0 * HALF + lane];
+      sn = p.sin[(long)pos0 * HALF + lane];
+    }
+    const int v = wave;
+    if (v == G + 1) {                       // value row, stored as is
+      const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
+      const float x1 = qkv_at(col + lane), x2 = qkv_at(col + lane + HALF);
+      st_elem<KVT>(vc, (long)pos0 * D + lane, x1);
+      st_elem<KVT>(vc, (long)pos0 * D + lane + HALF, x2);
+      vnew[lane] = kv_round<KVT>(x1);
+      vnew[lane + HALF] = kv_round<KVT>(x2);
+    } else {
+      const long col = v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D;
+      const float* gain = v < G ? p.q_gain : p.k_gain;
+      const float x1 = qkv_at(col + lane), x2 = qkv_at(col + lane + HALF);
+      const float g1 = gain[lane], g2 = gain[lane + HALF];
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float rden = 1.f / sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 * rden * g1, y2 = x2 * rden * g2;
+      const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
+      if (v < G) {
+        qs[v][lane] = o1;
+        qs[v][lane + HALF] = o2;
+      } else {
+        st_elem<KVT>(kc, (long)pos0 * D + lane, o1);
+        st_elem<KVT>(kc, (long)pos0 * D + lane + HALF, o2);
+        knew[lane] = kv_round<KVT>(o1);
+        knew[lane + HALF] = kv_round<KVT>(o2);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave >= G) return;
+  const int hh = wave, L = pos0 + 1;
+  float x[32];
+  if (jk < pos0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) unpack_chunk<KVT>(kr[c], x + 8 * c);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = jk == pos0 ? knew[32 * qd + e] : 0.f;
+  }
+  const f32x4* q4 = (const f32x4*)&qs[hh][32 * qd];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const f32x4 qa = q4[e], qb = q4[e + 1];
+    s0 = fmaf(qa.x, x[4 * e], s0); s0 = fmaf(qa.y, x[4 * e + 1], s0); s0 = fmaf(qa.z, x[4 * e + 2], s0); s0 = fmaf(qa.w, x[4 * e + 3], s0);
+    s1 = fmaf(qb.x, x[4 * e + 4], s1); s1 = fmaf(qb.y, x[4 * e + 5], s1); s1 = fmaf(qb.z, x[4 * e + 6], s1); s1 = fmaf(qb.w, x[4 * e + 7], s1);
+  }
+  float sc = s0 + s1;
+  sc += __shfl_xor(sc, 16);
+  sc += __shfl_xor(sc, 32);
+  sc = jk < L ? sc * p.scale : -INFINITY;
+  float mx = sc;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float ew = jk < L ? expf(sc - mx) : 0.f;
+  float lsum = ew;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float pj = __shfl(ew, j);        // lanes 0..15 hold the key weights
+    float v0, v1;
+    if (j < pos0) {
+      if constexpr (std::is_same<KVT, _Float16>::value) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 h = __builtin_bit_cast(h2, vr[j]);
+        v0 = (float)h[0]; v1 = (float)h[1];
+      } else {
+        v0 = bf_lo(vr[j]); v1 = bf_hi(vr[j]);
+      }
+    } else if (j == pos0) {
+      v0 = vnew[2 * lane]; v1 = vnew[2 * lane + 1];
+    } else {
+      v0 = 0.f; v1 = 0.f;
+    }
+    a0 = fmaf(pj, v0, a0);
+    a1 = fmaf(pj, v1, a1);
+  }
+  const float rl = 1.f / lsum;
+  float* o = p.out + ar * p.ld_out + (long)(g * G + hh) * D + 2 * lane;
+  *(float2*)o = make_float2(a0 * rl, a1 * rl);
+}
+
 template <typename KVT, int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
   constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
   const size_t lds = ((size_t)(2 * G + 1) * D + 2 * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  if constexpr (D == 128 && G == 2 && sizeof(KVT) == 2) {
+    if (a.single_token && a.mode == ATT_WRITE_ATTEND && (a.ntok <= 1) && a.max_pos <= 16 && a.n_runs > 1 &&
+        a.ld_out % 2 == 0) {
+      hipLaunchKernelGGL((attn_short_kernel<KVT, G>), dim3(a.nkv, a.n_runs), dim3((G + 2) * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (D == 128 && G <= 4) {
     const int nt = a.ntok > 0 ? a.ntok : 1;
     if (a.single_token && a.mode == ATT_WRITE_ATTEND && (nt == 1 || (nt == 2 && a.tok_stride == 2 && a.tok_off == 0))) {
       constexpr int big = 512 / sizeof(KVT), small = 64;
       const dim3 grid(a.nkv, a.n_runs);
-      const bool one_wave = (long)a.nkv * a.n_runs <= 256;   // at most one block per compute unit
+      // large chunks when the grid is at most one block per compute unit and
+      // contexts can be long (not the code predictor's 16 positions: 64-key
+      // chunks measured 5.1 against 5.7 us there)
+      const bool one_wave = (long)a.nkv * a.n_runs <= 256 && a.max_pos > small;
       if (nt == 1 && a.split_buf && (a.kv_split == 2 || a.kv_split == 4 || a.kv_split == 8 || a.kv_split == 16)) {
         hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small, true>), dim3(a.nkv, a.n_runs, a.kv_split), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
