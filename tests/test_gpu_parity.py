@@ -169,6 +169,22 @@ def test_qwen06b_bf16_b8_sampling_parity():
     eng.close()
 
 
+def test_qwen06b_bf16_b16_sampling_parity():
+    """Batch 16 (between the benchmarked sizes): the talker attention runs
+    over 4 key ranges, 16-row projections take the 16-row matrix-core GEMV and
+    the skinny kernel, the predictor's two-token pass the 32-row paths; rows
+    0 and 15 are checked against the oracle over 2 frames."""
+    wl = synth.workload("qwen06b_bf16_b8_sampling")
+    dm = synth.dims(wl["model"])
+    w = weights(wl["model"], "bf16")
+    lens = synth.prompt_lengths(16, *wl["prompt"], seed=5)
+    prompts = synth.split_rows(synth.make_prompts(lens, 1024, seed=1), lens)
+    pad = synth.make_tts_pad(1024, seed=3)
+    eng = binding.Engine(dm, w, "bf16", max_batch=16, max_positions=wl["max_positions"])
+    teacher_forced_check(eng, w, dm, prompts, lens, pad, wl["talker"], wl["predictor"], 0, 2, 5e-2, rows=[0, 15])
+    eng.close()
+
+
 def test_qwen06b_b8_sampling_200_frames_stay_finite():
     """The whole batch-8 sampling request (200 frames, contexts up to 450
     keys, the talker attention split over key ranges) completes without a
