@@ -157,6 +157,7 @@ class Workload:
         eng.prefill(self.prompt, self.lens, self.pad, wl["talker"], wl["predictor"], 0, self.frames)
         prefill_ms = (time.perf_counter() - tp) * 1000   # qt_prefill ends with its stream synchronised
         eng.step_frame()  # the first frame after a prefill runs eagerly; later ones replay the graph
+        ttfa_ms = (time.perf_counter() - tp) * 1000      # prompt in HBM -> first 16-code frame on the host
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nf = 0
         ev0.record(stream)
@@ -176,7 +177,7 @@ class Workload:
         fb = frame_bytes(self.dm, self.B, mean_ctx, wbytes, 2 if self.kv != "f32" else 4)
         value = row_frames / dt
         return dict(value=value, dt=dt, steps=steps, total_frames=total_frames, frame_ms=frame_ms, fb=fb,
-                    ms_per_step=dt * 1000 / steps, prefill_ms=prefill_ms,
+                    ms_per_step=dt * 1000 / steps, prefill_ms=prefill_ms, ttfa_ms=ttfa_ms,
                     prefill_flops=prefill_linear_flops(self.dm, int(np.sum(self.lens))))
 
     def config(self, total_frames, steps):
@@ -259,6 +260,7 @@ def main():
                         "rtf": round(FRAMES_PER_AUDIO_SECOND * x.B / q["value"], 6) if q["value"] else None,
                         "frame_roofline": roof(q["fb"], q["frame_ms"]),
                         "prefill_tokens": int(np.sum(x.lens)),
+                        "ttfa_ms": round(q["ttfa_ms"], 3),
                         "prefill_roofline": prefill_roof(q),
                         "config": x.config(q["total_frames"], 1)})
         x.eng.close()
@@ -287,6 +289,8 @@ def main():
         # per-row real-time factor: wall time / audio time (audio = frames / 12.5 Hz)
         "rtf": round(FRAMES_PER_AUDIO_SECOND * B / r["value"], 6) if r["value"] else None,
         "decode_ms_per_frame": round(r["frame_ms"], 4),
+        # time to first audio frame: qt_prefill (talker over the prompt, selection 0) + the first frame
+        "ttfa_ms": round(r["ttfa_ms"], 3),
         "frame_roofline": roof(r["fb"], r["frame_ms"]),
         "roofline": {"kernel": "gemv_kernel (gate/up SwiGLU projection, N=%d K=%d M=%d)" % (2 * I, H, B),
                      "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
