@@ -3616,9 +3616,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 #pragma unroll
       for (int q = 0; q < MPT; ++q) pv[q] = pv[q] / sum;
     }
-    // Few survivors (p > 0): one wave gathers them (in any order: the sort
-    // below makes the result independent of it), sorts them by (p desc, id
-    // asc) in registers, runs the sequential top-p sum and the race.
+    // Few survivors (p > 0): they are gathered (in any order: the ranks below
+    // make the result independent of it) and one wave ranks them by (p desc,
+    // id asc), runs the sequential top-p sum in rank order and the race.
     if (tid == 0) sh_int[2] = 0;
     __syncthreads();
     int* tid_list = (int*)cid;
@@ -3637,34 +3637,49 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     if (nsv <= 64) {
       if (tid < 64) {
         const int lane = tid;
-        float pp = lane < nsv ? tp_list[lane] : -1.f;
-        int id = lane < nsv ? tid_list[lane] : 0x7fffffff;
-        // bitonic sort of 64 (p, id) pairs, lane order = (p desc, id asc)
+        const float pp = lane < nsv ? tp_list[lane] : -1.f;
+        const int id = lane < nsv ? tid_list[lane] : 0x7fffffff;
+        // rank in (p desc, id asc) order: every lane against every survivor,
+        // broadcast with lane reads, 4 survivors per step (padding lanes hold
+        // p = -1 and never rank above a survivor)
+        int rank = 0;
+        for (int j0 = 0; j0 < nsv; j0 += 4) {
 #pragma unroll
-        for (int k = 2; k <= 64; k <<= 1)
-#pragma unroll
-          for (int j = k >> 1; j > 0; j >>= 1) {
-            const float po = __shfl_xor(pp, j);
-            const int io = __shfl_xor(id, j);
-            const bool o_first = po > pp || (po == pp && io < id);
-            const bool lower = (lane & j) == 0, up = (lane & k) == 0;
-            // the lower lane of a pair keeps the element that comes first in an up block
-            const bool take = (lower == up) ? o_first : !o_first;
-            if (take) { pp = po; id = io; }
+          for (int u = 0; u < 4; ++u) {
+            const int j = min(j0 + u, 63);
+            const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), j));
+            const int ij = __builtin_amdgcn_readlane(id, j);
+            // bitwise, not short-circuit: no branch per compare
+            rank += (int)((j0 + u < nsv) & ((pj > pp) | ((pj == pp) & (ij < id))));
           }
-        // sequential fp32 running sum in that order (lane 0 of the wave)
+        }
+        // sequential fp32 running sum in that order, 4 ranks per step: the
+        // survivor of rank r is the lane whose rank is r
         int keep = nsv;
         if (top_p < 1.0f) {
           float cs = 0.f;
-          keep = nsv;
-          for (int j = 0; j < nsv; ++j) {
-            cs += __shfl(pp, j);
-            if (cs >= top_p) { keep = j + 1; break; }
+          bool found = false;
+          for (int r0 = 0; r0 < nsv && !found; r0 += 4) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const unsigned long long bm = __ballot(rank == r0 + u);
+              const int src = bm ? __ffsll(bm) - 1 : 0;
+              v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), src));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bool act = !found & (r0 + u < nsv);
+              cs = act ? cs + v[u] : cs;
+              const bool hit = act & (cs >= top_p);
+              keep = hit ? r0 + u + 1 : keep;
+              found = found | hit;
+            }
           }
         }
         float sc = -INFINITY;
         int bi = 0x7fffffff;
-        if (lane < keep) {
+        if (lane < nsv && rank < keep) {
           const float e = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, r, a.stream, jsel, id);
           sc = pp / e;
           bi = id;
