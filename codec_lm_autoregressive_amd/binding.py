@@ -88,6 +88,8 @@ def lib():
                                  i32, vp, vp, vp], i32),
             "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
                                  C.c_int64], i32),
+            "qt_debug_prefill_attention": ([vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp,
+                                            vp, i32, vp, C.c_int64], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -298,6 +300,28 @@ def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", r
                                  _ptr(W), N, K, _ptr(X), M, _ptr(gain), eps, epilogue, _ptr(Y), _ptr(scratch),
                                  n_scratch if matrix_cores else 0, reps, copies, N * K * W.element_size()))
     return Y
+
+
+def debug_prefill_attention(qkv, lens, q_gain, k_gain, cos, sin, kc, vc, nq, nkv, eps=1e-6, kv_dtype="f16",
+                            tiled=True):
+    """Prefill attention of one layer on device tensors; returns out [T, nq d].
+
+    qkv [T, (nq + 2 nkv) d] float32; kc, vc [B, nkv, max_pos, d] of the cache
+    type (written); cos, sin [max_pos, d / 2]."""
+    import torch
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    T = int(lens.sum())
+    d = qkv.shape[1] // (nq + 2 * nkv)
+    max_pos = kc.shape[2]
+    out = torch.zeros((T, nq * d), dtype=torch.float32, device=qkv.device)
+    n_runs = 4 * (T + T // 32 + lens.size)
+    runs = torch.zeros(n_runs, dtype=torch.int32, device=qkv.device)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().qt_debug_prefill_attention(C.c_void_p(s), _DTYPES[kv_dtype], d, nq, nkv, int(lens.size),
+                                            _np_ptr(lens), max_pos, _ptr(qkv), _ptr(q_gain), _ptr(k_gain), eps,
+                                            _ptr(cos), _ptr(sin), _ptr(kc), _ptr(vc), _ptr(out), int(bool(tiled)),
+                                            _ptr(runs), n_runs))
+    return out
 
 
 def debug_select(logits, samp, seen=None, noise=None, probs=None, processors=False, eos=2150,

@@ -241,7 +241,10 @@ Layout plan_layout(const qt_config& c) {
   L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
   L.seen_words = (int)((V + 31) / 32);
   L.seen = p.take(p.sz.mul({B, (size_t)L.seen_words, 4}));
-  L.max_runs = (int)std::min<size_t>((size_t)1 << 30, 3 * B + B * MP);
+  // decode runs, one per prompt token, and the prefill's tiles: at most
+  // total / kAttnTileTokens + one partial tile per (row, chunk) piece
+  const size_t BMP = (size_t)B * MP;
+  L.max_runs = (int)std::min<size_t>((size_t)1 << 30, 3 * B + BMP + BMP / kAttnTileTokens + B + BMP / kPrefillChunk + 1);
   L.runs = p.take(p.sz.mul({(size_t)L.max_runs, sizeof(Run)}));
   L.idx = p.take(B * 4);
   L.frame_out = p.take(p.sz.mul({1 + B + B * kGroups, 4}));
@@ -360,8 +363,11 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 // ---- the decoder stack over M tokens
 // pass0: the code predictor's 2-token pass (row r's tokens are activation rows
 // 2r and 2r + 1 at positions 0 and 1).
+// prefill: tiles (n_tiles > 0) are the runs of up to kAttnTileTokens tokens
+// the attend pass takes instead of one run per token.
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
-                     int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false) {
+                     int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false,
+                     const Run* tiles = nullptr, int n_tiles = 0) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -406,6 +412,7 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
       t.mode = ATT_WRITE;
       HIPCK(launch_attention(t, s));
       t.mode = ATT_ATTEND;
+      if (n_tiles > 0) { t.runs = tiles; t.n_runs = n_tiles; t.max_ntok = kAttnTileTokens; }
       HIPCK(launch_attention(t, s));
     } else if (pass0 && d.d <= 128) {
       // tokens 0 and 1 of every row (positions 0 and 1); token 1 attends to
@@ -754,11 +761,12 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
   }
   std::vector<long> start(B + 1, 0);
   for (int r = 0; r < B; ++r) start[r + 1] = start[r] + prompt_lens[r];
-  struct Chunk { long t0; int n; int run0, nrun; int last0, nlast, lastrow0; };
+  struct Chunk { long t0; int n; int run0, nrun; int last0, nlast, lastrow0; int tile0, ntile; };
+  const bool tiled = attn_prefill_tiles(T.d, T.nq, T.nkv, c.kv_dtype);
   std::vector<Chunk> chunks;
   std::vector<int> lastidx;
   for (long t0 = 0; t0 < total; t0 += kPrefillChunk) {
-    Chunk ch{t0, (int)std::min<long>(kPrefillChunk, total - t0), (int)runs.size(), 0, (int)lastidx.size(), 0, -1};
+    Chunk ch{t0, (int)std::min<long>(kPrefillChunk, total - t0), (int)runs.size(), 0, (int)lastidx.size(), 0, -1, 0, 0};
     for (int r = 0; r < B; ++r) {
       const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
       if (a >= b) continue;
@@ -770,6 +778,15 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
         lastidx.push_back((int)(start[r + 1] - 1 - t0));
         ch.nlast++;
       }
+    }
+    if (tiled) {   // the attend pass: runs of up to kAttnTileTokens tokens of one row
+      ch.tile0 = (int)runs.size();
+      for (int r = 0; r < B; ++r) {
+        const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
+        for (long tk = a; tk < b; tk += kAttnTileTokens)
+          runs.push_back(Run{r, (int)(tk - t0), (int)std::min<long>(kAttnTileTokens, b - tk), (int)(tk - start[r])});
+      }
+      ch.ntile = (int)runs.size() - ch.tile0;
     }
     chunks.push_back(ch);
   }
@@ -799,7 +816,8 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
 
   for (const Chunk& ch : chunks) {
     HIPCK(hipMemcpyAsync(ctx->x_t, prompt + ch.t0 * T.H, (size_t)ch.n * T.H * 4, hipMemcpyDeviceToDevice, s));
-    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s, true);
+    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s, true, false,
+                             false, ctx->runs + ch.tile0, ch.ntile);
     if (r != QT_OK) return r;
     if (ch.nlast > 0)
       HIPCK(launch_copy_rows(ctx->x_t, T.H, ctx->idx + ch.last0, ch.nlast, ctx->xlast + (size_t)ch.lastrow0 * T.H, T.H,
@@ -1015,6 +1033,72 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
     hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
     if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   }
+  return QT_OK;
+}
+
+qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t head_dim, int32_t nq, int32_t nkv,
+                                     int32_t B, const int32_t* lens, int32_t max_pos, const float* qkv,
+                                     const float* q_gain, const float* k_gain, float eps, const float* cos,
+                                     const float* sin, void* kc, void* vc, float* out, int32_t tiled,
+                                     int32_t* runs, int64_t runs_ints) {
+  if (kv_dtype != QT_DTYPE_F32 && kv_dtype != QT_DTYPE_BF16 && kv_dtype != QT_DTYPE_F16) {
+    set_err(g_err, "bad kv_dtype");
+    return QT_E_INVALID;
+  }
+  const int G = nkv > 0 ? nq / nkv : 0;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256) || nkv < 1 ||
+      nq % nkv || !(G == 1 || G == 2 || G == 4 || G == 8) || B < 1 || max_pos < 1 || !(eps > 0.f)) {
+    set_err(g_err, "bad shape");
+    return QT_E_INVALID;
+  }
+  if (!lens || !qkv || !q_gain || !k_gain || !cos || !sin || !kc || !vc || !out || !runs) {
+    set_err(g_err, "NULL argument");
+    return QT_E_INVALID;
+  }
+  if (tiled && !attn_prefill_tiles(head_dim, nq, nkv, kv_dtype)) {
+    set_err(g_err, "no tiled prefill attention for this shape");
+    return QT_E_INVALID;
+  }
+  std::vector<Run> rv;
+  long T = 0;
+  for (int r = 0; r < B; ++r) {
+    if (lens[r] < 1 || lens[r] > max_pos) { set_err(g_err, "lens[%d] out of 1..max_pos", r); return QT_E_INVALID; }
+    T += lens[r];
+  }
+  if (T > (1L << 24) || runs_ints < 4 * (T + T / kAttnTileTokens + B)) {
+    set_err(g_err, "run scratch too small or too many tokens");
+    return QT_E_INVALID;
+  }
+  // one run per token (the write pass), then runs of up to kAttnTileTokens
+  long t0 = 0;
+  for (int r = 0; r < B; ++r) {
+    for (int i = 0; i < lens[r]; ++i) rv.push_back(Run{r, (int)(t0 + i), 1, i});
+    t0 += lens[r];
+  }
+  const int ntok = (int)rv.size();
+  t0 = 0;
+  for (int r = 0; r < B; ++r) {
+    for (int i = 0; i < lens[r]; i += kAttnTileTokens)
+      rv.push_back(Run{r, (int)(t0 + i), std::min(kAttnTileTokens, lens[r] - i), i});
+    t0 += lens[r];
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipError_t e = hipMemcpyAsync(runs, rv.data(), rv.size() * sizeof(Run), hipMemcpyHostToDevice, s);
+  AttnArgs t{};
+  t.qkv = qkv; t.ld_qkv = (long)(nq + 2 * nkv) * head_dim; t.out = out; t.ld_out = (long)nq * head_dim;
+  t.q_gain = q_gain; t.k_gain = k_gain; t.eps = eps; t.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  t.cos = cos; t.sin = sin; t.kc = kc; t.vc = vc; t.kvdtype = kv_dtype;
+  t.row_stride = (long)nkv * max_pos * head_dim; t.max_pos = max_pos;
+  t.nq = nq; t.nkv = nkv; t.d = head_dim;
+  t.runs = (const Run*)runs; t.n_runs = ntok;
+  t.mode = ATT_WRITE;
+  if (e == hipSuccess) e = launch_attention(t, s);
+  t.mode = ATT_ATTEND;
+  if (tiled) { t.runs = (const Run*)runs + ntok; t.n_runs = (int)rv.size() - ntok; t.max_ntok = kAttnTileTokens; }
+  if (e == hipSuccess) e = launch_attention(t, s);
+  const hipError_t e2 = hipStreamSynchronize(s);   // also keeps rv alive until the copy has been made
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) { set_err(g_err, "prefill attention failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   return QT_OK;
 }
 

@@ -68,8 +68,15 @@ struct AttnArgs {
   // split_buf[row][kv head][range][head of the group][d + 2], and a second
   // launch combines the ranges in order
   int kv_split; float* split_buf;
+  // prefill attend pass (ATT_ATTEND) over runs of at most max_ntok tokens
+  // (1 .. kAttnTileTokens) on the matrix cores; 0: the per-token kernel
+  int max_ntok;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Whether the prefill attend pass has the tiled matrix-core kernel for this
+// head shape and cache type (runs of up to kAttnTileTokens tokens).
+constexpr int kAttnTileTokens = 32;
+bool attn_prefill_tiles(int d, int nq, int nkv, int kvdtype);
 // Single-token code-predictor attention (one batch row, <= 16 positions)
 // fused with the o-projection o (x += W_o . attention, o.X == a.out, bf16
 // weights, 16-bit cache). Returns hipErrorNotSupported, doing nothing, for

@@ -3051,11 +3051,270 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
   *(float2*)o = make_float2(a0 * rl, a1 * rl);
 }
 
+// ---------------------------------------------------------------- prefill attention on the matrix cores
+// Causal attention of the prompt prefill for head_dim 128 and a 16-bit cache
+// (attend pass: the cache already holds every key). Block = (kv head, run of
+// up to FA_TOK consecutive tokens of one row); wave w takes q head w % G and
+// tokens 16 (w / G) .. 16 (w / G) + 15. Keys 0 .. (last token's position) go
+// through LDS in blocks of FA_KB, double-buffered: K as rows, V transposed.
+// Scores are formed transposed, S^T = K Q^T, so a lane holds one query's
+// scores for 16 keys; that is the B-operand layout of P^T in O^T = V^T P^T
+// (the contraction may visit the keys in any order as long as the V^T rows
+// follow the same order), so the running max and sum stay per query lane
+// and no shuffle moves them. q and P are split into 16-bit hi + lo parts,
+// two products each, which keeps fp32-level accuracy against the cache's
+// exact 16-bit keys and values.
+#define FA_TOK kAttnTileTokens
+#define FA_KB 64
+#define FA_KP 136   // K rows in LDS: pitch in 16-bit elements (128 + 8)
+#define FA_VP 68    // V^T rows in LDS: pitch in 16-bit elements (64 + 4)
+
+template <typename KVT>
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (std::is_same<KVT, _Float16>::value) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  }
+}
+
+// (a, b) -> packed 16-bit hi = round(x) and lo = round(x - hi)
+template <typename KVT>
+__device__ __forceinline__ void split16_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  if constexpr (std::is_same<KVT, _Float16>::value) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(_Float16)a, (_Float16)b};
+    const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+  } else {
+    split_pk(a, b, hi, lo);
+  }
+}
+
+template <typename KVT, int G>
+__global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs p) {
+  constexpr int D = 128, HALF = 64, NTH = 2 * G * 64;
+  static_assert(NTH == 256, "one (key quad, 16-byte column) load item per thread");
+  const int g = blockIdx.x;
+  const Run rn = p.runs[blockIdx.y];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int hh = wave % G, tw0 = 16 * (wave / G);
+  extern __shared__ __align__(16) uint16_t fsm[];
+  constexpr int STAGE = FA_KB * FA_KP + D * FA_VP;   // K rows, then V^T rows, per buffer
+  const KVT* kc = (const KVT*)p.kc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  const KVT* vc = (const KVT*)p.vc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  const int L = rn.pos0 + rn.ntok;                  // keys of the block: positions 0 .. L - 1
+  const int nkb = (L + FA_KB - 1) / FA_KB;
+
+  // load role: keys 4 m .. 4 m + 3 of a key block, 16-byte column c
+  const int lm = tid >> 4, lcol = tid & 15;
+  u32x4 kr[4], vr[4];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = min(kb * FA_KB + 4 * lm + u, L - 1);   // rows past L: clamped, weighted 0
+      kr[u] = *(const u32x4*)(kc + (long)key * D + 8 * lcol);
+      vr[u] = *(const u32x4*)(vc + (long)key * D + 8 * lcol);
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(u32x4*)(fsm + buf * STAGE + (4 * lm + u) * FA_KP + 8 * lcol) = kr[u];
+    // V^T: dims 8 c .. 8 c + 7, keys 4 m .. 4 m + 3 (one 8-byte row piece per dim)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 16 * (e & 1);
+      uint32_t x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 v = vr[u];
+        const uint32_t word = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+        x[u] = (word >> sh) & 0xffffu;
+      }
+      *(uint2*)(fsm + buf * STAGE + FA_KB * FA_KP + (8 * lcol + e) * FA_VP + 4 * lm) = make_uint2(x[0] | (x[1] << 16), x[2] | (x[3] << 16));
+    }
+  };
+  load_block(0);
+
+  // this lane's query: token tw0 + col of the run (padding lanes repeat the
+  // last token and store nothing)
+  const int tok = tw0 + col;
+  const bool tok_ok = tok < rn.ntok;
+  const int tk = min(tok, rn.ntok - 1);
+  const int qpos = rn.pos0 + tk;
+  const int wlast = rn.pos0 + min(tw0 + 15, rn.ntok - 1);   // the wave's last query position
+  const bool wave_live = tw0 < rn.ntok;
+  // q: dims 32 s + 8 quad .. + 7 for s = 0..3, RMSNorm with the q gain, rope
+  // pairs (j, j + 64) = (s, s + 2) in the same lane
+  u32x4 qh[4], ql[4];
+  {
+    const float* src = p.qkv + ((long)rn.tok0 + tk) * p.ld_qkv + (long)(g * G + hh) * D;
+    float x[4][8], gn[4][8], cs[2][8], sn[2][8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int d0 = 32 * s + 8 * quad;
+      const f32x4 a0 = *(const f32x4*)(src + d0), a1 = *(const f32x4*)(src + d0 + 4);
+      const f32x4 g0 = *(const f32x4*)(p.q_gain + d0), g1 = *(const f32x4*)(p.q_gain + d0 + 4);
+      x[s][0] = a0.x; x[s][1] = a0.y; x[s][2] = a0.z; x[s][3] = a0.w;
+      x[s][4] = a1.x; x[s][5] = a1.y; x[s][6] = a1.z; x[s][7] = a1.w;
+      gn[s][0] = g0.x; gn[s][1] = g0.y; gn[s][2] = g0.z; gn[s][3] = g0.w;
+      gn[s][4] = g1.x; gn[s][5] = g1.y; gn[s][6] = g1.z; gn[s][7] = g1.w;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const long j0 = (long)qpos * HALF + 32 * s + 8 * quad;
+      const f32x4 c0 = *(const f32x4*)(p.cos + j0), c1 = *(const f32x4*)(p.cos + j0 + 4);
+      const f32x4 s0 = *(const f32x4*)(p.sin + j0), s1 = *(const f32x4*)(p.sin + j0 + 4);
+      cs[s][0] = c0.x; cs[s][1] = c0.y; cs[s][2] = c0.z; cs[s][3] = c0.w;
+      cs[s][4] = c1.x; cs[s][5] = c1.y; cs[s][6] = c1.z; cs[s][7] = c1.w;
+      sn[s][0] = s0.x; sn[s][1] = s0.y; sn[s][2] = s0.z; sn[s][3] = s0.w;
+      sn[s][4] = s1.x; sn[s][5] = s1.y; sn[s][6] = s1.z; sn[s][7] = s1.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(x[s][e], x[s][e], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float den = sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[s][e] = x[s][e] / den * gn[s][e];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = x[s][e], x2 = x[s + 2][e];
+        x[s][e] = x1 * cs[s][e] - x2 * sn[s][e];
+        x[s + 2][e] = x2 * cs[s][e] + x1 * sn[s][e];
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split16_pk<KVT>(x[s][2 * e], x[s][2 * e + 1], h[e], l[e]);
+      qh[s] = (u32x4){h[0], h[1], h[2], h[3]};
+      ql[s] = (u32x4){l[0], l[1], l[2], l[3]};
+    }
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  store_block(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) load_block(kb + 1);
+    const int k0 = kb * FA_KB;
+    if (wave_live && k0 <= wlast) {
+      const uint16_t* Kl = fsm + cur * STAGE;
+      const uint16_t* Vl = Kl + FA_KB * FA_KP;
+      // S^T tiles: keys 16 kt + (4 quad + r), query col
+      f32x4 sc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 a = *(const u32x4*)(Kl + (16 * kt + col) * FA_KP + 32 * s + 8 * quad);
+          c = mfma16x16x32<KVT>(a, qh[s], c);
+          c = mfma16x16x32<KVT>(a, ql[s], c);
+        }
+        sc[kt] = c;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kt + 4 * quad + r;
+          const float v = key <= qpos ? sc[kt][r] * p.scale : -INFINITY;
+          sc[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx);     // finite: key 0 is in every query's range
+      const float corr = expf(m - mnew);
+      m = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kt + 4 * quad + r;
+          const float e = key <= qpos ? expf(sc[kt][r] - mnew) : 0.f;
+          sc[kt][r] = e;
+          ps += e;
+        }
+      lsum = lsum * corr + ps;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= corr;
+      // O^T += V^T P^T over two 32-key steps; slot 8 quad + e is key
+      // 32 ks + 4 quad + e (e < 4) or 32 ks + 16 + 4 quad + e - 4
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t h[4], l[4];
+        split16_pk<KVT>(sc[2 * ks][0], sc[2 * ks][1], h[0], l[0]);
+        split16_pk<KVT>(sc[2 * ks][2], sc[2 * ks][3], h[1], l[1]);
+        split16_pk<KVT>(sc[2 * ks + 1][0], sc[2 * ks + 1][1], h[2], l[2]);
+        split16_pk<KVT>(sc[2 * ks + 1][2], sc[2 * ks + 1][3], h[3], l[3]);
+        const u32x4 ph = (u32x4){h[0], h[1], h[2], h[3]}, pl = (u32x4){l[0], l[1], l[2], l[3]};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const uint16_t* vrow = Vl + (16 * dt + col) * FA_VP + 32 * ks + 4 * quad;
+          const uint2 v0 = *(const uint2*)vrow, v1 = *(const uint2*)(vrow + 16);
+          const u32x4 a = (u32x4){v0.x, v0.y, v1.x, v1.y};
+          acc[dt] = mfma16x16x32<KVT>(a, ph, acc[dt]);
+          acc[dt] = mfma16x16x32<KVT>(a, pl, acc[dt]);
+        }
+      }
+    }
+    if (more) store_block(cur ^ 1);
+    __syncthreads();
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (!wave_live || !tok_ok) return;
+  float* o = p.out + ((long)rn.tok0 + tok) * p.ld_out + (long)(g * G + hh) * D + 4 * quad;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt) = acc[dt] / lsum;
+}
+
+template <typename KVT, int G>
+static hipError_t launch_attn_prefill_mfma(const AttnArgs& a, hipStream_t s) {
+  constexpr size_t lds = (size_t)2 * (FA_KB * FA_KP + 128 * FA_VP) * sizeof(uint16_t);
+  static size_t have = 0;
+  hipError_t e = ensure_lds((const void*)attn_prefill_mfma_kernel<KVT, G>, lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_prefill_mfma_kernel<KVT, G>), dim3(a.nkv, a.n_runs), dim3(2 * G * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+bool attn_prefill_tiles(int d, int nq, int nkv, int kvdtype) {
+  return d == 128 && nkv > 0 && nq == 2 * nkv && (kvdtype == DT_F16 || kvdtype == DT_BF16);
+}
+
+
 template <typename KVT, int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
   constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
   const size_t lds = ((size_t)(2 * G + 1) * D + 2 * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
   if constexpr (D == 128 && G == 2 && sizeof(KVT) == 2) {
+    // prompt prefill, attend pass over runs of up to FA_TOK tokens
+    if (a.mode == ATT_ATTEND && !a.single_token && a.max_ntok > 0) {
+      if (a.max_ntok > FA_TOK) return hipErrorInvalidValue;
+      return launch_attn_prefill_mfma<KVT, G>(a, s);
+    }
     if (a.single_token && a.mode == ATT_WRITE_ATTEND && (a.ntok <= 1) && a.max_pos <= 16 && a.n_runs > 1 &&
         a.ld_out % 2 == 0) {
       hipLaunchKernelGGL((attn_short_kernel<KVT, G>), dim3(a.nkv, a.n_runs), dim3((G + 2) * 64), 0, s, a);

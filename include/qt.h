@@ -246,6 +246,36 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
                           float* Y, float* scratch, int64_t scratch_floats, int32_t reps,
                           int32_t w_copies, int64_t w_copy_stride);
 
+/* The prompt prefill's attention of one decoder layer with the frame's
+ * kernels (no context): per-head RMSNorm of q and k with their gains, rope of
+ * both, the K/V rows written to the cache, then causal GQA attention of every
+ * prompt token over the positions up to its own, scaled by 1/sqrt(head_dim)
+ * (ncnn port discussion 6798, section 1 "structure": Qwen3 decoders with
+ * GQA 16/8, head_dim 128 and QK-Norm; ncnn port section 5: the prompt
+ * prefill).
+ *   kv_dtype QT_DTYPE_F32, QT_DTYPE_BF16 or QT_DTYPE_F16; head_dim 16, 32, 64,
+ *   128 or 256; nq a multiple of nkv with nq / nkv in {1, 2, 4, 8}.
+ *   B rows; lens host int32 [B], 1 .. max_pos tokens each; the tokens sit in
+ *   activation rows row after row, T = sum of lens.
+ *   qkv device float [T, (nq + 2 nkv) head_dim]: q heads, then k, then v.
+ *   q_gain, k_gain device float [head_dim]; eps > 0.
+ *   cos, sin device float [max_pos, head_dim / 2] (angle of pair (i, i + d/2)).
+ *   kc, vc device [B, nkv, max_pos, head_dim] of kv_dtype: rows 0 .. lens[r] - 1
+ *   of row r are written, others untouched.
+ *   out device float [T, nq head_dim].
+ *   tiled 1: the attend pass takes runs of up to 32 tokens of one row on the
+ *   matrix cores (head_dim 128, nq = 2 nkv, 16-bit cache; other shapes
+ *   return QT_E_INVALID); 0: one run per token.
+ *   runs device int32 [runs_ints] scratch for the run tables, at least
+ *   4 (T + T / 32 + B) ints.
+ * Returns after the stream has finished. QT_E_INVALID on a bad argument,
+ * QT_E_HIP on a launch failure. */
+qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t head_dim, int32_t nq, int32_t nkv,
+                                     int32_t B, const int32_t* lens, int32_t max_pos, const float* qkv,
+                                     const float* q_gain, const float* k_gain, float eps, const float* cos,
+                                     const float* sin, void* kc, void* vc, float* out, int32_t tiled,
+                                     int32_t* runs, int64_t runs_ints);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,3 +128,16 @@ def test_debug_entry_points_validate_before_launch():
     sm = binding.sampling(dict(synth.SAMPLING, temperature=0.0))
     assert L.qt_debug_select(None, 1, 3072, C.c_void_p(16), None, None, None, 1, 2150, 2048, 3072, C.byref(sm), 0,
                              0, 0, C.c_void_p(16), None, C.c_void_p(16)) == binding.QT_E_INVALID
+    fake = C.c_void_p(256)
+    lens = (C.c_int32 * 2)(5, 9)
+
+    def pa(kv, d, nq, nkv, tiled, lens=lens, max_pos=64, runs_ints=1000):
+        return L.qt_debug_prefill_attention(None, kv, d, nq, nkv, 2, lens, max_pos, fake, fake, fake, 1e-6, fake,
+                                            fake, fake, fake, fake, tiled, fake, runs_ints)
+    assert pa(binding.QT_DTYPE_F16, 64, 4, 2, 1) == binding.QT_E_INVALID     # no tiled kernel for head_dim 64
+    assert pa(binding.QT_DTYPE_F32, 128, 4, 2, 1) == binding.QT_E_INVALID    # nor for an fp32 cache
+    assert pa(binding.QT_DTYPE_F16, 128, 8, 2, 1) == binding.QT_E_INVALID    # nor for 4 q heads per kv head
+    assert pa(binding.QT_DTYPE_F16, 96, 4, 2, 0) == binding.QT_E_INVALID     # head_dim
+    assert pa(binding.QT_DTYPE_F16, 128, 6, 4, 0) == binding.QT_E_INVALID    # nq not a multiple of nkv
+    assert pa(binding.QT_DTYPE_F16, 128, 4, 2, 1, max_pos=8) == binding.QT_E_INVALID   # a row longer than max_pos
+    assert pa(binding.QT_DTYPE_F16, 128, 4, 2, 1, runs_ints=50) == binding.QT_E_INVALID  # run scratch too small

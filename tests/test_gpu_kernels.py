@@ -8,7 +8,9 @@
     probabilities and noise the sampled id is bit-exact (top-p + race);
     Philox noise drawn on the device equals the oracle's Philox4x64-10;
     sampling from logits agrees with the oracle except near ties; a NaN row
-    fails closed.
+    fails closed;
+  * prompt-prefill attention (tiled matrix-core kernel and per-token kernel)
+    vs the oracle's RMSNorm, rope and attention in float64.
 """
 import numpy as np
 import pytest
@@ -247,3 +249,74 @@ def test_select_nan_fails_closed():
     L[1, 17] = 0.0
     out, _, st = binding.debug_select(torch.from_numpy(L).cuda(), dict(synth.GREEDY), processors=True)
     assert int(st[0]) == 0
+
+
+def _ref_prefill_attention(qkv, lens, q_gain, k_gain, cos, sin, nq, nkv, eps, kv):
+    """Per row: the oracle's per-head RMSNorm and rope in float64, keys and
+    values rounded to the cache type (through float32, as the kernel stores
+    them), causal GQA attention in float64."""
+    d = qkv.shape[1] // (nq + 2 * nkv)
+    out, t0 = [], 0
+    for L in lens:
+        x = qkv[t0:t0 + L].astype(np.float64)
+        q = x[:, :nq * d].reshape(L, nq, d)
+        k = x[:, nq * d:(nq + nkv) * d].reshape(L, nkv, d)
+        v = x[:, (nq + nkv) * d:].reshape(L, nkv, d)
+        pos = np.arange(L)
+        q = model.apply_rope(model.rms_norm(q, q_gain, eps, np.float64), pos, cos, sin, np.float64)
+        k = model.apply_rope(model.rms_norm(k, k_gain, eps, np.float64), pos, cos, sin, np.float64)
+        if kv == "f16":
+            k = k.astype(np.float32).astype(np.float16).astype(np.float64)
+            v = v.astype(np.float32).astype(np.float16).astype(np.float64)
+        else:
+            k = synth.bf16_round(k).astype(np.float64)
+            v = synth.bf16_round(v).astype(np.float64)
+        o = model.attention(q, k.transpose(1, 0, 2), v.transpose(1, 0, 2), pos, nkv, np.float64)
+        out.append(o.reshape(L, nq * d))
+        t0 += L
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+@pytest.mark.parametrize("lens,gain_scale", [([1, 45, 130], 1.0), ([33, 64, 65, 7, 96], 3.0), ([1500, 3], 2.0)])
+def test_prefill_attention_tiled_matches_oracle(kv, lens, gain_scale):
+    """The prompt prefill's attention at the talker's head shape (16 q / 8 kv
+    heads, head_dim 128): runs of up to 32 tokens on the matrix cores
+    (ragged last run, 64-key blocks with a ragged last block, a 1500-token
+    row), against the oracle in float64 with the cache's rounding, and
+    against the per-token kernel on the same cache.
+
+    Tolerances. Oracle: the kernel stores keys rounded from its float32 rope,
+    the oracle from float64 through float32, so a few stored key elements may
+    differ by one unit of the cache type; one such unit moves a score by up
+    to |q_i| ulp(k_i) / sqrt(d), which grows with both gains: 2e-3 for fp16,
+    2e-3 g^2 for bf16 (8x coarser). Per-token kernel, same cache: the q and P
+    operands are split into 16-bit hi + lo parts, 22 significant bits with
+    fp16 (5e-5) and 16 with bf16 (5e-4)."""
+    torch = _torch()
+    nq, nkv, d, eps = 16, 8, 128, 1e-6
+    lens = np.array(lens, dtype=np.int32)
+    T, B, max_pos = int(lens.sum()), len(lens), 1536
+    rng = np.random.default_rng(int(lens.sum()) + (7 if kv == "f16" else 8))
+    qkv = rng.standard_normal((T, (nq + 2 * nkv) * d)).astype(np.float32)
+    q_gain = (gain_scale * (1.0 + 0.1 * rng.standard_normal(d))).astype(np.float32)
+    k_gain = (gain_scale * (1.0 + 0.1 * rng.standard_normal(d))).astype(np.float32)
+    cos, sin = model.rope_tables(max_pos, d, 1.0e6)
+    ref = _ref_prefill_attention(qkv, lens, q_gain, k_gain, cos, sin, nq, nkv, eps, kv)
+    dev = [torch.from_numpy(a).cuda() for a in (qkv, q_gain, k_gain, cos, sin)]
+    g2 = max(1.0, gain_scale) ** 2
+    tol_oracle, tol_cross = (2e-3, 5e-5) if kv == "f16" else (2e-3 * g2, 5e-4)
+    outs, errs = {}, {}
+    for tiled in (True, False):
+        kc = torch.zeros((B, nkv, max_pos, d), dtype=torch.float16 if kv == "f16" else torch.int16, device="cuda")
+        vc = torch.zeros_like(kc)
+        print(f"prefill attention kv={kv} lens={list(lens)} tiled={tiled}", flush=True)
+        outs[tiled] = binding.debug_prefill_attention(dev[0], lens, dev[1], dev[2], dev[3], dev[4], kc, vc, nq, nkv,
+                                                      eps, kv, tiled).cpu().numpy()
+        errs[tiled] = float(np.max(np.abs(outs[tiled] - ref)))
+        print(f"  max|out - oracle| {errs[tiled]:.3e} (tol {tol_oracle:.1e})", flush=True)
+    cross = float(np.max(np.abs(outs[True] - outs[False])))
+    print(f"  max|tiled - per-token| {cross:.3e} (tol {tol_cross:.1e})", flush=True)
+    assert np.all(np.isfinite(outs[True])) and np.all(np.isfinite(outs[False]))
+    assert cross <= tol_cross, cross
+    assert errs[True] <= tol_oracle and errs[False] <= tol_oracle, errs
