@@ -3305,10 +3305,49 @@ bool attn_prefill_tiles(int d, int nq, int nkv, int kvdtype) {
 }
 
 
+// Prefill write pass for head_dim 128: one wave per (token, kv head). Lane j
+// holds the rope pair (j, j + 64) of k and of v: RMSNorm of k with its gain
+// (one wave sum), rope, and both rows to the cache; a wave's 2- or 4-byte
+// stores cover whole row segments.
+template <typename KVT>
+__global__ __launch_bounds__(256) void kv_write_kernel(AttnArgs p) {
+  constexpr int D = 128, HALF = 64;
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)p.n_runs * p.nkv) return;   // whole waves
+  const int g = (int)(w % p.nkv);
+  const Run rn = p.runs[w / p.nkv];
+  const int pos0 = rn.pos0 + p.pos_base + (p.row_pos ? p.row_pos[rn.row] : 0);
+  KVT* kc = (KVT*)p.kc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)rn.row * p.row_stride + (long)g * p.max_pos * D;
+  const float g1 = p.k_gain[lane], g2 = p.k_gain[lane + HALF];
+  for (int i = 0; i < rn.ntok; ++i) {
+    const float* src = p.qkv + ((long)rn.tok0 + i) * p.ld_qkv + (long)p.nq * D + (long)g * D;
+    const float* vsrc = src + (long)p.nkv * D;
+    const int pos = pos0 + i;
+    const float x1 = src[lane], x2 = src[lane + HALF], v1 = vsrc[lane], v2 = vsrc[lane + HALF];
+    const float c = p.cos[(long)pos * HALF + lane], sn = p.sin[(long)pos * HALF + lane];
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float den = sqrtf(ss / (float)D + p.eps);
+    const float y1 = x1 / den * g1, y2 = x2 / den * g2;
+    st_elem<KVT>(kc, (long)pos * D + lane, y1 * c - y2 * sn);
+    st_elem<KVT>(kc, (long)pos * D + lane + HALF, y2 * c + y1 * sn);
+    st_elem<KVT>(vc, (long)pos * D + lane, v1);
+    st_elem<KVT>(vc, (long)pos * D + lane + HALF, v2);
+  }
+}
+
 template <typename KVT, int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
   constexpr int EPC = 16 / sizeof(KVT), CPK = D / EPC, TPK = CPK < 4 ? CPK : 4, KCH = NT / TPK;
   const size_t lds = ((size_t)(2 * G + 1) * D + 2 * D + (size_t)G * KCH + 4 * (size_t)G * D + 8 * G) * sizeof(float);
+  if constexpr (D == 128) {
+    if (a.mode == ATT_WRITE && !a.single_token) {
+      const long waves = (long)a.n_runs * a.nkv;
+      hipLaunchKernelGGL((kv_write_kernel<KVT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (D == 128 && G == 2 && sizeof(KVT) == 2) {
     // prompt prefill, attend pass over runs of up to FA_TOK tokens
     if (a.mode == ATT_ATTEND && !a.single_token && a.max_ntok > 0) {
