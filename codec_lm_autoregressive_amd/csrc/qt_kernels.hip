@@ -775,12 +775,16 @@ template <int SW> struct SplitLds {
   }
 };
 
-template <int TM, int TN, int SW>
+// FA (no gain: the o and down projections): the activations are read as
+// fp32 rows instead and split into the hi + lo LDS planes on the way in, so
+// no prologue writes the planes.
+template <int TM, int TN, int SW, bool FA = false>
 __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
   using LT = SplitLds<SW>;
   constexpr int GLD_ = LT::LD;
   constexpr int BM = 64 * TM, BN = 64 * TN;
-  constexpr int AV = BM * GK / 8 / NT;            // 16-byte chunks per thread per stage, each A plane
+  constexpr int AF = FA ? BM * GK / 4 / NT : 1;  // fp32 16-byte chunks per thread per stage (FA)
+  constexpr int AV = FA ? 1 : BM * GK / 8 / NT;  // 16-byte chunks per thread per stage, each A plane
   constexpr int BV = BN * GK / 8 / NT;            // and of W
   constexpr int BUF = (2 * BM + BN) * GLD_;        // bf16 elements of one stage: A hi, A lo, W
   __shared__ __attribute__((aligned(16))) uint16_t sm[2 * BUF];
@@ -793,6 +797,7 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
   const uint16_t* al_src[AV];
   const uint16_t* w_src[BV];
   int a_off[AV], w_off[BV];
+  if constexpr (!FA)
 #pragma unroll
   for (int q = 0; q < AV; ++q) {
     const int idx = tid + q * NT, r = idx >> 2, c = (idx & 3) * 8;
@@ -801,6 +806,19 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
     al_src[q] = xs + ((long)M + row) * K + c;
     a_off[q] = LT::at(r, c);
   }
+  // FA staging slots: A rows idx / 8 (8 chunks of 4 floats per 32-k row);
+  // chunk c lands in half c & 4 of the 8-element LDS chunk c & ~7
+  const float* af_src[AF];
+  int af_off[AF];
+  if constexpr (FA)
+#pragma unroll
+  for (int q = 0; q < AF; ++q) {
+    const int idx = tid + q * NT, r = idx >> 3, c = (idx & 7) * 4;
+    const long row = min(m0 + r, M - 1);
+    af_src[q] = p.X + row * p.ldx + c;
+    af_off[q] = LT::at(r, c & ~7) + (c & 4);
+  }
+  u32x4 raf[AF];
 #pragma unroll
   for (int q = 0; q < BV; ++q) {
     const int idx = tid + q * NT, r = idx >> 2, c = (idx & 3) * 8;
@@ -809,17 +827,34 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
   }
   u32x4 ra_h[AV], ra_l[AV], rw[BV];
   auto load = [&](int k0) __attribute__((always_inline)) {
+    if constexpr (FA) {
 #pragma unroll
-    for (int q = 0; q < AV; ++q) { ra_h[q] = *(const u32x4*)(ah_src[q] + k0); ra_l[q] = *(const u32x4*)(al_src[q] + k0); }
+      for (int q = 0; q < AF; ++q) raf[q] = *(const u32x4*)(af_src[q] + k0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < AV; ++q) { ra_h[q] = *(const u32x4*)(ah_src[q] + k0); ra_l[q] = *(const u32x4*)(al_src[q] + k0); }
+    }
 #pragma unroll
     for (int q = 0; q < BV; ++q) rw[q] = *(const u32x4*)(w_src[q] + k0);
   };
   auto store = [&](int b) __attribute__((always_inline)) {
     uint16_t* base = sm + b * BUF;
+    if constexpr (FA) {
 #pragma unroll
-    for (int q = 0; q < AV; ++q) {
-      *(u32x4*)&base[a_off[q]] = ra_h[q];
-      *(u32x4*)&base[BM * GLD_ + a_off[q]] = ra_l[q];
+      for (int q = 0; q < AF; ++q) {
+        const f32x4 v = __builtin_bit_cast(f32x4, raf[q]);
+        uint32_t h0, l0, h1, l1;
+        split_pk(v.x, v.y, h0, l0);
+        split_pk(v.z, v.w, h1, l1);
+        *(uint2*)&base[af_off[q]] = make_uint2(h0, h1);
+        *(uint2*)&base[BM * GLD_ + af_off[q]] = make_uint2(l0, l1);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < AV; ++q) {
+        *(u32x4*)&base[a_off[q]] = ra_h[q];
+        *(u32x4*)&base[BM * GLD_ + a_off[q]] = ra_l[q];
+      }
     }
 #pragma unroll
     for (int q = 0; q < BV; ++q) *(u32x4*)&base[2 * BM * GLD_ + w_off[q]] = rw[q];
@@ -892,18 +927,25 @@ static bool gemm_split_fits(const LinearArgs& a) {
   return a.wdtype == DT_BF16 && a.K % GK == 0 && a.ldx % 4 == 0 && a.xs && a.xs_floats >= (long)a.M * a.K;
 }
 
+// Without a gain and from 2048 rows the GEMM splits fp32 activation tiles
+// itself (FA): 4096 rows, o 64 us and down 88 us against 74 and 108 with the
+// prologue; with a gain (an extra gain load per chunk, fewer waves) and at
+// 1051 rows the prologue path measured as fast or faster.
 static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
   uint16_t* xs = (uint16_t*)a.xs;
-  hipLaunchKernelGGL(split_rows_kernel, dim3(a.M), dim3(NT), 0, s, a, xs);
+  const bool fa = !a.gain && !a.norm_out && a.M >= 2048;
+  if (!fa) hipLaunchKernelGGL(split_rows_kernel, dim3(a.M), dim3(NT), 0, s, a, xs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (big >= 512) {
     dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-    hipLaunchKernelGGL((gemm_split_kernel<2, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
+    if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, GEMM_SPLIT_SW, true>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<2, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
   } else {
     dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
-    hipLaunchKernelGGL((gemm_split_kernel<1, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
+    if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, GEMM_SPLIT_SW, true>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<1, 2, GEMM_SPLIT_SW>), grid, dim3(NT), 0, s, a, xs);
   }
   return hipGetLastError();
 }
