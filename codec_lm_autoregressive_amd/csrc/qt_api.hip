@@ -22,7 +22,7 @@ thread_local char g_err[512] = "";
 
 constexpr int kGroups = 16;       // codes per frame
 constexpr int kPredPositions = 16;
-constexpr int kPrefillChunk = 4096;
+constexpr int kPrefillChunk = 8192;
 constexpr int kMaxVocab = 6144;
 #ifndef QT_MAX_KV_SPLIT
 #define QT_MAX_KV_SPLIT 16
@@ -196,7 +196,9 @@ Layout plan_layout(const qt_config& c) {
   const size_t kvp = p.sz.mul({(size_t)q.L, B, (size_t)q.nkv, (size_t)kPredPositions, (size_t)q.d, kvs});
   L.kc_p = p.take(kvp);
   L.vc_p = p.take(kvp);
-  L.tmax = std::max(kPrefillChunk, 2 * c.max_batch);
+  // activation rows: one prefill chunk (never more than the prompt tokens
+  // max_batch * max_positions can hold) or the predictor's two-token pass
+  L.tmax = (int)std::max<long>(std::min<long>(kPrefillChunk, (long)c.max_batch * c.max_positions), 2L * c.max_batch);
   const size_t T = L.tmax;
   const size_t Hm = std::max(t.H, q.H), QKVm = std::max(t.qkv, q.qkv), NQm = std::max(t.nqd, q.nqd),
                Im = std::max(t.I, q.I);

@@ -225,7 +225,7 @@ def _full_size(name, rows, frames, seed=0, lens=None):
 
 
 def test_qwen06b_bf16_b64_sampling_parity():
-    """Batch 64 with prompts of 128..512 tokens: the prefill runs 4096-token
+    """Batch 64 with prompts of 128..512 tokens: the prefill runs 8192-token
     chunks through the split-activation MFMA GEMM, decode runs 64 / 128 rows
     through the split-K GEMM; rows 0, 29 and 63 are checked against the
     oracle, and so is the row whose prompt straddles the first chunk boundary
@@ -233,7 +233,7 @@ def test_qwen06b_bf16_b64_sampling_parity():
     wl = synth.workload("qwen06b_bf16_b64_sampling")
     lens = synth.prompt_lengths(wl["B"], *wl["prompt"], seed=2)
     ends = np.cumsum(lens)
-    straddle = int(np.nonzero((ends - lens < 4096) & (ends > 4096))[0][0])
+    straddle = int(np.nonzero((ends - lens < 8192) & (ends > 8192))[0][0])
     eng, *_ = _full_size("qwen06b_bf16_b64_sampling", sorted({0, straddle, 29, 63}), 2)
     eng.close()
 
