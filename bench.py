@@ -103,7 +103,7 @@ def parse():
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop and a 64 MiB copy (for counter runs)")
     ap.add_argument("--gemm-kernels", action="store_true",
-                    help="only the batched projections (4096-row prefill chunk, 64-row decode) at the "
+                    help="only the batched projections (4096 prefill rows, 64-row decode) at the "
                          "0.6B shapes, timed per launch (for counter runs)")
     return ap.parse_args()
 
@@ -334,7 +334,7 @@ def kernel_timing(torch, binding, w, dm, wl, B, reps, copies=40):
 
 def gemm_kernel_timing(torch, binding, synth, reps=10):
     """The batched projections of one 0.6B decoder layer through the
-    library's projection entry point: a 4096-row prefill chunk (split
+    library's projection entry point: 4096 prefill rows (split
     activations + matrix-core GEMM) and 64 decode rows (one-range row GEMM +
     reduce), bf16 weights from a seeded N(0, 0.02) draw. Useful flops count
     2 per weight per row; the hi/lo split doubles the matrix-core work."""
