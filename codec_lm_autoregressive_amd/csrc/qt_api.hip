@@ -789,6 +789,10 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
           runs.push_back(Run{r, (int)(tk - t0), (int)std::min<long>(kAttnTileTokens, b - tk), (int)(tk - start[r])});
       }
       ch.ntile = (int)runs.size() - ch.tile0;
+      // longest first (a tile's keys end at its last position), so the
+      // heaviest blocks do not form the tail of the grid
+      std::stable_sort(runs.begin() + ch.tile0, runs.end(),
+                       [](const Run& x, const Run& y) { return x.pos0 + x.ntok > y.pos0 + y.ntok; });
     }
     chunks.push_back(ch);
   }
