@@ -3260,17 +3260,21 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
     if (wave_live && k0 <= wlast) {
       const uint16_t* Kl = fsm + cur * STAGE;
       const uint16_t* Vl = Kl + FA_KB * FA_KP;
-      // S^T tiles: keys 16 kt + (4 quad + r), query col
+      // S^T tiles: keys 16 kt + (4 quad + r), query col. Tiles whose keys all
+      // lie past the wave's last query (the causal edge) are skipped: their
+      // scores are masked below and their P rows are 0.
+      const int ktn = min(4, (wlast - k0) / 16 + 1);
       f32x4 sc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (kt < ktn)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 a = *(const u32x4*)(Kl + (16 * kt + col) * FA_KP + 32 * s + 8 * quad);
-          c = mfma16x16x32<KVT>(a, qh[s], c);
-          c = mfma16x16x32<KVT>(a, ql[s], c);
-        }
+          for (int s = 0; s < 4; ++s) {
+            const u32x4 a = *(const u32x4*)(Kl + (16 * kt + col) * FA_KP + 32 * s + 8 * quad);
+            c = mfma16x16x32<KVT>(a, qh[s], c);
+            c = mfma16x16x32<KVT>(a, ql[s], c);
+          }
         sc[kt] = c;
       }
       float mx = -INFINITY;
@@ -3305,6 +3309,7 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
       // 32 ks + 4 quad + e (e < 4) or 32 ks + 16 + 4 quad + e - 4
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        if (2 * ks >= ktn) break;   // both key tiles past the edge: P is 0
         uint32_t h[4], l[4];
         split16_pk<KVT>(sc[2 * ks][0], sc[2 * ks][1], h[0], l[0]);
         split16_pk<KVT>(sc[2 * ks][2], sc[2 * ks][3], h[1], l[1]);
