@@ -53,8 +53,11 @@ def uniform_open(x: int) -> float:
     return ((x >> 12) + 0.5) * (2.0 ** -52)
 
 
+def noise_from_word(x: int) -> np.float32:
+    """E = -ln u of the uniform that the 64-bit word x maps to, rounded once to float32."""
+    return np.float32(-math.log(uniform_open(x)))
+
+
 def exp_noise(seed: int, row: int, stream: int, index: int, vocab_id: int) -> np.float32:
     """E ~ Exp(1) for one vocabulary id of one selection."""
-    x = philox4x64_10((vocab_id, stream, index, row), (seed, 0))[0]
-    u = uniform_open(x)
-    return np.float32(-math.log(u))
+    return noise_from_word(philox4x64_10((vocab_id, stream, index, row), (seed, 0))[0])

@@ -136,32 +136,128 @@ def race(p, keep, noise):
 def select(processed, samp, noise):
     """Choose one id from processed logits.
 
-    Returns (id, info). info['margin'] is the decision margin that the
-    parity tests use: greedy -> top-2 gap of the processed logits; sampling ->
-    min(race gap / temperature-free log units converted back to logit units,
-    top-k threshold gap), all in units of raw logits.
+    Returns (id, info). Greedy: info['margin'] is the top-2 gap of the
+    processed logits. Sampling: info['race_gap'] is the gap between the two
+    best race scores ln p - ln E, times the temperature (logit units), and
+    info['keep'] the number of ids that survive top-k and top-p.
     """
     if not samp["do_sample"]:
         return greedy(processed), dict(margin=top2_margin(processed))
     z, p, keep = warp(processed, samp)
     cid, gap = race(p, keep, noise)
+    return cid, dict(race_gap=gap * float(samp["temperature"]), keep=len(keep))
+
+
+# ---------------------------------------------------------------- decision margins
+# A selection made from logits l' with max_i |l'_i - l_i| <= delta can differ
+# from the selection made from l only if the perturbation can move one of the
+# comparisons the selection rests on. flip_possible() answers, for a given
+# pair of ids (a = the choice from l, b = another id), whether some such
+# perturbation could make b the choice; it errs only towards True (a
+# sufficient test for "cannot flip"). Every bound is in raw-logit units:
+# temperature divides the logits, so tempered logits move by delta / T.
+
+def _topk_member_can_flip(l, k, i, delta):
+    """Can top-k membership of id i (kept iff fewer than k ids are strictly
+    above it) change when every finite logit moves by at most delta?"""
+    others = np.delete(l, i)
+    others = others[np.isfinite(others)]
+    if l[i] >= np.sort(np.concatenate([others, [l[i]]]))[::-1][k - 1]:
+        # kept: drops out only if k others can end strictly above it
+        return int(np.sum(others >= l[i] - 2.0 * delta)) >= k
+    # dropped: enters only if fewer than k others can stay strictly above it
+    return int(np.sum(others > l[i] + 2.0 * delta)) < k
+
+
+def _topp_member_can_flip(l, samp, i, delta):
+    """Can top-p membership of id i change under a delta perturbation?
+
+    i is kept iff the probability mass S of the ids ordered ahead of it
+    (p desc, id asc) is below top_p. With the set ahead of it fixed, a
+    perturbation scales each tempered weight by at most e^(delta/T) either
+    way, so S' lies within [S / (S + (1 - S) r), S r / (S r + 1 - S)] with
+    r = e^(2 delta / T). Ids whose logits lie within 2 delta of l_i may change
+    sides, and ids within 2 delta of the top-k threshold may enter or leave
+    the normalising set; both widen the interval.
+    """
     T = float(samp["temperature"])
-    info = dict(race_gap=gap * T, keep=len(keep))
-    # threshold gaps: how far the k-th value sits from the (k+1)-th, and how far
-    # the top-p running sum sits from top_p at the cut (both in logit units)
+    top_p = float(samp["top_p"])
     k = int(samp["top_k"])
-    fz = np.sort(processed[np.isfinite(processed)])[::-1]
-    info["topk_gap"] = float(fz[k - 1] - fz[k]) if 0 < k < fz.size else float("inf")
-    tp = float(samp["top_p"])
-    if tp < 1.0:
-        ids = sorted([i for i in range(p.size) if p[i] > 0], key=lambda i: (-p[i], i))
-        csum = np.cumsum(p[ids], dtype=np.float64)
-        n = len(keep)
-        # distance of top_p from the running sums on either side of the cut
-        lo = csum[n - 2] if n >= 2 else 0.0
-        hi = csum[n - 1]
-        info["topp_gap"] = float(min(abs(tp - lo), abs(hi - tp)))
-    else:
-        info["topp_gap"] = float("inf")
-    info["margin"] = min(info["race_gap"], info["topk_gap"])
-    return cid, info
+    z, p = tempered_softmax(l, samp)
+    p = p.astype(np.float64)
+    ids = [j for j in range(p.size) if p[j] > 0]
+    ids.sort(key=lambda j: (-p[j], j))
+    pos = ids.index(i)
+    S = float(np.sum(p[ids[:pos]]))
+    near = [j for j in ids if j != i and abs(float(l[j]) - float(l[i])) <= 2.0 * delta]
+    ahead_near = sum(p[j] for j in near if ids.index(j) < pos)
+    behind_near = sum(p[j] for j in near if ids.index(j) > pos)
+    # mass that may leave / enter the top-k set (tail ids near its threshold)
+    p_out = p_in = 0.0
+    fin = l[np.isfinite(l)]
+    if 0 < k < fin.size:
+        srt = np.sort(fin)[::-1]
+        kth, nxt = float(srt[k - 1]), float(srt[k])
+        m = float(np.max(z[np.isfinite(z)]))
+        Z = float(np.sum(np.exp(z[np.isfinite(z)].astype(np.float64) - m)))
+        for j in range(l.size):
+            if j == i or not np.isfinite(l[j]):
+                continue
+            if p[j] > 0 and float(l[j]) - nxt <= 2.0 * delta:
+                p_out += p[j]
+            elif p[j] == 0 and kth - float(l[j]) <= 2.0 * delta:
+                p_in += float(np.exp(np.float64(l[j]) / T - m)) / Z
+    r = float(np.exp(2.0 * delta / T))
+    if S < top_p:   # kept: can the mass ahead reach top_p?
+        s_plus = S + behind_near
+        rest = max(0.0, 1.0 - s_plus - p_out)
+        return s_plus * r / (s_plus * r + rest) >= top_p if s_plus > 0 else False
+    s_minus = max(0.0, S - ahead_near)
+    rest = 1.0 - s_minus + p_in * r
+    return s_minus / (s_minus + rest * r) < top_p
+
+
+def member_can_flip(l, samp, i, delta):
+    """Can the survival of id i through top-k and top-p change under a delta
+    perturbation of the processed logits l? (-inf ids never survive.)"""
+    l = np.asarray(l, dtype=np.float64)
+    if not np.isfinite(l[i]):
+        return False
+    k = int(samp["top_k"])
+    n_fin = int(np.sum(np.isfinite(l)))
+    if 0 < k < n_fin:
+        if _topk_member_can_flip(l, k, i, delta):
+            return True
+        kth = np.sort(l[np.isfinite(l)])[::-1][k - 1]
+        if l[i] < kth:
+            return False          # out of top-k and cannot enter
+    if float(samp["top_p"]) >= 1.0:
+        return False
+    return _topp_member_can_flip(np.asarray(l, dtype=np.float32), samp, i, delta)
+
+
+def flip_possible(processed, samp, noise, a, b, delta):
+    """Could logits within delta (max norm) of `processed` make the selection
+    b instead of a (a = the selection from `processed`)?
+
+    Greedy: only if l_a - l_b <= 2 delta. Sampling (exponential race): b can
+    win only if both race scores ln p - ln E can meet, i.e.
+    (l_a - l_b) / T - ln E_a + ln E_b <= 2 delta / T (the normaliser is common
+    to both), and b survives top-k / top-p on the perturbed side; or a itself
+    can drop out of the survivors, after which any survivor may win.
+    """
+    l = np.asarray(processed, dtype=np.float32)
+    if a == b:
+        return True
+    if not np.isfinite(l[b]):
+        return False
+    if not samp["do_sample"]:
+        return float(l[a]) - float(l[b]) <= 2.0 * delta
+    if member_can_flip(l, samp, a, delta):
+        return True
+    T = float(samp["temperature"])
+    ds = (float(l[a]) - float(l[b])) / T - float(np.log(np.float64(noise(a)))) + float(np.log(np.float64(noise(b))))
+    if ds > 2.0 * delta / T:
+        return False
+    _, _, keep = warp(l, samp)
+    return b in keep or member_can_flip(l, samp, b, delta)

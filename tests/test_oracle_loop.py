@@ -137,6 +137,51 @@ def test_trailing_text_switch():
     assert list(r["talker_choice"][1:4]) == marks
 
 
+def test_predictor_input_projection_closed_form():
+    """The 1.7B-class predictor sits behind a [Hp, H] input projection that
+    applies to every predictor input: the talker hidden and the talker table
+    row of pass 0 and every table row of steps 1..14; the feedback sum stays
+    at talker width. Talker width 128, predictor width 64; W_proj selects the
+    coordinates rho(0..63) (W[i, rho(i)] = 1), table j maps code c to the talker
+    one-hot e_rho(kappa_j(c)), so its projection is the predictor one-hot
+    e_kappa_j(c), and head s is a permutation sigma_s. With identity layers
+    every code is then c_{s+1} = sigma_s^-1(kappa_{s-1}(c_s)) and the next code 0
+    is the most frequent coordinate of the feedback sum. An input left
+    unprojected, or the projection applied to the feedback, has the wrong
+    width and fails; a transposed projection fails the same way."""
+    C, H, Hp = 64, 128, 64
+    dm = synth.small_dims(layers_t=1, layers_p=2, hidden=H, codebook=C, pred_in_proj=True, pred_hidden=Hp)
+    w = _zero_layers(synth.make_weights(dm, seed=33, dtype="f32"))
+    g = np.random.default_rng(33)
+    rho = g.permutation(H)[:Hp]                 # injective map of predictor coords into talker coords
+    kappa = [g.permutation(C) for _ in range(15)]
+    sig = [g.permutation(C) for _ in range(15)]
+    eyeH = np.eye(H, dtype=np.float32)
+    eyeC = np.eye(C, dtype=np.float32)
+    proj = np.zeros((Hp, H), dtype=np.float32)
+    proj[np.arange(Hp), rho] = 1.0
+    w["pred_in_proj"] = proj
+    w["talker_codec_embed"] = eyeH[rho[np.arange(3072) % C]]
+    w["talker_codec_head"] = eyeH[rho[np.arange(3072) % C]]
+    w["pred_embeds"] = np.concatenate([eyeH[rho[kappa[j]]] for j in range(15)])
+    w["pred_heads"] = np.concatenate([eyeC[sig[s]] for s in range(15)])
+    prompt = np.zeros((4, H), dtype=np.float32)
+    prompt[:, rho[17]] = 1.0                    # selection 0: code 0 = 17
+    pad = np.zeros(H, dtype=np.float32)
+    r = oracle.generate(w, dm, [prompt], pad, GREEDY, GREEDY, 0, max_frames=5)[0]
+    frames, sel = _closed_form_frames(17, kappa, sig, 5)
+    np.testing.assert_array_equal(r["codes"], frames)
+    np.testing.assert_array_equal(r["talker_choice"], sel)
+    # the projection is load-bearing: without it the predictor sees 128-wide rows
+    w_bad = dict(w, pred_in_proj=None)
+    with pytest.raises(ValueError):
+        oracle.generate(w_bad, dm, [prompt], pad, GREEDY, GREEDY, 0, max_frames=1)
+    # and a different projection (another coordinate choice) changes the codes
+    w_perm = dict(w, pred_in_proj=proj[g.permutation(Hp)])
+    r2 = oracle.generate(w_perm, dm, [prompt], pad, GREEDY, GREEDY, 0, max_frames=5)[0]
+    assert not np.array_equal(r2["codes"], r["codes"])
+
+
 SAMPLING = dict(do_sample=True, temperature=0.9, top_k=50, top_p=0.8, repetition_penalty=1.05, min_new_tokens=2)
 PSAMP = dict(do_sample=True, temperature=0.9, top_k=50, top_p=0.8, repetition_penalty=1.0, min_new_tokens=0)
 
