@@ -14,8 +14,7 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# QT_LIB points at another build of the same library (developer A/B runs).
-LIB_PATH = os.environ.get("QT_LIB") or os.path.join(_PKG, "libqt.so")
+LIB_PATH = os.path.join(_PKG, "libqt.so")
 
 QT_OK, QT_E_INVALID, QT_E_RANGE, QT_E_CAPACITY, QT_E_NOMEM, QT_E_HIP, QT_E_NAN, QT_E_STATE = range(8)
 QT_DTYPE_F32, QT_DTYPE_BF16, QT_DTYPE_F16 = 0, 1, 2
@@ -86,6 +85,7 @@ def lib():
             "qt_debug_talker_logits": ([vp, vp], i32),
             "qt_debug_select": ([vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, C.POINTER(Sampling), u64, i32,
                                  i32, vp, vp, vp], i32),
+            "qt_debug_exp_noise": ([vp, i32, vp, C.c_int64, u64, vp], i32),
             "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
                                  C.c_int64], i32),
             "qt_debug_prefill_attention": ([vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp,
@@ -321,6 +321,19 @@ def debug_prefill_attention(qkv, lens, q_gain, k_gain, cos, sin, kc, vc, nq, nkv
                                             _np_ptr(lens), max_pos, _ptr(qkv), _ptr(q_gain), _ptr(k_gain), eps,
                                             _ptr(cos), _ptr(sin), _ptr(kc), _ptr(vc), _ptr(out), int(bool(tiled)),
                                             _ptr(runs), n_runs))
+    return out
+
+
+def debug_exp_noise(words, mode=0, seed=0):
+    """Device Exp(1) noise: words is a device uint64 tensor ([n, 4] counters
+    (vocab id, stream, index, row) for mode 0, [n] raw words for mode 1)
+    stored as int64; returns a float32 tensor [n]."""
+    import torch
+    n = words.shape[0]
+    out = torch.zeros(n, dtype=torch.float32, device=words.device)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().qt_debug_exp_noise(C.c_void_p(s), int(mode), _ptr(words), n, C.c_uint64(seed), _ptr(out)))
+    torch.cuda.synchronize()
     return out
 
 

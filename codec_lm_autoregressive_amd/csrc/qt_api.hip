@@ -24,10 +24,7 @@ constexpr int kGroups = 16;       // codes per frame
 constexpr int kPredPositions = 16;
 constexpr int kPrefillChunk = 8192;
 constexpr int kMaxVocab = 6144;
-#ifndef QT_MAX_KV_SPLIT
-#define QT_MAX_KV_SPLIT 16
-#endif
-constexpr int kMaxKvSplit = QT_MAX_KV_SPLIT;   // key ranges of one decode attention row
+constexpr int kMaxKvSplit = 16;   // key ranges of one decode attention row
 
 // Key ranges for the talker's single-token decode attention at `rows` batch
 // rows: about 512 blocks (a power of two ranges, at most kMaxKvSplit) when
@@ -1006,6 +1003,16 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
   a.processed_out = processed; a.status = status; a.epi = 0;
   hipError_t e = launch_select(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) { set_err(g_err, "select launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+  return QT_OK;
+}
+
+qt_status qt_debug_exp_noise(void* hip_stream, int32_t mode, const uint64_t* in, int64_t n, uint64_t seed,
+                             float* out) {
+  if (mode != 0 && mode != 1) { set_err(g_err, "mode must be 0 (counters) or 1 (words)"); return QT_E_INVALID; }
+  if (n < 0 || n > (1L << 30)) { set_err(g_err, "n must be in 0..2^30"); return QT_E_INVALID; }
+  if (n > 0 && (!in || !out)) { set_err(g_err, "in and out must not be NULL"); return QT_E_INVALID; }
+  hipError_t e = launch_noise(in, mode, seed, out, n, (hipStream_t)hip_stream);
+  if (e != hipSuccess) { set_err(g_err, "noise launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   return QT_OK;
 }
 

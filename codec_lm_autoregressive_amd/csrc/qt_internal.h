@@ -153,6 +153,10 @@ hipError_t launch_copy_rows(const float* src, long ld_src, const int* idx, int c
 // Copy/convert [rows, n] from f32 or bf16 into the packed weight layout.
 hipError_t launch_convert(const void* src, int sdtype, long ld_src, void* dst, int ddtype, long ld_dst,
                           long rows, int n, hipStream_t s);
+// Exp(1) noise of the selection kernel for n counters (mode 0: [n][4] words
+// (vocab id, stream, selection index, row), key (seed, 0)) or n raw 64-bit
+// words (mode 1).
+hipError_t launch_noise(const uint64_t* in, int mode, uint64_t seed, float* out, long n, hipStream_t s);
 // Fill an int32 buffer.
 hipError_t launch_fill_i32(int* p, int v, long n, hipStream_t s);
 

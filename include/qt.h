@@ -225,6 +225,20 @@ qt_status qt_debug_select(void* hip_stream, int32_t B, int32_t V, const float* l
                           const qt_sampling* samp, uint64_t seed, int32_t stream, int32_t sel_index,
                           int32_t* out_code, float* processed, int32_t* status);
 
+/* The Exp(1) noise of the selection kernel's single-sample race, for
+ * comparing it bit for bit with an independent implementation (Mizuoto
+ * engine page, "Speed": one multinomial draw computed as argmax(p / E) with
+ * E ~ Exp(1)). Same device function as the selection kernel.
+ *   mode 0: in = device uint64 [n][4] counters (vocab id, stream, selection
+ *           index, row), each in 0..2^31-1; the noise is that of Philox4x64-10
+ *           with key (seed, 0), first output word x;
+ *   mode 1: in = device uint64 [n] words x.
+ *   out     device float [n]: E = -ln u, u = ((x >> 12) + 1/2) 2^-52, the
+ *           logarithm in double, rounded once to float.
+ * Enqueued on hip_stream; QT_E_INVALID for a bad mode, n or NULL pointer. */
+qt_status qt_debug_exp_noise(void* hip_stream, int32_t mode, const uint64_t* in, int64_t n, uint64_t seed,
+                             float* out);
+
 /* Y = op(W · norm(X)) with the projection kernels of the frame (no context).
  *   W [N, K] device, element type wdtype; X device float [M, K];
  *   gain device float [K] or NULL (RMSNorm prologue with eps);

@@ -13,7 +13,14 @@ from codec_lm_autoregressive_amd import binding, synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qt.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="libqt.so not built")
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    """The library these checks load: built in-tree first when it is missing."""
+    if not os.path.exists(binding.LIB_PATH):
+        from codec_lm_autoregressive_amd import build
+        build.build()
+    yield
 
 
 def declared():
@@ -129,6 +136,9 @@ def test_debug_entry_points_validate_before_launch():
     assert L.qt_debug_select(None, 1, 3072, C.c_void_p(16), None, None, None, 1, 2150, 2048, 3072, C.byref(sm), 0,
                              0, 0, C.c_void_p(16), None, C.c_void_p(16)) == binding.QT_E_INVALID
     fake = C.c_void_p(256)
+    assert L.qt_debug_exp_noise(None, 2, fake, 4, 0, fake) == binding.QT_E_INVALID    # mode
+    assert L.qt_debug_exp_noise(None, 0, None, 4, 0, fake) == binding.QT_E_INVALID    # NULL input
+    assert L.qt_debug_exp_noise(None, 1, fake, -1, 0, fake) == binding.QT_E_INVALID   # n < 0
     lens = (C.c_int32 * 2)(5, 9)
 
     def pa(kv, d, nq, nkv, tiled, lens=lens, max_pos=64, runs_ints=1000):
