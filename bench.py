@@ -11,10 +11,20 @@ Default workload (`value`): the 0.6B-shaped talker + predictor, bf16 weights
 (fp32 accumulate), fp16 KV cache, batch 1, greedy, 32-token prompt, 100
 frames. The same line reports, under `batches`, one timed request each of the
 batch-8 (sampling, prompts 32..256, 200 frames) and batch-64 (sampling,
-prompts 128..512, 1024 frames) workloads, and the oracle timed on the host
-cores on a bounded sample (row 0 of the batch-1 workload, up to 100 frames).
+prompts 128..512, 1024 frames) workloads and of the 1.7B-class shape at
+batch 1 and 8 (greedy, 64-token prompts, 250 frames), and the oracle timed on
+the host cores on bounded samples.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--batches A,B]
+
+Measurement modes for profiler runs (rocprofv3 wraps the same command):
+    --kernel-only      the dominant kernel's timing loop and a 64 MiB copy
+    --frame-counters   a prompt prefill and --counter-frames eager frames of a
+                       workload, then a 64 MiB copy (byte counters per frame)
+    --gemm-kernels     the batched projections at the 0.6B shapes
+and a summariser of their rocprofv3 CSV output:
+    --summarize DIR    per-kernel statistics of a --kernel-trace run, or the
+                       counters of a --pmc run, per dispatch or per frame
 """
 from __future__ import annotations
 
@@ -33,45 +43,71 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, vendor figure
 FRAMES_PER_AUDIO_SECOND = 12.5
 
-# HBM bytes per launch of the gate/up projection from two rocprofv3 --pmc runs
-# of `bench.py --kernel-only` (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000, scaled by
-# a 64 MiB copy), valid while the SHA-256 prefix of dominant_kernel_source()
-# is this one.
-COUNTED_TRAFFIC = {"kernel_src_sha256_16": "9b2c6fb1fe7e2013", "bytes": 12726352}
+# Counter results of the committed profiles, each valid while the SHA-256
+# prefix of the source it depends on is unchanged (else reported as null):
+#  * the gate/up projection launch (bench.py --kernel-only): HBM bytes per
+#    launch from FETCH_SIZE / WRITE_SIZE scaled by a 64 MiB copy, and its
+#    rocprofv3 kernel-trace average duration
+#    (profiles/gemv_gate_up_qwen06b_b1_counters.md);
+#  * HBM bytes per decode frame of the batch-1 and batch-64 workloads
+#    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
+COUNTED = {
+    "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
+    "frame": {"src_sha256_16": "030a9d8d6a07ed5b", "bytes_per_frame": {
+        # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
+        "qwen06b_bf16_b1": (3421800000, 35.5, 3313377280),
+        "qwen06b_bf16_b64_sampling": (11344900000, 339.9, 5804343296),
+    }},
+}
+CSRC = os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc")
+
+
+def _sha16(text):
+    import hashlib
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def dominant_kernel_source():
-    """Source text the byte counters depend on: the weight-load helper and the
-    register GEMV from its comment through its launch-shape choice (try_gemv);
-    None when the markers are not found."""
-    src = open(os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc", "qt_kernels.hip")).read()
+    """Source text the dominant kernel's counters depend on: the weight-load
+    helper and the register GEMV from its comment through its launch-shape
+    choice; None when the markers are not found."""
+    dev = open(os.path.join(CSRC, "qt_device.h")).read()
+    lin = open(os.path.join(CSRC, "qt_linear.hip")).read()
     try:
-        a = src.index("__device__ __forceinline__ u32x4 ld_weight(")
-        b = src.index("}", a)
-        c = src.index("// Register-only projection for a few activation rows")
-        d = src.index("static hipError_t launch_linear_t(", c)
+        a = dev.index("__device__ __forceinline__ u32x4 ld_weight(")
+        b = dev.index("}", a)
+        c = lin.index("// Register-only projection for a few activation rows")
+        d = lin.index("static hipError_t launch_linear_t(", c)
     except ValueError:
         return None
-    return src[a:b + 1] + src[c:d]
+    return dev[a:b + 1] + lin[c:d]
 
 
-def counted_traffic():
-    import hashlib
-    text = dominant_kernel_source()
-    if text is None:
+def all_kernel_source():
+    """Every kernel and launch source of the library (the frame counters depend on all of them)."""
+    names = ("qt_device.h", "qt_internal.h", "qt_linear.hip", "qt_attn.hip", "qt_select.hip", "qt_api.hip")
+    return "".join(open(os.path.join(CSRC, n)).read() for n in names)
+
+
+def counted(kind):
+    """The committed counter results of `kind` if their source is unchanged, else None."""
+    c = COUNTED[kind]
+    if not c["src_sha256_16"]:
         return None
-    h = hashlib.sha256(text.encode()).hexdigest()[:16]
-    return COUNTED_TRAFFIC["bytes"] if h == COUNTED_TRAFFIC["kernel_src_sha256_16"] else None
+    text = dominant_kernel_source() if kind == "kernel" else all_kernel_source()
+    return c if text is not None and _sha16(text) == c["src_sha256_16"] else None
 
 
-def frame_bytes(dm, B, mean_ctx, wbytes=2, kvbytes=2):
+def frame_bytes(dm, B, mean_ctx, wbytes=2, kvbytes=2, unique=False):
     """Algorithmic bytes one frame step must read for B rows.
 
-    Each forward pass reads its layer weights once: the talker once, the
-    predictor 15 times (2-token prefill + 14 steps), one predictor head per
-    step and the talker codec head; the talker KV cache is read once per step
-    (mean context mean_ctx positions per row). Gathers of single embedding
-    rows are negligible and left out.
+    Streamed model (default): each forward pass reads its layer weights once:
+    the talker once, the predictor 15 times (2-token prefill + 14 steps), one
+    predictor head per step and the talker codec head; the talker KV cache is
+    read once per step (mean context mean_ctx positions per row). Unique model:
+    the predictor's layer weights are counted once per frame (the floor if a
+    cache holds them across the 15 passes). Gathers of single embedding rows
+    are negligible and left out.
     """
     def layer_params(d):
         qkv = (d["n_heads"] + 2 * d["n_kv_heads"]) * d["head_dim"] * d["hidden"]
@@ -80,9 +116,10 @@ def frame_bytes(dm, B, mean_ctx, wbytes=2, kvbytes=2):
         return qkv + o + mlp
     t, p = dm["talker"], dm["predictor"]
     talker = t["layers"] * layer_params(t) + dm["talker_vocab"] * t["hidden"]
-    pred = 15 * (p["layers"] * layer_params(p)) + 15 * dm["codebook"] * p["hidden"]
+    passes = 1 if unique else 15
+    pred = passes * (p["layers"] * layer_params(p)) + 15 * dm["codebook"] * p["hidden"]
     if dm["pred_in_proj"]:
-        pred += 15 * p["hidden"] * t["hidden"]
+        pred += passes * p["hidden"] * t["hidden"]
     kv = B * mean_ctx * t["layers"] * 2 * t["n_kv_heads"] * t["head_dim"] * kvbytes
     return (talker + pred) * wbytes + kv
 
@@ -94,7 +131,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen06b_bf16_b1")
     ap.add_argument("--frames", type=int, default=None, help="override the frame cap of the workload")
-    ap.add_argument("--batches", default="qwen06b_bf16_b8_sampling,qwen06b_bf16_b64_sampling",
+    ap.add_argument("--batches", default="qwen06b_bf16_b8_sampling,qwen06b_bf16_b64_sampling,qwen17b_bf16_b1,"
+                                         "qwen17b_bf16_b8",
                     help="further workloads reported under 'batches' (one timed request each; '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=100,
@@ -102,9 +140,16 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop and a 64 MiB copy (for counter runs)")
+    ap.add_argument("--frame-counters", action="store_true",
+                    help="only a prefill and --counter-frames eager frames of --workload, then a 64 MiB copy")
+    ap.add_argument("--counter-frames", type=int, default=8)
     ap.add_argument("--gemm-kernels", action="store_true",
                     help="only the batched projections (4096 prefill rows, 64-row decode) at the "
                          "0.6B shapes, timed per launch (for counter runs)")
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="summarise the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--per-frame", action="store_true",
+                    help="with --summarize: sum counters per frame (dispatches from the first frame_start_kernel)")
     return ap.parse_args()
 
 
@@ -174,9 +219,11 @@ class Workload:
         frame_ms = ev0.elapsed_time(ev1) / max(nf, 1)
         mean_ctx = float(np.mean(self.lens)) + (self.frames - 1) / 2.0 + 1
         wbytes = 2 if wl["dtype"] == "bf16" else 4
-        fb = frame_bytes(self.dm, self.B, mean_ctx, wbytes, 2 if self.kv != "f32" else 4)
+        kvb = 2 if self.kv != "f32" else 4
+        fb = frame_bytes(self.dm, self.B, mean_ctx, wbytes, kvb)
+        fbu = frame_bytes(self.dm, self.B, mean_ctx, wbytes, kvb, unique=True)
         value = row_frames / dt
-        return dict(value=value, dt=dt, steps=steps, total_frames=total_frames, frame_ms=frame_ms, fb=fb,
+        return dict(value=value, dt=dt, steps=steps, total_frames=total_frames, frame_ms=frame_ms, fb=fb, fbu=fbu,
                     ms_per_step=dt * 1000 / steps, prefill_ms=prefill_ms, ttfa_ms=ttfa_ms,
                     prefill_flops=prefill_linear_flops(self.dm, int(np.sum(self.lens))))
 
@@ -185,8 +232,8 @@ class Workload:
         return {"workload": self.name, "batch": self.B, "prompt_lens": [int(x) for x in self.lens][:8],
                 "frames_cap": self.frames, "frames_per_step": total_frames // max(steps, 1),
                 "talker_layers": dm["talker"]["layers"], "predictor_layers": dm["predictor"]["layers"],
-                "hidden": dm["talker"]["hidden"], "kv_cache": self.kv,
-                "sampling": "sampled" if wl["talker"]["do_sample"] else "greedy"}
+                "hidden": dm["talker"]["hidden"], "predictor_hidden": dm["predictor"]["hidden"],
+                "kv_cache": self.kv, "sampling": "sampled" if wl["talker"]["do_sample"] else "greedy"}
 
 
 def prefill_linear_flops(dm, tokens):
@@ -205,14 +252,30 @@ def prefill_roof(q):
             "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "flops": q["prefill_flops"], "ms": round(q["prefill_ms"], 3)}
 
 
-def roof(fb, frame_ms):
+def roof(q, workload):
+    """Frame roofline under both byte models, and the HBM bytes per frame the
+    counters measured for this workload (null when not counted or stale)."""
+    fb, fbu, frame_ms = q["fb"], q["fbu"], q["frame_ms"]
     gbs = fb / (frame_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "bytes_per_frame": int(fb), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    gbu = fbu / (frame_ms * 1e-3) / 1e9
+    c = counted("frame")
+    hbm = c["bytes_per_frame"].get(workload) if c else None
+    out = {"bound": "hbm", "bytes_per_frame": int(fb), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "unique_bytes_per_frame": int(fbu), "unique_achieved": round(gbu, 1),
+           "unique_frac": round(gbu / HBM_PEAK_GBS, 4), "counted": None}
+    if hbm:
+        # counted on the first frames after the prefill (their own mean context)
+        out["counted"] = {"hbm_bytes_per_frame": hbm[0], "mean_context": hbm[1],
+                          "streamed_model_at_context": hbm[2], "ratio": round(hbm[0] / hbm[2], 3)}
+    return out
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.per_frame)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(rows would shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -230,13 +293,12 @@ def main():
         dm = synth.dims(wl["model"])
         w = synth.make_weights(dm, seed=0, dtype=wl["dtype"])
         us, nbytes = kernel_timing(torch, binding, w, dm, wl, wl["B"], args.kernel_reps)
-        # a plain copy of known size, to scale the byte counters
-        a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+        copy_64mib(torch)
         print(json.dumps({"kernel_avg_us": round(us, 3), "kernel_bytes": nbytes,
                           "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "copy_bytes": 64 << 20}))
+        return
+    if args.frame_counters:
+        frame_counter_run(torch, binding, synth, args.workload, args.counter_frames)
         return
 
     main_wl = Workload(torch, binding, synth, args.workload, args.frames)
@@ -245,7 +307,11 @@ def main():
     kern_us, kern_bytes = kernel_timing(torch, binding, w, dm, wl, B, args.kernel_reps)
     kern_gbs = kern_bytes / (kern_us * 1e-6) / 1e9
     H, I = dm["talker"]["hidden"], dm["talker"]["intermediate"]
+    main_cfg = main_wl.config(r["total_frames"], args.steps)
     main_wl.eng.close()
+    main_lens, main_prompt, main_pad = main_wl.lens, main_wl.prompt_np, main_wl.pad_np
+    del main_wl
+    torch.cuda.empty_cache()
 
     batches = []
     for name in [x for x in args.batches.split(",") if x]:
@@ -258,7 +324,7 @@ def main():
                         "decode_ms_per_frame": round(q["frame_ms"], 4),
                         "decode_frames_per_s": round(x.B * 1000.0 / q["frame_ms"], 1),
                         "rtf": round(FRAMES_PER_AUDIO_SECOND * x.B / q["value"], 6) if q["value"] else None,
-                        "frame_roofline": roof(q["fb"], q["frame_ms"]),
+                        "frame_roofline": roof(q, name),
                         "prefill_tokens": int(np.sum(x.lens)),
                         "ttfa_ms": round(q["ttfa_ms"], 3),
                         "prefill_roofline": prefill_roof(q),
@@ -269,9 +335,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, dm, wl, main_wl.lens, main_wl.prompt_np, main_wl.pad_np,
-                           min(args.cpu_frames, main_wl.frames))
+        cpu = cpu_baseline(synth, w, dm, wl, main_lens, main_prompt, main_pad,
+                           min(args.cpu_frames, args.frames or wl["frames"]))
 
+    kc = counted("kernel")
     out = {
         "metric": "16-code frames/sec (0.6B-shaped talker + code predictor)",
         "value": round(r["value"], 3),
@@ -285,21 +352,122 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 weights, fp32 accumulate" if wl["dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded random weights and prompt embeddings)",
-        "config": main_wl.config(r["total_frames"], args.steps),
+        "config": main_cfg,
         # per-row real-time factor: wall time / audio time (audio = frames / 12.5 Hz)
         "rtf": round(FRAMES_PER_AUDIO_SECOND * B / r["value"], 6) if r["value"] else None,
         "decode_ms_per_frame": round(r["frame_ms"], 4),
         # time to first audio frame: qt_prefill (talker over the prompt, selection 0) + the first frame
         "ttfa_ms": round(r["ttfa_ms"], 3),
-        "frame_roofline": roof(r["fb"], r["frame_ms"]),
+        "frame_roofline": roof(r, args.workload),
         "roofline": {"kernel": "gemv_kernel (gate/up SwiGLU projection, N=%d K=%d M=%d)" % (2 * I, H, B),
                      "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
-                     "avg_launch_us": round(kern_us, 3), "bytes_per_launch": int(kern_bytes)},
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": kc["bytes"] if kc else None,
+                     "avg_launch_us": round(kern_us, 3), "bytes_per_launch": int(kern_bytes),
+                     # the same launch loop under rocprofv3 --kernel-trace (committed profile)
+                     "trace_avg_us": kc["trace_avg_us"] if kc else None,
+                     "trace_frac": round(kern_bytes / (kc["trace_avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                     if kc else None},
         "batches": batches,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_64mib(torch):
+    """A plain 64 MiB device copy: the calibration kernel of known size for the byte counters."""
+    a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def frame_counter_run(torch, binding, synth, name, frames):
+    """A prompt prefill and `frames` eager frames of a workload (the frame's
+    kernels; teacher-forced codes, which do not change what is read), then a
+    64 MiB copy for the counter calibration. The frames are launched one by
+    one through qt_debug_step_forced, so a counter run sees every dispatch."""
+    x = Workload(torch, binding, synth, name)
+    wl = x.wl
+    x.eng.prefill(x.prompt, x.lens, x.pad, wl["talker"], wl["predictor"], 0, x.frames)
+    B = x.B
+    for k in range(frames):
+        forced = np.zeros((B, 16), dtype=np.int32)
+        forced[:, 0] = (97 * k + 13 * np.arange(B)) % 2048
+        forced[:, 1:] = (np.arange(1, 16)[None, :] * 131 + 7 * k + np.arange(B)[:, None]) % 2048
+        x.eng.step_forced(forced)
+    torch.cuda.synchronize()
+    copy_64mib(torch)
+    print(json.dumps({"workload": name, "batch": B, "frames": frames, "prompt_lens": [int(v) for v in x.lens][:8],
+                      "copy_bytes": 64 << 20}), flush=True)
+    x.eng.close()
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(d, per_frame):
+    """Print a summary of the rocprofv3 CSV output under d: kernel statistics
+    (kernel_stats.csv of a --kernel-trace --stats run) and/or counters per
+    kernel (counter_collection.csv of a --pmc run), with the 64 MiB copy as
+    the calibration of each counter (scale = copy bytes / copy counter value).
+    With per_frame, counters are also summed over the dispatches from the
+    first frame_start_kernel on (runtime copy kernels excluded) and divided
+    by the number of frame_start_kernel dispatches."""
+    import glob
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    ctrs = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    for path in stats:
+        rows = _csv_rows(path)
+        total = sum(float(r["TotalDurationNs"]) for r in rows)
+        print(f"kernel statistics ({os.path.relpath(path, d)}): total {total / 1e6:.2f} ms")
+        print("| kernel | calls | total ms | avg us | min us | max us | % |")
+        print("|---|---|---|---|---|---|---|")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            print(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                  f"{float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                  f"{float(r['Percentage']):.2f} |")
+    for path in ctrs:
+        rows = _csv_rows(path)
+        by = {}
+        order = []
+        for r in rows:
+            key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Counter_Name"])
+            if key not in by:
+                order.append(key)
+                by[key] = [r["Kernel_Name"], 0.0]
+            by[key][1] += float(r["Counter_Value"])
+        names = sorted({k[1] for k in order})
+        for cn in names:
+            disp = [(int(k[0]), by[k][0], by[k][1]) for k in order if k[1] == cn]
+            disp.sort()
+            copies = [v for _, n, v in disp if n.startswith("__amd_rocclr_copyBuffer")]
+            cal = copies[-1] if copies else None
+            scale = (64 << 10) / cal if cal else None   # KiB of the 64 MiB copy / counted KiB
+            print(f"counter {cn} ({os.path.relpath(path, d)}): {len(disp)} dispatches; "
+                  f"calibration copy {cal} -> scale {scale and round(scale, 4)}")
+            agg = {}
+            for _, n, v in disp:
+                a = agg.setdefault(n, [0, 0.0])
+                a[0] += 1
+                a[1] += v
+            print(f"| kernel | dispatches | {cn} KiB / dispatch | scaled MB / dispatch |")
+            print("|---|---|---|---|")
+            for n, (c, v) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:25]:
+                sc = f"{v / c * scale * 1024 / 1e6:.4f}" if scale else "-"
+                print(f"| `{n[:90]}` | {c} | {v / c:.1f} | {sc} |")
+            if per_frame:
+                first = next((i for i, (_, n, _) in enumerate(disp) if "frame_start_kernel" in n), None)
+                if first is None:
+                    print("no frame_start_kernel dispatch found")
+                    continue
+                frames = sum(1 for _, n, _ in disp[first:] if "frame_start_kernel" in n)
+                tot = sum(v for _, n, v in disp[first:] if not n.startswith("__amd_rocclr"))
+                print(f"per frame: {frames} frames, {tot / frames:.1f} KiB counted"
+                      + (f" = {tot / frames * scale * 1024 / 1e9:.4f} GB scaled" if scale else ""))
 
 
 def kernel_timing(torch, binding, w, dm, wl, B, reps, copies=40):
@@ -364,22 +532,58 @@ def gemm_kernel_timing(torch, binding, synth, reps=10):
     return out
 
 
-def cpu_baseline(w, dm, wl, lens, prompt_np, pad_np, n_frames):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import oracle
-    from codec_lm_autoregressive_amd import synth
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _time_oracle(oracle, w, dm, wl, prompt_rows, pad, n_frames, row=0):
+    t0 = time.perf_counter()
+    r = oracle.generate(w, dm, prompt_rows, pad, wl["talker"], wl["predictor"], 0, n_frames, rows=[row],
+                        record=False)[0]
+    return r["n_frames"], time.perf_counter() - t0
+
+
+def cpu_baseline(synth, w, dm, wl, lens, prompt_np, pad_np, n_frames):
+    """The oracle, as it stands, on bounded samples of the workloads: row 0 of
+    the batch-1 workload (prefill + n_frames frames) with the BLAS threads the
+    host gives it, the same row on 1 thread (prefill + 10 frames), and row 0 of
+    the batch-8 and batch-64 workloads (their prefill + 16 / 32 frames)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         cores = os.cpu_count()
     rows = synth.split_rows(prompt_np, lens)[:1]
-    t0 = time.perf_counter()
-    r = oracle.generate(w, dm, rows, pad_np, wl["talker"], wl["predictor"], 0, n_frames, record=False)[0]
-    dt = time.perf_counter() - t0
-    return {"value": round(r["n_frames"] / dt, 4), "unit": "frames/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"row 0: prefill of {int(lens[0])} tokens + {r['n_frames']} frames "
-                      f"(workload: {len(lens)} row(s), {wl['frames']} frames), numpy fp32, {dt:.1f}s"}
+    nf, dt = _time_oracle(oracle, w, dm, wl, rows, pad_np, n_frames)
+    out = {"value": round(nf / dt, 4), "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+           "cpu_model": _cpu_model(),
+           "sample": f"row 0: prefill of {int(lens[0])} tokens + {nf} frames "
+                     f"(workload: {len(lens)} row(s), {wl['frames']} frames), numpy fp32, {dt:.1f}s"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            nf1, dt1 = _time_oracle(oracle, w, dm, wl, rows, pad_np, 10)
+        out["one_thread"] = {"value": round(nf1 / dt1, 4), "unit": "frames/s", "cores": 1,
+                             "sample": f"row 0: prefill of {int(lens[0])} tokens + {nf1} frames, {dt1:.1f}s"}
+    more = []
+    for name, frames in (("qwen06b_bf16_b8_sampling", 16), ("qwen06b_bf16_b64_sampling", 32)):
+        wl2 = synth.workload(name)
+        l2 = synth.prompt_lengths(wl2["B"], *wl2["prompt"], seed=2)
+        H = dm["talker"]["hidden"]
+        p2 = synth.split_rows(synth.make_prompts(l2[:1], H, seed=1), l2[:1])
+        nf2, dt2 = _time_oracle(oracle, w, dm, wl2, p2, pad_np, frames)
+        more.append({"workload": name, "value": round(nf2 / dt2, 4), "unit": "frames/s", "cores": int(cores),
+                     "sample": f"row 0: prefill of {int(l2[0])} tokens + {nf2} frames "
+                               f"(workload: {wl2['B']} rows, {wl2['frames']} frames), {dt2:.1f}s"})
+    out["batches"] = more
+    return out
 
 
 if __name__ == "__main__":
