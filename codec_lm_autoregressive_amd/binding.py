@@ -88,6 +88,7 @@ def lib():
             "qt_debug_exp_noise": ([vp, i32, vp, C.c_int64, u64, vp], i32),
             "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
                                  C.c_int64], i32),
+            "qt_linear_noalloc": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp], i32),
             "qt_debug_prefill_attention": ([vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp,
                                             vp, i32, vp, C.c_int64], i32),
         }
@@ -299,6 +300,20 @@ def debug_linear(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", r
     _check(lib().qt_debug_linear(C.c_void_p(s), QT_DTYPE_BF16 if wdtype == "bf16" else QT_DTYPE_F32,
                                  _ptr(W), N, K, _ptr(X), M, _ptr(gain), eps, epilogue, _ptr(Y), _ptr(scratch),
                                  n_scratch if matrix_cores else 0, reps, copies, N * K * W.element_size()))
+    return Y
+
+
+def linear_noalloc(W, X, gain=None, eps=1e-6, epilogue=0, Y=None, wdtype="bf16", stream=None):
+    """Y = op(W · norm(X)) through qt_linear_noalloc (the library's static
+    scratch; nothing allocated by the library). torch tensors as debug_linear."""
+    import torch
+    N, K = W.shape
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.zeros((M, N // 2 if epilogue == 2 else N), dtype=torch.float32, device=X.device)
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(lib().qt_linear_noalloc(C.c_void_p(s), QT_DTYPE_BF16 if wdtype == "bf16" else QT_DTYPE_F32, _ptr(W), N,
+                                   K, _ptr(X), M, _ptr(gain), eps, epilogue, _ptr(Y)))
     return Y
 
 

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -560,6 +561,43 @@ qt_status read_status(qt_ctx* ctx) {
 
 }  // namespace
 
+// ---- scratch of the allocation-free projection entry point (qt_linear_noalloc)
+// One array per device, held until the process ends. In host code `scratch`
+// names only a host-side stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, cached per device.
+constexpr long kNoallocScratchFloats = 8L << 20;   // 32 MiB
+static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+constexpr int kMaxDevices = 64;
+static float* g_scratch_dev[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static qt_status noalloc_scratch(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_err(g_err, "no current HIP device (or device index >= %d)", kMaxDevices);
+    return QT_E_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_err(g_err, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return QT_E_HIP;
+    }
+    g_scratch_dev[dev] = (float*)ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return QT_OK;
+}
+
+// Scratch floats a projection of M rows needs for the matrix-core paths:
+// the row denominators (rounded up to 64 floats) and either the K-range
+// partial sums (up to 128 rows) or the hi/lo split planes of the rows.
+static long linear_scratch_floats(long M, long N, long K) {
+  return (M + 63) / 64 * 64 + (M <= 128 ? (K / 256) * M * (N + 1) : M * K);
+}
+
 extern "C" {
 
 qt_status qt_config_check(const qt_config* cfg) { return check_config(cfg, g_err); }
@@ -1046,6 +1084,36 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
     hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
     if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   }
+  return QT_OK;
+}
+
+qt_status qt_linear_noalloc(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
+                            int32_t M, const float* gain, float eps, int32_t epilogue, float* Y) {
+  if (wdtype != QT_DTYPE_F32 && wdtype != QT_DTYPE_BF16) { set_err(g_err, "bad wdtype"); return QT_E_INVALID; }
+  if (!W || !X || !Y) { set_err(g_err, "W, X and Y must not be NULL"); return QT_E_INVALID; }
+  if (N < 1 || K < 8 || K % 8 || M < 1 || epilogue < 0 || epilogue > 2 || (epilogue == 2 && N % 2)) {
+    set_err(g_err, "bad shape: need N >= 1, K a positive multiple of 8, M >= 1, even N for SwiGLU");
+    return QT_E_INVALID;
+  }
+  if (K > 24576) { set_err(g_err, "K too large for the LDS activation tile"); return QT_E_INVALID; }
+  const long need = linear_scratch_floats(M, N, K);
+  if (need > kNoallocScratchFloats) {
+    set_err(g_err, "projection needs %ld scratch floats, above the %ld of the static scratch", need,
+            kNoallocScratchFloats);
+    return QT_E_CAPACITY;
+  }
+  float* sc = nullptr;
+  const qt_status st = noalloc_scratch(&sc);
+  if (st != QT_OK) return st;
+  LinearArgs a{};
+  a.W = W; a.wdtype = wdtype; a.N = N; a.K = K; a.X = X; a.ldx = K; a.M = M; a.gain = gain; a.eps = eps;
+  a.Y = Y; a.ldy = epilogue == 2 ? N / 2 : N; a.epi = epilogue;
+  const long den = ((long)M + 63) / 64 * 64;
+  a.row_den = sc;
+  a.part = sc + den; a.part_floats = need - den;
+  a.xs = a.part; a.xs_floats = a.part_floats;
+  const hipError_t e = launch_linear(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) { set_err(g_err, "linear launch failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
   return QT_OK;
 }
 

@@ -260,6 +260,22 @@ qt_status qt_debug_linear(void* hip_stream, int32_t wdtype, const void* W, int32
                           float* Y, float* scratch, int64_t scratch_floats, int32_t reps,
                           int32_t w_copies, int64_t w_copy_stride);
 
+/* Y = op(W · norm(X)) exactly as qt_debug_linear computes it with full
+ * matrix-core scratch, but allocating nothing: for callers that cannot call
+ * hipMalloc (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation). The scratch (row RMS denominators, K-range partial
+ * sums, hi/lo split planes) is a static device array of 8 Mi floats (32 MiB)
+ * per GPU, held until the process ends; its address is looked up once per
+ * device on the first call there. Arguments as qt_debug_linear (one launch,
+ * one weight copy). A projection whose scratch need, (M rounded up to 64) +
+ * (K / 256) * M * (N + 1) floats for M <= 128 or + M * K floats above, exceeds
+ * the static array returns QT_E_CAPACITY before any device work. Every call
+ * on one GPU shares that array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. Enqueued on
+ * hip_stream; nothing is synchronised. */
+qt_status qt_linear_noalloc(void* hip_stream, int32_t wdtype, const void* W, int32_t N, int32_t K, const float* X,
+                            int32_t M, const float* gain, float eps, int32_t epilogue, float* Y);
+
 /* The prompt prefill's attention of one decoder layer with the frame's
  * kernels (no context): per-head RMSNorm of q and k with their gains, rope of
  * both, the K/V rows written to the cache, then causal GQA attention of every
