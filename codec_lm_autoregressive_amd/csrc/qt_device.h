@@ -19,6 +19,9 @@ constexpr int MFMA_MIN_ROWS = 16;  // activation rows from which projections use
 
 // Weight rows are streamed once per pass, with nontemporal loads.
 __device__ __forceinline__ u32x4 ld_weight(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+// Ordinary cached loads of weight rows, for kernels whose blocks share a row
+// group (the 17..128-row GEMMs: measured faster there, slower in the GEMVs).
+__device__ __forceinline__ u32x4 ld_weight_cached(const void* p) { return *(const u32x4*)p; }
 
 // ---------------------------------------------------------------- helpers
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

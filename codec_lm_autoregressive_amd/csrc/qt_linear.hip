@@ -1064,7 +1064,7 @@ __global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
 #pragma unroll
-      for (int q = 0; q < WV; ++q) wv[st][q] = ld_weight(wrow[q] + k0 + st * SG_GK);
+      for (int q = 0; q < WV; ++q) wv[st][q] = ld_weight_cached(wrow[q] + k0 + st * SG_GK);
 #pragma unroll
       for (int q = 0; q < XV; ++q) xv[st][q] = *(const f32x4*)(xrow[q] + k0 + st * SG_GK);
     }
@@ -1214,7 +1214,7 @@ __global__ __launch_bounds__(NT) void rows_gemm1_kernel(LinearArgs p) {
   for (int q = 0; q < WV; ++q) {
     const uint16_t* wr = (const uint16_t*)p.W + (long)min(n0 + (tid >> 3) + 32 * q, N - 1) * K + kb + wc;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) wv[st][q] = ld_weight(wr + st * SG_GK);
+    for (int st = 0; st < NS; ++st) wv[st][q] = ld_weight_cached(wr + st * SG_GK);
   }
   if constexpr (NORM)
 #pragma unroll
