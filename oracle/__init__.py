@@ -18,10 +18,12 @@ available for the pins:
   loop.py      prompt prefill, the per-frame loop (talker step, 2-token
                predictor prefill + 14 steps, embedding-sum feedback), stop
                rules and counters
+  frontend.py  token-id frontend: text embedding, ResizeMLP, dual-track
+               prompt assembly
 
 Pinned by tests/test_oracle_*.py (closed forms, invariants, library
 routines, brute force, golden values under tests/golden/). Parity with the
 real Qwen3-TTS checkpoints is unpinned: no weights or golden codes exist here.
 """
 from .loop import generate, prefill_row, OracleNonFinite  # noqa: F401
-from . import model, sampling, philox  # noqa: F401
+from . import model, sampling, philox, frontend  # noqa: F401
