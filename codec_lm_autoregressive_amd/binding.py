@@ -60,6 +60,15 @@ class Sampling(C.Structure):
                 ("top_p", C.c_float), ("repetition_penalty", C.c_float), ("min_new_tokens", C.c_int32)]
 
 
+class FrontendConfig(C.Structure):
+    _fields_ = [("text_vocab", C.c_int32), ("text_hidden", C.c_int32), ("mlp_hidden", C.c_int32),
+                ("max_rows", C.c_int32)]
+
+
+class FrontendWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("text_embed", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
 _lib = None
 
 
@@ -85,6 +94,11 @@ def lib():
             "qt_debug_talker_logits": ([vp, vp], i32),
             "qt_debug_select": ([vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, C.POINTER(Sampling), u64, i32,
                                  i32, vp, vp, vp], i32),
+            "qt_frontend_bytes": ([C.POINTER(Config), C.POINTER(FrontendConfig), C.POINTER(C.c_size_t)], i32),
+            "qt_attach_frontend": ([vp, C.POINTER(FrontendConfig), C.POINTER(FrontendWeights), vp, C.c_size_t], i32),
+            "qt_embed_ids": ([vp, i32, vp, vp, vp, vp], i32),
+            "qt_prefill_ids": ([vp, i32, vp, vp, vp, vp, vp, i32, C.POINTER(Sampling), C.POINTER(Sampling), u64, i32],
+                               i32),
             "qt_debug_exp_noise": ([vp, i32, vp, C.c_int64, u64, vp], i32),
             "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
                                  C.c_int64], i32),
@@ -256,6 +270,58 @@ class Engine:
                                  C.byref(ts), C.byref(ps), C.c_uint64(seed), int(max_frames),
                                  _np_ptr(codes), _np_ptr(n), _np_ptr(fin)), self.ctx)
         return codes, n, fin
+
+    # ---- token-id frontend
+    def attach_frontend(self, fw, max_rows):
+        """fw: dict text_embed, fc1_w, fc1_b, fc2_w, fc2_b (numpy, biases may be None)."""
+        torch = self.torch
+        V, Ti = fw["text_embed"].shape
+        Hm = fw["fc1_w"].shape[0]
+        self.fcfg = FrontendConfig(V, Ti, Hm, int(max_rows))
+        keep = []
+
+        def up(a):
+            if a is None:
+                return None
+            x = to_device_weight(a, self.dtype)
+            keep.append(x)
+            return _ptr(x)
+        with torch.cuda.stream(self.stream):
+            w = FrontendWeights(up(fw["text_embed"]), up(fw["fc1_w"]), up(fw.get("fc1_b")), up(fw["fc2_w"]),
+                                up(fw.get("fc2_b")))
+        torch.cuda.synchronize()
+        _check(lib().qt_attach_frontend(self.ctx, C.byref(self.fcfg), C.byref(w), None, 0), self.ctx)
+        keep.clear()   # the library holds its own repacked copy
+
+    def embed_ids(self, text_ids, codec_ids, extra=None):
+        """Dual-track rows [n, H] (device tensor) for host id arrays."""
+        torch = self.torch
+        ti = np.ascontiguousarray(text_ids, dtype=np.int32)
+        ci = np.ascontiguousarray(codec_ids, dtype=np.int32)
+        n = int(ti.size)
+        out = torch.empty((n, self.dm["talker"]["hidden"]), dtype=torch.float32, device="cuda")
+        ex = None
+        if extra is not None:
+            ex = extra if isinstance(extra, torch.Tensor) else torch.from_numpy(
+                np.ascontiguousarray(extra, dtype=np.float32)).cuda()
+        torch.cuda.synchronize()
+        _check(lib().qt_embed_ids(self.ctx, n, _np_ptr(ti), _np_ptr(ci), _ptr(ex), _ptr(out)), self.ctx)
+        torch.cuda.synchronize()
+        return out
+
+    def prefill_ids(self, text_ids, codec_ids, lens, trailing_ids, trailing_lens, tts_pad_id, talker, predictor, seed,
+                    max_frames):
+        ti = np.ascontiguousarray(text_ids, dtype=np.int32)
+        ci = np.ascontiguousarray(codec_ids, dtype=np.int32)
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        tr = np.ascontiguousarray(trailing_ids, dtype=np.int32) if trailing_ids is not None else None
+        tl = np.ascontiguousarray(trailing_lens, dtype=np.int32) if trailing_lens is not None else None
+        self.B = int(lens.size)
+        self._keep = []
+        ts, ps = sampling(talker), sampling(predictor)
+        _check(lib().qt_prefill_ids(self.ctx, self.B, _np_ptr(ti), _np_ptr(ci), _np_ptr(lens), _np_ptr(tr),
+                                    _np_ptr(tl), int(tts_pad_id), C.byref(ts), C.byref(ps), C.c_uint64(seed),
+                                    int(max_frames)), self.ctx)
 
     # ---- test entry points
     def step_forced(self, forced):

@@ -254,6 +254,60 @@ Layout plan_layout(const qt_config& c) {
   return L;
 }
 
+// Workspace of the token-id frontend: packed weights, id arrays, the MLP's
+// row buffers for chunks of up to kFrontendChunk rows with the projections'
+// matrix-core scratch, and the assembled rows of qt_prefill_ids (prompt
+// rows, then trailing text rows, then tts_pad's row).
+constexpr int kFrontendChunk = 8192;
+struct FeLayout {
+  size_t embed, fc1, fc2, b1, b2, tids, cids, x0, h1, y, scratch, rows, total;
+  long scratch_floats;
+  int chunk;
+  bool ovf;
+};
+
+bool frontend_ok(const qt_config& c, const qt_frontend_config* f, char* err) {
+  if (!f) { set_err(err, "frontend config is NULL"); return false; }
+  if (f->text_vocab < 1 || f->text_vocab > (1 << 24)) { set_err(err, "text_vocab must be in 1..2^24"); return false; }
+  if (f->text_hidden < 8 || f->text_hidden > 24576 || f->text_hidden % 8) {
+    set_err(err, "text_hidden must be a multiple of 8 in 8..24576"); return false;
+  }
+  if (f->mlp_hidden < 8 || f->mlp_hidden > 24576 || f->mlp_hidden % 8) {
+    set_err(err, "mlp_hidden must be a multiple of 8 in 8..24576"); return false;
+  }
+  if (f->max_rows < 1 || f->max_rows > (1 << 24)) { set_err(err, "max_rows must be in 1..2^24"); return false; }
+  (void)c;
+  return true;
+}
+
+FeLayout plan_frontend(const qt_config& c, const qt_frontend_config& f) {
+  FeLayout L;
+  Plan p;
+  const size_t es = esize(c.weight_dtype), H = c.talker.hidden, Ti = f.text_hidden, Hm = f.mlp_hidden;
+  const size_t R = f.max_rows, ch = std::min<size_t>(R, kFrontendChunk);
+  L.chunk = (int)ch;
+  L.embed = p.take(p.sz.mul({(size_t)f.text_vocab, Ti, es}));
+  L.fc1 = p.take(p.sz.mul({Hm, Ti, es}));
+  L.fc2 = p.take(p.sz.mul({H, Hm, es}));
+  L.b1 = p.take(Hm * 4);
+  L.b2 = p.take(H * 4);
+  L.tids = p.take(p.sz.mul(R, 4));
+  L.cids = p.take(p.sz.mul(R, 4));
+  L.x0 = p.take(p.sz.mul({ch, Ti, 4}));
+  L.h1 = p.take(p.sz.mul({ch, Hm, 4}));
+  L.y = p.take(p.sz.mul({ch, H, 4}));
+  // row denominators + the larger of: the hi/lo planes of a full chunk, or
+  // the K-range partial sums of a chunk of up to 128 rows
+  const size_t kmax = std::max(Ti, Hm), nmax = std::max(Hm, H);
+  const size_t need = (ch + 63) / 64 * 64 + std::max(ch > 128 ? ch * kmax : 0, (kmax / 256) * std::min<size_t>(ch, 128) * (nmax + 1));
+  L.scratch_floats = (long)need;
+  L.scratch = p.take(p.sz.mul(need, 4));
+  L.rows = p.take(p.sz.mul({R, H, 4}));
+  L.total = p.off;
+  L.ovf = p.sz.ovf;
+  return L;
+}
+
 struct DevLayer {
   void *wqkv, *wo, *wgu, *wd;
   float *attn_norm, *q_norm, *k_norm, *mlp_norm;
@@ -300,6 +354,20 @@ struct qt_ctx {
   hipGraphExec_t gexec = nullptr;
   int graph_B = -1;
   int eager_frames = 0;
+  // token-id frontend (qt_attach_frontend)
+  struct Frontend {
+    bool on = false;
+    qt_frontend_config fc{};
+    char* ws = nullptr;
+    bool own_ws = false;
+    void *embed = nullptr, *fc1 = nullptr, *fc2 = nullptr;
+    float *b1 = nullptr, *b2 = nullptr;
+    int *tids = nullptr, *cids = nullptr;
+    float *x0 = nullptr, *h1 = nullptr, *y = nullptr, *scratch = nullptr;
+    long scratch_floats = 0;
+    int chunk = 0;
+    float *prompt = nullptr, *trail = nullptr, *pad = nullptr;   // qt_prefill_ids outputs
+  } fe;
 };
 
 namespace {
@@ -750,6 +818,7 @@ void qt_destroy(qt_ctx* ctx) {
   if (ctx->stream || ctx->cap) (void)hipDeviceSynchronize();
   if (ctx->gexec) (void)hipGraphExecDestroy(ctx->gexec);
   if (ctx->own_ws && ctx->ws) (void)hipFree(ctx->ws);
+  if (ctx->fe.own_ws && ctx->fe.ws) (void)hipFree(ctx->fe.ws);
   if (ctx->hout) (void)hipHostFree(ctx->hout);
   if (ctx->ev) (void)hipEventDestroy(ctx->ev);
   if (ctx->cap) (void)hipStreamDestroy(ctx->cap);
@@ -972,6 +1041,160 @@ qt_status qt_generate(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t
     }
   }
   return QT_OK;
+}
+
+// ---- token-id frontend
+
+// out[i] = ResizeMLP(text_embed[tids[i]]) + codec_embed[cids[i]] (+ extra[i]),
+// empty tracks (-1) as zero rows; ids already validated, n <= max_rows.
+static qt_status fe_embed(qt_ctx* ctx, int n, const int* tids, const int* cids, const float* extra, float* out) {
+  auto& fe = ctx->fe;
+  const hipStream_t s = ctx->stream;
+  const int H = ctx->t.H, Ti = fe.fc.text_hidden, Hm = fe.fc.mlp_hidden, wd = ctx->cfg.weight_dtype;
+  HIPCK(hipMemcpyAsync(fe.tids, tids, (size_t)n * 4, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(fe.cids, cids, (size_t)n * 4, hipMemcpyHostToDevice, s));
+  HIPCK(hipStreamSynchronize(s));   // the host id arrays may go away after this call
+  for (int r0 = 0; r0 < n; r0 += fe.chunk) {
+    const int m = std::min(fe.chunk, n - r0);
+    HIPCK(launch_gather_rows(fe.embed, wd, Ti, fe.tids + r0, m, fe.x0, s));
+    LinearArgs a{};
+    a.wdtype = wd; a.eps = 1e-6f; a.M = m; a.epi = EPI_STORE;
+    const long den = ((long)m + 63) / 64 * 64;
+    a.row_den = fe.scratch; a.part = fe.scratch + den; a.part_floats = fe.scratch_floats - den;
+    a.xs = a.part; a.xs_floats = a.part_floats;
+    a.W = fe.fc1; a.N = Hm; a.K = Ti; a.X = fe.x0; a.ldx = Ti; a.Y = fe.h1; a.ldy = Hm;
+    HIPCK(launch_linear(a, s));
+    HIPCK(launch_bias_silu(fe.h1, m, Hm, fe.b1, s));
+    a.W = fe.fc2; a.N = H; a.K = Hm; a.X = fe.h1; a.ldx = Hm; a.Y = fe.y; a.ldy = H;
+    HIPCK(launch_linear(a, s));
+    HIPCK(launch_assemble_rows(fe.y, fe.b2, fe.tids + r0, fe.cids + r0, ctx->temb, wd,
+                               extra ? extra + (size_t)r0 * H : nullptr, out + (size_t)r0 * H, m, H, s));
+  }
+  return QT_OK;
+}
+
+static qt_status check_ids(qt_ctx* ctx, int n, const int* ids, int hi, const char* who) {
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < -1 || ids[i] >= hi) {
+      set_err(ctx->err, "%s[%d]=%d outside -1..%d", who, i, ids[i], hi - 1);
+      return QT_E_RANGE;
+    }
+  return QT_OK;
+}
+
+qt_status qt_frontend_bytes(const qt_config* cfg, const qt_frontend_config* fc, size_t* bytes) {
+  qt_status s = check_config(cfg, g_err);
+  if (s != QT_OK) return s;
+  if (!frontend_ok(*cfg, fc, g_err)) return QT_E_INVALID;
+  if (!bytes) { set_err(g_err, "bytes is NULL"); return QT_E_INVALID; }
+  FeLayout L = plan_frontend(*cfg, *fc);
+  if (L.ovf) { set_err(g_err, "frontend workspace size overflows size_t"); return QT_E_CAPACITY; }
+  *bytes = L.total;
+  return QT_OK;
+}
+
+qt_status qt_attach_frontend(qt_ctx* ctx, const qt_frontend_config* fc, const qt_frontend_weights* fw, void* workspace,
+                             size_t ws_bytes) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!frontend_ok(ctx->cfg, fc, ctx->err)) return QT_E_INVALID;
+  if (!fw || !fw->text_embed || !fw->fc1_w || !fw->fc2_w) {
+    set_err(ctx->err, "frontend weights (text_embed, fc1_w, fc2_w) must not be NULL");
+    return QT_E_INVALID;
+  }
+  FeLayout L = plan_frontend(ctx->cfg, *fc);
+  if (L.ovf) { set_err(ctx->err, "frontend workspace size overflows size_t"); return QT_E_CAPACITY; }
+  if (workspace && ws_bytes < L.total) {
+    set_err(ctx->err, "frontend workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    return QT_E_NOMEM;
+  }
+  auto& fe = ctx->fe;
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  if (fe.own_ws && fe.ws) (void)hipFree(fe.ws);
+  fe = qt_ctx::Frontend{};
+  if (workspace) {
+    fe.ws = (char*)workspace;
+  } else {
+    if (hipMalloc((void**)&fe.ws, L.total) != hipSuccess) {
+      set_err(ctx->err, "hipMalloc of %zu frontend bytes failed", L.total);
+      fe.ws = nullptr;
+      return QT_E_NOMEM;
+    }
+    fe.own_ws = true;
+  }
+  fe.fc = *fc;
+  fe.embed = fe.ws + L.embed; fe.fc1 = fe.ws + L.fc1; fe.fc2 = fe.ws + L.fc2;
+  fe.b1 = (float*)(fe.ws + L.b1); fe.b2 = (float*)(fe.ws + L.b2);
+  fe.tids = (int*)(fe.ws + L.tids); fe.cids = (int*)(fe.ws + L.cids);
+  fe.x0 = (float*)(fe.ws + L.x0); fe.h1 = (float*)(fe.ws + L.h1); fe.y = (float*)(fe.ws + L.y);
+  fe.scratch = (float*)(fe.ws + L.scratch); fe.scratch_floats = L.scratch_floats; fe.chunk = L.chunk;
+  fe.prompt = (float*)(fe.ws + L.rows);
+  const int wd = ctx->cfg.weight_dtype, H = ctx->t.H, Ti = fc->text_hidden, Hm = fc->mlp_hidden;
+  const hipStream_t s = ctx->stream;
+  HIPCK(launch_convert(fw->text_embed, wd, Ti, fe.embed, wd, Ti, fc->text_vocab, Ti, s));
+  HIPCK(launch_convert(fw->fc1_w, wd, Ti, fe.fc1, wd, Ti, Hm, Ti, s));
+  HIPCK(launch_convert(fw->fc2_w, wd, Hm, fe.fc2, wd, Hm, H, Hm, s));
+  if (fw->fc1_b) HIPCK(launch_convert(fw->fc1_b, wd, Hm, fe.b1, DT_F32, Hm, 1, Hm, s));
+  else HIPCK(launch_fill_i32((int*)fe.b1, 0, Hm, s));
+  if (fw->fc2_b) HIPCK(launch_convert(fw->fc2_b, wd, H, fe.b2, DT_F32, H, 1, H, s));
+  else HIPCK(launch_fill_i32((int*)fe.b2, 0, H, s));
+  HIPCK(hipStreamSynchronize(s));
+  fe.on = true;
+  return QT_OK;
+}
+
+qt_status qt_embed_ids(qt_ctx* ctx, int32_t n, const int32_t* text_ids, const int32_t* codec_ids, const float* extra,
+                       float* out) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!ctx->fe.on) { set_err(ctx->err, "no frontend attached (qt_attach_frontend)"); return QT_E_STATE; }
+  if (n < 1 || n > ctx->fe.fc.max_rows) { set_err(ctx->err, "n=%d outside 1..max_rows=%d", n, ctx->fe.fc.max_rows); return QT_E_CAPACITY; }
+  if (!text_ids || !codec_ids || !out) { set_err(ctx->err, "text_ids, codec_ids and out must not be NULL"); return QT_E_INVALID; }
+  if (((uintptr_t)out | (uintptr_t)extra) % 16) { set_err(ctx->err, "out and extra must be 16-byte aligned"); return QT_E_INVALID; }
+  QTCK(check_ids(ctx, n, text_ids, ctx->fe.fc.text_vocab, "text_ids"));
+  QTCK(check_ids(ctx, n, codec_ids, ctx->cfg.talker_vocab, "codec_ids"));
+  return fe_embed(ctx, n, text_ids, codec_ids, extra, out);
+}
+
+qt_status qt_prefill_ids(qt_ctx* ctx, int32_t B, const int32_t* text_ids, const int32_t* codec_ids,
+                         const int32_t* prompt_lens, const int32_t* trailing_ids, const int32_t* trailing_lens,
+                         int32_t tts_pad_id, const qt_sampling* talker, const qt_sampling* predictor, uint64_t seed,
+                         int32_t max_frames) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  if (!ctx->fe.on) { set_err(ctx->err, "no frontend attached (qt_attach_frontend)"); return QT_E_STATE; }
+  if (B < 1 || B > ctx->cfg.max_batch) { set_err(ctx->err, "B=%d outside 1..max_batch=%d", B, ctx->cfg.max_batch); return QT_E_CAPACITY; }
+  if (!text_ids || !codec_ids || !prompt_lens) { set_err(ctx->err, "text_ids, codec_ids and prompt_lens must not be NULL"); return QT_E_INVALID; }
+  long P = 0, Tn = 0;
+  for (int r = 0; r < B; ++r) {
+    if (prompt_lens[r] < 1) { set_err(ctx->err, "prompt_lens[%d]=%d must be >= 1", r, prompt_lens[r]); return QT_E_RANGE; }
+    P += prompt_lens[r];
+    if (trailing_lens) {
+      if (trailing_lens[r] < 0) { set_err(ctx->err, "trailing_lens[%d] must be >= 0", r); return QT_E_RANGE; }
+      Tn += trailing_lens[r];
+    }
+  }
+  if (Tn > 0 && !trailing_ids) { set_err(ctx->err, "trailing_ids is NULL but trailing_lens are positive"); return QT_E_INVALID; }
+  const long rows = P + Tn + 1;
+  if (rows > ctx->fe.fc.max_rows) {
+    set_err(ctx->err, "%ld prompt + trailing + pad rows exceed the frontend's max_rows=%d", rows, ctx->fe.fc.max_rows);
+    return QT_E_CAPACITY;
+  }
+  if (tts_pad_id < 0 || tts_pad_id >= ctx->fe.fc.text_vocab) { set_err(ctx->err, "tts_pad_id out of range"); return QT_E_RANGE; }
+  QTCK(check_ids(ctx, (int)P, text_ids, ctx->fe.fc.text_vocab, "text_ids"));
+  QTCK(check_ids(ctx, (int)P, codec_ids, ctx->cfg.talker_vocab, "codec_ids"));
+  if (Tn > 0) {
+    QTCK(check_ids(ctx, (int)Tn, trailing_ids, ctx->fe.fc.text_vocab, "trailing_ids"));
+    for (long i = 0; i < Tn; ++i)
+      if (trailing_ids[i] < 0) { set_err(ctx->err, "trailing_ids[%ld] must be a text id", i); return QT_E_RANGE; }
+  }
+  std::vector<int> tid((size_t)rows), cid((size_t)rows, -1);
+  memcpy(tid.data(), text_ids, (size_t)P * 4);
+  memcpy(cid.data(), codec_ids, (size_t)P * 4);
+  if (Tn > 0) memcpy(tid.data() + P, trailing_ids, (size_t)Tn * 4);
+  tid[(size_t)rows - 1] = tts_pad_id;
+  QTCK(fe_embed(ctx, (int)rows, tid.data(), cid.data(), nullptr, ctx->fe.prompt));
+  const int H = ctx->t.H;
+  return qt_prefill(ctx, B, ctx->fe.prompt, prompt_lens, Tn > 0 ? ctx->fe.prompt + (size_t)P * H : nullptr,
+                    Tn > 0 ? trailing_lens : nullptr, ctx->fe.prompt + (size_t)(P + Tn) * H, talker, predictor, seed,
+                    max_frames);
 }
 
 qt_status qt_debug_step_forced(qt_ctx* ctx, const int32_t* forced, float* talker_logits, float* pred_logits,

@@ -157,6 +157,15 @@ hipError_t launch_convert(const void* src, int sdtype, long ld_src, void* dst, i
 // (vocab id, stream, selection index, row), key (seed, 0)) or n raw 64-bit
 // words (mode 1).
 hipError_t launch_noise(const uint64_t* in, int mode, uint64_t seed, float* out, long n, hipStream_t s);
+// Token-id frontend: X[i] = float(embed[ids[i]]) (zeros for ids[i] < 0),
+// rows of `width` (a multiple of 8) elements of type wdtype.
+hipError_t launch_gather_rows(const void* embed, int wdtype, int width, const int* ids, int n, float* X, hipStream_t s);
+// Hd[i] = silu(Hd[i] + b) over n rows of `width` (a multiple of 4); b may be null.
+hipError_t launch_bias_silu(float* Hd, int n, int width, const float* b, hipStream_t s);
+// out[i] = (tids[i] >= 0 ? Y[i] + b2 : 0) + (cids[i] >= 0 ? codec[cids[i]] : 0) + (extra ? extra[i] : 0),
+// n rows of `width` (a multiple of 4) floats; codec rows of type wdtype; b2 and extra may be null.
+hipError_t launch_assemble_rows(const float* Y, const float* b2, const int* tids, const int* cids, const void* codec,
+                                int wdtype, const float* extra, float* out, int n, int width, hipStream_t s);
 // Fill an int32 buffer.
 hipError_t launch_fill_i32(int* p, int v, long n, hipStream_t s);
 

@@ -270,3 +270,51 @@ def workload(name: str) -> dict:
                     frames=1024, talker=SAMPLING, predictor=PRED_SAMPLING,
                     max_positions=1536)
     raise KeyError(name)
+
+
+# ---------------------------------------------------------------- token-id frontend
+def frontend_dims(name: str) -> dict:
+    """Text embedding and ResizeMLP shapes (ncnn port section 1: Qwen2 BPE
+    vocabulary of 151936 ids, 2048-wide rows, ResizeMLP 2048 -> 2048 -> talker
+    width); "tiny" is a reduced vocabulary and width for fast tests."""
+    if name == "tiny":
+        return dict(text_vocab=3000, text_hidden=256, mlp_hidden=384)
+    return dict(text_vocab=151936, text_hidden=2048, mlp_hidden=2048)
+
+
+def make_frontend_weights(fd: dict, talker_hidden: int, seed: int = 0, dtype: str = "bf16") -> dict:
+    """Text embedding rows ~ N(0, 1) (so the MLP sees its SiLU's curved range),
+    the two layers' weights and biases ~ N(0, 0.02)."""
+    V, Ti, Hm = fd["text_vocab"], fd["text_hidden"], fd["mlp_hidden"]
+    w = dict(text_embed=_Normal("frontend.text_embed", (V, Ti), 1.0),
+             fc1_w=_Normal("frontend.fc1_w", (Hm, Ti), 0.02), fc1_b=_Normal("frontend.fc1_b", (Hm,), 0.02),
+             fc2_w=_Normal("frontend.fc2_w", (talker_hidden, Hm), 0.02),
+             fc2_b=_Normal("frontend.fc2_b", (talker_hidden,), 0.02))
+    leaves = []
+    map_arrays(w, lambda x: leaves.append(x) or x)
+    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        drawn = dict(zip(map(id, leaves), ex.map(lambda x: x.draw(seed, dtype == "bf16"), leaves)))
+    return map_arrays(w, lambda x: drawn[id(x)])
+
+
+def make_prompt_ids(lens, text_vocab: int, seed: int):
+    """Dual-track id arrays for prompts of the given lengths, packed row after
+    row, laid out like the pages' prompts: a few text-only positions (a role
+    prefix: codec track empty, -1), then language-prefix codec ids
+    (2050..2071), one built-in speaker id (3063..3071, a codec-table row),
+    codec_pad (2148) under the rest of the text, and codec_bos (2149) last.
+    Text ids are uniform over the vocabulary. Returns (text_ids, codec_ids)."""
+    g = np.random.default_rng(seed)
+    tids, cids = [], []
+    for P in np.asarray(lens):
+        P = int(P)
+        t = g.integers(0, text_vocab, P).astype(np.int32)
+        c = np.full(P, 2148, dtype=np.int32)
+        c[:min(3, P)] = -1
+        if P > 5:
+            c[3] = g.integers(2050, 2072)
+            c[4] = g.integers(3063, 3072)
+        c[-1] = 2149
+        tids.append(t)
+        cids.append(c)
+    return np.concatenate(tids), np.concatenate(cids)

@@ -192,6 +192,68 @@ void qt_destroy(qt_ctx* ctx);
  * errors of qt_create / qt_config_check). Never NULL. */
 const char* qt_last_error(const qt_ctx* ctx);
 
+/* ---- token-id frontend (ncnn port discussion 6798, section 1 "structure",
+ * Talker and generation-loop bullets; section 8 on built-in voices) ----
+ * Text ids index a text embedding table whose rows a ResizeMLP maps to the
+ * talker's width: row = W2 · silu(W1 · text_embed[id] + b1) + b2 (the text
+ * track). A prompt row adds, position by position, the text track of a text
+ * id and the codec track of a codec id, talker_codec_embed[id] (role,
+ * language and think prefixes, codec_bos / codec_pad; a built-in voice's
+ * speaker row is the codec row of its speaker id). Id -1 leaves a track
+ * empty (a zero row). The tokenizer that makes the ids is not part of this
+ * library. */
+typedef struct qt_frontend_config {
+  int32_t text_vocab;   /* rows of the text embedding (151936 for the Qwen2 vocabulary)   */
+  int32_t text_hidden;  /* width of a text embedding row (2048), multiple of 8, <= 24576   */
+  int32_t mlp_hidden;   /* inner width of the ResizeMLP (2048), multiple of 8, <= 24576    */
+  int32_t max_rows;     /* most rows one qt_embed_ids / qt_prefill_ids call embeds          */
+} qt_frontend_config;
+
+/* Device pointers, element type qt_config.weight_dtype, row-major [out, in]. */
+typedef struct qt_frontend_weights {
+  const void* text_embed; /* [text_vocab, text_hidden]                        */
+  const void* fc1_w;      /* [mlp_hidden, text_hidden]                        */
+  const void* fc1_b;      /* [mlp_hidden] or NULL (zero bias)                 */
+  const void* fc2_w;      /* [talker.hidden, mlp_hidden]                      */
+  const void* fc2_b;      /* [talker.hidden] or NULL (zero bias)              */
+} qt_frontend_weights;
+
+/* Device bytes qt_attach_frontend needs (packed weights, id arrays, the MLP's
+ * row buffers and scratch, the assembled rows of qt_prefill_ids). */
+qt_status qt_frontend_bytes(const qt_config* cfg, const qt_frontend_config* fc, size_t* bytes);
+
+/* Copy / repack the frontend weights into `workspace` (device, at least
+ * qt_frontend_bytes, caller-owned until qt_destroy; NULL: the library
+ * allocates and frees it). Replaces an earlier frontend. Synchronises the
+ * context's stream. */
+qt_status qt_attach_frontend(qt_ctx* ctx, const qt_frontend_config* fc, const qt_frontend_weights* fw,
+                             void* workspace, size_t ws_bytes);
+
+/* Dual-track rows for n positions: out[i] = text track(text_ids[i]) + codec
+ * track(codec_ids[i]) (+ extra[i]).
+ *   text_ids   host int32 [n], each -1 or in 0..text_vocab-1
+ *   codec_ids  host int32 [n], each -1 or in 0..talker_vocab-1
+ *   extra      device float [n, talker.hidden] or NULL (e.g. x-vector rows)
+ *   out        device float [n, talker.hidden]
+ * out and extra 16-byte aligned; 1 <= n <= max_rows. Ids are checked on the
+ * host before any device work (QT_E_RANGE). Enqueued on the context's stream
+ * (the host id arrays are free to reuse on return). QT_E_STATE without a
+ * frontend. */
+qt_status qt_embed_ids(qt_ctx* ctx, int32_t n, const int32_t* text_ids, const int32_t* codec_ids,
+                       const float* extra, float* out);
+
+/* qt_prefill from ids: the prompt rows of every row (prompt_lens[r] positions
+ * each, packed row after row in text_ids / codec_ids), the trailing text rows
+ * (trailing_ids packed the same way, trailing_lens[r] each, text track only;
+ * trailing_lens NULL: none) and tts_pad's row (the text track of
+ * tts_pad_id) are embedded by the frontend into its own workspace, where
+ * they stay for the frames of this request; then exactly qt_prefill. Rows
+ * embedded: sum(prompt_lens) + sum(trailing_lens) + 1 <= max_rows. */
+qt_status qt_prefill_ids(qt_ctx* ctx, int32_t B, const int32_t* text_ids, const int32_t* codec_ids,
+                         const int32_t* prompt_lens, const int32_t* trailing_ids, const int32_t* trailing_lens,
+                         int32_t tts_pad_id, const qt_sampling* talker, const qt_sampling* predictor, uint64_t seed,
+                         int32_t max_frames);
+
 /* ---- test and measurement entry points (same kernels as the frame) ---- */
 
 /* Teacher-forced frame: like qt_step_frame, but code 0 of this frame is

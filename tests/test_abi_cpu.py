@@ -136,6 +136,16 @@ def test_debug_entry_points_validate_before_launch():
     assert L.qt_debug_select(None, 1, 3072, C.c_void_p(16), None, None, None, 1, 2150, 2048, 3072, C.byref(sm), 0,
                              0, 0, C.c_void_p(16), None, C.c_void_p(16)) == binding.QT_E_INVALID
     fake = C.c_void_p(256)
+    fc = binding.FrontendConfig(151936, 2048, 2048, 4096)
+    n = C.c_size_t(0)
+    assert L.qt_frontend_bytes(C.byref(cfg06()), C.byref(fc), C.byref(n)) == binding.QT_OK
+    assert n.value > 151936 * 2048 * 2 + 2048 * 2048 * 2 + 1024 * 2048 * 2   # packed bf16 weights and buffers
+    for bad in (binding.FrontendConfig(0, 2048, 2048, 16), binding.FrontendConfig(10, 2044, 2048, 16),
+                binding.FrontendConfig(10, 2048, 2048, 0)):
+        assert L.qt_frontend_bytes(C.byref(cfg06()), C.byref(bad), C.byref(n)) == binding.QT_E_INVALID
+    ids = (C.c_int32 * 1)(0)
+    assert L.qt_embed_ids(None, 1, ids, ids, None, fake) == binding.QT_E_INVALID
+    assert L.qt_prefill_ids(None, 1, ids, ids, ids, None, None, 0, None, None, 0, 1) == binding.QT_E_INVALID
     assert L.qt_debug_exp_noise(None, 2, fake, 4, 0, fake) == binding.QT_E_INVALID    # mode
     assert L.qt_debug_exp_noise(None, 0, None, 4, 0, fake) == binding.QT_E_INVALID    # NULL input
     assert L.qt_debug_exp_noise(None, 1, fake, -1, 0, fake) == binding.QT_E_INVALID   # n < 0

@@ -74,8 +74,11 @@ class Tally:
 
 
 def teacher_forced_check(eng, w, dm, prompts, lens, pad, tsamp, psamp, seed, frames, tol, rows=None, texts=None,
-                         text_packed=None, text_lens=None, max_exempt_frac=0.2):
-    """Oracle free run -> force its codes into the GPU loop, compare logits and choices."""
+                         text_packed=None, text_lens=None, max_exempt_frac=0.2, prefill=None):
+    """Oracle free run -> force its codes into the GPU loop, compare logits and choices.
+
+    prefill: a callable that starts the GPU request instead of eng.prefill on
+    the float prompt rows (e.g. the token-id frontend's prefill)."""
     B = len(lens)
     rows = list(range(B)) if rows is None else rows
     ref = []
@@ -84,8 +87,11 @@ def teacher_forced_check(eng, w, dm, prompts, lens, pad, tsamp, psamp, seed, fra
                                texts=None if texts is None else [texts[r]])
         if len(rows) > 1:
             log(f"  oracle row {r}: {ref[-1]['n_frames']} frames")
-    eng.prefill(np.concatenate(prompts), lens, pad, tsamp, psamp, seed, frames, text=text_packed,
-                text_lens=text_lens)
+    if prefill is not None:
+        prefill()
+    else:
+        eng.prefill(np.concatenate(prompts), lens, pad, tsamp, psamp, seed, frames, text=text_packed,
+                    text_lens=text_lens)
     tl0 = eng.talker_logits()
     worst = 0.0
     tally = Tally()
