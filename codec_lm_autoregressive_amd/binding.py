@@ -94,6 +94,7 @@ def lib():
             "qt_debug_talker_logits": ([vp, vp], i32),
             "qt_debug_select": ([vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, C.POINTER(Sampling), u64, i32,
                                  i32, vp, vp, vp], i32),
+            "qt_admit": ([vp, i32, vp, i32, vp, i32, u64, i32, i32], i32),
             "qt_frontend_bytes": ([C.POINTER(Config), C.POINTER(FrontendConfig), C.POINTER(C.c_size_t)], i32),
             "qt_attach_frontend": ([vp, C.POINTER(FrontendConfig), C.POINTER(FrontendWeights), vp, C.c_size_t], i32),
             "qt_embed_ids": ([vp, i32, vp, vp, vp, vp], i32),
@@ -270,6 +271,21 @@ class Engine:
                                  C.byref(ts), C.byref(ps), C.c_uint64(seed), int(max_frames),
                                  _np_ptr(codes), _np_ptr(n), _np_ptr(fin)), self.ctx)
         return codes, n, fin
+
+    def admit(self, slot, prompt, text=None, seed=0, noise_row=None, max_frames=1):
+        """Start a new request in a finished slot (continuous batching)."""
+        torch = self.torch
+        dev = lambda a: a if isinstance(a, torch.Tensor) else torch.from_numpy(  # noqa: E731
+            np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        with torch.cuda.stream(self.stream):
+            p = dev(prompt)
+            tx = dev(text) if text is not None and len(text) else None
+        torch.cuda.synchronize()
+        self._keep_slot = getattr(self, "_keep_slot", {})
+        self._keep_slot[slot] = (p, tx)   # trailing text is read during the request's frames
+        _check(lib().qt_admit(self.ctx, int(slot), _ptr(p), int(p.shape[0]), _ptr(tx),
+                              0 if tx is None else int(tx.shape[0]), C.c_uint64(seed),
+                              int(slot if noise_row is None else noise_row), int(max_frames)), self.ctx)
 
     # ---- token-id frontend
     def attach_frontend(self, fw, max_rows):

@@ -151,7 +151,7 @@ struct Layout {
   size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
   size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den, part, xsplit, ksplit;
   long part_floats, xsplit_floats;
-  size_t rowstate, seen, runs, idx, frame_out, req;
+  size_t rowstate, row64, seen, runs, idx, frame_out, req;
   size_t total;
   int tmax, seen_words, max_runs;
   bool ovf;
@@ -237,8 +237,11 @@ Layout plan_layout(const qt_config& c) {
   L.ksplit = p.take(p.sz.mul({B, (size_t)t.nkv, (size_t)kMaxKvSplit, (size_t)(t.nq / std::max(t.nkv, 1)),
                               (size_t)t.d + 2, 4}));
   (void)Hm;
-  // row state: code0_next, finished, pos, text_off, text_len [B]; frame_k; own/forced [B,16]
-  L.rowstate = p.take(p.sz.mul({B, 5 + 2 * kGroups, 4}) + 64);
+  // row state: code0_next, finished, pos, noise_row, text_len, max_frames,
+  // frame_k [B]; own / forced [B, 16]; then the 64-bit seed and trailing-text
+  // pointer of each row
+  L.rowstate = p.take(p.sz.mul({B, 7 + 2 * kGroups, 4}));
+  L.row64 = p.take(p.sz.mul({B, 2, 8}));
   L.seen_words = (int)((V + 31) / 32);
   L.seen = p.take(p.sz.mul({B, (size_t)L.seen_words, 4}));
   // decode runs, one per prompt token, and the prefill's tiles: at most
@@ -333,7 +336,9 @@ struct qt_ctx {
   void *kc_t, *vc_t, *kc_p, *vc_p;
   float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den, *part, *xsplit, *ksplit;
   long part_floats, xsplit_floats;
-  int *code0_next, *finished, *pos, *text_off, *text_len, *frame_k, *own, *forced;
+  int *code0_next, *finished, *pos, *noise_row, *text_len, *max_frames_row, *frame_k, *own, *forced;
+  uint64_t* row_seed;
+  const float** text_ptr;
   uint32_t* seen;
   Run* runs;
   int* idx;
@@ -529,7 +534,7 @@ SelectArgs select_base(qt_ctx* ctx, const qt_sampling& sm, bool talker) {
   a.penalty = sm.repetition_penalty; a.min_new = sm.min_new_tokens;
   a.eos = ctx->cfg.eos_id; a.sup_b = ctx->cfg.suppress_begin; a.sup_e = ctx->cfg.suppress_end;
   a.do_sample = sm.do_sample; a.temperature = sm.temperature; a.top_k = sm.top_k; a.top_p = sm.top_p;
-  a.seed = ctx->seed;
+  a.seed = ctx->seed; a.row_seed = ctx->row_seed; a.noise_row = ctx->noise_row;
   a.status = ctx->frame_out;
   return a;
 }
@@ -587,7 +592,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     sa.tab = ctx->pemb; sa.tab_dtype = wd; sa.tab_dim = T.H; sa.tab_off = (long)st * C;
     sa.next_in = st < 14 ? (proj ? ctx->xin_w : ctx->x_p) : nullptr; sa.next_ld = T.H;
     sa.fb = ctx->x_t; sa.fb_ld = T.H;
-    sa.add_text = st == 14; sa.text_off = ctx->text_off; sa.text_len = ctx->text_len;
+    sa.add_text = st == 14; sa.text_ptr = ctx->text_ptr; sa.text_len = ctx->text_len;
     sa.frame_k = ctx->frame_k;
     HIPCK(launch_select(sa, s));
   }
@@ -605,10 +610,10 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   sa.stream = 0; sa.ctr = ctx->frame_k; sa.ctr_add = 1;
   sa.used = ctx->code0_next; sa.used_ld = 1; sa.used_col = 0;
   sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = 0;
-  sa.epi = forced ? 0 : 2; sa.finished = ctx->finished; sa.state = state;
+  sa.epi = forced ? 0 : 2; sa.finished = ctx->finished; sa.state = state; sa.row_max = ctx->max_frames_row;
   sa.frame_k = ctx->frame_k;
   HIPCK(launch_select(sa, s));
-  HIPCK(launch_frame_advance(ctx->frame_k, ctx->pos, B, s));
+  HIPCK(launch_frame_advance(ctx->frame_k, ctx->pos, ctx->finished, B, s));
   return QT_OK;
 }
 
@@ -765,9 +770,11 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
   ctx->ksplit = at<float>(ctx, L.ksplit);
   int* rs = at<int>(ctx, L.rowstate);
   const int MB = cfg->max_batch;
-  ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->text_off = rs + 3 * MB;
-  ctx->text_len = rs + 4 * MB; ctx->own = rs + 5 * MB; ctx->forced = rs + 5 * MB + kGroups * MB;
-  ctx->frame_k = rs + 5 * MB + 2 * kGroups * MB;
+  ctx->code0_next = rs; ctx->finished = rs + MB; ctx->pos = rs + 2 * MB; ctx->noise_row = rs + 3 * MB;
+  ctx->text_len = rs + 4 * MB; ctx->max_frames_row = rs + 5 * MB; ctx->frame_k = rs + 6 * MB;
+  ctx->own = rs + 7 * MB; ctx->forced = rs + 7 * MB + kGroups * MB;
+  ctx->row_seed = at<uint64_t>(ctx, L.row64);
+  ctx->text_ptr = (const float**)(ctx->row_seed + MB);
   ctx->seen = at<uint32_t>(ctx, L.seen);
   ctx->runs = at<Run>(ctx, L.runs);
   ctx->idx = at<int>(ctx, L.idx);
@@ -825,6 +832,127 @@ void qt_destroy(qt_ctx* ctx) {
   delete ctx;
 }
 
+// Device state of rows row0 .. row0 + n - 1 for a new request each: code 0
+// pending, not finished, talker position at the prompt's end, frame counter
+// 0, the noise key and row, the frame cap, the trailing text; seen bits,
+// own codes and the frame output slots cleared.
+static qt_status init_rows(qt_ctx* ctx, int row0, int n, const int32_t* lens, const float* const* text,
+                           const int32_t* text_lens, uint64_t seed, const int32_t* noise_rows, int32_t max_frames) {
+  const hipStream_t s = ctx->stream;
+  std::vector<int> pos(n), nrow(n), tlen(n), mf(n, max_frames);
+  std::vector<uint64_t> sd(n, seed);
+  std::vector<const float*> tp(n, nullptr);
+  for (int i = 0; i < n; ++i) {
+    pos[i] = lens[i];
+    nrow[i] = noise_rows ? noise_rows[i] : row0 + i;
+    tlen[i] = text_lens ? text_lens[i] : 0;
+    tp[i] = tlen[i] > 0 ? text[i] : nullptr;
+  }
+  const size_t ib = (size_t)n * sizeof(int);
+  HIPCK(launch_fill_i32(ctx->code0_next + row0, 0, n, s));
+  HIPCK(launch_fill_i32(ctx->finished + row0, 0, n, s));
+  HIPCK(launch_fill_i32(ctx->frame_k + row0, 0, n, s));
+  HIPCK(hipMemcpyAsync(ctx->pos + row0, pos.data(), ib, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->noise_row + row0, nrow.data(), ib, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->text_len + row0, tlen.data(), ib, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->max_frames_row + row0, mf.data(), ib, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->row_seed + row0, sd.data(), (size_t)n * 8, hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync((void*)(ctx->text_ptr + row0), tp.data(), (size_t)n * 8, hipMemcpyHostToDevice, s));
+  HIPCK(launch_fill_i32((int*)ctx->seen + (size_t)row0 * ctx->lay.seen_words, 0, (long)n * ctx->lay.seen_words, s));
+  HIPCK(launch_fill_i32(ctx->own + (size_t)row0 * kGroups, 0, (long)n * kGroups, s));
+  HIPCK(launch_fill_i32(ctx->frame_out + 1 + row0, 0, n, s));
+  HIPCK(launch_fill_i32(ctx->frame_out + 1 + ctx->cfg.max_batch + (size_t)row0 * kGroups, 0, (long)n * kGroups, s));
+  // the pageable host vectors above must outlive their copies
+  HIPCK(hipStreamSynchronize(s));
+  return QT_OK;
+}
+
+// The prompt prefill of rows row0 .. row0 + n - 1 (their rows' state
+// initialised): the talker over each prompt at positions 0..P_r-1 in chunks
+// of up to kPrefillChunk tokens (K/V rows into the rows' caches), the codec
+// head at each row's last position and talker selection 0 (ncnn CustomVoice
+// port section 3.1). Synchronises; states of the rows in ctx->hout[1 + row].
+static qt_status prefill_rows(qt_ctx* ctx, int row0, int n, const float* prompt, const int32_t* lens) {
+  const qt_config& c = ctx->cfg;
+  const Dec& T = ctx->t;
+  const hipStream_t s = ctx->stream;
+  const int MB = c.max_batch;
+  long total = 0;
+  std::vector<long> start(n + 1, 0);
+  for (int r = 0; r < n; ++r) start[r + 1] = start[r] + lens[r];
+  total = start[n];
+  // run tables after the 3 MB fixed decode entries
+  std::vector<Run> runs;
+  struct Chunk { long t0; int n; int run0, nrun; int last0, nlast, lastrow0; int tile0, ntile; };
+  const bool tiled = attn_prefill_tiles(T.d, T.nq, T.nkv, c.kv_dtype);
+  std::vector<Chunk> chunks;
+  std::vector<int> lastidx;
+  const int base = 3 * MB;
+  for (long t0 = 0; t0 < total; t0 += kPrefillChunk) {
+    Chunk ch{t0, (int)std::min<long>(kPrefillChunk, total - t0), base + (int)runs.size(), 0, (int)lastidx.size(), 0,
+             -1, 0, 0};
+    for (int r = 0; r < n; ++r) {
+      const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
+      if (a >= b) continue;
+      for (long tk = a; tk < b; ++tk)  // one run per prompt token
+        runs.push_back(Run{row0 + r, (int)(tk - t0), 1, (int)(tk - start[r])});
+      ch.nrun += (int)(b - a);
+      if (start[r + 1] - 1 >= t0 && start[r + 1] - 1 < t0 + ch.n) {
+        if (ch.lastrow0 < 0) ch.lastrow0 = row0 + r;
+        lastidx.push_back((int)(start[r + 1] - 1 - t0));
+        ch.nlast++;
+      }
+    }
+    if (tiled) {   // the attend pass: runs of up to kAttnTileTokens tokens of one row
+      ch.tile0 = base + (int)runs.size();
+      const size_t first = runs.size();
+      for (int r = 0; r < n; ++r) {
+        const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
+        for (long tk = a; tk < b; tk += kAttnTileTokens)
+          runs.push_back(Run{row0 + r, (int)(tk - t0), (int)std::min<long>(kAttnTileTokens, b - tk),
+                             (int)(tk - start[r])});
+      }
+      ch.ntile = (int)(runs.size() - first);
+      // longest first (a tile's keys end at its last position), so the
+      // heaviest blocks do not form the tail of the grid
+      std::stable_sort(runs.begin() + first, runs.end(),
+                       [](const Run& x, const Run& y) { return x.pos0 + x.ntok > y.pos0 + y.ntok; });
+    }
+    chunks.push_back(ch);
+  }
+  if (base + (long)runs.size() > ctx->lay.max_runs) { set_err(ctx->err, "internal: run table overflow"); return QT_E_CAPACITY; }
+  HIPCK(hipMemcpyAsync(ctx->runs + base, runs.data(), runs.size() * sizeof(Run), hipMemcpyHostToDevice, s));
+  HIPCK(hipMemcpyAsync(ctx->idx, lastidx.data(), lastidx.size() * sizeof(int), hipMemcpyHostToDevice, s));
+  for (const Chunk& ch : chunks) {
+    HIPCK(hipMemcpyAsync(ctx->x_t, prompt + ch.t0 * T.H, (size_t)ch.n * T.H * 4, hipMemcpyDeviceToDevice, s));
+    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s, true, false,
+                             false, ctx->runs + ch.tile0, ch.ntile);
+    if (r != QT_OK) return r;
+    if (ch.nlast > 0)
+      HIPCK(launch_copy_rows(ctx->x_t, T.H, ctx->idx + ch.last0, ch.nlast, ctx->xlast + (size_t)ch.lastrow0 * T.H, T.H,
+                             T.H, s));
+  }
+  LinearArgs ta{};
+  ta.row_den = ctx->row_den; ta.xs = ctx->xsplit; ta.xs_floats = ctx->xsplit_floats;
+  ta.part = ctx->part; ta.part_floats = ctx->part_floats;
+  ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H;
+  ta.X = ctx->xlast + (size_t)row0 * T.H; ta.ldx = T.H; ta.M = n; ta.gain = ctx->talker_norm; ta.eps = T.eps;
+  ta.Y = ctx->logits_t + (size_t)row0 * c.talker_vocab; ta.ldy = c.talker_vocab;
+  ta.epi = EPI_STORE; ta.norm_out = ctx->h + (size_t)row0 * T.H; ta.ld_norm = T.H;
+  HIPCK(launch_linear(ta, s));
+  SelectArgs sa = select_base(ctx, ctx->ts, true);
+  sa.B = n; sa.row0 = row0;
+  sa.logits = ctx->logits_t; sa.ld = c.talker_vocab; sa.stream = 0; sa.ctr = nullptr; sa.ctr_add = 0;
+  sa.used = ctx->code0_next; sa.used_ld = 1; sa.used_col = 0;
+  sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = 0;
+  sa.epi = 2; sa.finished = ctx->finished; sa.state = ctx->frame_out + 1;
+  sa.frame_k = nullptr;
+  HIPCK(launch_select(sa, s));
+  HIPCK(hipMemcpyAsync(ctx->hout, ctx->frame_out, (1 + MB) * sizeof(int), hipMemcpyDeviceToHost, s));
+  HIPCK(hipStreamSynchronize(s));
+  return read_status(ctx);
+}
+
 qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t* prompt_lens, const float* text,
                      const int32_t* text_lens, const float* tts_pad, const qt_sampling* talker,
                      const qt_sampling* predictor, uint64_t seed, int32_t max_frames) {
@@ -856,103 +984,59 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
   ctx->eager_frames = 0;
   const Dec& T = ctx->t;
   hipStream_t s = ctx->stream;
-
-  // host-side run tables
   const int MB = c.max_batch;
+  // fixed run tables of the frame: one token per row
   std::vector<Run> runs((size_t)3 * MB, Run{0, 0, 0, 0});
-  for (int r = 0; r < B; ++r) {
+  for (int r = 0; r < MB; ++r) {
     runs[r] = Run{r, r, 1, 0};                 // talker decode (pos from the device)
     runs[MB + r] = Run{r, 2 * r, 2, 0};        // predictor pass 0: positions 0, 1
     runs[2 * MB + r] = Run{r, r, 1, 0};        // predictor step s: position s + 1
   }
-  std::vector<long> start(B + 1, 0);
-  for (int r = 0; r < B; ++r) start[r + 1] = start[r] + prompt_lens[r];
-  struct Chunk { long t0; int n; int run0, nrun; int last0, nlast, lastrow0; int tile0, ntile; };
-  const bool tiled = attn_prefill_tiles(T.d, T.nq, T.nkv, c.kv_dtype);
-  std::vector<Chunk> chunks;
-  std::vector<int> lastidx;
-  for (long t0 = 0; t0 < total; t0 += kPrefillChunk) {
-    Chunk ch{t0, (int)std::min<long>(kPrefillChunk, total - t0), (int)runs.size(), 0, (int)lastidx.size(), 0, -1, 0, 0};
-    for (int r = 0; r < B; ++r) {
-      const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
-      if (a >= b) continue;
-      for (long tk = a; tk < b; ++tk)  // one run per prompt token
-        runs.push_back(Run{r, (int)(tk - t0), 1, (int)(tk - start[r])});
-      ch.nrun += (int)(b - a);
-      if (start[r + 1] - 1 >= t0 && start[r + 1] - 1 < t0 + ch.n) {
-        if (ch.lastrow0 < 0) ch.lastrow0 = r;
-        lastidx.push_back((int)(start[r + 1] - 1 - t0));
-        ch.nlast++;
-      }
-    }
-    if (tiled) {   // the attend pass: runs of up to kAttnTileTokens tokens of one row
-      ch.tile0 = (int)runs.size();
-      for (int r = 0; r < B; ++r) {
-        const long a = std::max(start[r], t0), b = std::min(start[r + 1], t0 + ch.n);
-        for (long tk = a; tk < b; tk += kAttnTileTokens)
-          runs.push_back(Run{r, (int)(tk - t0), (int)std::min<long>(kAttnTileTokens, b - tk), (int)(tk - start[r])});
-      }
-      ch.ntile = (int)runs.size() - ch.tile0;
-      // longest first (a tile's keys end at its last position), so the
-      // heaviest blocks do not form the tail of the grid
-      std::stable_sort(runs.begin() + ch.tile0, runs.end(),
-                       [](const Run& x, const Run& y) { return x.pos0 + x.ntok > y.pos0 + y.ntok; });
-    }
-    chunks.push_back(ch);
-  }
-  if ((int)runs.size() > ctx->lay.max_runs) { set_err(ctx->err, "internal: run table overflow"); return QT_E_CAPACITY; }
-  std::vector<int> rowinit((size_t)5 * MB, 0);
-  long to = 0;
-  for (int r = 0; r < B; ++r) {
-    rowinit[2 * MB + r] = prompt_lens[r];                 // pos
-    rowinit[3 * MB + r] = (int)to;                        // text_off
-    rowinit[4 * MB + r] = text_lens ? text_lens[r] : 0;   // text_len
-    to += text_lens ? text_lens[r] : 0;
-  }
+  HIPCK(hipMemcpyAsync(ctx->runs, runs.data(), runs.size() * sizeof(Run), hipMemcpyHostToDevice, s));
   ReqParams rq{};
   const qt_sampling* sm[2] = {talker, predictor};
   for (int i = 0; i < 2; ++i)
     rq.samp[i] = SampParams{sm[i]->do_sample, sm[i]->temperature, sm[i]->top_k, sm[i]->top_p,
                             sm[i]->repetition_penalty, sm[i]->min_new_tokens};
-  rq.seed = seed; rq.max_frames = max_frames; rq.has_text = text_total > 0; rq.text = text; rq.pad = tts_pad;
+  rq.pad = tts_pad;
   HIPCK(hipMemcpyAsync(ctx->req, &rq, sizeof rq, hipMemcpyHostToDevice, s));
-  HIPCK(hipMemcpyAsync(ctx->runs, runs.data(), runs.size() * sizeof(Run), hipMemcpyHostToDevice, s));
-  HIPCK(hipMemcpyAsync(ctx->idx, lastidx.data(), lastidx.size() * sizeof(int), hipMemcpyHostToDevice, s));
-  HIPCK(hipMemcpyAsync(ctx->code0_next, rowinit.data(), rowinit.size() * sizeof(int), hipMemcpyHostToDevice, s));
-  HIPCK(launch_fill_i32(ctx->frame_k, 0, 1, s));
-  HIPCK(launch_fill_i32((int*)ctx->seen, 0, (long)MB * ctx->lay.seen_words, s));
   HIPCK(launch_fill_i32(ctx->frame_out, 0, 1 + MB + (long)MB * kGroups, s));
-  HIPCK(launch_fill_i32(ctx->own, 0, (long)MB * kGroups, s));
-
-  for (const Chunk& ch : chunks) {
-    HIPCK(hipMemcpyAsync(ctx->x_t, prompt + ch.t0 * T.H, (size_t)ch.n * T.H * 4, hipMemcpyDeviceToDevice, s));
-    qt_status r = run_layers(ctx, true, ctx->x_t, ch.n, ctx->runs + ch.run0, ch.nrun, nullptr, 0, s, true, false,
-                             false, ctx->runs + ch.tile0, ch.ntile);
-    if (r != QT_OK) return r;
-    if (ch.nlast > 0)
-      HIPCK(launch_copy_rows(ctx->x_t, T.H, ctx->idx + ch.last0, ch.nlast, ctx->xlast + (size_t)ch.lastrow0 * T.H, T.H,
-                             T.H, s));
+  std::vector<const float*> tp(B, nullptr);
+  long to = 0;
+  for (int r = 0; r < B; ++r) {
+    tp[r] = text ? text + to * T.H : nullptr;
+    to += text_lens ? text_lens[r] : 0;
   }
-  LinearArgs ta{};
-  ta.row_den = ctx->row_den; ta.xs = ctx->xsplit; ta.xs_floats = ctx->xsplit_floats;
-  ta.part = ctx->part; ta.part_floats = ctx->part_floats;
-  ta.wdtype = c.weight_dtype; ta.W = ctx->thead; ta.N = c.talker_vocab; ta.K = T.H; ta.X = ctx->xlast; ta.ldx = T.H;
-  ta.M = B; ta.gain = ctx->talker_norm; ta.eps = T.eps; ta.Y = ctx->logits_t; ta.ldy = c.talker_vocab;
-  ta.epi = EPI_STORE; ta.norm_out = ctx->h; ta.ld_norm = T.H;
-  HIPCK(launch_linear(ta, s));
-  SelectArgs sa = select_base(ctx, ctx->ts, true);
-  sa.logits = ctx->logits_t; sa.ld = c.talker_vocab; sa.stream = 0; sa.ctr = nullptr; sa.ctr_add = 0;
-  sa.used = ctx->code0_next; sa.used_ld = 1; sa.used_col = 0;
-  sa.own = ctx->own; sa.own_ld = kGroups; sa.own_col = 0;
-  sa.epi = 2; sa.finished = ctx->finished; sa.state = ctx->frame_out + 1;
-  sa.frame_k = nullptr;
-  HIPCK(launch_select(sa, s));
-  HIPCK(hipMemcpyAsync(ctx->hout, ctx->frame_out, (1 + MB) * sizeof(int), hipMemcpyDeviceToHost, s));
-  HIPCK(hipStreamSynchronize(s));
-  qt_status r = read_status(ctx);
+  QTCK(init_rows(ctx, 0, B, prompt_lens, tp.data(), text_lens, seed, nullptr, max_frames));
+  qt_status r = prefill_rows(ctx, 0, B, prompt, prompt_lens);
   if (r != QT_OK) return r;
   for (int i = 0; i < B; ++i) ctx->done[i] = ctx->hout[1 + i] == 1;
   ctx->prefilled = true;
+  return QT_OK;
+}
+
+qt_status qt_admit(qt_ctx* ctx, int32_t slot, const float* prompt, int32_t prompt_len, const float* text,
+                   int32_t text_len, uint64_t seed, int32_t noise_row, int32_t max_frames) {
+  if (!ctx) { set_err(g_err, "ctx is NULL"); return QT_E_INVALID; }
+  const qt_config& c = ctx->cfg;
+  if (!ctx->prefilled || ctx->failed) { set_err(ctx->err, "qt_admit needs a successful qt_prefill first"); return QT_E_STATE; }
+  if (slot < 0 || slot >= ctx->B) { set_err(ctx->err, "slot %d outside 0..B-1=%d", slot, ctx->B - 1); return QT_E_RANGE; }
+  if (!ctx->done[slot]) { set_err(ctx->err, "slot %d still holds an active request", slot); return QT_E_STATE; }
+  if (!prompt) { set_err(ctx->err, "prompt must not be NULL"); return QT_E_INVALID; }
+  if (prompt_len < 1) { set_err(ctx->err, "prompt_len must be >= 1"); return QT_E_RANGE; }
+  if (max_frames < 1) { set_err(ctx->err, "max_frames must be >= 1"); return QT_E_INVALID; }
+  if ((long)prompt_len + max_frames > c.max_positions) {
+    set_err(ctx->err, "prompt %d + max_frames %d exceeds max_positions %d", prompt_len, max_frames, c.max_positions);
+    return QT_E_CAPACITY;
+  }
+  if (text_len < 0) { set_err(ctx->err, "text_len must be >= 0"); return QT_E_RANGE; }
+  if (text_len > 0 && !text) { set_err(ctx->err, "text is NULL but text_len is positive"); return QT_E_INVALID; }
+  if (noise_row < 0) { set_err(ctx->err, "noise_row must be >= 0"); return QT_E_RANGE; }
+  const float* tp[1] = {text};
+  QTCK(init_rows(ctx, slot, 1, &prompt_len, tp, &text_len, seed, &noise_row, max_frames));
+  qt_status r = prefill_rows(ctx, slot, 1, prompt, &prompt_len);
+  if (r != QT_OK) return r;
+  ctx->done[slot] = ctx->hout[1 + slot] == 1;
   return QT_OK;
 }
 
@@ -998,7 +1082,7 @@ qt_status qt_step_frame(qt_ctx* ctx, int32_t* codes, uint8_t* state) {
   if (!ctx->prefilled || ctx->failed) { set_err(ctx->err, "qt_step_frame needs a successful qt_prefill first"); return QT_E_STATE; }
   bool any = false;
   for (int r = 0; r < ctx->B; ++r) any |= !ctx->done[r];
-  if (!any || ctx->frames_done >= ctx->max_frames) { set_err(ctx->err, "every row has finished"); return QT_E_STATE; }
+  if (!any) { set_err(ctx->err, "every row has finished"); return QT_E_STATE; }
   qt_status r = frame_common(ctx, nullptr);
   if (r != QT_OK) return r;
   const int MB = ctx->cfg.max_batch;

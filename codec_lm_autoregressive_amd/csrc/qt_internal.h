@@ -88,9 +88,7 @@ hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStr
 struct SampParams { int do_sample; float temperature; int top_k; float top_p; float penalty; int min_new; };
 struct ReqParams {
   SampParams samp[2];                  // [0] talker, [1] code predictor
-  uint64_t seed;
-  int max_frames; int has_text;
-  const float* text; const float* pad; // trailing text rows / tts_pad (device)
+  const float* pad;                    // tts_pad row (device)
 };
 
 // Logits processing + selection for one batch of rows (one block per row).
@@ -99,13 +97,18 @@ struct ReqParams {
 struct SelectArgs {
   const ReqParams* req; int which;
   const float* logits; long ld; int V; int B;
+  int row0;                            // the launch covers rows row0 .. row0 + B - 1
   // talker processors
   int processors;
   uint32_t* seen; int seen_words;
   float penalty; int min_new; int eos; int sup_b; int sup_e;
   // warpers
   int do_sample; float temperature; int top_k; float top_p;
+  // noise: key (seed, 0), counter (id, stream, selection index, noise row);
+  // per-row seeds / noise rows when row_seed / noise_row are given, else
+  // `seed` and the row itself; selection index = ctr[row] + ctr_add
   uint64_t seed; int stream; const int* ctr; int ctr_add;
+  const uint64_t* row_seed; const int* noise_row;
   // debug inputs (nullable): explicit Exp(1) noise / probabilities [B, V]
   const float* noise_in; const float* probs_in;
   // outputs
@@ -119,10 +122,12 @@ struct SelectArgs {
   const void* tab; int tab_dtype; int tab_dim; long tab_off;
   float* next_in; long next_ld;
   float* fb; long fb_ld;
-  int add_text; const float* text; const int* text_off; const int* text_len; const float* pad;
-  const int* frame_k;
-  // epilogue 2: talker lookahead, finish state
-  int* finished; int* state; int max_frames;
+  // trailing text: row r adds text_ptr[r][frame_k[r]] while frame_k[r] < text_len[r], then the pad row
+  int add_text; const float* const* text_ptr; const int* text_len; const float* pad;
+  const int* frame_k;                  // per-row frame counters
+  // epilogue 2: talker lookahead, finish state (length once frame_k[r] + 1
+  // reaches row_max[r], or max_frames without per-row caps)
+  int* finished; int* state; int max_frames; const int* row_max;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
@@ -143,8 +148,9 @@ struct FrameStartArgs {
 };
 hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s);
 
-// Frame end: frame counter and per-row talker positions advance by one.
-hipError_t launch_frame_advance(int* frame_k, int* pos, int B, hipStream_t s);
+// Frame end: per-row frame counters and talker positions advance by one
+// (rows that have finished stay where they ended).
+hipError_t launch_frame_advance(int* frame_k, int* pos, const int* finished, int B, hipStream_t s);
 
 // Row gather / scatter copies dst[i] = src[idx[i]] (fp32 rows of width n).
 hipError_t launch_copy_rows(const float* src, long ld_src, const int* idx, int count,

@@ -69,7 +69,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // trips whatever V is.
 template <int MPT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
-  const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
+  const int r = blockIdx.x + a.row0, tid = threadIdx.x, V = a.V;
   extern __shared__ float sm[];
   int P2 = 1;                            // V rounded up to a power of two
   while (P2 < V) P2 <<= 1;
@@ -105,24 +105,25 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (epi_fast)
 #pragma unroll
     for (int q = 0; q < EPT; ++q) fbv[q] = a.fb[(long)r * a.fb_ld + min(tid + q * NT, a.tab_dim - 1)];
-  const int kf0 = a.frame_k ? *a.frame_k : 0, kf = kf0;
+  const int kf0 = a.frame_k ? a.frame_k[r] : 0, kf = kf0;
   const int forced_v = a.forced ? a.forced[(long)r * a.forced_ld + a.forced_col] : 0;
   const int fin = a.epi == 2 ? a.finished[r] : 0;
 
   // settings: from the request block when given
-  int do_sample = a.do_sample, top_k = a.top_k, min_new = a.min_new, max_frames = a.max_frames;
+  int do_sample = a.do_sample, top_k = a.top_k, min_new = a.min_new;
   float temperature = a.temperature, top_p = a.top_p, penalty = a.penalty;
-  uint64_t seed = a.seed;
-  const float* text = a.text;
+  const uint64_t seed = a.row_seed ? a.row_seed[r] : a.seed;
+  const int nrow = a.noise_row ? a.noise_row[r] : r;
+  const int max_frames = a.row_max ? a.row_max[r] : a.max_frames;
+  const float* text = a.text_ptr ? a.text_ptr[r] : nullptr;
   const float* pad = a.pad;
-  int has_text = a.text_len != nullptr;
+  const int has_text = text != nullptr && a.text_len != nullptr;
   if (a.req) {
     const SampParams sp = a.req->samp[a.which];
     do_sample = sp.do_sample; top_k = sp.top_k; min_new = sp.min_new; temperature = sp.temperature;
-    top_p = sp.top_p; penalty = sp.penalty; seed = a.req->seed; max_frames = a.req->max_frames;
-    text = a.req->text; pad = a.req->pad; has_text = a.req->has_text;
+    top_p = sp.top_p; penalty = sp.penalty; pad = a.req->pad;
   }
-  const int jsel = (a.ctr ? *a.ctr : 0) + a.ctr_add;
+  const int jsel = (a.ctr ? a.ctr[r] : 0) + a.ctr_add;
   float padv[EPT] = {};
   if (epi_fast && a.add_text)
 #pragma unroll
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         float sc = -INFINITY;
         int bi = 0x7fffffff;
         if (lane < nsv && rank < keep) {
-          const float e = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, r, a.stream, jsel, id);
+          const float e = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, nrow, a.stream, jsel, id);
           sc = pp / e;
           bi = id;
         }
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int j = tid; j < keep; j += NT) {
       const int id = sido[j];
       const float e = a.noise_in ? a.noise_in[(long)r * V + id]
-                                 : exp_noise(seed, r, a.stream, jsel, id);
+                                 : exp_noise(seed, nrow, a.stream, jsel, id);
       better(bv, bi, spo[j] / e, id);
     }
     choice = block_argmax(bv, bi, redf, redi);
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int q = 0; q < EPT; ++q) {
       const int k = min(tid + q * NT, a.tab_dim - 1);
       tv[q] = ld_any(a.tab, a.tab_dtype, base + k);
-      xt[q] = txt ? text[((long)a.text_off[r] + kf) * a.tab_dim + k] : padv[q];
+      xt[q] = txt ? text[(long)kf * a.tab_dim + k] : padv[q];
     }
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const float val = ld_any(a.tab, a.tab_dtype, base + k);
       if (a.next_in) a.next_in[(long)r * a.next_ld + k] = val;
       float f = a.fb[(long)r * a.fb_ld + k] + val;
-      if (a.add_text) f = f + (txt ? text[((long)a.text_off[r] + kf) * a.tab_dim + k] : pad[k]);
+      if (a.add_text) f = f + (txt ? text[(long)kf * a.tab_dim + k] : pad[k]);
       a.fb[(long)r * a.fb_ld + k] = f;
     }
   }
@@ -555,14 +556,16 @@ hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void frame_advance_kernel(int* frame_k, int* pos, int B) {
-  const int t = threadIdx.x;
-  for (int r = t; r < B; r += blockDim.x) pos[r] += 1;
-  if (t == 0) *frame_k += 1;
+__global__ void frame_advance_kernel(int* frame_k, int* pos, const int* finished, int B) {
+  for (int r = threadIdx.x; r < B; r += blockDim.x) {
+    if (finished[r]) continue;   // a finished row stays where it ended (fed EOS until refilled)
+    pos[r] += 1;
+    frame_k[r] += 1;
+  }
 }
 
-hipError_t launch_frame_advance(int* frame_k, int* pos, int B, hipStream_t s) {
-  hipLaunchKernelGGL(frame_advance_kernel, dim3(1), dim3(NT), 0, s, frame_k, pos, B);
+hipError_t launch_frame_advance(int* frame_k, int* pos, const int* finished, int B, hipStream_t s) {
+  hipLaunchKernelGGL(frame_advance_kernel, dim3(1), dim3(NT), 0, s, frame_k, pos, finished, B);
   return hipGetLastError();
 }
 

@@ -173,8 +173,33 @@ qt_status qt_prefill(qt_ctx* ctx, int32_t B, const float* prompt, const int32_t*
  *          lookahead is EOS: reason stop); 2 finished with this frame
  *          (max_frames reached: reason length, lookahead discarded); 3 row
  *          had already finished (codes undefined; the row is fed EOS).
- * Returns QT_E_STATE when every row has finished or no prefill was done. */
+ * Each row ends on its own frame cap (max_frames of qt_prefill or
+ * qt_admit). Returns QT_E_STATE when every row has finished or no prefill
+ * was done. */
 qt_status qt_step_frame(qt_ctx* ctx, int32_t* codes, uint8_t* state);
+
+/* Continuous batching (Mizuoto engine page, "Matching upstream", sampler
+ * bullet: finished rows of a batch are fed EOS; the SGLang-Omni case runs
+ * the talker as a serving stage with requests joining a running batch): start
+ * a new request in a slot whose request has finished, between two frames,
+ * while the other rows keep generating. The slot's talker prefill over its
+ * prompt (its K/V rows), selection 0 and its row state (position, frame
+ * counter, seen ids, noise key) are reset; the other rows are untouched and
+ * the next qt_step_frame carries the slot with them.
+ *   slot        0..B-1 of the running batch; its request must have finished
+ *               (state 1 or 2 reported earlier), else QT_E_STATE
+ *   prompt      device float [prompt_len, H]; prompt_len >= 1
+ *   text        device float [text_len, H] trailing text rows, or NULL
+ *               (text_len 0); kept by the caller until the request ends
+ *   seed, noise_row  the sampling noise of this request: key (seed, 0),
+ *               counter row noise_row (a request reproduces row noise_row of
+ *               a batch started with this seed)
+ *   max_frames  this request's frame cap; prompt_len + max_frames <= max_positions
+ * The sampling settings and tts_pad are those of qt_prefill. Synchronises.
+ * The slot's first frame comes with the next qt_step_frame; a slot whose
+ * selection 0 is already EOS is reported finished (state 3) there. */
+qt_status qt_admit(qt_ctx* ctx, int32_t slot, const float* prompt, int32_t prompt_len, const float* text,
+                   int32_t text_len, uint64_t seed, int32_t noise_row, int32_t max_frames);
 
 /* qt_prefill + qt_step_frame until every row finished.
  *   codes    host int32 [B, max_frames, 16]; frames past n_frames[r] untouched

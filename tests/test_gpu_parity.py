@@ -184,6 +184,35 @@ def test_tiny_trailing_text_parity():
     eng.close()
 
 
+def free_run_agreement(codes, n, ref, dm, tsamp, psamp, seed, noise_row, tol):
+    """Frames of a GPU free run (codes [>= n, 16], n frames) equal to the
+    oracle's free run `ref` of the same request, frame by frame. At the first
+    differing code the oracle's decision must lie inside the margin (logits
+    moved by at most tol / 2 could change it); the runs may part there. A
+    run compared to its end must also end alike. Returns the equal frames."""
+    equal = 0
+    for k in range(min(int(n), ref["n_frames"])):
+        if np.array_equal(codes[k], ref["codes"][k]):
+            equal += 1
+            continue
+        s = int(np.nonzero(codes[k] != ref["codes"][k])[0][0])
+        if s == 0:
+            seen = [int(c) for c in ref["codes"][:k, 0]]
+            lo = _processed(dm, ref["talker_logits"][k], tsamp, True, seen, k)
+            noise = lambda i: philox.exp_noise(seed, noise_row, 0, k, i)  # noqa: E731
+            assert sampling.flip_possible(lo, tsamp, noise, int(ref["codes"][k, 0]), int(codes[k, 0]), tol / 2), \
+                (noise_row, k, s)
+        else:
+            lo = np.asarray(ref["pred_logits"][k][s - 1], np.float32)
+            noise = lambda i: philox.exp_noise(seed, noise_row, s, k, i)  # noqa: E731
+            assert sampling.flip_possible(lo, psamp, noise, int(ref["codes"][k, s]), int(codes[k, s]), tol / 2), \
+                (noise_row, k, s)
+        log(f"request row {noise_row}: free runs part at frame {k} code {s} (inside the margin)")
+        return equal
+    assert int(n) == ref["n_frames"], (noise_row, int(n), ref["n_frames"])
+    return equal
+
+
 def test_tiny_fp32_sampled_free_run_codes():
     """Free-run sampled codes (talker and predictor sampling, penalty,
     min-new, suppress) of the GPU loop against the oracle's own free run:
@@ -201,30 +230,8 @@ def test_tiny_fp32_sampled_free_run_codes():
     codes, n, fin = eng.generate(np.concatenate(prompts), lens, pad, synth.SAMPLING, synth.PRED_SAMPLING, seed, F)
     eng.close()
     ref = oracle.generate(w, dm, prompts, pad, synth.SAMPLING, synth.PRED_SAMPLING, seed, F)
-    compared = 0
-    for r in range(2):
-        x = ref[r]
-        for k in range(min(int(n[r]), x["n_frames"])):
-            if np.array_equal(codes[r, k], x["codes"][k]):
-                compared += 1
-                continue
-            s = int(np.nonzero(codes[r, k] != x["codes"][k])[0][0])
-            # the first differing code: its oracle decision must sit inside the margin
-            if s == 0:
-                seen = [int(c) for c in x["codes"][:k, 0]]
-                lo = _processed(dm, x["talker_logits"][k], synth.SAMPLING, True, seen, k)
-                noise = lambda i: philox.exp_noise(seed, r, 0, k, i)  # noqa: E731
-                assert sampling.flip_possible(lo, synth.SAMPLING, noise, int(x["codes"][k, 0]),
-                                              int(codes[r, k, 0]), 1e-3), (r, k, s)
-            else:
-                lo = np.asarray(x["pred_logits"][k][s - 1], np.float32)
-                noise = lambda i: philox.exp_noise(seed, r, s, k, i)  # noqa: E731
-                assert sampling.flip_possible(lo, synth.PRED_SAMPLING, noise, int(x["codes"][k, s]),
-                                              int(codes[r, k, s]), 1e-3), (r, k, s)
-            log(f"row {r}: free runs part at frame {k} code {s} (inside the margin)")
-            break
-        else:
-            assert int(n[r]) == x["n_frames"]
+    compared = sum(free_run_agreement(codes[r], n[r], ref[r], dm, synth.SAMPLING, synth.PRED_SAMPLING, seed, r, 2e-3)
+                   for r in range(2))
     log(f"free-run sampled frames equal to the oracle's: {compared}")
     assert compared >= 6
 
