@@ -318,3 +318,82 @@ def make_prompt_ids(lens, text_vocab: int, seed: int):
         tids.append(t)
         cids.append(c)
     return np.concatenate(tids), np.concatenate(cids)
+
+
+# ---------------------------------------------------------------- 12 Hz codec decoder
+def codec_dims(name: str) -> dict:
+    """Shapes of the codec decoder (ncnn port section 1, Codec Decoder bullet:
+    16 codebooks of 2048 x 256, an 8-layer window-72 transformer with hidden
+    512, head_dim 64 and rope theta 1e4, two upsampling stages, a vocoder
+    upsampling by 8, 5, 4, 3; Mizuoto page: 300-frame chunks with 25 frames
+    of left context). "tiny" is a reduced shape for fast tests."""
+    if name == "tiny":
+        return dict(n_q=16, codebook=2048, codebook_dim=16, hidden=64, layers=2, heads=2, head_dim=32, ffn=128,
+                    window=8, rope_theta=1.0e4, up_ffn=128, voc_channels=[96, 48, 24], strides=[2, 3],
+                    dilations=[1, 3, 9], chunk=12, context=3)
+    return dict(n_q=16, codebook=2048, codebook_dim=256, hidden=512, layers=8, heads=8, head_dim=64, ffn=2048,
+                window=72, rope_theta=1.0e4, up_ffn=2048, voc_channels=[1536, 768, 384, 192, 96],
+                strides=[8, 5, 4, 3], dilations=[1, 3, 9], chunk=300, context=25)
+
+
+def make_codec_weights(cd: dict, seed: int = 0, dtype: str = "bf16") -> dict:
+    """Random codec-decoder weights: codebook rows ~ N(0, 1); linear and
+    convolution weights ~ N(0, 1 / fan_in) (the residual branches' 1x1
+    convolutions and the output convolution smaller, so the residual stream
+    stays O(1) and the final tanh works mostly in its linear range);
+    LayerNorm gains 1 + N(0, 0.02), biases N(0, 0.02); LayerScale gains
+    N(0.1, 0.02); SnakeBeta log-parameters N(0, 0.1). Convolution weights
+    tap-major [k][out][in]."""
+    D, Hd, F = cd["hidden"], cd["heads"] * cd["head_dim"], cd["ffn"]
+    cdim = cd["codebook_dim"]
+    w = dict(codebooks=_Normal("codec.codebooks", (cd["n_q"], cd["codebook"], cdim), 1.0),
+             proj_sem=_Normal("codec.proj_sem", (D, cdim), cdim ** -0.5),
+             proj_ac=_Normal("codec.proj_ac", (D, cdim), (15 * cdim) ** -0.5),
+             layers=[], up_blocks=[], voc_blocks=[])
+    for i in range(cd["layers"]):
+        p = f"codec.tf.{i}."
+        w["layers"].append(dict(
+            ln1_g=_Normal(p + "ln1_g", (D,), 0.02, 1.0), ln1_b=_Normal(p + "ln1_b", (D,), 0.02),
+            wqkv=_Normal(p + "wqkv", (3 * Hd, D), D ** -0.5), wo=_Normal(p + "wo", (D, Hd), Hd ** -0.5),
+            ls1=_Normal(p + "ls1", (D,), 0.02, 0.1),
+            ln2_g=_Normal(p + "ln2_g", (D,), 0.02, 1.0), ln2_b=_Normal(p + "ln2_b", (D,), 0.02),
+            fc1=_Normal(p + "fc1", (F, D), D ** -0.5), fc2=_Normal(p + "fc2", (D, F), F ** -0.5),
+            ls2=_Normal(p + "ls2", (D,), 0.02, 0.1)))
+    w["ln_f_g"] = _Normal("codec.ln_f_g", (D,), 0.02, 1.0)
+    w["ln_f_b"] = _Normal("codec.ln_f_b", (D,), 0.02)
+    for i in range(2):
+        p = f"codec.up.{i}."
+        w["up_blocks"].append(dict(
+            up=_Normal(p + "up", (2, D, D), D ** -0.5), dw=_Normal(p + "dw", (7, D), 7 ** -0.5),
+            ln_g=_Normal(p + "ln_g", (D,), 0.02, 1.0), ln_b=_Normal(p + "ln_b", (D,), 0.02),
+            fc1=_Normal(p + "fc1", (cd["up_ffn"], D), D ** -0.5),
+            fc2=_Normal(p + "fc2", (D, cd["up_ffn"]), cd["up_ffn"] ** -0.5),
+            gamma=_Normal(p + "gamma", (D,), 0.02, 0.1)))
+    ch = cd["voc_channels"]
+    w["voc_in"] = _Normal("codec.voc_in", (7, ch[0], D), (7 * D) ** -0.5)
+    for b, s in enumerate(cd["strides"]):
+        p = f"codec.voc.{b}."
+        ci, co = ch[b], ch[b + 1]
+        units = []
+        for u in range(len(cd["dilations"])):
+            q = p + f"u{u}."
+            units.append(dict(a1=_Normal(q + "a1", (co,), 0.1), b1=_Normal(q + "b1", (co,), 0.1),
+                              conv7=_Normal(q + "conv7", (7, co, co), (7 * co) ** -0.5),
+                              a2=_Normal(q + "a2", (co,), 0.1), b2=_Normal(q + "b2", (co,), 0.1),
+                              conv1=_Normal(q + "conv1", (1, co, co), 0.3 * co ** -0.5)))
+        w["voc_blocks"].append(dict(snake_a=_Normal(p + "snake_a", (ci,), 0.1),
+                                    snake_b=_Normal(p + "snake_b", (ci,), 0.1),
+                                    up=_Normal(p + "up", (2 * s, co, ci), (2 * ci) ** -0.5), units=units))
+    w["voc_out_a"] = _Normal("codec.voc_out_a", (ch[-1],), 0.1)
+    w["voc_out_b"] = _Normal("codec.voc_out_b", (ch[-1],), 0.1)
+    w["voc_out"] = _Normal("codec.voc_out", (7, 1, ch[-1]), 0.15 * (7 * ch[-1]) ** -0.5)
+    leaves = []
+    map_arrays(w, lambda x: leaves.append(x) or x)
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        drawn = dict(zip(map(id, leaves), ex.map(lambda x: x.draw(seed, dtype == "bf16"), leaves)))
+    return map_arrays(w, lambda x: drawn[id(x)])
+
+
+def make_codes(T: int, seed: int, codebook: int = CODEBOOK) -> np.ndarray:
+    """Random frames of 16 codes, [T, 16] int32, uniform over the codebook."""
+    return np.random.default_rng(seed).integers(0, codebook, (T, N_GROUPS)).astype(np.int32)
