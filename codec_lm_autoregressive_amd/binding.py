@@ -69,6 +69,43 @@ class FrontendWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("text_embed", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
 
 
+CODEC_MAX_BLOCKS, CODEC_UNITS = 6, 3
+
+
+class CodecConfig(C.Structure):
+    _fields_ = [("n_q", C.c_int32), ("codebook", C.c_int32), ("codebook_dim", C.c_int32), ("hidden", C.c_int32),
+                ("layers", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("window", C.c_int32), ("rope_theta", C.c_float), ("up_ffn", C.c_int32), ("n_blocks", C.c_int32),
+                ("channels", C.c_int32 * (CODEC_MAX_BLOCKS + 1)), ("strides", C.c_int32 * CODEC_MAX_BLOCKS),
+                ("dilations", C.c_int32 * CODEC_UNITS), ("chunk", C.c_int32), ("context", C.c_int32),
+                ("weight_dtype", C.c_int32)]
+
+
+class CodecLayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("ln1_g", "ln1_b", "wqkv", "wo", "ls1", "ln2_g", "ln2_b", "fc1", "fc2",
+                                          "ls2")]
+
+
+class CodecUpWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("up", "dw", "ln_g", "ln_b", "fc1", "fc2", "gamma")]
+
+
+class CodecUnitWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("a1", "b1", "conv7", "a2", "b2", "conv1")]
+
+
+class CodecBlockWeights(C.Structure):
+    _fields_ = [("snake_a", C.c_void_p), ("snake_b", C.c_void_p), ("up", C.c_void_p),
+                ("units", CodecUnitWeights * CODEC_UNITS)]
+
+
+class CodecWeights(C.Structure):
+    _fields_ = [("codebooks", C.c_void_p), ("proj_sem", C.c_void_p), ("proj_ac", C.c_void_p),
+                ("layers", C.POINTER(CodecLayerWeights)), ("ln_f_g", C.c_void_p), ("ln_f_b", C.c_void_p),
+                ("up", CodecUpWeights * 2), ("voc_in", C.c_void_p), ("blocks", CodecBlockWeights * CODEC_MAX_BLOCKS),
+                ("voc_out_a", C.c_void_p), ("voc_out_b", C.c_void_p), ("voc_out", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -100,6 +137,14 @@ def lib():
             "qt_embed_ids": ([vp, i32, vp, vp, vp, vp], i32),
             "qt_prefill_ids": ([vp, i32, vp, vp, vp, vp, vp, i32, C.POINTER(Sampling), C.POINTER(Sampling), u64, i32],
                                i32),
+            "qt_codec_workspace_bytes": ([C.POINTER(CodecConfig), C.POINTER(C.c_size_t)], i32),
+            "qt_codec_create": ([C.POINTER(CodecConfig), C.POINTER(CodecWeights), vp, C.c_size_t, vp, C.POINTER(vp)],
+                                i32),
+            "qt_codec_destroy": ([vp], None),
+            "qt_codec_last_error": ([vp], C.c_char_p),
+            "qt_codec_decode": ([vp, vp, i32, vp], i32),
+            "qt_codec_decode_chunked": ([vp, vp, i32, vp], i32),
+            "qt_codec_stream": ([vp, vp, i32, C.c_int64, vp], i32),
             "qt_debug_exp_noise": ([vp, i32, vp, C.c_int64, u64, vp], i32),
             "qt_debug_linear": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp, vp, C.c_int64, i32, i32,
                                  C.c_int64], i32),
@@ -449,3 +494,86 @@ def debug_select(logits, samp, seen=None, noise=None, probs=None, processors=Fal
                                  C.c_uint64(seed), stream_id, sel_index, _ptr(out), _ptr(proc), _ptr(st)))
     torch.cuda.synchronize()
     return out, proc, st
+
+
+def codec_config(cd, dtype="bf16"):
+    ch = list(cd["voc_channels"]) + [0] * (CODEC_MAX_BLOCKS + 1 - len(cd["voc_channels"]))
+    st = list(cd["strides"]) + [0] * (CODEC_MAX_BLOCKS - len(cd["strides"]))
+    return CodecConfig(cd["n_q"], cd["codebook"], cd["codebook_dim"], cd["hidden"], cd["layers"], cd["heads"],
+                       cd["head_dim"], cd["ffn"], cd["window"], cd["rope_theta"], cd["up_ffn"], len(cd["strides"]),
+                       (C.c_int32 * (CODEC_MAX_BLOCKS + 1))(*ch), (C.c_int32 * CODEC_MAX_BLOCKS)(*st),
+                       (C.c_int32 * CODEC_UNITS)(*cd["dilations"]), cd["chunk"], cd["context"],
+                       QT_DTYPE_BF16 if dtype == "bf16" else QT_DTYPE_F32)
+
+
+class Codec:
+    """One qt_codec on the current device, on a private torch stream."""
+
+    def __init__(self, cd, w, dtype="bf16"):
+        import torch
+        self.torch = torch
+        self.cd = cd
+        self.hop = 4 * int(np.prod(cd["strides"]))
+        self.cfg = codec_config(cd, dtype)
+        self.stream = torch.cuda.Stream()
+        keep = []
+
+        def up(a):
+            x = to_device_weight(a, dtype)
+            keep.append(x)
+            return _ptr(x)
+        with torch.cuda.stream(self.stream):
+            layers = (CodecLayerWeights * max(1, len(w["layers"])))()
+            for i, lw in enumerate(w["layers"]):
+                layers[i] = CodecLayerWeights(*[up(lw[n]) for n in ("ln1_g", "ln1_b", "wqkv", "wo", "ls1", "ln2_g",
+                                                                     "ln2_b", "fc1", "fc2", "ls2")])
+            ups = (CodecUpWeights * 2)(*[CodecUpWeights(*[up(u[n]) for n in ("up", "dw", "ln_g", "ln_b", "fc1", "fc2",
+                                                                             "gamma")]) for u in w["up_blocks"]])
+            blocks = (CodecBlockWeights * CODEC_MAX_BLOCKS)()
+            for b, bw in enumerate(w["voc_blocks"]):
+                units = (CodecUnitWeights * CODEC_UNITS)(*[CodecUnitWeights(*[up(u[n]) for n in (
+                    "a1", "b1", "conv7", "a2", "b2", "conv1")]) for u in bw["units"]])
+                blocks[b] = CodecBlockWeights(up(bw["snake_a"]), up(bw["snake_b"]), up(bw["up"]), units)
+            cw = CodecWeights(up(w["codebooks"]), up(w["proj_sem"]), up(w["proj_ac"]), layers, up(w["ln_f_g"]),
+                              up(w["ln_f_b"]), ups, up(w["voc_in"]), blocks, up(w["voc_out_a"]), up(w["voc_out_b"]),
+                              up(w["voc_out"]))
+        torch.cuda.synchronize()
+        n = C.c_size_t(0)
+        _check(lib().qt_codec_workspace_bytes(C.byref(self.cfg), C.byref(n)))
+        self.ws_bytes = n.value
+        ctx = C.c_void_p()
+        st = lib().qt_codec_create(C.byref(self.cfg), C.byref(cw), None, 0, C.c_void_p(self.stream.cuda_stream),
+                                   C.byref(ctx))
+        if st != QT_OK:
+            raise QtError(st, lib().qt_codec_last_error(None).decode())
+        self.ctx = ctx
+        keep.clear()
+        torch.cuda.synchronize()
+
+    def _run(self, fn, codes, *extra, n_out):
+        torch = self.torch
+        codes = np.ascontiguousarray(codes, dtype=np.int32)
+        out = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+        st = fn(self.ctx, _np_ptr(codes), int(codes.shape[0]), *extra, _ptr(out))
+        if st != QT_OK:
+            raise QtError(st, lib().qt_codec_last_error(self.ctx).decode())
+        torch.cuda.synchronize()
+        return out
+
+    def decode(self, codes):
+        """One causal pass over codes [T, 16] -> device float [T * hop]."""
+        return self._run(lib().qt_codec_decode, codes, n_out=len(codes) * self.hop)
+
+    def decode_chunked(self, codes):
+        return self._run(lib().qt_codec_decode_chunked, codes, n_out=len(codes) * self.hop)
+
+    def stream_step(self, codes, sent):
+        """New samples sent .. T * hop - 1 for all frames so far (DecodeStream rule)."""
+        return self._run(lib().qt_codec_stream, codes, C.c_int64(int(sent)), n_out=len(codes) * self.hop - int(sent))
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            lib().qt_codec_destroy(self.ctx)
+            self.ctx = None
+
+    __del__ = close

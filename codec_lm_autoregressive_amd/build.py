@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SRC = [os.path.join(CSRC, n) for n in ("qt_linear.hip", "qt_attn.hip", "qt_select.hip", "qt_frontend.hip", "qt_api.hip")]
+SRC = [os.path.join(CSRC, n) for n in ("qt_linear.hip", "qt_attn.hip", "qt_select.hip", "qt_frontend.hip", "qt_codec.hip", "qt_api.hip")]
 LIB = os.path.join(PKG, "libqt.so")
 HIPCC = "/opt/rocm/bin/hipcc"
 

@@ -279,6 +279,113 @@ qt_status qt_prefill_ids(qt_ctx* ctx, int32_t B, const int32_t* text_ids, const 
                          int32_t tts_pad_id, const qt_sampling* talker, const qt_sampling* predictor, uint64_t seed,
                          int32_t max_frames);
 
+/* ---- the 12 Hz codec decoder: codes -> 24 kHz audio (ncnn port discussion
+ * 6798, section 1 "structure", Codec Decoder bullet; Mizuoto engine page,
+ * "Matching upstream" codec bullet and "Speed" frame-streaming bullet) ----
+ * Per frame of 16 codes: SplitRVQ dequantisation (code 0 from the semantic
+ * codebook, codes 1..15 from the acoustic ones; each group's sum projected
+ * codebook_dim -> hidden and the two added), a transformer whose attention
+ * sees `window` frames (pre-norm LayerNorm blocks, rope at positions from 0,
+ * GELU MLP, LayerScale), a final LayerNorm, two upsampling stages (causal
+ * transposed convolution kernel 2 stride 2, then a ConvNeXt block: causal
+ * depthwise convolution kernel 7, LayerNorm, GELU MLP, LayerScale, residual),
+ * and a DAC-style vocoder (causal convolution kernel 7 to channels[0]; per
+ * block b: SnakeBeta, causal transposed convolution kernel 2 strides[b] to
+ * channels[b+1], residual units with the given dilations: SnakeBeta, causal
+ * dilated convolution kernel 7, SnakeBeta, convolution kernel 1, add; then
+ * SnakeBeta, causal convolution kernel 7 to one channel, tanh). The decoder
+ * is causal: samples of frames 0..t depend on codes of frames 0..t only.
+ * hop = 4 * prod(strides) samples per frame (1920 at 24 kHz for 8, 5, 4, 3).
+ * Weight element type weight_dtype; matrices [out, in]; convolution weights
+ * tap-major [k][out][in]; depthwise weights [7][channels]. */
+#define QT_CODEC_MAX_BLOCKS 6
+#define QT_CODEC_UNITS 3
+typedef struct qt_codec_config {
+  int32_t n_q;            /* codebooks per frame: 16                                   */
+  int32_t codebook;       /* entries per codebook: 2048                                */
+  int32_t codebook_dim;   /* 256, multiple of 8                                        */
+  int32_t hidden;         /* transformer / upsampling width: 512, multiple of 64       */
+  int32_t layers;         /* transformer layers: 8                                     */
+  int32_t heads;          /* 8                                                         */
+  int32_t head_dim;       /* 64 (even, <= 128)                                         */
+  int32_t ffn;            /* transformer MLP width: 2048, multiple of 8                */
+  int32_t window;         /* attention window in frames: 72                            */
+  float rope_theta;       /* 1e4                                                       */
+  int32_t up_ffn;         /* ConvNeXt MLP width: 2048, multiple of 8                   */
+  int32_t n_blocks;       /* vocoder blocks: 4 (<= QT_CODEC_MAX_BLOCKS)                */
+  int32_t channels[QT_CODEC_MAX_BLOCKS + 1]; /* 1536, 768, 384, 192, 96; multiples of 8 */
+  int32_t strides[QT_CODEC_MAX_BLOCKS];      /* 8, 5, 4, 3                              */
+  int32_t dilations[QT_CODEC_UNITS];         /* 1, 3, 9                                 */
+  int32_t chunk;          /* frames per chunk of the chunk grid: 300                   */
+  int32_t context;        /* left-context frames per chunk: 25                         */
+  int32_t weight_dtype;   /* QT_DTYPE_F32 | QT_DTYPE_BF16                              */
+} qt_codec_config;
+
+typedef struct qt_codec_layer_weights {
+  const void *ln1_g, *ln1_b, *wqkv /* [3 heads head_dim, hidden] */, *wo /* [hidden, heads head_dim] */, *ls1;
+  const void *ln2_g, *ln2_b, *fc1 /* [ffn, hidden] */, *fc2 /* [hidden, ffn] */, *ls2;
+} qt_codec_layer_weights;
+
+typedef struct qt_codec_up_weights {
+  const void *up /* [2][hidden][hidden] */, *dw /* [7][hidden] */, *ln_g, *ln_b;
+  const void *fc1 /* [up_ffn, hidden] */, *fc2 /* [hidden, up_ffn] */, *gamma;
+} qt_codec_up_weights;
+
+typedef struct qt_codec_unit_weights {
+  const void *a1, *b1, *conv7 /* [7][c][c] */, *a2, *b2, *conv1 /* [1][c][c] */;  /* SnakeBeta logs a, b */
+} qt_codec_unit_weights;
+
+typedef struct qt_codec_block_weights {
+  const void *snake_a, *snake_b;  /* [channels[b]]                                          */
+  const void *up;                 /* [2 strides[b]][channels[b+1]][channels[b]]             */
+  qt_codec_unit_weights units[QT_CODEC_UNITS];
+} qt_codec_block_weights;
+
+typedef struct qt_codec_weights {
+  const void* codebooks;                 /* [n_q][codebook][codebook_dim]               */
+  const void *proj_sem, *proj_ac;        /* [hidden, codebook_dim] each                 */
+  const qt_codec_layer_weights* layers;  /* host array [layers]                         */
+  const void *ln_f_g, *ln_f_b;           /* [hidden]                                    */
+  qt_codec_up_weights up[2];
+  const void* voc_in;                    /* [7][channels[0]][hidden]                    */
+  qt_codec_block_weights blocks[QT_CODEC_MAX_BLOCKS];
+  const void *voc_out_a, *voc_out_b;     /* [channels[n_blocks]]                        */
+  const void* voc_out;                   /* [7][1][channels[n_blocks]]                  */
+} qt_codec_weights;
+
+typedef struct qt_codec qt_codec;
+
+/* Device bytes qt_codec_create needs for decodes of up to chunk + context
+ * frames (packed weights, activations, GEMM scratch). Host arithmetic only. */
+qt_status qt_codec_workspace_bytes(const qt_codec_config* cfg, size_t* bytes);
+
+/* Create a decoder on the current device; weights are copied / repacked into
+ * `workspace` (or a library allocation when NULL). hip_stream as qt_create. */
+qt_status qt_codec_create(const qt_codec_config* cfg, const qt_codec_weights* w, void* workspace, size_t ws_bytes,
+                          void* hip_stream, qt_codec** out);
+void qt_codec_destroy(qt_codec* c);
+const char* qt_codec_last_error(const qt_codec* c);
+
+/* One causal pass over frames 0..T-1 (positions from 0):
+ *   codes  host int32 [T, n_q], each in 0..codebook-1 (checked first)
+ *   audio  device float [T * hop]
+ * 1 <= T <= chunk + context. Enqueued on the decoder's stream. */
+qt_status qt_codec_decode(qt_codec* c, const int32_t* codes, int32_t T, float* audio);
+
+/* The chunk grid over any number of frames: chunk k covers frames
+ * [k chunk, (k+1) chunk) and is decoded from frame max(0, k chunk - context),
+ * the context's samples dropped. audio device float [T * hop]. */
+qt_status qt_codec_decode_chunked(qt_codec* c, const int32_t* codes, int32_t T, float* audio);
+
+/* Streaming step (the DecodeStream rule): given all T frames so far and the
+ * number of samples already emitted (`sent`, a multiple of hop, < T * hop),
+ * decode from the chunk grid's regular start of the chunk that holds sample
+ * `sent` up to frame T (one decode per chunk touched) and write the new
+ * samples sent .. T * hop - 1 to out (device float, at least T * hop - sent).
+ * The caller chooses when to call (the pages: after 4 frames, then every
+ * 12). The samples equal those of qt_codec_decode_chunked up to rounding. */
+qt_status qt_codec_stream(qt_codec* c, const int32_t* codes, int32_t T, int64_t sent, float* out);
+
 /* ---- test and measurement entry points (same kernels as the frame) ---- */
 
 /* Teacher-forced frame: like qt_step_frame, but code 0 of this frame is

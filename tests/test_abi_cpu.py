@@ -146,6 +146,16 @@ def test_debug_entry_points_validate_before_launch():
     ids = (C.c_int32 * 1)(0)
     assert L.qt_embed_ids(None, 1, ids, ids, None, fake) == binding.QT_E_INVALID
     assert L.qt_prefill_ids(None, 1, ids, ids, ids, None, None, 0, None, None, 0, 1) == binding.QT_E_INVALID
+    ccfg = binding.codec_config(synth.codec_dims("12hz"))
+    assert L.qt_codec_workspace_bytes(C.byref(ccfg), C.byref(n)) == binding.QT_OK
+    assert n.value > 16 * 2048 * 256 * 2
+    ccfg.dilations[2] = 11                                            # 6 x 11 rows > the zeroed padding
+    assert L.qt_codec_workspace_bytes(C.byref(ccfg), C.byref(n)) == binding.QT_E_INVALID
+    ccfg = binding.codec_config(synth.codec_dims("12hz"))
+    ccfg.channels[2] = 100                                            # not a multiple of 8
+    assert L.qt_codec_workspace_bytes(C.byref(ccfg), C.byref(n)) == binding.QT_E_INVALID
+    assert L.qt_codec_decode(None, fake, 1, fake) == binding.QT_E_INVALID
+    assert L.qt_codec_stream(None, fake, 1, 0, fake) == binding.QT_E_INVALID
     assert L.qt_debug_exp_noise(None, 2, fake, 4, 0, fake) == binding.QT_E_INVALID    # mode
     assert L.qt_debug_exp_noise(None, 0, None, 4, 0, fake) == binding.QT_E_INVALID    # NULL input
     assert L.qt_debug_exp_noise(None, 1, fake, -1, 0, fake) == binding.QT_E_INVALID   # n < 0
