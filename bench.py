@@ -135,6 +135,8 @@ def parse():
                                          "qwen17b_bf16_b8",
                     help="further workloads reported under 'batches' (one timed request each; '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the codec decoder, token-id frontend and continuous-batching measurements")
     ap.add_argument("--cpu-frames", type=int, default=100,
                     help="frames of the oracle's timed sample (row 0 of the workload)")
     ap.add_argument("--kernel-reps", type=int, default=200)
@@ -333,6 +335,15 @@ def main():
         del x
         torch.cuda.empty_cache()
 
+    extra = {}
+    if not args.no_next:
+        extra["codec"] = codec_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+        extra["frontend"] = frontend_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+        extra["serving"] = serving_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(synth, w, dm, wl, main_lens, main_prompt, main_pad,
@@ -369,6 +380,7 @@ def main():
                      "trace_frac": round(kern_bytes / (kc["trace_avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                      if kc else None},
         "batches": batches,
+        **extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -468,6 +480,145 @@ def summarize(d, per_frame):
                 tot = sum(v for _, n, v in disp[first:] if not n.startswith("__amd_rocclr"))
                 print(f"per frame: {frames} frames, {tot / frames:.1f} KiB counted"
                       + (f" = {tot / frames * scale * 1024 / 1e9:.4f} GB scaled" if scale else ""))
+
+
+def codec_flops_per_frame(cd):
+    """Multiply-adds x 2 of the codec decoder's linear maps and convolutions
+    for one frame of codes (attention and elementwise work left out)."""
+    D, Hd, dim = cd["hidden"], cd["heads"] * cd["head_dim"], cd["codebook_dim"]
+    f = 2 * D * dim                                                    # the two SplitRVQ projections
+    f += cd["layers"] * (3 * Hd * D + D * Hd + 2 * D * cd["ffn"])     # transformer
+    f += 2 * D * D + 2 * (2 * D * cd["up_ffn"])                       # upsampling stage 1 (2 rows per frame)
+    f += 4 * D * D // 2 * 2 + 4 * (2 * D * cd["up_ffn"])              # stage 2 (4 rows per frame)
+    ch, rows = cd["voc_channels"], 4
+    f += rows * 7 * ch[0] * D                                          # vocoder input convolution
+    for b, s in enumerate(cd["strides"]):
+        f += rows * s * 2 * ch[b] * ch[b + 1]                          # transposed convolution, 2 taps per output
+        rows *= s
+        f += len(cd["dilations"]) * rows * (7 * ch[b + 1] ** 2 + ch[b + 1] ** 2)
+    f += rows * 7 * ch[-1]
+    return 2.0 * f
+
+
+def codec_timing(torch, binding, synth, frames=300):
+    """The codec decoder at its full shape on one 300-frame chunk (24 s of
+    audio) with qt_codec_decode_chunked, and the first streamed piece (4
+    frames) as the decode part of the time to first audio."""
+    cd = synth.codec_dims("12hz")
+    w = synth.make_codec_weights(cd, seed=3, dtype="bf16")
+    cod = binding.Codec(cd, w, "bf16")
+    codes = synth.make_codes(frames, seed=5)
+    cod.decode_chunked(codes)
+    cod.stream_step(codes[:4], 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 3
+    for _ in range(reps):
+        cod.decode_chunked(codes)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000 / reps
+    t1 = time.perf_counter()
+    cod.stream_step(codes[:4], 0)
+    first_ms = (time.perf_counter() - t1) * 1000
+    cod.close()
+    fl = codec_flops_per_frame(cd) * frames
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": "codec 12 Hz decoder, 300-frame chunk, bf16 weights", "frames": frames,
+            "ms": round(ms, 3), "frames_per_s": round(frames * 1000 / ms, 1),
+            "audio_s_per_s": round(frames / FRAMES_PER_AUDIO_SECOND * 1000 / ms, 1),
+            "first_piece_ms": round(first_ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "flops": fl}}
+
+
+def frontend_timing(torch, binding, synth):
+    """qt_embed_ids at the full frontend shape (151936 x 2048 text embedding,
+    ResizeMLP 2048 -> 2048 -> 1024) over the batch-64 workload's prompt
+    positions (synthetic dual-track ids)."""
+    wl = synth.workload("qwen06b_bf16_b64_sampling")
+    dm = synth.dims(wl["model"])
+    fd = synth.frontend_dims("qwen06b")
+    fw = synth.make_frontend_weights(fd, dm["talker"]["hidden"], seed=5, dtype="bf16")
+    lens = synth.prompt_lengths(wl["B"], *wl["prompt"], seed=2)
+    n = int(np.sum(lens))
+    ti, ci = synth.make_prompt_ids(lens, fd["text_vocab"], seed=3)
+    small = dict(dm, talker=dict(dm["talker"], layers=1), predictor=dict(dm["predictor"], layers=1))
+    eng = binding.Engine(small, synth.make_weights(small, seed=0, dtype="bf16"), "bf16", max_batch=1,
+                         max_positions=16)
+    eng.attach_frontend(fw, max_rows=n)
+    eng.embed_ids(ti, ci)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 3
+    for _ in range(reps):
+        eng.embed_ids(ti, ci)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000 / reps
+    eng.close()
+    fl = 2.0 * n * (fd["text_hidden"] * fd["mlp_hidden"] + fd["mlp_hidden"] * dm["talker"]["hidden"])
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": "token-id frontend over the batch-64 prompts", "rows": n, "ms": round(ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "flops": fl}}
+
+
+def serving_timing(torch, binding, synth, slots=8, n_req=32):
+    """Continuous batching at the 0.6B shape: a queue of requests (prompts
+    32..256, sampling, frame caps 40..200) through 8 slots, a finished slot
+    refilled by qt_admit before the next frame; against the same requests
+    served as static batches of 8 (each batch runs until its longest row
+    ends, finished rows fed EOS). Row-frames per second of each."""
+    wl = synth.workload("qwen06b_bf16_b8_sampling")
+    dm = synth.dims(wl["model"])
+    H = dm["talker"]["hidden"]
+    w = synth.make_weights(dm, seed=0, dtype="bf16")
+    g = np.random.default_rng(13)
+    lens = g.integers(32, 257, n_req).astype(np.int32)
+    caps = g.integers(40, 201, n_req).astype(np.int32)
+    caps[:slots] = caps[0]          # qt_prefill takes one frame cap for the first batch
+    prompts = [torch.from_numpy(synth.make_prompts([int(P)], H, seed=100 + i)).cuda() for i, P in enumerate(lens)]
+    pad = torch.from_numpy(synth.make_tts_pad(H, seed=3)).cuda()
+    eng = binding.Engine(dm, w, "bf16", max_batch=slots, max_positions=512)
+    tsamp, psamp = wl["talker"], wl["predictor"]
+    # static batches: every row of a batch gets the batch's largest cap (one prefill per batch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    static_rows = 0
+    for b0 in range(0, n_req, slots):
+        idx = list(range(b0, min(n_req, b0 + slots)))
+        P = torch.cat([prompts[i] for i in idx])
+        _, n, _ = eng.generate(P, lens[idx], pad, tsamp, psamp, 0, int(caps[idx].max()))
+        static_rows += int(sum(min(int(n[j]), int(caps[i])) for j, i in enumerate(idx)))
+    torch.cuda.synchronize()
+    static_s = time.perf_counter() - t0
+    # continuous batching
+    t0 = time.perf_counter()
+    first = list(range(slots))
+    eng.prefill(torch.cat([prompts[i] for i in first]), lens[first], pad, tsamp, psamp, 0, int(caps[0]))
+    holder = list(first)
+    got = [0] * n_req
+    nxt = slots
+    while any(h is not None for h in holder):
+        _, st = eng.step_frame()
+        for s in range(slots):
+            q = holder[s]
+            if q is None or st[s] == 3:
+                continue
+            got[q] += 1
+            if st[s] in (1, 2):
+                holder[s] = None
+                if nxt < n_req:
+                    eng.admit(s, prompts[nxt], None, 0, nxt, int(caps[nxt]))
+                    holder[s] = nxt
+                    nxt += 1
+    torch.cuda.synchronize()
+    cont_s = time.perf_counter() - t0
+    eng.close()
+    cont_rows = int(sum(got))
+    return {"workload": f"{n_req} requests of the batch-8 shape through {slots} slots (prompts 32..256, caps 40..200)",
+            "continuous_row_frames_per_s": round(cont_rows / cont_s, 1), "continuous_s": round(cont_s, 3),
+            "static_row_frames_per_s": round(static_rows / static_s, 1), "static_s": round(static_s, 3),
+            "row_frames": cont_rows}
 
 
 def kernel_timing(torch, binding, w, dm, wl, B, reps, copies=40):
