@@ -410,8 +410,27 @@ hipError_t gemm(qt_codec* c, const void* W, int N, int K, const float* X, long l
 
 size_t wbytes(const qt_codec* c, size_t n) { return n * (c->cfg.weight_dtype == QT_DTYPE_BF16 ? 2 : 4); }
 
-// causal convolution, kernel k, dilation d: W tap-major [k][Cout][Cin]; X padded
+// A convolution over Cin channels with bf16 weights and Cin % 32 == 0 runs as
+// one GEMM of K = taps x Cin whose activation loader reads the shifted rows
+// itself (implicit im2col); its weights are stored [Cout][tap][Cin], oldest
+// input row first. Otherwise the weights stay tap-major and each tap is its own
+// accumulated GEMM.
+bool conv_packed(const qt_codec* c, int Cin) { return c->cfg.weight_dtype == QT_DTYPE_BF16 && Cin % 32 == 0; }
+
+hipError_t conv_gemm(qt_codec* c, const void* W, int taps, int d, int Cin, int Cout, const float* X, long T, float* Y,
+                     long ldy) {
+  LinearArgs a{};
+  a.W = W; a.wdtype = DT_BF16; a.N = Cout; a.K = taps * Cin;
+  a.X = X; a.ldx = Cin; a.M = (int)T; a.eps = 1e-6f;
+  a.Y = Y; a.ldy = ldy; a.epi = EPI_STORE;
+  a.conv_taps = taps; a.conv_cin = Cin; a.conv_dil = d;
+  return launch_linear(a, c->stream);
+}
+
+// causal convolution, kernel k, dilation d: W [Cout][k][Cin] (packed) or
+// tap-major [k][Cout][Cin]; X padded
 hipError_t conv(qt_codec* c, const void* W, int k, int d, int Cin, int Cout, const float* X, long T, float* Y, int epi0) {
+  if (conv_packed(c, Cin) && epi0 == EPI_STORE) return conv_gemm(c, W, k, d, Cin, Cout, X, T, Y, Cout);
   for (int j = 0; j < k; ++j) {
     const long sh = (long)(k - 1 - j) * d;
     const hipError_t e = gemm(c, (const char*)W + wbytes(c, (size_t)j * Cout * Cin), Cout, Cin, X - sh * Cin, Cin, T,
@@ -421,8 +440,18 @@ hipError_t conv(qt_codec* c, const void* W, int k, int d, int Cin, int Cout, con
   return hipSuccess;
 }
 
-// causal transposed convolution, K taps, stride s: Y[m s + p] = sum_i W_(p + i s) X[m - i]
+// causal transposed convolution, K taps, stride s: Y[m s + p] = sum_i W_(p + i s) X[m - i];
+// packed (K / s > 1): phase p's weights [Cout][K / s][Cin] at p Cout K Cin,
+// tap p + (K / s - 1 - j) s in slot j
 hipError_t convT(qt_codec* c, const void* W, int K, int s, int Cin, int Cout, const float* X, long T, float* Y) {
+  if (conv_packed(c, Cin) && K / s > 1) {
+    for (int p = 0; p < s; ++p) {
+      const hipError_t e = conv_gemm(c, (const char*)W + wbytes(c, (size_t)p * Cout * (K / s) * Cin), K / s, 1, Cin,
+                                     Cout, X, T, Y + (long)p * Cout, (long)s * Cout);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   for (int p = 0; p < s; ++p)
     for (int i = 0; i * s + p < K; ++i) {
       const hipError_t e = gemm(c, (const char*)W + wbytes(c, (size_t)(p + i * s) * Cout * Cin), Cout, Cin,
@@ -664,7 +693,24 @@ qt_status qt_codec_create(const qt_codec_config* cfg, const qt_codec_weights* w,
     cp(x.fc1, L.up[u].fc1, cfg->up_ffn, D, wd); cp(x.fc2, L.up[u].fc2, D, cfg->up_ffn, wd);
     cp(x.gamma, L.up[u].gamma, 1, D, DT_F32);
   }
-  cp(w->voc_in, L.voc_in, 7L * cfg->channels[0], D, wd);
+  // tap-major [k][Cout][Cin] source; packed: slot j of output row n at (n k + j) Cin
+  auto cp_conv = [&](const void* src, size_t dst, int k, int Cout, int Cin) {
+    if (!conv_packed(c, Cin)) { cp(src, dst, (long)k * Cout, Cin, wd); return; }
+    for (int j = 0; j < k && ok; ++j)
+      ok = launch_convert((const char*)src + (size_t)j * Cout * Cin * (wd == QT_DTYPE_BF16 ? 2 : 4), wd, Cin,
+                          c->ws + dst + (size_t)j * Cin * 2, wd, (long)k * Cin, Cout, Cin, s) == hipSuccess;
+  };
+  // transposed, K = kt taps of stride st: phase p's taps p + i st, slot kt / st - 1 - i
+  auto cp_convT = [&](const void* src, size_t dst, int kt, int st, int Cout, int Cin) {
+    if (!conv_packed(c, Cin) || kt / st <= 1) { cp(src, dst, (long)kt * Cout, Cin, wd); return; }
+    const int n = kt / st;
+    for (int p = 0; p < st; ++p)
+      for (int i = 0; i < n && ok; ++i)
+        ok = launch_convert((const char*)src + (size_t)(p + i * st) * Cout * Cin * 2, wd, Cin,
+                            c->ws + dst + ((size_t)p * Cout * n + (n - 1 - i)) * Cin * 2, wd, (long)n * Cin, Cout, Cin,
+                            s) == hipSuccess;
+  };
+  cp_conv(w->voc_in, L.voc_in, 7, cfg->channels[0], D);
   auto prep = [&](const void* a, const void* b, size_t alpha, size_t bden, int C) {
     if (!ok) return;
     if (wd == QT_DTYPE_BF16)
@@ -679,12 +725,12 @@ qt_status qt_codec_create(const qt_codec_config* cfg, const qt_codec_weights* w,
     const qt_codec_block_weights& x = w->blocks[b];
     const int ci = cfg->channels[b], co = cfg->channels[b + 1];
     prep(x.snake_a, x.snake_b, L.blocks[b].alpha, L.blocks[b].bden, ci);
-    cp(x.up, L.blocks[b].up, 2L * cfg->strides[b] * co, ci, wd);
+    cp_convT(x.up, L.blocks[b].up, 2 * cfg->strides[b], cfg->strides[b], co, ci);
     for (int u = 0; u < QT_CODEC_UNITS; ++u) {
       const qt_codec_unit_weights& y = x.units[u];
       const CLayout::Un& un = L.blocks[b].units[u];
       prep(y.a1, y.b1, un.alpha1, un.bden1, co);
-      cp(y.conv7, un.conv7, 7L * co, co, wd);
+      cp_conv(y.conv7, un.conv7, 7, co, co);
       prep(y.a2, y.b2, un.alpha2, un.bden2, co);
       cp(y.conv1, un.conv1, co, co, wd);
     }

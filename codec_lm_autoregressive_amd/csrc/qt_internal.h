@@ -27,6 +27,11 @@ struct LinearArgs {
   int defer;                           // split K: leave the partial sums for the consumer (no reduce)
   void* xs; long xs_floats;            // > 128 rows: scratch for the bf16 hi/lo split of the
                                        // (normalised) activations, M * K floats (nullptr: not used)
+  // Causal convolution as one GEMM (conv_taps > 0; bf16 weights, no gain):
+  // K = conv_taps * conv_cin and activation element (t, j * conv_cin + c) is
+  // X[(t - (conv_taps - 1 - j) * conv_dil) * ldx + c], the rows before X being
+  // readable (zeroed padding); conv_cin a multiple of 32.
+  int conv_taps; int conv_cin; int conv_dil;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 // K ranges the launch of a would split into (partial sums in a.part: range z,

@@ -665,8 +665,14 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
   u32x4 ra_h[AV], ra_l[AV], rw[BV];
   auto load = [&](int k0) __attribute__((always_inline)) {
     if constexpr (FA) {
+      // a convolution's K slice k0 lies in one tap j: its rows are shifted back
+      long a_k = k0;
+      if (p.conv_taps > 0) {
+        const int j = k0 / p.conv_cin;
+        a_k = (long)(k0 - j * p.conv_cin) - (long)(p.conv_taps - 1 - j) * p.conv_dil * p.ldx;
+      }
 #pragma unroll
-      for (int q = 0; q < AF; ++q) raf[q] = *(const u32x4*)(af_src[q] + k0);
+      for (int q = 0; q < AF; ++q) raf[q] = *(const u32x4*)(af_src[q] + a_k);
     } else {
 #pragma unroll
       for (int q = 0; q < AV; ++q) { ra_h[q] = *(const u32x4*)(ah_src[q] + k0); ra_l[q] = *(const u32x4*)(al_src[q] + k0); }
@@ -770,7 +776,7 @@ static bool gemm_split_fits(const LinearArgs& a) {
 // 1051 rows the prologue path measured as fast or faster.
 static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
   uint16_t* xs = (uint16_t*)a.xs;
-  const bool fa = !a.gain && !a.norm_out && a.M >= 2048;
+  const bool fa = a.conv_taps > 0 || (!a.gain && !a.norm_out && a.M >= 2048);
   if (!fa) hipLaunchKernelGGL(split_rows_kernel, dim3(a.M), dim3(NT), 0, s, a, xs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1872,6 +1878,14 @@ static hipError_t launch_mfma_gemv8(const LinearArgs& a, int ksw, int ns, int ti
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
+  // a causal convolution as one GEMM: only the split GEMM's fp32 loader
+  // reads shifted rows
+  if (a.conv_taps > 0) {
+    if (a.wdtype != DT_BF16 || a.gain || a.norm_out || a.epi == EPI_SWIGLU || a.conv_cin % GK ||
+        a.K != a.conv_taps * a.conv_cin || a.ldx % 4 || a.conv_dil < 1)
+      return hipErrorInvalidValue;
+    return launch_gemm_split(a, s);
+  }
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
   {
     hipError_t e = hipSuccess;
