@@ -142,6 +142,52 @@ __global__ __launch_bounds__(NT) void out_conv_kernel(const float* __restrict__ 
   if (t < T && t >= skip && sub == 0) out[t - skip] = tanhf(acc);
 }
 
+// The same output convolution with the SnakeBeta before it fused in: a block
+// takes OC_R samples; rows t0 - 6 .. t0 + OC_R - 1 of x are read once,
+// coalesced, passed through SnakeBeta (alpha, bden per channel) and staged in
+// LDS with row stride C + 4; two threads per sample then contract half the
+// channels of its 7 rows each. C % 8 == 0; x has >= 6 zeroed rows before row
+// 0 (SnakeBeta keeps them zero).
+constexpr int OC_R = 128;
+__global__ __launch_bounds__(NT) void out_conv_snake_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                            const float* __restrict__ alpha,
+                                                            const float* __restrict__ bden, long T, int C, long skip,
+                                                            float* __restrict__ out) {
+  extern __shared__ float xs[];   // [OC_R + 6][C + 4]
+  const long t0 = (long)blockIdx.x * OC_R;
+  const int L = C + 4, n4 = (OC_R + 6) * C / 4;
+  const float* src = x + (t0 - 6) * C;
+  for (int i = threadIdx.x; i < n4; i += NT) {
+    const int e = 4 * i, r = e / C, c = e - r * C;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (t0 - 6 + r < T) {
+      v = *(const f32x4*)(src + e);
+      const f32x4 a = *(const f32x4*)(alpha + c), b = *(const f32x4*)(bden + c);
+      v = (f32x4){snake_beta(v.x, a.x, b.x), snake_beta(v.y, a.y, b.y), snake_beta(v.z, a.z, b.z),
+                  snake_beta(v.w, a.w, b.w)};
+    }
+    *(f32x4*)&xs[r * L + c] = v;
+  }
+  __syncthreads();
+  const int sidx = threadIdx.x >> 1, half = C / 2, c0 = (threadIdx.x & 1) * half;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float* xr = xs + (sidx + j) * L;
+    const float* wr = w + j * C;
+    for (int c = c0; c < c0 + half; c += 4) {
+      const f32x4 xv = *(const f32x4*)(xr + c), wv = *(const f32x4*)(wr + c);
+      acc = fmaf(wv.x, xv.x, acc);
+      acc = fmaf(wv.y, xv.y, acc);
+      acc = fmaf(wv.z, xv.z, acc);
+      acc = fmaf(wv.w, xv.w, acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  const long t = t0 + sidx;
+  if (t < T && t >= skip && !(threadIdx.x & 1)) out[t - skip] = tanhf(acc);
+}
+
 // Windowed causal attention of the codec transformer: block = (16 queries, head);
 // query t sees keys max(0, t - W + 1) .. t. q and k are rotated (rotate-half
 // rope at positions = row index) while staged in LDS; 16 threads per query.
@@ -417,13 +463,30 @@ size_t wbytes(const qt_codec* c, size_t n) { return n * (c->cfg.weight_dtype == 
 // accumulated GEMM.
 bool conv_packed(const qt_codec* c, int Cin) { return c->cfg.weight_dtype == QT_DTYPE_BF16 && Cin % 32 == 0; }
 
+// The vocoder runs fused (SnakeBeta in convolution epilogues, the fused output
+// convolution) when every convolution in it is packed and the output
+// convolution's staged tile fits 64 KiB of LDS.
+bool vocoder_fused(const qt_codec* c) {
+  const qt_codec_config& g = c->cfg;
+  if (!conv_packed(c, g.hidden)) return false;
+  for (int b = 0; b <= g.n_blocks; ++b)
+    if (!conv_packed(c, g.channels[b])) return false;
+  const int cl = g.channels[g.n_blocks];
+  return cl % 8 == 0 && (size_t)(OC_R + 6) * (cl + 4) * 4 <= 65536;
+}
+
+// Optional SnakeBeta epilogue (per output channel alpha / bden): into Y2 when
+// given, else applied to Y itself.
+struct Snk { const float* alpha = nullptr; const float* bden = nullptr; float* Y2 = nullptr; long ldy2 = 0; };
+
 hipError_t conv_gemm(qt_codec* c, const void* W, int taps, int d, int Cin, int Cout, const float* X, long T, float* Y,
-                     long ldy) {
+                     long ldy, int epi = EPI_STORE, Snk sk = {}) {
   LinearArgs a{};
   a.W = W; a.wdtype = DT_BF16; a.N = Cout; a.K = taps * Cin;
   a.X = X; a.ldx = Cin; a.M = (int)T; a.eps = 1e-6f;
-  a.Y = Y; a.ldy = ldy; a.epi = EPI_STORE;
+  a.Y = Y; a.ldy = ldy; a.epi = epi;
   a.conv_taps = taps; a.conv_cin = Cin; a.conv_dil = d;
+  a.snake_alpha = sk.alpha; a.snake_bden = sk.bden; a.Y2 = sk.Y2; a.ldy2 = sk.ldy2;
   return launch_linear(a, c->stream);
 }
 
@@ -551,6 +614,45 @@ qt_status decode_frames(qt_codec* c, long T, long skip, float* out) {
   float* r = c->at<float>(L.r) + c->pad_elems;
   float* sbuf = c->at<float>(L.s) + c->pad_elems;
   long rows = 4 * T;
+  const int cl = g.channels[g.n_blocks];
+  if (vocoder_fused(c)) {
+    // every SnakeBeta rides on the epilogue of the convolution before it, the
+    // last one on the output convolution; each convolution reads the SnakeBeta
+    // output in cur and writes the next one to the other of r, sbuf
+    auto snk = [&](size_t alpha, size_t bden, float* y2, long ld) {
+      Snk k; k.alpha = c->at<float>(alpha); k.bden = c->at<float>(bden); k.Y2 = y2; k.ldy2 = ld; return k;
+    };
+    float* cur = r;
+    float* oth = sbuf;
+    CHK(conv_gemm(c, c->ws + L.voc_in, 7, 1, D, g.channels[0], ba, rows, q, g.channels[0], EPI_STORE,
+                  snk(L.blocks[0].alpha, L.blocks[0].bden, cur, g.channels[0])));
+    for (int b = 0; b < g.n_blocks; ++b) {
+      const int ci = g.channels[b], co = g.channels[b + 1], st = g.strides[b];
+      const CLayout::B& B = L.blocks[b];
+      for (int ph = 0; ph < st; ++ph)
+        CHK(conv_gemm(c, c->ws + B.up + wbytes(c, (size_t)ph * co * 2 * ci), 2, 1, ci, co, cur, rows,
+                      q + (long)ph * co, (long)st * co, EPI_STORE,
+                      snk(B.units[0].alpha1, B.units[0].bden1, oth + (long)ph * co, (long)st * co)));
+      std::swap(cur, oth);
+      rows *= st;
+      for (int u = 0; u < QT_CODEC_UNITS; ++u) {
+        const CLayout::Un& un = B.units[u];
+        CHK(conv_gemm(c, c->ws + un.conv7, 7, g.dilations[u], co, co, cur, rows, oth, co, EPI_STORE,
+                      snk(un.alpha2, un.bden2, nullptr, 0)));
+        std::swap(cur, oth);
+        Snk next;
+        if (u + 1 < QT_CODEC_UNITS) next = snk(B.units[u + 1].alpha1, B.units[u + 1].bden1, oth, co);
+        else if (b + 1 < g.n_blocks) next = snk(L.blocks[b + 1].alpha, L.blocks[b + 1].bden, oth, co);
+        CHK(conv_gemm(c, c->ws + un.conv1, 1, 1, co, co, cur, rows, q, co, EPI_RESIDUAL, next));
+        std::swap(cur, oth);
+      }
+    }
+    hipLaunchKernelGGL(out_conv_snake_kernel, dim3((unsigned)((rows + OC_R - 1) / OC_R)), dim3(NT),
+                       (size_t)(OC_R + 6) * (cl + 4) * 4, s, q, c->at<float>(L.voc_out), c->at<float>(L.out_alpha),
+                       c->at<float>(L.out_bden), rows, cl, skip, out);
+    CHK(hipGetLastError());
+    return QT_OK;
+  }
   CHK(conv(c, c->ws + L.voc_in, 7, 1, D, g.channels[0], ba, rows, q, EPI_STORE));
   for (int b = 0; b < g.n_blocks; ++b) {
     const int ci = g.channels[b], co = g.channels[b + 1], st = g.strides[b];
@@ -566,7 +668,6 @@ qt_status decode_frames(qt_codec* c, long T, long skip, float* out) {
       CHK(gemm(c, c->ws + un.conv1, co, co, r, co, rows, q, co, EPI_RESIDUAL));
     }
   }
-  const int cl = g.channels[g.n_blocks];
   CHK(snake(c, q, r, L.out_alpha, L.out_bden, cl, rows));
   hipLaunchKernelGGL(out_conv_kernel, dim3((unsigned)((rows + NT / 4 - 1) / (NT / 4))), dim3(NT), 0, s, r,
                      c->at<float>(L.voc_out), rows, cl, skip, out);

@@ -51,6 +51,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// SnakeBeta x + sin(alpha x)^2 / bden with the hardware sine: the argument is
+// taken to revolutions, reduced to [-1/2, 1/2] (rounding to nearest), then
+// v_sin_f32; the reciprocal is v_rcp_f32. Within float32 rounding of the
+// argument's product for |alpha x| up to a few hundred, which covers the
+// decoder's activations.
+__device__ __forceinline__ float snake_beta(float x, float alpha, float bden) {
+  float rev = alpha * x * 0.15915494309189535f;
+  rev -= rintf(rev);
+  const float s = __builtin_amdgcn_sinf(rev);
+  return x + s * s * __builtin_amdgcn_rcpf(bden);
+}
+
 template <typename T> __device__ __forceinline__ float ld_elem(const T* p, long i);
 template <> __device__ __forceinline__ float ld_elem<float>(const float* p, long i) { return p[i]; }
 template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, long i) { return bf16_to_f32(p[i]); }

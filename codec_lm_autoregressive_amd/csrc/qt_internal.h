@@ -32,6 +32,10 @@ struct LinearArgs {
   // X[(t - (conv_taps - 1 - j) * conv_dil) * ldx + c], the rows before X being
   // readable (zeroed padding); conv_cin a multiple of 32.
   int conv_taps; int conv_cin; int conv_dil;
+  // SnakeBeta epilogue (convolutions only): with y the output value (after the
+  // residual add), writes y + sin(snake_alpha[col] y)^2 / snake_bden[col]
+  // to Y, or y to Y and that value to Y2 (row stride ldy2) when Y2 is set.
+  const float* snake_alpha; const float* snake_bden; float* Y2; long ldy2;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 // K ranges the launch of a would split into (partial sums in a.part: range z,

@@ -615,7 +615,8 @@ template <int SW> struct SplitLds {
 // FA (no gain: the o and down projections): the activations are read as
 // fp32 rows instead and split into the hi + lo LDS planes on the way in, so
 // no prologue writes the planes.
-template <int TM, int TN, int SW, bool FA = false>
+// SNK: the SnakeBeta epilogue of a convolution.
+template <int TM, int TN, int SW, bool FA = false, bool SNK = false>
 __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
   using LT = SplitLds<SW>;
   constexpr int GLD_ = LT::LD;
@@ -758,7 +759,18 @@ __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint
           if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * u;
         } else if (row < M && col < N) {
           float* y = p.Y + (long)row * p.ldy + col;
-          *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+          const float o = p.epi == EPI_RESIDUAL ? *y + v : v;
+          if constexpr (SNK) {
+            const float so = snake_beta(o, p.snake_alpha[col], p.snake_bden[col]);
+            if (p.Y2) {
+              *y = o;
+              p.Y2[(long)row * p.ldy2 + col] = so;
+            } else {
+              *y = so;
+            }
+          } else {
+            *y = o;
+          }
         }
       }
 }
@@ -783,11 +795,13 @@ static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
   const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (big >= 512) {
     dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-    if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
     else hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2>), grid, dim3(NT), 0, s, a, xs);
   } else {
     dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
-    if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
     else hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2>), grid, dim3(NT), 0, s, a, xs);
   }
   return hipGetLastError();
@@ -1882,10 +1896,11 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   // reads shifted rows
   if (a.conv_taps > 0) {
     if (a.wdtype != DT_BF16 || a.gain || a.norm_out || a.epi == EPI_SWIGLU || a.conv_cin % GK ||
-        a.K != a.conv_taps * a.conv_cin || a.ldx % 4 || a.conv_dil < 1)
+        a.K != a.conv_taps * a.conv_cin || a.ldx % 4 || a.conv_dil < 1 || (a.snake_alpha && !a.snake_bden))
       return hipErrorInvalidValue;
     return launch_gemm_split(a, s);
   }
+  if (a.snake_alpha) return hipErrorInvalidValue;
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
   {
     hipError_t e = hipSuccess;
