@@ -599,16 +599,15 @@ __global__ __launch_bounds__(NT) void split_rows_kernel(LinearArgs p, uint16_t* 
   }
 }
 
-// LDS tile addressing: SW = 0 pads rows to GLD elements; SW = 1 / 2 keep
-// 32-element rows and place 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
-// (1) or c ^ ((r >> 1) & 3) (2), so the lanes of one access fall on distinct
-// banks without padding.
-template <int SW> struct SplitLds {
-  static constexpr int LD = SW == 0 ? GLD : GK;
+// LDS tile addressing: 32-element (64-byte) rows, 16-byte chunk c of row r
+// stored at chunk c ^ ((r >> 2) & 3). The MFMA operand reads (rows r .. r + 31,
+// one chunk each, two chunks per row across the wave halves) then fall on
+// distinct banks: measured on gfx950, this layout and 80-byte padded rows read
+// without bank conflicts, c ^ ((r >> 1) & 3) is 2-way conflicted.
+struct SplitLds {
+  static constexpr int LD = GK;
   __device__ static int at(int r, int c) {   // c: element offset, a multiple of 8
-    if constexpr (SW == 0) return r * LD + c;
-    else if constexpr (SW == 1) return r * LD + (((c >> 3) ^ ((r >> 2) & 3)) << 3);
-    else return r * LD + (((c >> 3) ^ ((r >> 1) & 3)) << 3);
+    return r * LD + (((c >> 3) ^ ((r >> 2) & 3)) << 3);
   }
 };
 
@@ -616,9 +615,9 @@ template <int SW> struct SplitLds {
 // fp32 rows instead and split into the hi + lo LDS planes on the way in, so
 // no prologue writes the planes.
 // SNK: the SnakeBeta epilogue of a convolution.
-template <int TM, int TN, int SW, bool FA = false, bool SNK = false>
+template <int TM, int TN, bool FA = false, bool SNK = false>
 __global__ __launch_bounds__(NT) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
-  using LT = SplitLds<SW>;
+  using LT = SplitLds;
   constexpr int GLD_ = LT::LD;
   constexpr int BM = 64 * TM, BN = 64 * TN;
   constexpr int AF = FA ? BM * GK / 4 / NT : 1;  // fp32 16-byte chunks per thread per stage (FA)
@@ -795,14 +794,14 @@ static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
   const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (big >= 512) {
     dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
-    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
-    else hipLaunchKernelGGL((gemm_split_kernel<2, 2, 2>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<2, 2>), grid, dim3(NT), 0, s, a, xs);
   } else {
     dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
-    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
-    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2, true>), grid, dim3(NT), 0, s, a, xs);
-    else hipLaunchKernelGGL((gemm_split_kernel<1, 2, 2>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<1, 2>), grid, dim3(NT), 0, s, a, xs);
   }
   return hipGetLastError();
 }
