@@ -49,7 +49,8 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
                                    (2048, 256, 4), (2056, 1536, 11), (6144, 1024, 32), (2048, 3072, 20),
                                    (6144, 1024, 64), (1024, 256, 40), (4096, 1024, 48),
                                    (3072, 1024, 8), (2048, 1024, 6), (1000, 2048, 4),
-                                   (1024, 2048, 2100), (2056, 256, 4100)])
+                                   (1024, 2048, 2100), (2056, 256, 4100), (4096, 1024, 2100),
+                                   (4104, 512, 2050)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row and split-K scratch, which routes bf16
@@ -60,7 +61,9 @@ def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     GEMV when N >= 2048 (also up to 32 rows) and the skinny MFMA kernel
     otherwise, either way. From 2048 rows without a gain the split GEMM reads
     fp32 activation tiles and splits them itself (2100 rows on 64 x 128
-    tiles, 4100 rows on 128 x 128 tiles, both with ragged tails)."""
+    tiles, 4100 rows on 128 x 128 tiles, both with ragged tails); from 4096
+    columns and 2048 rows it runs 8 waves on 128 x 256 tiles (4096 and a
+    ragged 4104 columns)."""
     if not mc and (wdt != "bf16" or M < 16):
         pytest.skip("same kernel as the mc=True case")
     torch = _torch()
