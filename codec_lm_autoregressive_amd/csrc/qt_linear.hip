@@ -440,7 +440,8 @@ constexpr int GLD = GK + 8;   // padded LDS row (bf16 elements)
 
 
 template <int BM, int BN>
-__global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float* __restrict__ den) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 3 : 8)))
+void mfma_gemm_kernel(LinearArgs p, const float* __restrict__ den) {
   constexpr int TM = BM / 64, TN = BN / 64;      // 32x32 MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) uint16_t sah[BM * GLD];
   __shared__ __attribute__((aligned(16))) uint16_t sal[BM * GLD];
@@ -522,11 +523,21 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float
         }
     }
   }
-  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4;
+  // a tile's residual values are all loaded before its first store
 #pragma unroll
   for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < TN; ++tj)
+    for (int tj = 0; tj < TN; ++tj) {
+      float yo[16];
+      if (p.epi == EPI_RESIDUAL)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int row = min(m0 + wm * (BM / 2) + ti * 32 + i, M - 1);
+          const int col = min(n0 + wn * (BN / 2) + tj * 32 + (lane & 31), N - 1);
+          yo[r] = p.Y[(long)row * p.ldy + col];
+        }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -537,10 +548,10 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(LinearArgs p, const float
           const float u = __shfl_xor(v, 1);   // the (gate, up) pair sits in lanes 2c, 2c+1
           if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * u;
         } else if (row < M && col < N) {
-          float* y = p.Y + (long)row * p.ldy + col;
-          *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+          p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yo[r] + v : v;
         }
       }
+    }
 }
 
 // den[m] = sqrt(mean(X[m]^2) + eps); optionally the normalised rows.
@@ -615,9 +626,11 @@ struct SplitLds {
 // fp32 rows instead and split into the hi + lo LDS planes on the way in, so
 // no prologue writes the planes.
 // SNK: the SnakeBeta epilogue of a convolution. WN: waves along N (2 or 4;
-// 4 gives a 512-thread block on a 64 TM x 128 TN tile).
-template <int TM, int TN, bool FA = false, bool SNK = false, int WN = 2>
-__global__ __launch_bounds__(128 * WN) void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
+// 4 gives a 512-thread block on a 64 TM x 128 TN tile). RES: the residual
+// epilogue (its old values take registers only in this variant).
+template <int TM, int TN, bool FA = false, bool SNK = false, int WN = 2, bool RES = false>
+__global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN == 4 ? 4 : SNK && RES ? 2 : 3)))
+void gemm_split_kernel(LinearArgs p, const uint16_t* __restrict__ xs) {
   using LT = SplitLds;
   constexpr int GLD_ = LT::LD;
   constexpr int NT = 128 * WN;                    // threads: 2 x WN waves
@@ -744,25 +757,46 @@ __global__ __launch_bounds__(128 * WN) void gemm_split_kernel(LinearArgs p, cons
     if (st + 1 < S) store((st + 1) & 1);
     __syncthreads();
   }
-  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  // D(i, j) of a 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4.
+  // A tile's residual values (and the lane's SnakeBeta parameters) are all
+  // loaded before its first store, so the tile costs one memory round trip
+  // rather than one per element.
+  float sa[TN], sb[TN];
+  if constexpr (SNK)
+#pragma unroll
+    for (int tj = 0; tj < TN; ++tj) {
+      const int col = min(n0 + wn * (BN / WN) + tj * 32 + (lane & 31), N - 1);
+      sa[tj] = p.snake_alpha[col];
+      sb[tj] = p.snake_bden[col];
+    }
 #pragma unroll
   for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < TN; ++tj)
+    for (int tj = 0; tj < TN; ++tj) {
+      float yo[16];
+      if constexpr (RES)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int row = min(m0 + wm * (BM / 2) + ti * 32 + i, M - 1);
+          const int col = min(n0 + wn * (BN / WN) + tj * 32 + (lane & 31), N - 1);
+          yo[r] = p.Y[(long)row * p.ldy + col];
+        }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int row = m0 + wm * (BM / 2) + ti * 32 + i;
         const int col = n0 + wn * (BN / WN) + tj * 32 + (lane & 31);
         const float v = acc[ti][tj][r];
-        if (p.epi == EPI_SWIGLU) {
+        if (!RES && p.epi == EPI_SWIGLU) {
           const float u = __shfl_xor(v, 1);   // the (gate, up) pair sits in lanes 2c, 2c+1
           if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * u;
         } else if (row < M && col < N) {
           float* y = p.Y + (long)row * p.ldy + col;
-          const float o = p.epi == EPI_RESIDUAL ? *y + v : v;
+          float o = v;
+          if constexpr (RES) o += yo[r];
           if constexpr (SNK) {
-            const float so = snake_beta(o, p.snake_alpha[col], p.snake_bden[col]);
+            const float so = snake_beta(o, sa[tj], sb[tj]);
             if (p.Y2) {
               *y = o;
               p.Y2[(long)row * p.ldy2 + col] = so;
@@ -774,6 +808,7 @@ __global__ __launch_bounds__(128 * WN) void gemm_split_kernel(LinearArgs p, cons
           }
         }
       }
+    }
 }
 
 // The split GEMM needs K % 32 == 0, rows of 16-byte aligned activations and
@@ -787,31 +822,39 @@ static bool gemm_split_fits(const LinearArgs& a) {
 // itself (FA): 4096 rows, o 64 us and down 88 us against 74 and 108 with the
 // prologue; with a gain (an extra gain load per chunk, fewer waves) and at
 // 1051 rows the prologue path measured as fast or faster.
-static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
+template <bool RES>
+static hipError_t launch_gemm_split_t(const LinearArgs& a, hipStream_t s) {
   uint16_t* xs = (uint16_t*)a.xs;
   const bool fa = a.conv_taps > 0 || (!a.gain && !a.norm_out && a.M >= 2048);
   if (!fa) hipLaunchKernelGGL(split_rows_kernel, dim3(a.M), dim3(NT), 0, s, a, xs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long big = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (a.N >= 4096 && a.M >= 2048 && !a.snake_alpha) {
+  if (!RES && a.N >= 4096 && a.M >= 2048 && !a.snake_alpha) {
     // wide projections (q/k/v, gate/up): 8 waves on 128 x 256 tiles, measured
     // 5-18 % faster than 4 waves on 128 x 128 at 8192 rows
     dim3 grid((a.N + 255) / 256, (a.M + 127) / 128);
-    if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, false, 4>), grid, dim3(512), 0, s, a, xs);
-    else hipLaunchKernelGGL((gemm_split_kernel<2, 2, false, false, 4>), grid, dim3(512), 0, s, a, xs);
+    if constexpr (!RES) {
+      if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, false, 4>), grid, dim3(512), 0, s, a, xs);
+      else hipLaunchKernelGGL((gemm_split_kernel<2, 2, false, false, 4>), grid, dim3(512), 0, s, a, xs);
+    }
   } else if (big >= 512) {
     dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
-    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true>), grid, dim3(NT), 0, s, a, xs);
-    else hipLaunchKernelGGL((gemm_split_kernel<2, 2>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, true, 2, RES>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<2, 2, true, false, 2, RES>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<2, 2, false, false, 2, RES>), grid, dim3(NT), 0, s, a, xs);
   } else {
     dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
-    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true, true>), grid, dim3(NT), 0, s, a, xs);
-    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true>), grid, dim3(NT), 0, s, a, xs);
-    else hipLaunchKernelGGL((gemm_split_kernel<1, 2>), grid, dim3(NT), 0, s, a, xs);
+    if (a.snake_alpha) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true, true, 2, RES>), grid, dim3(NT), 0, s, a, xs);
+    else if (fa) hipLaunchKernelGGL((gemm_split_kernel<1, 2, true, false, 2, RES>), grid, dim3(NT), 0, s, a, xs);
+    else hipLaunchKernelGGL((gemm_split_kernel<1, 2, false, false, 2, RES>), grid, dim3(NT), 0, s, a, xs);
   }
   return hipGetLastError();
+}
+
+static hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t s) {
+  if (a.epi == EPI_RESIDUAL) return launch_gemm_split_t<true>(a, s);
+  return launch_gemm_split_t<false>(a, s);
 }
 
 static hipError_t launch_mfma(const LinearArgs& a, float* den, hipStream_t s) {
@@ -1183,8 +1226,16 @@ __global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
         }
   }
   if (grp > 0) return;   // no barrier follows
-  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4;
+  // the residual's old values are all loaded before the first store
   const int col = n0 + wn * 32 + (lane & 31);
+  float yo[16];
+  if (direct && p.epi == EPI_RESIDUAL)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = min(m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), M - 1);
+      yo[r] = p.Y[(long)row * p.ldy + min(col, N - 1)];
+    }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), row = m0 + lr;
@@ -1198,8 +1249,7 @@ __global__ __launch_bounds__(NT * KW) void rows_gemm_kernel(LinearArgs p) {
       const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
       if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
     } else if (row < M && col < N) {
-      float* y = p.Y + (long)row * p.ldy + col;
-      *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yo[r] + v : v;
     }
   }
 }
@@ -1312,8 +1362,16 @@ __global__ __launch_bounds__(NT) void rows_gemm1_kernel(LinearArgs p) {
           }
     }
   }
-  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4
+  // D(i, j) of the 32x32 tile: lane j + 32 * ((i / 4) % 2), register (i / 8) * 4 + i % 4;
+  // the residual's old values are all loaded before the first store
   const int col = n0 + wn * 32 + (lane & 31);
+  float yo[16];
+  if (direct && p.epi == EPI_RESIDUAL)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = min(m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), M - 1);
+      yo[r] = p.Y[(long)row * p.ldy + min(col, N - 1)];
+    }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), row = m0 + lr;
@@ -1327,8 +1385,7 @@ __global__ __launch_bounds__(NT) void rows_gemm1_kernel(LinearArgs p) {
       const float up = __shfl_xor(v, 1);   // (gate, up) rows 2c, 2c + 1 sit in lanes 2c, 2c + 1
       if (!(lane & 1) && row < M && col + 1 < N) p.Y[(long)row * p.ldy + (col >> 1)] = v / (1.f + expf(-v)) * up;
     } else if (row < M && col < N) {
-      float* y = p.Y + (long)row * p.ldy + col;
-      *y = p.epi == EPI_RESIDUAL ? *y + v : v;
+      p.Y[(long)row * p.ldy + col] = p.epi == EPI_RESIDUAL ? yo[r] + v : v;
     }
   }
 }
