@@ -1432,18 +1432,24 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 // head) while its rows of W_o are in flight, then applies them: one launch
 // instead of two. NTOK new tokens (1: a step, 2: the two-token pass at
 // positions 0 and 1) sit in activation rows 0 .. NTOK-1. Block b owns output
-// rows [b RO, (b + 1) RO); block 0 also writes the new K/V rows.
+// rows [b RO, (b + 1) RO) (with RO < NKV, NKV / RO waves share a row, each
+// taking a K part, and the parts are added in order through LDS); block 0
+// also writes the new K/V rows.
 // Scores: lane = (key j, quarter of the head dims); P·V: lane = (8-dim
 // column chunk, key slot j mod 4).
 template <typename KVT, int NKV, int G, int RO, int NTOK>
 __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, LinearArgs o) {
   constexpr int D = 128, HALF = 64, NQ = NKV * G, KO = NQ * D;
   constexpr int EPC = 8;                       // 16-bit cache elements per 16-byte chunk
-  constexpr int RW = RO / NKV;                 // o rows per wave
-  constexpr int KC = KO / 512;                 // 16-byte weight chunks per lane and row
-  static_assert(sizeof(KVT) == 2 && RO % NKV == 0 && KO % 512 == 0, "layout");
+  constexpr int RW = RO >= NKV ? RO / NKV : 1; // o rows per wave
+  constexpr int KS = RO >= NKV ? 1 : NKV / RO; // waves sharing one o row (K split, RO < NKV)
+  constexpr int KC = KO / 512 / KS;            // 16-byte weight chunks per lane and row
+  static_assert(sizeof(KVT) == 2 && (RO % NKV == 0 || NKV % RO == 0) && KO % (512 * KS) == 0, "layout");
   const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * RO + g * RW;
+  const int ks = KS > 1 ? g / RO : 0;          // this wave's K part of its row
+  const int n0 = KS > 1 ? blockIdx.x * RO + g % RO : blockIdx.x * RO + g * RW;
+  const int kc0 = ks * KC;                     // first weight chunk of the K part
+  __shared__ float opart[KS > 1 ? NKV : 1][NTOK];
   __shared__ __align__(16) float qs[NKV][NTOK][G][D];
   __shared__ __align__(16) float knew[NKV][NTOK][D];
   __shared__ __align__(16) float vnew[NKV][NTOK][D];
@@ -1486,7 +1492,7 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) w[r][c] = ld_weight(W + (long)(n0 + r) * KO + c * 512 + lane * 8);
+    for (int c = 0; c < KC; ++c) w[r][c] = ld_weight(W + (long)(n0 + r) * KO + (kc0 + c) * 512 + lane * 8);
   // the residual's old values, so that the epilogue has no dependent load
   float yold[NTOK][RW];
 #pragma unroll
@@ -1629,7 +1635,7 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
       float ap[KC];                            // one partial sum per chunk: short dependence chains
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const f32x4* x4 = (const f32x4*)(&att[t][c * 512 + lane * 8]);
+        const f32x4* x4 = (const f32x4*)(&att[t][(kc0 + c) * 512 + lane * 8]);
         const f32x4 xa = x4[0], xb = x4[1];
         const u32x4 q = w[r][c];
         float b = bf_lo(q.x) * xa.x;
@@ -1643,16 +1649,34 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
 #pragma unroll
       for (int c = 1; c < KC; ++c) a += ap[c];
       a = wave_sum(a);
-      if (lane == 0) o.Y[(long)t * o.ldy + n0 + r] = yold[t][r] + a;
+      if constexpr (KS == 1) {
+        if (lane == 0) o.Y[(long)t * o.ldy + n0 + r] = yold[t][r] + a;
+      } else if (lane == 0) {
+        opart[g][t] = a;
+      }
     }
+  }
+  if constexpr (KS > 1) {
+    // the K parts of each row, added in part order
+    __syncthreads();
+    if (ks == 0 && lane == 0)
+#pragma unroll
+      for (int t = 0; t < NTOK; ++t) {
+        float a = opart[g][t];
+#pragma unroll
+        for (int q = 1; q < KS; ++q) a += opart[g + q * RO][t];
+        o.Y[(long)t * o.ldy + n0] = yold[t][0] + a;
+      }
   }
 }
 
 template <typename KVT>
 static hipError_t launch_pred_attn_o_t(const AttnArgs& a, const LinearArgs& o, hipStream_t s) {
-  // 8 output rows per block (one per wave): 128 blocks at the 0.6B shape;
-  // 16 rows per block (64 blocks) measured 0.6 us slower per launch
-  constexpr int RO = 8;
+  // 4 output rows per block, each row's dot product split over two waves:
+  // 256 blocks at the 0.6B shape. Per batch-1 frame (70 launches) this
+  // measured 2.081 ms against 2.085 with 8 rows per block (128 blocks); 16
+  // rows per block (64 blocks) measured 0.6 us slower per launch than 8.
+  constexpr int RO = 4;
   hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   return hipGetLastError();
 }
