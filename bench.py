@@ -53,10 +53,10 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 #    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
 COUNTED = {
     "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
-    "frame": {"src_sha256_16": "030a9d8d6a07ed5b", "bytes_per_frame": {
+    "frame": {"src_sha256_16": "69526dcddc2426ed", "bytes_per_frame": {
         # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
-        "qwen06b_bf16_b1": (3421800000, 35.5, 3313377280),
-        "qwen06b_bf16_b64_sampling": (11344900000, 339.9, 5804343296),
+        "qwen06b_bf16_b1": (3423600000, 35.5, 3313377280),
+        "qwen06b_bf16_b64_sampling": (11353000000, 339.9, 5804343296),
     }},
 }
 CSRC = os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc")
@@ -145,6 +145,8 @@ def parse():
     ap.add_argument("--frame-counters", action="store_true",
                     help="only a prefill and --counter-frames eager frames of --workload, then a 64 MiB copy")
     ap.add_argument("--counter-frames", type=int, default=8)
+    ap.add_argument("--codec-only", action="store_true",
+                    help="only the codec decoder measurement (one JSON line; for kernel traces)")
     ap.add_argument("--gemm-kernels", action="store_true",
                     help="only the batched projections (4096 prefill rows, 64-row decode) at the "
                          "0.6B shapes, timed per launch (for counter runs)")
@@ -289,6 +291,9 @@ def main():
     if args.gemm_kernels:
         for line in gemm_kernel_timing(torch, binding, synth):
             print(json.dumps(line), flush=True)
+        return
+    if args.codec_only:
+        print(json.dumps(codec_timing(torch, binding, synth)), flush=True)
         return
     if args.kernel_only:
         wl = synth.workload(args.workload)
