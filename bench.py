@@ -53,10 +53,10 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 #    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
 COUNTED = {
     "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
-    "frame": {"src_sha256_16": "69526dcddc2426ed", "bytes_per_frame": {
+    "frame": {"src_sha256_16": "d7ba8ba7520e5fbd", "bytes_per_frame": {
         # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
-        "qwen06b_bf16_b1": (3423600000, 35.5, 3313377280),
-        "qwen06b_bf16_b64_sampling": (11353000000, 339.9, 5804343296),
+        "qwen06b_bf16_b1": (3422800000, 35.5, 3313377280),
+        "qwen06b_bf16_b64_sampling": (11353800000, 339.9, 5804343296),
     }},
 }
 CSRC = os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc")
