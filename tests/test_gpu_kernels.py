@@ -50,7 +50,7 @@ def _ref_linear(W, X, gain, eps, epi, Y0):
                                    (6144, 1024, 64), (1024, 256, 40), (4096, 1024, 48),
                                    (3072, 1024, 8), (2048, 1024, 6), (1000, 2048, 4),
                                    (1024, 2048, 2100), (2056, 256, 4100), (4096, 1024, 2100),
-                                   (4104, 512, 2050)])
+                                   (4104, 512, 2050), (192, 512, 2100), (96, 256, 4100)])
 @pytest.mark.parametrize("epi,norm", [(0, True), (1, False), (2, True)])
 def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     """mc: hand the library its row and split-K scratch, which routes bf16
@@ -63,7 +63,8 @@ def test_linear_matches_oracle(mc, wdt, N, K, M, epi, norm):
     fp32 activation tiles and splits them itself (2100 rows on 64 x 128
     tiles, 4100 rows on 128 x 128 tiles, both with ragged tails); from 4096
     columns and 2048 rows it runs 8 waves on 128 x 256 tiles (4096 and a
-    ragged 4104 columns)."""
+    ragged 4104 columns); 96 and 192 columns (the codec's late stages) pad
+    their 128-wide tiles."""
     if not mc and (wdt != "bf16" or M < 16):
         pytest.skip("same kernel as the mc=True case")
     torch = _torch()
