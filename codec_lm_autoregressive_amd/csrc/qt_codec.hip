@@ -493,7 +493,7 @@ hipError_t conv_gemm(qt_codec* c, const void* W, int taps, int d, int Cin, int C
 // causal convolution, kernel k, dilation d: W [Cout][k][Cin] (packed) or
 // tap-major [k][Cout][Cin]; X padded
 hipError_t conv(qt_codec* c, const void* W, int k, int d, int Cin, int Cout, const float* X, long T, float* Y, int epi0) {
-  if (conv_packed(c, Cin) && epi0 == EPI_STORE) return conv_gemm(c, W, k, d, Cin, Cout, X, T, Y, Cout);
+  if (conv_packed(c, Cin)) return conv_gemm(c, W, k, d, Cin, Cout, X, T, Y, Cout, epi0);
   for (int j = 0; j < k; ++j) {
     const long sh = (long)(k - 1 - j) * d;
     const hipError_t e = gemm(c, (const char*)W + wbytes(c, (size_t)j * Cout * Cin), Cout, Cin, X - sh * Cin, Cin, T,
