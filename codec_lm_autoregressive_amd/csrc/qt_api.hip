@@ -358,6 +358,7 @@ struct qt_ctx {
   // graph of one frame for the current B
   hipGraphExec_t gexec = nullptr;
   int graph_B = -1;
+  int graph_pred_sample = -1;         // the predictor's do_sample the graph was taken with
   int eager_frames = 0;
   // token-id frontend (qt_attach_frontend)
   struct Frontend {
@@ -440,7 +441,7 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 // the attend pass takes instead of one run per token.
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
                      int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false,
-                     const Run* tiles = nullptr, int n_tiles = 0) {
+                     const Run* tiles = nullptr, int n_tiles = 0, const SelFold* sel = nullptr) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -464,7 +465,14 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     const bool decode_attn = !prefill && (single_token || pass0) && d.d <= 128;
     const int zq = decode_attn ? linear_split_ranges(a) : 1;
     a.defer = zq > 1;
-    HIPCK(launch_linear(a, s));
+    if (sel && l == 0) {
+      // the previous step's greedy selection picks this step's input row
+      LinearArgs aq = a;
+      aq.sel = *sel;
+      HIPCK(launch_linear(aq, s));
+    } else {
+      HIPCK(launch_linear(a, s));
+    }
     a.defer = 0;
     AttnArgs t{};
     if (zq > 1) { t.part = ctx->part; t.part_z = zq; t.part_rows = M; t.part_k = d.H; t.part_eps = d.eps; }
@@ -539,6 +547,32 @@ SelectArgs select_base(qt_ctx* ctx, const qt_sampling& sm, bool talker) {
   return a;
 }
 
+// The greedy selection of predictor head st - 1 (code st) as folded into
+// the first projection of predictor step st, at batch 1.
+static SelFold pred_sel_fold(qt_ctx* ctx, int st) {
+  const int C = ctx->cfg.codebook;
+  SelFold f{};
+  f.logits = ctx->logits_p + (size_t)(st - 1) * ctx->cfg.max_batch * C; f.V = C;
+  f.tab = ctx->pemb; f.tab_off = (long)(st - 1) * C;
+  f.used = ctx->frame_out + 1 + ctx->cfg.max_batch; f.own = ctx->own; f.code_ld = kGroups; f.col = st;
+  f.x = ctx->cfg.pred_in_proj ? nullptr : ctx->x_p; f.fb = ctx->x_t;
+  f.status = ctx->frame_out;
+  return f;
+}
+
+// Whether a free-running frame folds the predictor's selections 1..14 into
+// the next step's first projection: batch 1, greedy predictor, and that
+// projection on the register GEMV.
+static bool pred_folds(qt_ctx* ctx) {
+  if (ctx->B != 1 || ctx->ps.do_sample) return false;
+  LinearArgs f{};
+  f.wdtype = ctx->cfg.weight_dtype; f.M = 1; f.epi = EPI_STORE;
+  if (ctx->cfg.pred_in_proj) { f.N = ctx->p.H; f.K = ctx->t.H; }
+  else { f.N = ctx->p.qkv; f.K = ctx->p.H; f.gain = ctx->pl[0].attn_norm; }
+  f.sel = pred_sel_fold(ctx, 1);
+  return linear_sel_fits(f);
+}
+
 // One frame for all rows; forced != nullptr selects teacher forcing.
 qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   const int B = ctx->B;
@@ -568,11 +602,19 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   pa.wdtype = wd; pa.W = ctx->pproj; pa.N = P.H; pa.K = T.H; pa.X = ctx->xin_w; pa.ldx = T.H;
   pa.Y = ctx->x_p; pa.ldy = P.H; pa.epi = EPI_STORE;
 
+  const bool fold = !forced && pred_folds(ctx);
   for (int st = 0; st < 15; ++st) {
     const int M = st == 0 ? 2 * B : B;
-    if (proj) { pa.M = M; HIPCK(launch_linear(pa, s)); }
+    const SelFold sf = fold && st > 0 ? pred_sel_fold(ctx, st) : SelFold{};
+    const SelFold* sfp = sf.logits ? &sf : nullptr;
+    if (proj) {
+      LinearArgs pq = pa;
+      pq.M = M;
+      if (sfp) pq.sel = sf;
+      HIPCK(launch_linear(pq, s));
+    }
     if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s, false, false, true)); }
-    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true)); }
+    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true, false, nullptr, 0, proj ? nullptr : sfp)); }
     // head st on the last token of each row
     LinearArgs ha{};
     ha.row_den = ctx->row_den; ha.xs = ctx->xsplit; ha.xs_floats = ctx->xsplit_floats;
@@ -594,7 +636,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
     sa.fb = ctx->x_t; sa.fb_ld = T.H;
     sa.add_text = st == 14; sa.text_ptr = ctx->text_ptr; sa.text_len = ctx->text_len;
     sa.frame_k = ctx->frame_k;
-    HIPCK(launch_select(sa, s));
+    if (!(fold && st < 14)) HIPCK(launch_select(sa, s));
   }
   // talker step at position P_r + k
   QTCK(run_layers(ctx, true, ctx->x_t, B, runs_decode, B, ctx->pos, 0, s, false, true));
@@ -1048,7 +1090,7 @@ static qt_status frame_common(qt_ctx* ctx, const int* forced_dev) {
     if (r != QT_OK) return r;
   } else {
     // the first frame after a prefill runs eagerly; later frames replay one captured graph
-    if (ctx->gexec && ctx->graph_B == ctx->B) {
+    if (ctx->gexec && ctx->graph_B == ctx->B && ctx->graph_pred_sample == ctx->ps.do_sample) {
       HIPCK(hipGraphLaunch(ctx->gexec, s));
     } else if (ctx->eager_frames == 0) {
       qt_status r = enqueue_frame(ctx, s, nullptr);
@@ -1067,6 +1109,7 @@ static qt_status frame_common(qt_ctx* ctx, const int* forced_dev) {
       (void)hipGraphDestroy(g);
       if (e != hipSuccess) { ctx->gexec = nullptr; set_err(ctx->err, "graph instantiate failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
       ctx->graph_B = ctx->B;
+      ctx->graph_pred_sample = ctx->ps.do_sample;
       HIPCK(hipGraphLaunch(ctx->gexec, s));
     }
   }

@@ -103,6 +103,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int v, int id) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xb1, 0xf>(v, 0x7fffffff));
+  v = min(v, dpp_i<0x4e, 0xf>(v, 0x7fffffff));
+  v = min(v, dpp_i<0x141, 0xf>(v, 0x7fffffff));
+  v = min(v, dpp_i<0x140, 0xf>(v, 0x7fffffff));
+  v = min(v, dpp_i<0x142, 0xa>(v, 0x7fffffff));
+  v = min(v, dpp_i<0x143, 0xc>(v, 0x7fffffff));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Block-wide reductions for NT threads; `red` is LDS scratch of >= NT/64 floats.
 // All threads of the block must call them.
 __device__ inline float block_sum(float v, float* red) {

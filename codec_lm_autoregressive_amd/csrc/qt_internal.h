@@ -16,6 +16,22 @@ enum StatusBits : int { ST_NONFINITE = 1, ST_RANGE = 2 };
 // Y[m, :] (op)= W · norm(X[m, :]) for m < M.  W is [N, K] row-major
 // (nn.Linear layout), f32 or bf16; X, Y fp32.  With EPI_SWIGLU the rows of W
 // come in (gate j, up j) pairs and Y[m, j] = silu(gate) * up.
+// Greedy selection folded into a register GEMV's prologue (one activation
+// row): instead of reading X, the kernel takes the argmax (lowest id on ties)
+// of `logits` (V <= 2048 floats, 16-byte aligned) and uses row
+// tab_off + argmax of `tab` ([rows, K], weight dtype) as its activation row.
+// The waves of block 0 that span K also commit the code (used / own at
+// column col, row stride code_ld), store the row to x (fp32, nullable) and
+// add it to fb; a NaN or +inf logit sets ST_NONFINITE in status and takes
+// code 0, as the selection kernel does.
+struct SelFold {
+  const float* logits; int V;
+  const void* tab; long tab_off;
+  int* used; int* own; int code_ld; int col;
+  float* x; float* fb;
+  int* status;
+};
+
 struct LinearArgs {
   const void* W; int wdtype; int N; int K;
   const float* X; long ldx; int M;
@@ -36,12 +52,16 @@ struct LinearArgs {
   // residual add), writes y + sin(snake_alpha[col] y)^2 / snake_bden[col]
   // to Y, or y to Y and that value to Y2 (row stride ldy2) when Y2 is set.
   const float* snake_alpha; const float* snake_bden; float* Y2; long ldy2;
+  SelFold sel;                         // folded greedy selection (sel.logits != nullptr; M = 1)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 // K ranges the launch of a would split into (partial sums in a.part: range z,
 // row m, column n at part[(z * M + m) * N + n]; with a gain the row sums of
 // squares follow at part[Z * M * N + z * M + m]); 1 when it writes Y directly.
 int linear_split_ranges(const LinearArgs& a);
+// Whether a projection can take a folded greedy selection (a.sel): one
+// row on the register GEMV path, V <= 2048 and a multiple of 4, aligned rows.
+bool linear_sel_fits(const LinearArgs& a);
 
 // One contiguous run of tokens of one batch row: row, first token (row of the
 // activation arrays), token count, first position (before pos_base / row_pos).

@@ -388,6 +388,37 @@ def test_qwen06b_b64_graph_replay_equals_forced_eager():
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["qwen06b_bf16_b1", "qwen17b_bf16_b1"])
+def test_b1_greedy_graph_replay_equals_forced_eager(name):
+    """At batch 1 with a greedy predictor, free-running frames fold the
+    predictor's selections 1..14 into the next step's first projection (the
+    q/k/v projection, or the 1.7B-class input projection); the forced path
+    keeps the separate selection launches. The free-run codes (frames 2..
+    from graph replays) equal the eager forced replay bit for bit, so the
+    folded argmax, the predictor input row and the feedback sum are exact."""
+    wl = synth.workload(name)
+    dm = synth.dims(wl["model"])
+    H = dm["talker"]["hidden"]
+    w = weights(wl["model"], "bf16")
+    lens = synth.prompt_lengths(1, *wl["prompt"], seed=2)
+    prompt = synth.make_prompts(lens, H, seed=1)
+    pad = synth.make_tts_pad(H, seed=3)
+    eng = binding.Engine(dm, w, "bf16", max_batch=1, max_positions=wl["max_positions"])
+    F = 24
+    codes, n, _ = eng.generate(prompt, lens, pad, wl["talker"], wl["predictor"], 0, F)
+    assert int(n[0]) >= 3
+    assert np.all((codes[0, :int(n[0]), 1:] >= 0) & (codes[0, :int(n[0]), 1:] < dm["codebook"]))
+    eng.prefill(prompt, lens, pad, wl["talker"], wl["predictor"], 0, F)
+    for k in range(int(n[0])):
+        _, _, ch = eng.step_forced(codes[:, k].copy())
+        np.testing.assert_array_equal(ch[0, 1:], codes[0, k, 1:])
+        if k + 1 < int(n[0]):
+            assert ch[0, 0] == codes[0, k + 1, 0]
+    log(f"{name}: {int(n[0])} free-run frames equal the forced replay")
+    eng.close()
+
+
+@pytest.mark.timeout(900)
 def test_long_context_parity():
     """Talker attention over the batch-64 workload's full KV extent: a
     1500-token prompt (prefill attention over up to 1500 keys, decode at
