@@ -428,6 +428,17 @@ def test_long_context_parity():
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("plen", [250, 1500])
+def test_b1_long_context_parity(plen):
+    """One row at the batch-64 workload's cache length: the batch-1 decode
+    attention (one block per kv head, 256-key chunks) over a 250-token
+    prompt (the keys cross the first chunk boundary during the 20 frames)
+    and a 1500-token one (six chunks)."""
+    eng, *_ = _full_size("qwen06b_bf16_b64_sampling", [0], 20, lens=np.array([plen], dtype=np.int32))
+    eng.close()
+
+
+@pytest.mark.timeout(900)
 def test_qwen17b_bf16_b1_parity():
     """1.7B-class talker (hidden 2048, I 6144) with the 2048 -> 1024 predictor
     input projection, batch 1 greedy."""
