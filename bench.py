@@ -52,7 +52,7 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 #  * HBM bytes per decode frame of the batch-1 and batch-64 workloads
 #    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
 COUNTED = {
-    "kernel": {"src_sha256_16": "6eb5175505e9b4b5", "bytes": 12719091, "trace_avg_us": 4.860},
+    "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
     "frame": {"src_sha256_16": "d7ba8ba7520e5fbd", "bytes_per_frame": {
         # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
         "qwen06b_bf16_b1": (3422800000, 35.5, 3313377280),

@@ -147,7 +147,7 @@ struct LayerBuf { size_t wqkv, wo, wgu, wd, attn_norm, q_norm, k_norm, mlp_norm;
 
 struct Layout {
   std::vector<LayerBuf> tl, pl;
-  size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj;
+  size_t talker_norm, temb, thead, pred_norm, pemb, phead, pproj, plut, pxlut, lut_stage;
   size_t cos_t, sin_t, cos_p, sin_p, kc_t, vc_t, kc_p, vc_p;
   size_t x_t, qkv, attn, act, x_p, xin_w, h, xlast, logits_t, logits_p, rope_rows, row_den, part, xsplit, ksplit;
   long part_floats, xsplit_floats;
@@ -184,6 +184,12 @@ Layout plan_layout(const qt_config& c) {
   L.pemb = p.take(p.sz.mul({15, C, (size_t)t.H, es}));
   L.phead = p.take(p.sz.mul({15, C, (size_t)q.H, es}));
   L.pproj = c.pred_in_proj ? p.take(p.sz.mul({(size_t)q.H, (size_t)t.H, es})) : 0;
+  // code-indexed input side of the predictor's first layer for steps 1..14:
+  // the q/k/v rows of every code of tables 0..13 (with the input projection
+  // also the projected rows), fp32, and one table as fp32 rows to build them
+  L.plut = p.take(p.sz.mul({14, C, (size_t)q.qkv, 4}));
+  L.pxlut = c.pred_in_proj ? p.take(p.sz.mul({14, C, (size_t)q.H, 4})) : 0;
+  L.lut_stage = p.take(p.sz.mul({C, (size_t)t.H, 4}));
   L.cos_t = p.take(p.sz.mul({MP, (size_t)t.d / 2, 4}));
   L.sin_t = p.take(p.sz.mul({MP, (size_t)t.d / 2, 4}));
   L.cos_p = p.take((size_t)kPredPositions * q.d / 2 * 4);
@@ -332,6 +338,7 @@ struct qt_ctx {
   std::vector<DevLayer> tl, pl;
   float *talker_norm, *pred_norm;
   void *temb, *thead, *pemb, *phead, *pproj;
+  float *plut, *pxlut, *lut_stage;     // code-indexed first-layer tables of predictor steps 1..14
   float *cos_t, *sin_t, *cos_p, *sin_p;
   void *kc_t, *vc_t, *kc_p, *vc_p;
   float *x_t, *qkv, *attn, *act, *x_p, *xin_w, *h, *xlast, *logits_t, *logits_p, *rope_rows, *row_den, *part, *xsplit, *ksplit;
@@ -439,9 +446,15 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 // 2r and 2r + 1 at positions 0 and 1).
 // prefill: tiles (n_tiles > 0) are the runs of up to kAttnTileTokens tokens
 // the attend pass takes instead of one run per token.
+// A code predictor step's input from the code-indexed tables of the first
+// layer: q/k/v rows (row stride lut_ld) and, with the input projection, the
+// projected rows; sel: the step's greedy selection is folded into the
+// attention (batch 1), else the rows were gathered by code beforehand.
+struct StepIn { const float* lut; long lut_ld; const float* xlut; const SelFold* sel; };
+
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
                      int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false,
-                     const Run* tiles = nullptr, int n_tiles = 0, const SelFold* sel = nullptr) {
+                     const Run* tiles = nullptr, int n_tiles = 0, const StepIn* in = nullptr) {
   const Dec& d = talker ? ctx->t : ctx->p;
   std::vector<DevLayer>& layers = talker ? ctx->tl : ctx->pl;
   const int maxpos = talker ? ctx->cfg.max_positions : kPredPositions;
@@ -463,16 +476,12 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     // single-token decode attention adds split-K partial sums itself, so a
     // split projection needs no reduce launch
     const bool decode_attn = !prefill && (single_token || pass0) && d.d <= 128;
-    const int zq = decode_attn ? linear_split_ranges(a) : 1;
+    // a code predictor step's first layer takes its q/k/v rows from the
+    // code-indexed table (gathered into qkv, or read by the attention itself)
+    const bool from_lut = in && l == 0;
+    const int zq = decode_attn && !from_lut ? linear_split_ranges(a) : 1;
     a.defer = zq > 1;
-    if (sel && l == 0) {
-      // the previous step's greedy selection picks this step's input row
-      LinearArgs aq = a;
-      aq.sel = *sel;
-      HIPCK(launch_linear(aq, s));
-    } else {
-      HIPCK(launch_linear(a, s));
-    }
+    if (!from_lut) HIPCK(launch_linear(a, s));
     a.defer = 0;
     AttnArgs t{};
     if (zq > 1) { t.part = ctx->part; t.part_z = zq; t.part_rows = M; t.part_k = d.H; t.part_eps = d.eps; }
@@ -514,8 +523,15 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
     if (!prefill) {
       // the code predictor at one row: attention and o-projection in one launch
       if (!talker) {
-        const hipError_t e = launch_attention_oproj(t, ao, s);
-        if (e != hipErrorNotSupported) { HIPCK(e); fused = true; }
+        if (from_lut && in->sel) {
+          // the folded selection: the attention reads the selected code's table rows
+          t.lut = in->lut; t.lut_ld = in->lut_ld; t.xlut = in->xlut; t.sel = *in->sel;
+          HIPCK(launch_attention_oproj(t, ao, s));
+          fused = true;
+        } else {
+          const hipError_t e = launch_attention_oproj(t, ao, s);
+          if (e != hipErrorNotSupported) { HIPCK(e); fused = true; }
+        }
       }
       if (!fused) HIPCK(launch_attention(t, s));
     }
@@ -547,30 +563,27 @@ SelectArgs select_base(qt_ctx* ctx, const qt_sampling& sm, bool talker) {
   return a;
 }
 
-// The greedy selection of predictor head st - 1 (code st) as folded into
-// the first projection of predictor step st, at batch 1.
+// The greedy selection of predictor head st - 1 (code st), folded into the
+// fused attention of predictor step st at batch 1.
 static SelFold pred_sel_fold(qt_ctx* ctx, int st) {
   const int C = ctx->cfg.codebook;
   SelFold f{};
   f.logits = ctx->logits_p + (size_t)(st - 1) * ctx->cfg.max_batch * C; f.V = C;
-  f.tab = ctx->pemb; f.tab_off = (long)(st - 1) * C;
-  f.used = ctx->frame_out + 1 + ctx->cfg.max_batch; f.own = ctx->own; f.code_ld = kGroups; f.col = st;
-  f.x = ctx->cfg.pred_in_proj ? nullptr : ctx->x_p; f.fb = ctx->x_t;
+  f.tab = ctx->pemb; f.tab_off = (long)(st - 1) * C; f.tab_dim = ctx->t.H;
+  f.used = ctx->frame_out + 1 + ctx->cfg.max_batch; f.own = ctx->own; f.col = st;
+  f.fb = ctx->x_t;
   f.status = ctx->frame_out;
   return f;
 }
 
 // Whether a free-running frame folds the predictor's selections 1..14 into
-// the next step's first projection: batch 1, greedy predictor, and that
-// projection on the register GEMV.
+// the next step's fused attention: batch 1, greedy predictor, and a
+// predictor shape the fused kernel serves.
 static bool pred_folds(qt_ctx* ctx) {
-  if (ctx->B != 1 || ctx->ps.do_sample) return false;
-  LinearArgs f{};
-  f.wdtype = ctx->cfg.weight_dtype; f.M = 1; f.epi = EPI_STORE;
-  if (ctx->cfg.pred_in_proj) { f.N = ctx->p.H; f.K = ctx->t.H; }
-  else { f.N = ctx->p.qkv; f.K = ctx->p.H; f.gain = ctx->pl[0].attn_norm; }
-  f.sel = pred_sel_fold(ctx, 1);
-  return linear_sel_fits(f);
+  const qt_config& c = ctx->cfg;
+  return ctx->B == 1 && !ctx->ps.do_sample &&
+         attention_oproj_sel_ok(ctx->p.nq, ctx->p.nkv, ctx->p.d, c.kv_dtype, c.weight_dtype, c.codebook, ctx->t.H) &&
+         (c.pred_in_proj || ctx->t.H == ctx->p.H);
 }
 
 // One frame for all rows; forced != nullptr selects teacher forcing.
@@ -605,16 +618,20 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   const bool fold = !forced && pred_folds(ctx);
   for (int st = 0; st < 15; ++st) {
     const int M = st == 0 ? 2 * B : B;
-    const SelFold sf = fold && st > 0 ? pred_sel_fold(ctx, st) : SelFold{};
-    const SelFold* sfp = sf.logits ? &sf : nullptr;
-    if (proj) {
-      LinearArgs pq = pa;
-      pq.M = M;
-      if (sfp) pq.sel = sf;
-      HIPCK(launch_linear(pq, s));
+    if (st == 0) {
+      if (proj) { pa.M = M; HIPCK(launch_linear(pa, s)); }
+      QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s, false, false, true));
+    } else {
+      // step st's input row is the embedding of code st: its first-layer
+      // q/k/v (and projected row) come from the tables built at create
+      const float* lut = ctx->plut + (size_t)(st - 1) * C * P.qkv;
+      const float* xlut = proj ? ctx->pxlut + (size_t)(st - 1) * C * P.H : nullptr;
+      const SelFold sf = fold ? pred_sel_fold(ctx, st) : SelFold{};
+      if (!fold)
+        HIPCK(launch_lut_rows(codes + st, kGroups, B, C, lut, P.qkv, ctx->qkv, P.qkv, xlut, P.H, ctx->x_p, P.H, s));
+      const StepIn in{lut, (long)P.qkv, xlut, fold ? &sf : nullptr};
+      QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true, false, nullptr, 0, &in));
     }
-    if (st == 0) { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_pass0, B, nullptr, 0, s, false, false, true)); }
-    else { QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true, false, nullptr, 0, proj ? nullptr : sfp)); }
     // head st on the last token of each row
     LinearArgs ha{};
     ha.row_den = ctx->row_den; ha.xs = ctx->xsplit; ha.xs_floats = ctx->xsplit_floats;
@@ -656,6 +673,34 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
   sa.frame_k = ctx->frame_k;
   HIPCK(launch_select(sa, s));
   HIPCK(launch_frame_advance(ctx->frame_k, ctx->pos, ctx->finished, B, s));
+  return QT_OK;
+}
+
+// The code-indexed first-layer tables of predictor steps 1..14. Step st's
+// input row is row c of embedding table st - 1 (through the input
+// projection when there is one), so its first-layer q/k/v are a function of
+// c alone: for every c, lut row c = W_qkv RMSNorm(x_c) and xlut row c = x_c.
+// Built once from the packed weights with the scratch-free fp32 projection.
+qt_status build_pred_lut(qt_ctx* ctx, hipStream_t s) {
+  const Dec &T = ctx->t, &P = ctx->p;
+  const int wd = ctx->cfg.weight_dtype;
+  const long C = ctx->cfg.codebook;
+  for (int st = 1; st < 15; ++st) {
+    HIPCK(launch_convert((const char*)ctx->pemb + (size_t)(st - 1) * C * T.H * esize(wd), wd, T.H, ctx->lut_stage,
+                         DT_F32, T.H, C, T.H, s));
+    LinearArgs a{};
+    a.wdtype = wd; a.M = (int)C; a.epi = EPI_STORE; a.eps = P.eps;
+    const float* x = ctx->lut_stage;
+    if (ctx->cfg.pred_in_proj) {
+      a.W = ctx->pproj; a.N = P.H; a.K = T.H; a.X = x; a.ldx = T.H;
+      a.Y = ctx->pxlut + (size_t)(st - 1) * C * P.H; a.ldy = P.H;
+      HIPCK(launch_linear(a, s));
+      x = a.Y;
+    }
+    a.W = ctx->pl[0].wqkv; a.N = P.qkv; a.K = P.H; a.X = x; a.ldx = P.H; a.gain = ctx->pl[0].attn_norm;
+    a.Y = ctx->plut + (size_t)(st - 1) * C * P.qkv; a.ldy = P.qkv;
+    HIPCK(launch_linear(a, s));
+  }
   return QT_OK;
 }
 
@@ -794,6 +839,9 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
   ctx->pemb = at<void>(ctx, L.pemb);
   ctx->phead = at<void>(ctx, L.phead);
   ctx->pproj = cfg->pred_in_proj ? at<void>(ctx, L.pproj) : nullptr;
+  ctx->plut = at<float>(ctx, L.plut);
+  ctx->pxlut = cfg->pred_in_proj ? at<float>(ctx, L.pxlut) : nullptr;
+  ctx->lut_stage = at<float>(ctx, L.lut_stage);
   ctx->cos_t = at<float>(ctx, L.cos_t); ctx->sin_t = at<float>(ctx, L.sin_t);
   ctx->cos_p = at<float>(ctx, L.cos_p); ctx->sin_p = at<float>(ctx, L.sin_p);
   ctx->kc_t = at<void>(ctx, L.kc_t); ctx->vc_t = at<void>(ctx, L.vc_t);
@@ -843,6 +891,10 @@ qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, 
             conv(w->pred_embeds, ctx->pemb, wd, 15 * C, T.H) && conv(w->pred_heads, ctx->phead, wd, 15 * C, P.H) &&
             (!cfg->pred_in_proj || conv(w->pred_in_proj, ctx->pproj, wd, P.H, T.H));
   if (!ok) { set_err(ctx->err, "weight repack launch failed"); return fail(QT_E_HIP); }
+  {
+    qt_status r = build_pred_lut(ctx, st);
+    if (r != QT_OK) return fail(r);
+  }
   std::vector<float> cs, sn;
   host_rope(cfg->max_positions, T.d, T.theta, cs, sn);
   if (hipMemcpyAsync(ctx->cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess ||

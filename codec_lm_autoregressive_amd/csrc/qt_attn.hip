@@ -1441,7 +1441,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 // also writes the new K/V rows.
 // Scores: lane = (key j, quarter of the head dims); P·V: lane = (8-dim
 // column chunk, key slot j mod 4).
-template <typename KVT, int NKV, int G, int RO, int NTOK>
+// SEL (steps 1..14, one token): the step's code is the greedy selection over
+// the previous head's logits (AttnArgs::sel; each wave takes the argmax of
+// its 256 logits, one LDS exchange combines them), the q/k/v values are that
+// code's row of the first layer's code-indexed table and the residual row
+// that code's input row; block 0 commits the code and the feedback sum.
+template <typename KVT, int NKV, int G, int RO, int NTOK, bool SEL = false>
 __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, LinearArgs o) {
   constexpr int D = 128, HALF = 64, NQ = NKV * G, KO = NQ * D;
   constexpr int EPC = 8;                       // 16-bit cache elements per 16-byte chunk
@@ -1449,6 +1454,8 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
   constexpr int KS = RO >= NKV ? 1 : NKV / RO; // waves sharing one o row (K split, RO < NKV)
   constexpr int KC = KO / 512 / KS;            // 16-byte weight chunks per lane and row
   static_assert(sizeof(KVT) == 2 && (RO % NKV == 0 || NKV % RO == 0) && KO % (512 * KS) == 0, "layout");
+  static_assert(!SEL || NTOK == 1, "a folded selection feeds one token");
+  constexpr int FPT = SEL ? 2048 / (NKV * 64) : 1;   // feedback elements per thread (tab_dim <= 2048)
   const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ks = KS > 1 ? g / RO : 0;          // this wave's K part of its row
   const int n0 = KS > 1 ? blockIdx.x * RO + g % RO : blockIdx.x * RO + g * RW;
@@ -1458,6 +1465,8 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
   __shared__ __align__(16) float knew[NKV][NTOK][D];
   __shared__ __align__(16) float vnew[NKV][NTOK][D];
   __shared__ __align__(16) float att[NTOK][KO];
+  __shared__ float selv[SEL ? NKV : 1];
+  __shared__ int seli[SEL ? NKV : 1], selb[SEL ? NKV : 1];
 
   // Loads leave in the order they are needed (the vector-memory counter
   // drains in issue order): this wave's q/k/v values, gains and rope rows,
@@ -1470,15 +1479,32 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
   const int sj = lane >> 2, sq = lane & 3;     // score role: key, quarter
   const int vch = lane & 15, vsl = lane >> 4;  // P·V role: column chunk, key slot
   float xin[NTOK][G + 2][2], cs[NTOK], sn[NTOK];
+  auto load_xin = [&](const float* base, long ld) {
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+      const float* src = base + (long)t * ld;
+#pragma unroll
+      for (int v = 0; v < G + 2; ++v) {
+        const float* x = src + (v < G ? (long)(g * G + v) * D : (long)(NQ + (v - G) * NKV) * D + (long)g * D);
+        xin[t][v][0] = x[lane];
+        xin[t][v][1] = x[lane + HALF];
+      }
+    }
+  };
+  // SEL: this wave's 256 logits and (block 0) the feedback row's old values
+  // go first; the q/k/v row waits for the code
+  f32x4 lgv = {};
+  float fbo[FPT];
+  if constexpr (SEL) {
+    lgv = *(const f32x4*)(p.sel.logits + min((g * 64 + lane) * 4, p.sel.V - 4));
+    if (blockIdx.x == 0)
+#pragma unroll
+      for (int e = 0; e < FPT; ++e) fbo[e] = p.sel.fb[min((int)threadIdx.x + e * NKV * 64, p.sel.tab_dim - 1)];
+  } else {
+    load_xin(p.qkv, p.ld_qkv);
+  }
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
-    const float* src = p.qkv + (long)t * p.ld_qkv;
-#pragma unroll
-    for (int v = 0; v < G + 2; ++v) {
-      const float* x = src + (v < G ? (long)(g * G + v) * D : (long)(NQ + (v - G) * NKV) * D + (long)g * D);
-      xin[t][v][0] = x[lane];
-      xin[t][v][1] = x[lane + HALF];
-    }
     cs[t] = p.cos[(long)(pos0 + t) * HALF + lane];
     sn[t] = p.sin[(long)(pos0 + t) * HALF + lane];
   }
@@ -1499,11 +1525,56 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
     for (int c = 0; c < KC; ++c) w[r][c] = ld_weight(W + (long)(n0 + r) * KO + (kc0 + c) * 512 + lane * 8);
   // the residual's old values, so that the epilogue has no dependent load
   float yold[NTOK][RW];
+  if constexpr (!SEL)
 #pragma unroll
-  for (int t = 0; t < NTOK; ++t)
+    for (int t = 0; t < NTOK; ++t)
 #pragma unroll
-    for (int r = 0; r < RW; ++r) yold[t][r] = o.Y[(long)t * o.ldy + n0 + r];
+      for (int r = 0; r < RW; ++r) yold[t][r] = o.Y[(long)t * o.ldy + n0 + r];
   __builtin_amdgcn_sched_barrier(0);
+  float tabv[FPT];
+  int code = 0;
+  if constexpr (SEL) {
+    // argmax, lowest id on ties: per wave the largest value (NaN ignored,
+    // flagged) and the lowest id holding it, then the waves in order
+    const int V = p.sel.V;
+    const float lq[4] = {lgv.x, lgv.y, lgv.z, lgv.w};
+    float lv[4];
+    int badl = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = (g * 64 + lane) * 4 + e < V;
+      badl |= in && (isnan(lq[e]) || lq[e] == INFINITY);
+      lv[e] = in ? lq[e] : -INFINITY;
+    }
+    const float wmax = wave_max(fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3])));
+    int ci = 0x7fffffff;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) ci = lv[e] == wmax ? (g * 64 + lane) * 4 + e : ci;
+    const int wi = wave_min_i(ci);
+    const int wbad = __any(badl);
+    if (lane == 0) { selv[g] = wmax; seli[g] = wi; selb[g] = wbad; }
+    __syncthreads();
+    float bv = selv[0];
+    int bi = seli[0], bad = selb[0];
+#pragma unroll
+    for (int w = 1; w < NKV; ++w) { better(bv, bi, selv[w], seli[w]); bad |= selb[w]; }
+    code = bad || bi >= V ? 0 : bi;
+    // the code's q/k/v row, residual values and (block 0) table row
+    load_xin(p.lut + (long)code * p.lut_ld, 0);
+    const uint16_t* trow = (const uint16_t*)p.sel.tab + (p.sel.tab_off + code) * (long)p.sel.tab_dim;
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      yold[0][r] = p.xlut ? p.xlut[(long)code * o.N + n0 + r] : bf16_to_f32(trow[n0 + r]);
+    if (blockIdx.x == 0) {
+#pragma unroll
+      for (int e = 0; e < FPT; ++e) tabv[e] = bf16_to_f32(trow[min((int)threadIdx.x + e * NKV * 64, p.sel.tab_dim - 1)]);
+      if (threadIdx.x == 0) {
+        p.sel.used[p.sel.col] = code;
+        if (p.sel.own) p.sel.own[p.sel.col] = code;
+        if (bad) atomicOr(p.sel.status, ST_NONFINITE);
+      }
+    }
+  }
 
   // new tokens: QK-RMSNorm and rope (lane owns the pair (lane, lane + 64))
 #pragma unroll
@@ -1672,6 +1743,14 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
         o.Y[(long)t * o.ldy + n0] = yold[t][0] + a;
       }
   }
+  if constexpr (SEL) {
+    if (blockIdx.x == 0)
+#pragma unroll
+      for (int e = 0; e < FPT; ++e) {
+        const int k = threadIdx.x + e * NKV * 64;
+        if (k < p.sel.tab_dim) p.sel.fb[k] = fbo[e] + tabv[e];
+      }
+  }
 }
 
 template <typename KVT>
@@ -1681,8 +1760,14 @@ static hipError_t launch_pred_attn_o_t(const AttnArgs& a, const LinearArgs& o, h
   // measured 2.081 ms against 2.085 with 8 rows per block (128 blocks); 16
   // rows per block (64 blocks) measured 0.6 us slower per launch than 8.
   constexpr int RO = 4;
-  hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
+  if (a.sel.logits) hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1, true>), dim3(o.N / RO), dim3(512), 0, s, a, o);
+  else hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   return hipGetLastError();
+}
+
+bool attention_oproj_sel_ok(int nq, int nkv, int d, int kvdtype, int wdtype, int V, int tab_dim) {
+  return nq == 16 && nkv == 8 && d == 128 && (kvdtype == DT_F16 || kvdtype == DT_BF16) && wdtype == DT_BF16 &&
+         V >= 4 && V <= 2048 && V % 4 == 0 && tab_dim >= 1 && tab_dim <= 2048;
 }
 
 hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStream_t s) {
@@ -1696,6 +1781,15 @@ hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStr
                   o.wdtype == DT_BF16 && o.K == a.nq * a.d && o.N % 8 == 0 && o.M == nt && o.epi == EPI_RESIDUAL &&
                   !o.gain && o.ldx == o.K && o.X == a.out && a.ld_out == o.K;
   if (!ok) return hipErrorNotSupported;
+  if (a.sel.logits) {
+    // a folded selection must run here: every pointer set, the table rows
+    // within the weight layout, the residual rows the o-projection's width
+    const SelFold& f = a.sel;
+    if (nt != 1 || !a.lut || a.lut_ld < (long)(a.nq + 2 * a.nkv) * a.d || !f.tab || !f.used || !f.fb || !f.status ||
+        f.tab_off < 0 || !attention_oproj_sel_ok(a.nq, a.nkv, a.d, a.kvdtype, o.wdtype, f.V, f.tab_dim) ||
+        (!a.xlut && f.tab_dim != o.N))
+      return hipErrorInvalidValue;
+  }
   if (a.kvdtype == DT_F16) return launch_pred_attn_o_t<_Float16>(a, o, s);
   return launch_pred_attn_o_t<uint16_t>(a, o, s);
 }

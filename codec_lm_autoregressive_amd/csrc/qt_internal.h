@@ -16,22 +16,6 @@ enum StatusBits : int { ST_NONFINITE = 1, ST_RANGE = 2 };
 // Y[m, :] (op)= W · norm(X[m, :]) for m < M.  W is [N, K] row-major
 // (nn.Linear layout), f32 or bf16; X, Y fp32.  With EPI_SWIGLU the rows of W
 // come in (gate j, up j) pairs and Y[m, j] = silu(gate) * up.
-// Greedy selection folded into a register GEMV's prologue (one activation
-// row): instead of reading X, the kernel takes the argmax (lowest id on ties)
-// of `logits` (V <= 2048 floats, 16-byte aligned) and uses row
-// tab_off + argmax of `tab` ([rows, K], weight dtype) as its activation row.
-// The waves of block 0 that span K also commit the code (used / own at
-// column col, row stride code_ld), store the row to x (fp32, nullable) and
-// add it to fb; a NaN or +inf logit sets ST_NONFINITE in status and takes
-// code 0, as the selection kernel does.
-struct SelFold {
-  const float* logits; int V;
-  const void* tab; long tab_off;
-  int* used; int* own; int code_ld; int col;
-  float* x; float* fb;
-  int* status;
-};
-
 struct LinearArgs {
   const void* W; int wdtype; int N; int K;
   const float* X; long ldx; int M;
@@ -52,16 +36,12 @@ struct LinearArgs {
   // residual add), writes y + sin(snake_alpha[col] y)^2 / snake_bden[col]
   // to Y, or y to Y and that value to Y2 (row stride ldy2) when Y2 is set.
   const float* snake_alpha; const float* snake_bden; float* Y2; long ldy2;
-  SelFold sel;                         // folded greedy selection (sel.logits != nullptr; M = 1)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 // K ranges the launch of a would split into (partial sums in a.part: range z,
 // row m, column n at part[(z * M + m) * N + n]; with a gain the row sums of
 // squares follow at part[Z * M * N + z * M + m]); 1 when it writes Y directly.
 int linear_split_ranges(const LinearArgs& a);
-// Whether a projection can take a folded greedy selection (a.sel): one
-// row on the register GEMV path, V <= 2048 and a multiple of 4, aligned rows.
-bool linear_sel_fits(const LinearArgs& a);
 
 // One contiguous run of tokens of one batch row: row, first token (row of the
 // activation arrays), token count, first position (before pos_base / row_pos).
@@ -70,6 +50,20 @@ struct Run { int row, tok0, ntok, pos0; };
 // Per-head QK-RMSNorm + rope of q and k, K/V write into the cache, then causal
 // GQA attention of every token of the run over cached positions <= its own.
 enum AttnMode { ATT_WRITE_ATTEND = 0, ATT_WRITE = 1, ATT_ATTEND = 2 };
+// Greedy selection folded into the code predictor's fused attention +
+// o-projection at batch 1: the argmax (lowest id on ties) of `logits` (V <=
+// 2048 floats) picks the step's code; the first block commits it (used /
+// own at column col), adds row tab_off + code of `tab` ([rows, tab_dim],
+// weight dtype) to the feedback row fb, and sets ST_NONFINITE in status on a
+// NaN or +inf logit (code 0 then), as the selection kernel does.
+struct SelFold {
+  const float* logits; int V;
+  const void* tab; long tab_off; int tab_dim;
+  int* used; int* own; int col;
+  float* fb;
+  int* status;
+};
+
 struct AttnArgs {
   int mode;
   int single_token;                    // run i is token i of row i, at position pos_base + row_pos[i]
@@ -100,6 +94,12 @@ struct AttnArgs {
   // prefill attend pass (ATT_ATTEND) over runs of at most max_ntok tokens
   // (1 .. kAttnTileTokens) on the matrix cores; 0: the per-token kernel
   int max_ntok;
+  // code predictor steps 1..14 at batch 1 (fused attention + o-projection
+  // only): the first layer's q/k/v are row `code` of lut (row stride lut_ld,
+  // the q/k/v layout) and the residual row is row `code` of xlut (fp32) or,
+  // without xlut, of sel.tab; the code comes from the folded selection sel
+  const float* lut; long lut_ld; const float* xlut;
+  SelFold sel;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Whether the prefill attend pass has the tiled matrix-core kernel for this
@@ -111,6 +111,10 @@ bool attn_prefill_tiles(int d, int nq, int nkv, int kvdtype);
 // weights, 16-bit cache). Returns hipErrorNotSupported, doing nothing, for
 // other shapes.
 hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStream_t s);
+// Whether launch_attention_oproj takes a folded selection (a.sel) for a code
+// predictor of these dimensions: nq 16, nkv 8, head_dim 128, 16-bit cache,
+// bf16 weights, V <= 2048 and a multiple of 4, tab_dim <= 2048.
+bool attention_oproj_sel_ok(int nq, int nkv, int d, int kvdtype, int wdtype, int V, int tab_dim);
 
 // Per-request settings kept in device memory, so that one captured frame
 // graph serves every request of the same batch size.
@@ -182,6 +186,11 @@ hipError_t launch_frame_start(const FrameStartArgs& a, hipStream_t s);
 hipError_t launch_frame_advance(int* frame_k, int* pos, const int* finished, int B, hipStream_t s);
 
 // Row gather / scatter copies dst[i] = src[idx[i]] (fp32 rows of width n).
+// Rows of code-indexed tables: for each of the B rows, code = codes[r *
+// code_ld] (clamped to 0 .. C - 1), qkv row r = lut row code (n floats) and,
+// with xlut, x row r = xlut row code (nx floats).
+hipError_t launch_lut_rows(const int* codes, int code_ld, int B, int C, const float* lut, int n, float* qkv,
+                           long ld_qkv, const float* xlut, int nx, float* x, long ldx, hipStream_t s);
 hipError_t launch_copy_rows(const float* src, long ld_src, const int* idx, int count,
                             float* dst, long ld_dst, int n, hipStream_t s);
 

@@ -163,15 +163,11 @@ __global__ __launch_bounds__(NT) void linear_kernel(LinearArgs p) {
 // activation chunks go out in one batch (addresses clamped, no divergent
 // loads), the RMSNorm sum of squares comes from a wave reduction (plus one
 // LDS exchange between the KS waves of a row group), and no activation tile
-// is staged in LDS. SEL: the activation row is a table row picked by a
-// folded greedy selection (LinearArgs::sel); every wave takes the argmax
-// itself while its weight rows are in flight.
-template <typename WT, int R, int MT, int KS, int NC, bool SEL = false>
+// is staged in LDS.
+template <typename WT, int R, int MT, int KS, int NC>
 __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
   constexpr int EPC = 16 / sizeof(WT);
   constexpr int RG = 4 / KS;
-  constexpr int SQ = 8;                  // logit quads per lane (V <= 2048)
-  static_assert(!SEL || MT == 1, "a folded selection feeds one activation row");
   __shared__ float red[4][MT];
   __shared__ float part[4][R][MT];
   const int K = p.K, N = p.N;
@@ -187,34 +183,14 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
   bool kin[NC];
   // Activations and gains first, weights last: the vector-memory counter
   // drains in issue order, so the RMSNorm below waits only for the small
-  // activation loads while the weight rows are still in flight. SEL: the
-  // logits instead of the activations, and the feedback row's old values for
-  // the committing waves.
-  f32x4 lgv[SEL ? SQ : 1];
-  float fbo[SEL ? NC : 1][EPC];
-  const bool commit = SEL && blockIdx.x == 0 && wrow == 0;
-  if constexpr (SEL) {
-#pragma unroll
-    for (int q = 0; q < SQ; ++q) lgv[q] = *(const f32x4*)(p.sel.logits + min((q * 64 + lane) * 4, p.sel.V - 4));
-    if (commit)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
-        const int kc = k0 < K ? k0 : K - EPC;
-#pragma unroll
-        for (int e = 0; e < EPC; e += 4) {
-          const f32x4 v = *(const f32x4*)(p.sel.fb + kc + e);
-          fbo[c][e] = v.x; fbo[c][e + 1] = v.y; fbo[c][e + 2] = v.z; fbo[c][e + 3] = v.w;
-        }
-      }
-  }
+  // activation loads while the weight rows are still in flight.
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
     kin[c] = k0 < K;
     const int kc = kin[c] ? k0 : K - EPC;
 #pragma unroll
-    for (int m = 0; m < (SEL ? 0 : MT); ++m) {
+    for (int m = 0; m < MT; ++m) {
       const float* xr = p.X + (long)(m0 + min(m, mt - 1)) * p.ldx + kc;
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
@@ -250,73 +226,6 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (SEL) {
-    // argmax over the logits, lowest id on ties: the largest value (NaN
-    // ignored, flagged), then the lowest id holding it, each a register tree
-    // and one DPP wave reduction; then the chosen table row in the
-    // activation layout
-    const int V = p.sel.V;
-    constexpr int NV = SQ * 4;
-    float lv[NV], tv[NV];
-    int badl = 0;
-#pragma unroll
-    for (int q = 0; q < SQ; ++q) {
-      const float lq[4] = {lgv[q].x, lgv[q].y, lgv[q].z, lgv[q].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool in = (q * 64 + lane) * 4 + e < V;
-        badl |= in && (isnan(lq[e]) || lq[e] == INFINITY);
-        lv[q * 4 + e] = in ? lq[e] : -INFINITY;
-        tv[q * 4 + e] = lv[q * 4 + e];
-      }
-    }
-#pragma unroll
-    for (int w = NV / 2; w >= 1; w >>= 1)
-#pragma unroll
-      for (int j = 0; j < w; ++j) tv[j] = fmaxf(tv[j], tv[j + w]);
-    const float gmax = wave_max(tv[0]);
-    int ci[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) ci[j] = lv[j] == gmax ? ((j >> 2) * 64 + lane) * 4 + (j & 3) : 0x7fffffff;
-#pragma unroll
-    for (int w = NV / 2; w >= 1; w >>= 1)
-#pragma unroll
-      for (int j = 0; j < w; ++j) ci[j] = min(ci[j], ci[j + w]);
-    const int bi = wave_min_i(ci[0]);
-    const bool bad = __any(badl);
-    const int code = bad || bi >= V ? 0 : bi;
-    const WT* tr = (const WT*)p.sel.tab + (p.sel.tab_off + code) * (long)K;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
-      const int kc = kin[c] ? k0 : K - EPC;
-      const u32x4 t = *(const u32x4*)(tr + kc);
-      if constexpr (EPC == 8) {
-        x[c][0][0] = bf_lo(t.x); x[c][0][1] = bf_hi(t.x); x[c][0][2] = bf_lo(t.y); x[c][0][3] = bf_hi(t.y);
-        x[c][0][4] = bf_lo(t.z); x[c][0][5] = bf_hi(t.z); x[c][0][6] = bf_lo(t.w); x[c][0][7] = bf_hi(t.w);
-      } else {
-        x[c][0][0] = __uint_as_float(t.x); x[c][0][1] = __uint_as_float(t.y);
-        x[c][0][2] = __uint_as_float(t.z); x[c][0][3] = __uint_as_float(t.w);
-      }
-    }
-    if (commit) {
-      if (ks == 0 && lane == 0) {
-        p.sel.used[p.sel.col] = code;
-        if (p.sel.own) p.sel.own[p.sel.col] = code;
-        if (bad) atomicOr(p.sel.status, ST_NONFINITE);
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int k0 = ((c * KS + ks) * 64 + lane) * EPC;
-        if (kin[c])
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            if (p.sel.x) p.sel.x[k0 + e] = x[c][0][e];
-            p.sel.fb[k0 + e] = fbo[c][e] + x[c][0][e];
-          }
-      }
-    }
-  }
   if (p.gain) {
     float ss[MT];
 #pragma unroll
@@ -433,28 +342,28 @@ __global__ __launch_bounds__(NT) void gemv_kernel(LinearArgs p) {
   }
 }
 
-template <typename WT, int R, int MT, int KS, int NC, bool SEL>
+template <typename WT, int R, int MT, int KS, int NC>
 static hipError_t launch_gemv_t(const LinearArgs& a, hipStream_t s) {
   constexpr int RG = 4 / KS;
   dim3 grid((a.N + RG * R - 1) / (RG * R), (a.M + MT - 1) / MT);
-  hipLaunchKernelGGL((gemv_kernel<WT, R, MT, KS, NC, SEL>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gemv_kernel<WT, R, MT, KS, NC>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename WT, int R, int MT, int KS, bool SEL>
+template <typename WT, int R, int MT, int KS>
 static hipError_t launch_gemv_nc(const LinearArgs& a, int nc, hipStream_t s) {
   switch (nc) {
-    case 1: return launch_gemv_t<WT, R, MT, KS, 1, SEL>(a, s);
-    case 2: return launch_gemv_t<WT, R, MT, KS, 2, SEL>(a, s);
-    case 3: return launch_gemv_t<WT, R, MT, KS, 3, SEL>(a, s);
-    default: return launch_gemv_t<WT, R, MT, KS, 4, SEL>(a, s);
+    case 1: return launch_gemv_t<WT, R, MT, KS, 1>(a, s);
+    case 2: return launch_gemv_t<WT, R, MT, KS, 2>(a, s);
+    case 3: return launch_gemv_t<WT, R, MT, KS, 3>(a, s);
+    default: return launch_gemv_t<WT, R, MT, KS, 4>(a, s);
   }
 }
-template <typename WT, int R, int MT, bool SEL = false>
+template <typename WT, int R, int MT>
 static hipError_t launch_gemv_ks(const LinearArgs& a, int ks, int nc, hipStream_t s) {
-  if (ks == 4) return launch_gemv_nc<WT, R, MT, 4, SEL>(a, nc, s);
-  if (ks == 2) return launch_gemv_nc<WT, R, MT, 2, SEL>(a, nc, s);
-  return launch_gemv_nc<WT, R, MT, 1, SEL>(a, nc, s);
+  if (ks == 4) return launch_gemv_nc<WT, R, MT, 4>(a, nc, s);
+  if (ks == 2) return launch_gemv_nc<WT, R, MT, 2>(a, nc, s);
+  return launch_gemv_nc<WT, R, MT, 1>(a, nc, s);
 }
 
 // Register path when the batch is small and K fits in <= 4 chunks per lane.
@@ -466,13 +375,6 @@ static bool gemv_fits(const LinearArgs& a) {
   int ks = 1;
   while (ks < 4 && a.N / (4 / ks * R) < min_blocks) ks *= 2;
   return (a.K + ks * 64 * epc - 1) / (ks * 64 * epc) <= 4;
-}
-
-bool linear_sel_fits(const LinearArgs& a) {
-  const SelFold& f = a.sel;
-  const bool al = ((uintptr_t)f.logits % 16) == 0 && ((uintptr_t)f.tab % 16) == 0 && ((uintptr_t)f.fb % 16) == 0;
-  return a.M == 1 && a.conv_taps == 0 && !a.snake_alpha && !a.norm_out && gemv_fits(a) && f.logits && f.tab &&
-         f.used && f.fb && f.status && al && f.V >= 4 && f.V <= 2048 && f.V % 4 == 0 && f.tab_off >= 0;
 }
 
 template <typename WT>
@@ -490,8 +392,7 @@ static bool try_gemv(const LinearArgs& a, hipStream_t s, hipError_t* err) {
   const int nc = (a.K + per - 1) / per;
   if (nc > 4) return false;
   // both activation rows in one block: the weights stream once
-  if (a.sel.logits) *err = R == 2 ? launch_gemv_ks<WT, 2, 1, true>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 1, true>(a, ks, nc, s);
-  else if (a.M == 1) *err = R == 2 ? launch_gemv_ks<WT, 2, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 1>(a, ks, nc, s);
+  if (a.M == 1) *err = R == 2 ? launch_gemv_ks<WT, 2, 1>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 1>(a, ks, nc, s);
   else *err = R == 2 ? launch_gemv_ks<WT, 2, 2>(a, ks, nc, s) : launch_gemv_ks<WT, 1, 2>(a, ks, nc, s);
   return true;
 }
@@ -2064,7 +1965,6 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
     return launch_gemm_split(a, s);
   }
   if (a.snake_alpha) return hipErrorInvalidValue;
-  if (a.sel.logits && !linear_sel_fits(a)) return hipErrorInvalidValue;
   // one or two rows: register GEMV, the weights streamed once with fp32 FMA
   {
     hipError_t e = hipSuccess;

@@ -569,6 +569,30 @@ hipError_t launch_frame_advance(int* frame_k, int* pos, const int* finished, int
   return hipGetLastError();
 }
 
+// One block per batch row: the row's first-layer q/k/v (and projected
+// input) rows from the code-indexed tables, 16-byte copies.
+__global__ __launch_bounds__(NT) void lut_rows_kernel(const int* codes, int code_ld, int C, const float* lut, int n,
+                                                      float* qkv, long ld_qkv, const float* xlut, int nx, float* x,
+                                                      long ldx) {
+  const int r = blockIdx.x;
+  const int code = min(max(codes[(long)r * code_ld], 0), C - 1);
+  const f32x4* src = (const f32x4*)(lut + (long)code * n);
+  f32x4* dst = (f32x4*)(qkv + (long)r * ld_qkv);
+  for (int i = threadIdx.x; i < n / 4; i += NT) dst[i] = src[i];
+  if (xlut) {
+    const f32x4* xs = (const f32x4*)(xlut + (long)code * nx);
+    f32x4* xd = (f32x4*)(x + (long)r * ldx);
+    for (int i = threadIdx.x; i < nx / 4; i += NT) xd[i] = xs[i];
+  }
+}
+hipError_t launch_lut_rows(const int* codes, int code_ld, int B, int C, const float* lut, int n, float* qkv,
+                           long ld_qkv, const float* xlut, int nx, float* x, long ldx, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (C < 1 || n % 4 || ld_qkv % 4 || (xlut && (nx % 4 || ldx % 4))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lut_rows_kernel, dim3(B), dim3(NT), 0, s, codes, code_ld, C, lut, n, qkv, ld_qkv, xlut, nx, x, ldx);
+  return hipGetLastError();
+}
+
 __global__ void copy_rows_kernel(const float* src, long ld_src, const int* idx, float* dst, long ld_dst, int n) {
   const int i = blockIdx.x;
   const float* s = src + (long)idx[i] * ld_src;

@@ -85,8 +85,10 @@ def test_workspace_bytes():
     n = binding.workspace_bytes(cfg06())
     # packed bf16 weights alone: 33 layers of 15.73 M params + tables and heads
     params = 33 * (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) + 2 * 3072 * 1024 + 2 * 15 * 2048 * 1024
-    assert n >= 2 * params
-    assert n < 2 * params + (1 << 30)
+    # the predictor's code-indexed first-layer q/k/v tables: 14 steps x 2048 codes x 4096 fp32
+    lut = 14 * 2048 * 4096 * 4
+    assert n >= 2 * params + lut
+    assert n < 2 * params + lut + (1 << 30)
     # KV grows linearly with max_batch * max_positions
     n2 = binding.workspace_bytes(cfg06(max_batch=2))
     kv_row = 28 * 8 * 160 * 128 * 2 * 2
