@@ -447,10 +447,14 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
 // prefill: tiles (n_tiles > 0) are the runs of up to kAttnTileTokens tokens
 // the attend pass takes instead of one run per token.
 // A code predictor step's input from the code-indexed tables of the first
-// layer: q/k/v rows (row stride lut_ld) and, with the input projection, the
-// projected rows; sel: the step's greedy selection is folded into the
-// attention (batch 1), else the rows were gathered by code beforehand.
-struct StepIn { const float* lut; long lut_ld; const float* xlut; const SelFold* sel; };
+// layer: q/k/v rows (row stride lut_ld, `rows` codes) and, with the input
+// projection, the projected rows. sel: the step's greedy selection is folded
+// into the attention (batch 1); else the codes are codes[r * code_ld] and
+// the attention reads the table rows itself or they are gathered first.
+struct StepIn {
+  const float* lut; long lut_ld; const float* xlut; const SelFold* sel;
+  const int* codes; int code_ld; int rows;
+};
 
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
                      int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false,
@@ -519,6 +523,15 @@ qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs,
       t.single_token = single_token;
       t.rope_rows = (single_token && talker) ? ctx->rope_rows : nullptr;
       if (single_token && talker) { t.kv_split = kv_split_for(n_runs, d.nkv); t.split_buf = ctx->ksplit; }
+    }
+    if (from_lut && !in->sel) {
+      if (!in->xlut && attention_reads_lut(t)) {
+        t.lut = in->lut; t.lut_ld = in->lut_ld;
+        t.lut_codes = in->codes; t.lut_code_ld = in->code_ld; t.lut_rows = in->rows;
+      } else {
+        HIPCK(launch_lut_rows(in->codes, in->code_ld, M, in->rows, in->lut, (int)in->lut_ld, ctx->qkv, d.qkv, in->xlut,
+                              d.H, x, d.H, s));
+      }
     }
     if (!prefill) {
       // the code predictor at one row: attention and o-projection in one launch
@@ -627,9 +640,7 @@ qt_status enqueue_frame(qt_ctx* ctx, hipStream_t s, const int* forced) {
       const float* lut = ctx->plut + (size_t)(st - 1) * C * P.qkv;
       const float* xlut = proj ? ctx->pxlut + (size_t)(st - 1) * C * P.H : nullptr;
       const SelFold sf = fold ? pred_sel_fold(ctx, st) : SelFold{};
-      if (!fold)
-        HIPCK(launch_lut_rows(codes + st, kGroups, B, C, lut, P.qkv, ctx->qkv, P.qkv, xlut, P.H, ctx->x_p, P.H, s));
-      const StepIn in{lut, (long)P.qkv, xlut, fold ? &sf : nullptr};
+      const StepIn in{lut, (long)P.qkv, xlut, fold ? &sf : nullptr, codes + st, kGroups, C};
       QTCK(run_layers(ctx, false, ctx->x_p, M, runs_step, B, nullptr, st + 1, s, false, true, false, nullptr, 0, &in));
     }
     // head st on the last token of each row

@@ -901,8 +901,11 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) vr[j] = *(const uint32_t*)(vc + (long)min(j, last) * D + 2 * lane);
   }
-  // q/k/v of the new token: the projection's rows, or its split-K partial sums
+  // q/k/v of the new token: the projection's rows, its split-K partial sums,
+  // or the row of the code-indexed table that the row's code selects
   const long ar = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  const float* qrow = p.qkv + ar * p.ld_qkv;
+  if (p.lut_codes) qrow = p.lut + (long)min(max(p.lut_codes[(long)row * p.lut_code_ld], 0), p.lut_rows - 1) * p.lut_ld;
   // up to PZ ranges with every load issued before the first add (ranges past
   // part_z are clamped loads that are not added); more ranges: a loop
   constexpr int PZ = 8;
@@ -923,7 +926,7 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
     prs = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
   }
   auto qkv_at = [&](long col) -> float {
-    if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
+    if (p.part_z <= 0) return qrow[col];
     float v;
     if (pz_fast) {
       float q[PZ];
@@ -1339,8 +1342,7 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
       if (a.max_ntok > FA_TOK) return hipErrorInvalidValue;
       return launch_attn_prefill_mfma<KVT, G>(a, s);
     }
-    if (a.single_token && a.mode == ATT_WRITE_ATTEND && (a.ntok <= 1) && a.max_pos <= 16 && a.n_runs > 1 &&
-        a.ld_out % 2 == 0) {
+    if (attention_reads_lut(a)) {
       hipLaunchKernelGGL((attn_short_kernel<KVT, G>), dim3(a.nkv, a.n_runs), dim3((G + 2) * 64), 0, s, a);
       return hipGetLastError();
     }
@@ -1763,6 +1765,11 @@ static hipError_t launch_pred_attn_o_t(const AttnArgs& a, const LinearArgs& o, h
   if (a.sel.logits) hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1, true>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   else hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   return hipGetLastError();
+}
+
+bool attention_reads_lut(const AttnArgs& a) {
+  return a.d == 128 && a.nq == 2 * a.nkv && (a.kvdtype == DT_F16 || a.kvdtype == DT_BF16) && a.single_token &&
+         a.mode == ATT_WRITE_ATTEND && a.ntok <= 1 && a.max_pos <= 16 && a.n_runs > 1 && a.ld_out % 2 == 0;
 }
 
 bool attention_oproj_sel_ok(int nq, int nkv, int d, int kvdtype, int wdtype, int V, int tab_dim) {

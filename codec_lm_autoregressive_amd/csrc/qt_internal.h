@@ -100,6 +100,10 @@ struct AttnArgs {
   // without xlut, of sel.tab; the code comes from the folded selection sel
   const float* lut; long lut_ld; const float* xlut;
   SelFold sel;
+  // code predictor steps at batch rows > 1 (attention_reads_lut): row r's
+  // q/k/v are row lut_codes[r * lut_code_ld] (clamped to 0 .. lut_rows - 1)
+  // of lut instead of the projection's output
+  const int* lut_codes; int lut_code_ld; int lut_rows;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Whether the prefill attend pass has the tiled matrix-core kernel for this
@@ -115,6 +119,9 @@ hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStr
 // predictor of these dimensions: nq 16, nkv 8, head_dim 128, 16-bit cache,
 // bf16 weights, V <= 2048 and a multiple of 4, tab_dim <= 2048.
 bool attention_oproj_sel_ok(int nq, int nkv, int d, int kvdtype, int wdtype, int V, int tab_dim);
+// Whether launch_attention serves a (single-token decode) with the kernel
+// that reads q/k/v rows from a code-indexed table (AttnArgs::lut_codes).
+bool attention_reads_lut(const AttnArgs& a);
 
 // Per-request settings kept in device memory, so that one captured frame
 // graph serves every request of the same batch size.
