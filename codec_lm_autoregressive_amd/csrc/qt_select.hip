@@ -80,7 +80,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   int* sid = (int*)(sp + V);             // [V]
   __shared__ float redf[8];
   __shared__ int redi[8];
-  __shared__ __align__(16) int hist[NT / 64 * 256];
+  __shared__ __align__(16) int hist[2][NT / 64 * 256];
+  __shared__ __align__(16) float nzs[64];
   __shared__ int scan[NT];
   __shared__ int sh_int[4];
   __shared__ float sh_f[2];
@@ -206,23 +207,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       for (int q = 0; q < MPT; ++q) pv[q] = tid + q * NT < V ? lv[q] / temperature : -INFINITY;
       if (top_k > 0 && top_k < V) {
         // radix select of the k-th largest value, 8 bits at a time from the top;
-        // per-wave histograms, then a parallel suffix count finds the digit
+        // per-wave histograms, then a parallel suffix count finds the digit.
+        // Two histogram buffers: a pass clears the next pass's one, so a pass
+        // costs three barriers.
         uint32_t prefix = 0, mask = 0;
         int kk = top_k;
         const int lane = tid & 63, wv = tid >> 6;
-        for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-          for (int q = 0; q < NT / 64; ++q) hist[q * 256 + tid] = 0;
-          __syncthreads();
+        for (int q = 0; q < NT / 64; ++q) hist[0][q * 256 + tid] = 0;
+        __syncthreads();
+        for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
+          int* hb = hist[pass & 1];
 #pragma unroll
           for (int q = 0; q < MPT; ++q) {
             const uint32_t key = ord_key(pv[q]);
-            if (tid + q * NT < V && (key & mask) == prefix) atomicAdd(&hist[wv * 256 + ((key >> shift) & 255u)], 1);
+            if (tid + q * NT < V && (key & mask) == prefix) atomicAdd(&hb[wv * 256 + ((key >> shift) & 255u)], 1);
           }
+#pragma unroll
+          for (int q = 0; q < NT / 64; ++q) hist[(pass + 1) & 1][q * 256 + tid] = 0;
           __syncthreads();
           int h = 0;   // count of digit tid
 #pragma unroll
-          for (int q = 0; q < NT / 64; ++q) h += hist[q * 256 + tid];
+          for (int q = 0; q < NT / 64; ++q) h += hb[q * 256 + tid];
           int sfx = h;   // inclusive suffix count over digits >= tid, within the wave
 #pragma unroll
           for (int o = 1; o < 64; o <<= 1) {
@@ -238,10 +244,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
             sh_int[1] = kk - above;
           }
           __syncthreads();
+          // (sh_int and scan are rewritten only after the next pass's first barrier)
           prefix |= ((uint32_t)sh_int[0]) << shift;
           mask |= 255u << shift;
           kk = sh_int[1];
-          __syncthreads();
         }
         const float tau = key_float(prefix);
 #pragma unroll
@@ -281,57 +287,52 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __syncthreads();
     const int nsv = sh_int[2];
     if (nsv <= 64) {
+      // wave 0 ranks the survivors and finds the top-p cut while wave 1 draws
+      // their noise; then wave 0 runs the race
+      int rank = 0, keep = nsv;
+      const int lane = tid & 63;
+      const float pp = lane < nsv ? tp_list[lane] : -1.f;
+      const int id = lane < nsv ? tid_list[lane] : 0x7fffffff;
       if (tid < 64) {
-        const int lane = tid;
-        const float pp = lane < nsv ? tp_list[lane] : -1.f;
-        const int id = lane < nsv ? tid_list[lane] : 0x7fffffff;
-        // rank in (p desc, id asc) order: every lane against every survivor,
-        // broadcast with lane reads, 4 survivors per step (padding lanes hold
-        // p = -1 and never rank above a survivor)
-        int rank = 0;
-        for (int j0 = 0; j0 < nsv; j0 += 4) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int j = min(j0 + u, 63);
-            const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), j));
-            const int ij = __builtin_amdgcn_readlane(id, j);
-            // bitwise, not short-circuit: no branch per compare
-            rank += (int)((j0 + u < nsv) & ((pj > pp) | ((pj == pp) & (ij < id))));
-          }
+        // rank in (p desc, id asc) order against every survivor, read as LDS
+        // broadcasts (padding lanes hold p = -1 and rank after every survivor)
+#pragma unroll 8
+        for (int j = 0; j < nsv; ++j) {
+          const float pj = tp_list[j];
+          const int ij = tid_list[j];
+          rank += (int)((pj > pp) | ((pj == pp) & (ij < id)));
         }
-        // sequential fp32 running sum in that order, 4 ranks per step: the
-        // survivor of rank r is the lane whose rank is r
-        int keep = nsv;
+        // the sequential fp32 running sum in rank order, the same in every lane
         if (top_p < 1.0f) {
+          float* srt = sp;                    // p in rank order
+          if (lane < nsv) srt[rank] = pp;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          float v[64];
+#pragma unroll
+          for (int c = 0; c < 64; ++c) v[c] = c < nsv ? srt[c] : 0.f;
           float cs = 0.f;
           bool found = false;
-          for (int r0 = 0; r0 < nsv && !found; r0 += 4) {
-            float v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const unsigned long long bm = __ballot(rank == r0 + u);
-              const int src = bm ? __ffsll(bm) - 1 : 0;
-              v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), src));
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const bool act = !found & (r0 + u < nsv);
-              cs = act ? cs + v[u] : cs;
-              const bool hit = act & (cs >= top_p);
-              keep = hit ? r0 + u + 1 : keep;
-              found = found | hit;
-            }
+          for (int r0 = 0; r0 < 64; ++r0) {
+            const bool act = !found & (r0 < nsv);
+            cs = act ? cs + v[r0] : cs;
+            const bool hit = act & (cs >= top_p);
+            keep = hit ? r0 + 1 : keep;
+            found = found | hit;
           }
         }
-        float sc = -INFINITY;
-        int bi = 0x7fffffff;
-        if (lane < nsv && rank < keep) {
-          const float e = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, nrow, a.stream, jsel, id);
-          sc = pp / e;
-          bi = id;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) better(sc, bi, __shfl_xor(sc, o), __shfl_xor(bi, o));
+      } else if (tid < 128 && lane < nsv) {
+        nzs[lane] = a.noise_in ? a.noise_in[(long)r * V + id] : exp_noise(seed, nrow, a.stream, jsel, id);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // the race: largest p / E over the kept survivors, lowest id on ties
+        const bool kept = lane < nsv && rank < keep;
+        const float sc = kept ? pp / nzs[lane] : -INFINITY;
+        const float smax = wave_max(sc);
+        const int bi = wave_min_i(kept && sc == smax ? id : 0x7fffffff);
         if (lane == 0) sh_int[2] = bi < V ? bi : 0;
       }
       __syncthreads();
