@@ -53,10 +53,10 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 #    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
 COUNTED = {
     "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
-    "frame": {"src_sha256_16": "d7ba8ba7520e5fbd", "bytes_per_frame": {
+    "frame": {"src_sha256_16": "dcc600d9de789b20", "bytes_per_frame": {
         # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
-        "qwen06b_bf16_b1": (3422800000, 35.5, 3313377280),
-        "qwen06b_bf16_b64_sampling": (11353800000, 339.9, 5804343296),
+        "qwen06b_bf16_b1": (3304700000, 35.5, 3196166144),
+        "qwen06b_bf16_b64_sampling": (11101500000, 339.9, 5701422285),
     }},
 }
 CSRC = os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc")
@@ -104,8 +104,11 @@ def frame_bytes(dm, B, mean_ctx, wbytes=2, kvbytes=2, unique=False):
     Streamed model (default): each forward pass reads its layer weights once:
     the talker once, the predictor 15 times (2-token prefill + 14 steps), one
     predictor head per step and the talker codec head; the talker KV cache is
-    read once per step (mean context mean_ctx positions per row). Unique model:
-    the predictor's layer weights are counted once per frame (the floor if a
+    read once per step (mean context mean_ctx positions per row). The 14
+    single-token steps take their first layer's q/k/v (and the 1.7B-class
+    input projection's output) from code-indexed fp32 tables, so they read
+    one table row per batch row instead of those weights. Unique model: the
+    predictor's layer weights are counted once per frame (the floor if a
     cache holds them across the 15 passes). Gathers of single embedding rows
     are negligible and left out.
     """
@@ -116,12 +119,16 @@ def frame_bytes(dm, B, mean_ctx, wbytes=2, kvbytes=2, unique=False):
         return qkv + o + mlp
     t, p = dm["talker"], dm["predictor"]
     talker = t["layers"] * layer_params(t) + dm["talker_vocab"] * t["hidden"]
+    qkv_dim = (p["n_heads"] + 2 * p["n_kv_heads"]) * p["head_dim"]
     passes = 1 if unique else 15
     pred = passes * (p["layers"] * layer_params(p)) + 15 * dm["codebook"] * p["hidden"]
+    if not unique:
+        pred -= 14 * qkv_dim * p["hidden"]          # steps 1..14: first-layer q/k/v from the tables
     if dm["pred_in_proj"]:
-        pred += passes * p["hidden"] * t["hidden"]
+        pred += p["hidden"] * t["hidden"]             # the input projection runs in the 2-token pass only
+    table_rows = 14 * B * (qkv_dim + (p["hidden"] if dm["pred_in_proj"] else 0)) * 4
     kv = B * mean_ctx * t["layers"] * 2 * t["n_kv_heads"] * t["head_dim"] * kvbytes
-    return (talker + pred) * wbytes + kv
+    return (talker + pred) * wbytes + kv + table_rows
 
 
 def parse():
@@ -320,6 +327,17 @@ def main():
     del main_wl
     torch.cuda.empty_cache()
 
+    # the decoder, frontend and serving measurements run before the larger
+    # batch workloads, on a device heap that has seen only the main workload
+    extra = {}
+    if not args.no_next:
+        extra["codec"] = codec_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+        extra["frontend"] = frontend_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+        extra["serving"] = serving_timing(torch, binding, synth)
+        torch.cuda.empty_cache()
+
     batches = []
     for name in [x for x in args.batches.split(",") if x]:
         x = Workload(torch, binding, synth, name)
@@ -338,15 +356,6 @@ def main():
                         "config": x.config(q["total_frames"], 1)})
         x.eng.close()
         del x
-        torch.cuda.empty_cache()
-
-    extra = {}
-    if not args.no_next:
-        extra["codec"] = codec_timing(torch, binding, synth)
-        torch.cuda.empty_cache()
-        extra["frontend"] = frontend_timing(torch, binding, synth)
-        torch.cuda.empty_cache()
-        extra["serving"] = serving_timing(torch, binding, synth)
         torch.cuda.empty_cache()
 
     cpu = None
