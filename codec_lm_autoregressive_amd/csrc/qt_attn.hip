@@ -1762,7 +1762,8 @@ static hipError_t launch_pred_attn_o_t(const AttnArgs& a, const LinearArgs& o, h
   // measured 2.081 ms against 2.085 with 8 rows per block (128 blocks); 16
   // rows per block (64 blocks) measured 0.6 us slower per launch than 8.
   constexpr int RO = 4;
-  if (a.sel.logits) hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1, true>), dim3(o.N / RO), dim3(512), 0, s, a, o);
+  if (a.ntok == 2) hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 2>), dim3(o.N / RO), dim3(512), 0, s, a, o);
+  else if (a.sel.logits) hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1, true>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   else hipLaunchKernelGGL((pred_attn_o_kernel<KVT, 8, 2, RO, 1>), dim3(o.N / RO), dim3(512), 0, s, a, o);
   return hipGetLastError();
 }
@@ -1778,9 +1779,10 @@ bool attention_oproj_sel_ok(int nq, int nkv, int d, int kvdtype, int wdtype, int
 }
 
 hipError_t launch_attention_oproj(const AttnArgs& a, const LinearArgs& o, hipStream_t s) {
-  // one new token per launch: for the two-token pass the separate kernels are as fast
+  // one new token per launch, or the two-token pass (positions 0 and 1: 1.943
+  // against 1.962 ms per batch-1 frame with the separate attention and o-projection)
   const int nt = a.ntok > 0 ? a.ntok : 1;
-  const bool ok = nt == 1 && a.single_token && a.mode == ATT_WRITE_ATTEND && a.n_runs == 1 && a.d == 128 && a.nkv == 8 &&
+  const bool ok = a.single_token && a.mode == ATT_WRITE_ATTEND && a.n_runs == 1 && a.d == 128 && a.nkv == 8 &&
                   a.nq == 16 && a.ld_qkv >= (long)(a.nq + 2 * a.nkv) * a.d && a.part_z <= 0 && !a.row_pos && !a.rope_rows && a.max_pos <= 16 &&
                   a.pos_base >= 0 && a.pos_base + nt <= a.max_pos &&
                   (nt == 1 || (nt == 2 && a.tok_stride == 2 && a.tok_off == 0)) && (nt == 2 || a.tok_stride == 0) &&
