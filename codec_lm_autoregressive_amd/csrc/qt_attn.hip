@@ -721,8 +721,8 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
         }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          s[r][hh] += __shfl_xor(s[r][hh], 1);
-          s[r][hh] += __shfl_xor(s[r][hh], 2);
+          s[r][hh] += dpp_f<0xb1, 0xf>(s[r][hh], 0.f);   // quad_perm [1,0,3,2]: lane l ^ 1
+          s[r][hh] += dpp_f<0x4e, 0xf>(s[r][hh], 0.f);   // quad_perm [2,3,0,1]: lane l ^ 2
           s[r][hh] = j < L ? s[r][hh] * p.scale : -INFINITY;
         }
       }
@@ -789,8 +789,9 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         float v = acc[hh][e];
-#pragma unroll
-        for (int o = CPK; o < 64; o <<= 1) v += __shfl_xor(v, o);
+        static_assert(CPK == 16 || CPK == 32, "key slots 16 or 32 lanes apart");
+        if constexpr (CPK == 16) v = add_xor<16>(v);
+        v = add_xor<32>(v);
         acc[hh][e] = v;
       }
       l[hh] = wave_sum(l[hh]);
@@ -998,20 +999,25 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
     s1 = fmaf(qb.x, x[4 * e + 4], s1); s1 = fmaf(qb.y, x[4 * e + 5], s1); s1 = fmaf(qb.z, x[4 * e + 6], s1); s1 = fmaf(qb.w, x[4 * e + 7], s1);
   }
   float sc = s0 + s1;
-  sc += __shfl_xor(sc, 16);
-  sc += __shfl_xor(sc, 32);
+  sc = add_xor<16>(sc);
+  sc = add_xor<32>(sc);
   sc = jk < L ? sc * p.scale : -INFINITY;
+  // max and sum over the 16 keys of a row of 16 lanes: DPP quad permutes, then the half-row and row mirrors
   float mx = sc;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  mx = fmaxf(mx, dpp_f<0xb1, 0xf>(mx, -INFINITY));
+  mx = fmaxf(mx, dpp_f<0x4e, 0xf>(mx, -INFINITY));
+  mx = fmaxf(mx, dpp_f<0x141, 0xf>(mx, -INFINITY));
+  mx = fmaxf(mx, dpp_f<0x140, 0xf>(mx, -INFINITY));
   const float ew = jk < L ? expf(sc - mx) : 0.f;
   float lsum = ew;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o);
+  lsum += dpp_f<0xb1, 0xf>(lsum, 0.f);
+  lsum += dpp_f<0x4e, 0xf>(lsum, 0.f);
+  lsum += dpp_f<0x141, 0xf>(lsum, 0.f);
+  lsum += dpp_f<0x140, 0xf>(lsum, 0.f);
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float pj = __shfl(ew, j);        // lanes 0..15 hold the key weights
+    const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ew), j));   // lanes 0..15 hold the key weights
     float v0, v1;
     if (j < pos0) {
       if constexpr (std::is_same<KVT, _Float16>::value) {
@@ -1162,8 +1168,8 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(x[s][e], x[s][e], ss);
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = add_xor<16>(ss);
+    ss = add_xor<32>(ss);
     const float den = sqrtf(ss / (float)D + p.eps);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1228,8 +1234,8 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
           sc[kt][r] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor<16>(mx);
+      mx = max_xor<32>(mx);
       const float mnew = fmaxf(m, mx);     // finite: key 0 is in every query's range
       const float corr = expf(m - mnew);
       m = mnew;
@@ -1270,8 +1276,8 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
     if (more) store_block(cur ^ 1);
     __syncthreads();
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = add_xor<16>(lsum);
+  lsum = add_xor<32>(lsum);
   if (!wave_live || !tok_ok) return;
   float* o = p.out + ((long)rn.tok0 + tok) * p.ld_out + (long)(g * G + hh) * D + 4 * quad;
 #pragma unroll
@@ -1690,8 +1696,8 @@ __global__ __launch_bounds__(NKV * 64) void pred_attn_o_kernel(AttnArgs p, Linea
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         float v = acc[hh][e];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        v = add_xor<16>(v);
+        v = add_xor<32>(v);
         acc[hh][e] = v;
       }
     if (vsl == 0)

@@ -103,6 +103,31 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// v combined with its value in lane l ^ O: O = 16 and 32 on the VALU with the
+// gfx950 lane-swap instructions (a swap of v with itself leaves lane l's and
+// lane l ^ O's values in the two results), other O through a shuffle. The
+// same value in either lane order: add and max are commutative.
+template <int O>
+__device__ __forceinline__ float add_xor(float v) {
+  if constexpr (O == 32 || O == 16) {
+    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return v + __shfl_xor(v, O);
+  }
+}
+template <int O>
+__device__ __forceinline__ float max_xor(float v) {
+  if constexpr (O == 32 || O == 16) {
+    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(v, __shfl_xor(v, O));
+  }
+}
+
 template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_i(int v, int id) {
   return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xf, false);

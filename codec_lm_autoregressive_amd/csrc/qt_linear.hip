@@ -1676,8 +1676,8 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv_kernel(LinearArgs p) {
     *(f32x4*)red[w][t][lane] = acc[t];
     if constexpr (NORM) {
       float q = ss[t];
-      q += __shfl_xor(q, 16);
-      q += __shfl_xor(q, 32);
+      q = add_xor<16>(q);
+      q = add_xor<32>(q);
       if (lk == 0) ssr[w][16 * t + li] = q;
     }
   }
@@ -1858,9 +1858,9 @@ __global__ __launch_bounds__(KSW * 64) void mfma_gemv8_kernel(LinearArgs p) {
     *(f32x4*)red[w][t][lane] = acc[t] + hi;
   }
   if constexpr (NORM) {
-    ss += __shfl_xor(ss, 8);
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss += dpp_f<0x128, 0xf>(ss, 0.f);   // row_ror:8, lane l ^ 8 within its row of 16
+    ss = add_xor<16>(ss);
+    ss = add_xor<32>(ss);
     if (lane < 8) ssr[w][lane] = ss;
   }
   __syncthreads();
