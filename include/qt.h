@@ -129,8 +129,9 @@ typedef struct qt_sampling {
 
 typedef struct qt_ctx qt_ctx;
 
-/* Device bytes qt_create needs for this configuration (packed weights, KV
- * caches, activations, row state). Host-only arithmetic; overflow-checked. */
+/* Device bytes qt_create needs for this configuration (packed weights, the
+ * code predictor's code-indexed first-layer tables, KV caches, activations,
+ * row state). Host-only arithmetic; overflow-checked. */
 qt_status qt_workspace_bytes(const qt_config* cfg, size_t* bytes);
 
 /* Validate a configuration without touching any device. */
@@ -139,7 +140,11 @@ qt_status qt_config_check(const qt_config* cfg);
 /* Create a context on the current HIP device. Copies and repacks the weights
  * (fused q/k/v and gate/up matrices) into `workspace` (device memory of at
  * least qt_workspace_bytes bytes, owned by the caller and kept alive until
- * qt_destroy), so the caller may free its weight buffers afterwards. With
+ * qt_destroy), so the caller may free its weight buffers afterwards. It also
+ * tabulates, for each of the 14 single-token code predictor steps and every
+ * code of that step's input table, the first layer's q/k/v of the code's
+ * embedding row (the step's input depends on the code alone), so the frame
+ * reads one table row where it would stream the q/k/v weights. With
  * workspace == NULL the library allocates the workspace itself and frees it
  * in qt_destroy. hip_stream: a hipStream_t (NULL = the default stream). */
 qt_status qt_create(const qt_config* cfg, const qt_weights* w, void* workspace, size_t ws_bytes,
