@@ -441,11 +441,6 @@ qt_status pack_layer(qt_ctx* ctx, const qt_layer_weights& w, const Dec& d, DevLa
   return QT_OK;
 }
 
-// ---- the decoder stack over M tokens
-// pass0: the code predictor's 2-token pass (row r's tokens are activation rows
-// 2r and 2r + 1 at positions 0 and 1).
-// prefill: tiles (n_tiles > 0) are the runs of up to kAttnTileTokens tokens
-// the attend pass takes instead of one run per token.
 // A code predictor step's input from the code-indexed tables of the first
 // layer: q/k/v rows (row stride lut_ld, `rows` codes) and, with the input
 // projection, the projected rows. sel: the step's greedy selection is folded
@@ -455,6 +450,13 @@ struct StepIn {
   const float* lut; long lut_ld; const float* xlut; const SelFold* sel;
   const int* codes; int code_ld; int rows;
 };
+
+// ---- the decoder stack over M tokens
+// pass0: the code predictor's 2-token pass (row r's tokens are activation rows
+// 2r and 2r + 1 at positions 0 and 1).
+// prefill: tiles (n_tiles > 0) are the runs of up to kAttnTileTokens tokens
+// the attend pass takes instead of one run per token.
+// in: a code predictor step whose first layer reads the code-indexed tables.
 
 qt_status run_layers(qt_ctx* ctx, bool talker, float* x, int M, const Run* runs, int n_runs, const int* row_pos,
                      int pos_base, hipStream_t s, bool prefill = false, bool single_token = false, bool pass0 = false,
