@@ -512,6 +512,102 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs p) {
   }
 }
 
+// The new tokens of a decode step: the q heads and k through QK-RMSNorm and
+// rope (one wave per vector, waves wave, wave + nthreads / 64, ...; lane owns
+// the rope pair (lane, lane + 64)), the K and V rows to the cache (as stored)
+// and to LDS. Without owns_new only the q heads are formed and knew / vnew are
+// zeroed (masked keys past a key range may index them: 0 x NaN is NaN).
+template <typename KVT, int G, int NTOK>
+__device__ __forceinline__ void decode_new_rows(const AttnArgs& p, int g, int row, int pos0, bool owns_new, int nthreads,
+                                                float (*qs)[G][128], float (*knew)[128], float (*vnew)[128],
+                                                KVT* kc, KVT* vc) {
+  constexpr int D = 128, HALF = 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float prs[NTOK];
+  const long arow0 = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  // split-K partial sums: up to PZ ranges with every load issued before the
+  // first add (clamped ranges past part_z are loaded but not added)
+  constexpr int PZ = 8;
+  const bool pz_fast = p.part_z <= PZ;
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    prs[t] = 1.f;
+    if (p.part_z > 0) {
+      const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
+      float ssum = 0.f;
+      if (pz_fast) {
+        float q[PZ];
+#pragma unroll
+        for (int z = 0; z < PZ; ++z) q[z] = pss[(long)min(z, p.part_z - 1) * p.part_rows + arow0 + t];
+#pragma unroll
+        for (int z = 0; z < PZ; ++z) if (z < p.part_z) ssum += q[z];
+      } else {
+        for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow0 + t];
+      }
+      prs[t] = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
+    }
+  }
+  auto qkv_at = [&](int t, long col) -> float {
+    const long ar = arow0 + t;
+    if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
+    float v;
+    if (pz_fast) {
+      float q[PZ];
+#pragma unroll
+      for (int z = 0; z < PZ; ++z) q[z] = p.part[((long)min(z, p.part_z - 1) * p.part_rows + ar) * p.ld_qkv + col];
+      v = q[0];
+#pragma unroll
+      for (int z = 1; z < PZ; ++z) if (z < p.part_z) v += q[z];
+    } else {
+      v = p.part[ar * p.ld_qkv + col];
+      for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
+    }
+    return v * prs[t];
+  };
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int pos = pos0 + t;
+    float cs, sn;
+    if (p.rope_rows) {
+      cs = p.rope_rows[(long)row * D + lane];
+      sn = p.rope_rows[(long)row * D + HALF + lane];
+    } else {
+      cs = p.cos[(long)pos * HALF + lane];
+      sn = p.sin[(long)pos * HALF + lane];
+    }
+    if (!owns_new)
+      for (int i = tid; i < D; i += nthreads) { knew[t][i] = 0.f; vnew[t][i] = 0.f; }
+    for (int v = wave; v <= (owns_new ? G + 1 : G - 1); v += nthreads / 64) {
+      if (v == G + 1) {                       // value row, stored as is
+        const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
+        const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
+        st_elem<KVT>(vc, (long)pos * D + lane, x1);
+        st_elem<KVT>(vc, (long)pos * D + lane + HALF, x2);
+        vnew[t][lane] = kv_round<KVT>(x1);
+        vnew[t][lane + HALF] = kv_round<KVT>(x2);
+        continue;
+      }
+      const long col = v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D;
+      const float* gain = v < G ? p.q_gain : p.k_gain;
+      const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
+      const float g1 = gain[lane], g2 = gain[lane + HALF];
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float rden = 1.f / sqrtf(ss / (float)D + p.eps);
+      const float y1 = x1 * rden * g1, y2 = x2 * rden * g2;
+      const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
+      if (v < G) {
+        qs[t][v][lane] = o1;
+        qs[t][v][lane + HALF] = o2;
+      } else {
+        st_elem<KVT>(kc, (long)pos * D + lane, o1);
+        st_elem<KVT>(kc, (long)pos * D + lane + HALF, o2);
+        knew[t][lane] = kv_round<KVT>(o1);
+        knew[t][lane + HALF] = kv_round<KVT>(o2);
+      }
+    }
+  }
+}
+
 // Decode attention for head_dim 128, one kernel launch for the NTOK new
 // tokens of every row (NTOK = 1: a talker or predictor step; NTOK = 2: the
 // predictor's two-token pass at positions 0 and 1). Block = (kv head, row).
@@ -586,91 +682,9 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
   load_k(kb);
   load_v(kb);
 
-  // the new tokens: QK-RMSNorm + rope of q heads and k (one wave per vector;
-  // lane owns the rope pair (lane, lane + 64)), K/V rows to the cache and LDS
-  float prs[NTOK];
+  // the new tokens: QK-RMSNorm + rope of q heads and k, K/V rows to the cache and LDS
+  decode_new_rows<KVT, G, NTOK>(p, g, row, pos0, owns_new, NT, qs, knew, vnew, kc, vc);
   const long arow0 = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
-  // split-K partial sums: up to PZ ranges with every load issued before the
-  // first add (clamped ranges past part_z are loaded but not added)
-  constexpr int PZ = 8;
-  const bool pz_fast = p.part_z <= PZ;
-#pragma unroll
-  for (int t = 0; t < NTOK; ++t) {
-    prs[t] = 1.f;
-    if (p.part_z > 0) {
-      const float* pss = p.part + (long)p.part_z * p.part_rows * p.ld_qkv;
-      float ssum = 0.f;
-      if (pz_fast) {
-        float q[PZ];
-#pragma unroll
-        for (int z = 0; z < PZ; ++z) q[z] = pss[(long)min(z, p.part_z - 1) * p.part_rows + arow0 + t];
-#pragma unroll
-        for (int z = 0; z < PZ; ++z) if (z < p.part_z) ssum += q[z];
-      } else {
-        for (int z = 0; z < p.part_z; ++z) ssum += pss[(long)z * p.part_rows + arow0 + t];
-      }
-      prs[t] = 1.f / sqrtf(ssum / (float)p.part_k + p.part_eps);
-    }
-  }
-  auto qkv_at = [&](int t, long col) -> float {
-    const long ar = arow0 + t;
-    if (p.part_z <= 0) return p.qkv[ar * p.ld_qkv + col];
-    float v;
-    if (pz_fast) {
-      float q[PZ];
-#pragma unroll
-      for (int z = 0; z < PZ; ++z) q[z] = p.part[((long)min(z, p.part_z - 1) * p.part_rows + ar) * p.ld_qkv + col];
-      v = q[0];
-#pragma unroll
-      for (int z = 1; z < PZ; ++z) if (z < p.part_z) v += q[z];
-    } else {
-      v = p.part[ar * p.ld_qkv + col];
-      for (int z = 1; z < p.part_z; ++z) v += p.part[((long)z * p.part_rows + ar) * p.ld_qkv + col];
-    }
-    return v * prs[t];
-  };
-#pragma unroll
-  for (int t = 0; t < NTOK; ++t) {
-    const int pos = pos0 + t;
-    float cs, sn;
-    if (p.rope_rows) {
-      cs = p.rope_rows[(long)row * D + lane];
-      sn = p.rope_rows[(long)row * D + HALF + lane];
-    } else {
-      cs = p.cos[(long)pos * HALF + lane];
-      sn = p.sin[(long)pos * HALF + lane];
-    }
-    if (!owns_new)   // masked keys past this range may index the new rows: keep them finite (0 x NaN is NaN)
-      for (int i = tid; i < D; i += NT) { knew[t][i] = 0.f; vnew[t][i] = 0.f; }
-    for (int v = wave; v <= (owns_new ? G + 1 : G - 1); v += NT / 64) {
-      if (v == G + 1) {                       // value row, stored as is
-        const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
-        const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
-        st_elem<KVT>(vc, (long)pos * D + lane, x1);
-        st_elem<KVT>(vc, (long)pos * D + lane + HALF, x2);
-        vnew[t][lane] = kv_round<KVT>(x1);
-        vnew[t][lane + HALF] = kv_round<KVT>(x2);
-        continue;
-      }
-      const long col = v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D;
-      const float* gain = v < G ? p.q_gain : p.k_gain;
-      const float x1 = qkv_at(t, col + lane), x2 = qkv_at(t, col + lane + HALF);
-      const float g1 = gain[lane], g2 = gain[lane + HALF];
-      const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float rden = 1.f / sqrtf(ss / (float)D + p.eps);
-      const float y1 = x1 * rden * g1, y2 = x2 * rden * g2;
-      const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
-      if (v < G) {
-        qs[t][v][lane] = o1;
-        qs[t][v][lane + HALF] = o2;
-      } else {
-        st_elem<KVT>(kc, (long)pos * D + lane, o1);
-        st_elem<KVT>(kc, (long)pos * D + lane + HALF, o2);
-        knew[t][lane] = kv_round<KVT>(o1);
-        knew[t][lane + HALF] = kv_round<KVT>(o2);
-      }
-    }
-  }
   __syncthreads();
 
 #pragma unroll
@@ -819,6 +833,215 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
       }
     }
     if (t + 1 < NTOK) __syncthreads();
+  }
+}
+
+// Single-token decode attention for head_dim 128, G = 2 and a 16-bit cache,
+// streamed by independent waves. Block = (kv head, row[, key range]) of NW
+// waves. After the new token's prologue wave w takes the 16-key chunks w,
+// w + NW, ... of the block's cached keys with no block-wide synchronisation:
+// lane l holds 16 bytes (dims 8 (l % 16) .. + 7) of key 4 i + l / 16 (i =
+// 0..3) of a chunk, for K and for V, so every load instruction reads 1 KB
+// contiguous, and NB chunks per wave are in flight (a register set reloads
+// with the wave's chunk NB steps ahead as soon as it has been used). A lane's 8 partial dot products
+// (4 keys x 2 heads) are added over the 16 lanes of its row by a
+// reduce-scatter (lane distance 8, 2, 1, then a full add at distance 4), which
+// leaves key i = 2 b3 + b1 and head b0 in lane l (b: the bits of l, lanes l
+// and l ^ 4 alike). Each wave keeps its own running max and sums; the last
+// wave (the one with the fewest chunks) adds the new key from LDS, and the
+// waves are combined once at the end. SPLIT: the block's keys are one range
+// of kv_split, left as a partial for attn_split_combine_kernel.
+template <typename KVT, int NW, int NB, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void attn_stream_kernel(AttnArgs p) {
+  constexpr int G = 2, D = 128, CH = 16, NTH = NW * 64;
+  static_assert(sizeof(KVT) == 2 && NTH >= G * D, "16-bit cache, one thread per output");
+  const int g = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dsl = lane & 15, ksl = lane >> 4;       // dims slot, key slot
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+  __shared__ __align__(16) float qs[1][G][D];
+  __shared__ __align__(16) float knew[1][D], vnew[1][D];
+  __shared__ __align__(16) float wacc[NW][G][D];
+  __shared__ float wm[NW][G], wl[NW][G];
+  KVT* kc = (KVT*)p.kc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
+  const int pos0 = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
+  int kb = 0, ke = pos0;                            // cached keys kb .. ke - 1
+  bool owns_new = true;
+  if constexpr (SPLIT) {
+    const int S = gridDim.z, sp = blockIdx.z;
+    const int per = ((pos0 + S - 1) / S + CH * NW - 1) / (CH * NW) * (CH * NW);
+    kb = min(sp * per, pos0);
+    ke = min(kb + per, pos0);
+    owns_new = sp == S - 1;
+  }
+  const int nch = (ke - kb + CH - 1) / CH;
+  u32x4 kbuf[NB][4], vbuf[NB][4];
+  auto load = [&](u32x4 (&kd)[4], u32x4 (&vd)[4], int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long j = min(kb + n * CH + 4 * i + ksl, ke - 1);
+      kd[i] = *(const u32x4*)(kc + j * D + dsl * 8);
+      vd[i] = *(const u32x4*)(vc + j * D + dsl * 8);
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (wave + b * NW < nch) load(kbuf[b], vbuf[b], wave + b * NW);
+
+  decode_new_rows<KVT, G, 1>(p, g, row, pos0, owns_new, NTH, qs, knew, vnew, kc, vc);
+  __syncthreads();
+
+  // lane l ^ 4 of the row: quad_perm [3,2,1,0] (l ^ 3), then row_half_mirror
+  // (l ^ 7), both over the whole wave (a select between two row shifts would
+  // become a branch, and a lane move from disabled lanes reads nothing)
+  auto xor4 = [](float v) __attribute__((always_inline)) { return dpp_f<0x141, 0xf>(dpp_f<0x1b, 0xf>(v, 0.f), 0.f); };
+  float q[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] = qs[0][h][dsl * 8 + e];
+  float m[G] = {-INFINITY, -INFINITY}, acc[G][8], lsum = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  // one step of the online softmax: s is this lane's score (head b0; -inf if
+  // masked; lanes l and l ^ 4 alike), counted in the lane's sum if cnt;
+  // add_pv gets the lane's weight once the maxima and sums are rescaled
+  auto update = [&](float s, bool cnt, auto&& add_pv) __attribute__((always_inline)) {
+    float mx = fmaxf(s, dpp_f<0x4e, 0xf>(s, -INFINITY));
+    mx = fmaxf(mx, dpp_f<0x128, 0xf>(mx, -INFINITY));
+    mx = max_xor<16>(mx);
+    mx = max_xor<32>(mx);
+    const float other = dpp_f<0xb1, 0xf>(mx, -INFINITY);
+    float corr[G];
+    const float mc0 = fmaxf(m[0], b0 ? other : mx), mc1 = fmaxf(m[1], b0 ? mx : other);
+    corr[0] = expf(m[0] - mc0);
+    corr[1] = expf(m[1] - mc1);
+    m[0] = mc0;
+    m[1] = mc1;
+    const float pw = s == -INFINITY ? 0.f : expf(s - (b0 ? mc1 : mc0));
+    lsum = lsum * (b0 ? corr[1] : corr[0]) + (cnt ? pw : 0.f);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= corr[h];
+    add_pv(pw);
+  };
+  auto chunk = [&](const u32x4 (&kd)[4], const u32x4 (&vd)[4], int n) __attribute__((always_inline)) {
+    float sc[4][G];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[8];
+      unpack_chunk<KVT>(kd[i], x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(q[h][e], x[e], a);
+        sc[i][h] = a;
+      }
+    }
+    // reduce-scatter over the 16 lanes of the row: index t = 2 i + h
+    float v4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float lo = sc[t >> 1][t & 1], hi = sc[2 + (t >> 1)][t & 1];
+      v4[t] = (b3 ? hi : lo) + dpp_f<0x128, 0xf>(b3 ? lo : hi, 0.f);     // row_ror:8: lane l ^ 8
+    }
+    float v2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) v2[u] = (b1 ? v4[2 + u] : v4[u]) + dpp_f<0x4e, 0xf>(b1 ? v4[u] : v4[2 + u], 0.f);
+    float v1 = (b0 ? v2[1] : v2[0]) + dpp_f<0xb1, 0xf>(b0 ? v2[0] : v2[1], 0.f);
+    v1 += xor4(v1);
+    const int key = kb + n * CH + 4 * ((b3 ? 2 : 0) + (b1 ? 1 : 0)) + ksl;
+    update(key < ke ? v1 * p.scale : -INFINITY, !b2, [&](float pw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[8];
+        unpack_chunk<KVT>(vd[i], x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float w = __shfl(pw, (lane & 0x30) | ((i >> 1) << 3) | ((i & 1) << 1) | h);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, x[e], acc[h][e]);
+        }
+      }
+    });
+  };
+  for (int n0 = wave; n0 < nch; n0 += NB * NW) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int n = n0 + b * NW;
+      if (n >= nch) break;
+      chunk(kbuf[b], vbuf[b], n);
+      if (n + NB * NW < nch) load(kbuf[b], vbuf[b], n + NB * NW);   // the buffer's next chunk
+    }
+  }
+  if (owns_new && wave == NW - 1) {
+    // the new key (every row of the wave forms its score; row 0 adds its value)
+    float a[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = fmaf(q[h][e], knew[0][dsl * 8 + e], t);
+      t += dpp_f<0xb1, 0xf>(t, 0.f);
+      t += dpp_f<0x4e, 0xf>(t, 0.f);
+      t += dpp_f<0x141, 0xf>(t, 0.f);
+      t += dpp_f<0x140, 0xf>(t, 0.f);
+      a[h] = t * p.scale;
+    }
+    // every lane holds both scores; lanes 0 and 1 count head b0 in the sums
+    update(b0 ? a[1] : a[0], (lane & ~1) == 0, [&](float) __attribute__((always_inline)) {
+      if (ksl == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float w = expf(a[h] - m[h]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vnew[0][dsl * 8 + e], acc[h][e]);
+        }
+    });
+  }
+  // the wave's totals: rows of keys, then the softmax sums of each head
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = add_xor<32>(add_xor<16>(acc[h][e]));
+  float lt = lsum + dpp_f<0x4e, 0xf>(lsum, 0.f);
+  lt += xor4(lt);
+  lt += dpp_f<0x128, 0xf>(lt, 0.f);
+  lt = add_xor<32>(add_xor<16>(lt));
+  if (ksl == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *(f32x4*)&wacc[wave][h][dsl * 8] = (f32x4){acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *(f32x4*)&wacc[wave][h][dsl * 8 + 4] = (f32x4){acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+    }
+  }
+  if (lane < G) { wm[wave][lane] = m[lane]; wl[wave][lane] = lt; }
+  __syncthreads();
+  if (tid < G * D) {
+    const int hh = tid / D, dim = tid % D;
+    float M = wm[0][hh];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, wm[w][hh]);
+    float v = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = wm[w][hh] == -INFINITY ? 0.f : expf(wm[w][hh] - M);
+      v = fmaf(f, wacc[w][hh][dim], v);
+      ls = fmaf(f, wl[w][hh], ls);
+    }
+    if constexpr (SPLIT) {
+      float* sb = p.split_buf + ((((long)row * p.nkv + g) * gridDim.z + blockIdx.z) * G + hh) * (D + 2);
+      sb[dim] = v;
+      if (dim == 0) { sb[D] = M; sb[D + 1] = ls; }
+    } else {
+      const long arow = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+      p.out[arow * p.ld_out + (long)(g * G + hh) * D + dim] = v / ls;
+    }
   }
 }
 
@@ -1358,11 +1581,28 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
     if (a.single_token && a.mode == ATT_WRITE_ATTEND && (nt == 1 || (nt == 2 && a.tok_stride == 2 && a.tok_off == 0))) {
       constexpr int big = 512 / sizeof(KVT), small = 64;
       const dim3 grid(a.nkv, a.n_runs);
+      const bool split = nt == 1 && a.split_buf && (a.kv_split == 2 || a.kv_split == 4 || a.kv_split == 8 || a.kv_split == 16);
+      if constexpr (G == 2 && sizeof(KVT) == 2) {
+        // one token per row: the wave-streaming kernel (4 waves, 3 chunks in
+        // flight per wave), measured 4.3 against 5.2 us at 41 keys and batch 1,
+        // 9.5 against 10.6 us at batch 8 (4 key ranges) and 23.4 against
+        // 25.6 us at batch 64 (128..512-key prompts)
+        if (nt == 1) {
+          if (split) {
+            hipLaunchKernelGGL((attn_stream_kernel<KVT, 4, 3, true>), dim3(a.nkv, a.n_runs, a.kv_split), dim3(256), 0, s, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_split_combine<G>(a, s);
+          }
+          hipLaunchKernelGGL((attn_stream_kernel<KVT, 4, 3, false>), grid, dim3(256), 0, s, a);
+          return hipGetLastError();
+        }
+      }
       // large chunks when the grid is at most one block per compute unit and
       // contexts can be long (not the code predictor's 16 positions: 64-key
       // chunks measured 5.1 against 5.7 us there)
       const bool one_wave = (long)a.nkv * a.n_runs <= 256 && a.max_pos > small;
-      if (nt == 1 && a.split_buf && (a.kv_split == 2 || a.kv_split == 4 || a.kv_split == 8 || a.kv_split == 16)) {
+      if (split) {
         hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small, true>), dim3(a.nkv, a.n_runs, a.kv_split), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
