@@ -1598,4 +1598,48 @@ qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t
   return QT_OK;
 }
 
+qt_status qt_debug_decode_attention(void* hip_stream, int32_t kv_dtype, int32_t head_dim, int32_t nq, int32_t nkv,
+                                    int32_t B, const int32_t* pos, int32_t* pos_dev, int32_t max_pos,
+                                    const float* qkv, const float* q_gain, const float* k_gain, float eps,
+                                    const float* cos, const float* sin, void* kc, void* vc, float* out,
+                                    int32_t kv_split, float* split_buf) {
+  if (kv_dtype != QT_DTYPE_F32 && kv_dtype != QT_DTYPE_BF16 && kv_dtype != QT_DTYPE_F16) {
+    set_err(g_err, "bad kv_dtype");
+    return QT_E_INVALID;
+  }
+  const int G = nkv > 0 ? nq / nkv : 0;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256) || nkv < 1 ||
+      nq % nkv || !(G == 1 || G == 2 || G == 4 || G == 8) || B < 1 || B > 4096 || max_pos < 1 || !(eps > 0.f)) {
+    set_err(g_err, "bad shape");
+    return QT_E_INVALID;
+  }
+  if (!pos || !pos_dev || !qkv || !q_gain || !k_gain || !cos || !sin || !kc || !vc || !out) {
+    set_err(g_err, "NULL argument");
+    return QT_E_INVALID;
+  }
+  if (!(kv_split == 1 || ((kv_split == 2 || kv_split == 4 || kv_split == 8 || kv_split == 16) && split_buf &&
+                          head_dim == 128 && G <= 4))) {
+    set_err(g_err, "kv_split must be 1, or 2, 4, 8 or 16 with split_buf at head_dim 128 and nq / nkv <= 4");
+    return QT_E_INVALID;
+  }
+  for (int r = 0; r < B; ++r)
+    if (pos[r] < 0 || pos[r] >= max_pos) { set_err(g_err, "pos[%d] out of 0..max_pos - 1", r); return QT_E_INVALID; }
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipError_t e = hipMemcpyAsync(pos_dev, pos, (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  AttnArgs t{};
+  t.mode = ATT_WRITE_ATTEND; t.single_token = 1; t.ntok = 1;
+  t.qkv = qkv; t.ld_qkv = (long)(nq + 2 * nkv) * head_dim; t.out = out; t.ld_out = (long)nq * head_dim;
+  t.q_gain = q_gain; t.k_gain = k_gain; t.eps = eps; t.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  t.cos = cos; t.sin = sin; t.kc = kc; t.vc = vc; t.kvdtype = kv_dtype;
+  t.row_stride = (long)nkv * max_pos * head_dim; t.max_pos = max_pos;
+  t.nq = nq; t.nkv = nkv; t.d = head_dim;
+  t.n_runs = B; t.row_pos = pos_dev; t.pos_base = 0;
+  if (kv_split > 1) { t.kv_split = kv_split; t.split_buf = split_buf; }
+  if (e == hipSuccess) e = launch_attention(t, s);
+  const hipError_t e2 = hipStreamSynchronize(s);   // also keeps pos alive until the copy has been made
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) { set_err(g_err, "decode attention failed: %s", hipGetErrorString(e)); return QT_E_HIP; }
+  return QT_OK;
+}
+
 }  // extern "C"

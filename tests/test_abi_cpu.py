@@ -173,3 +173,17 @@ def test_debug_entry_points_validate_before_launch():
     assert pa(binding.QT_DTYPE_F16, 128, 6, 4, 0) == binding.QT_E_INVALID    # nq not a multiple of nkv
     assert pa(binding.QT_DTYPE_F16, 128, 4, 2, 1, max_pos=8) == binding.QT_E_INVALID   # a row longer than max_pos
     assert pa(binding.QT_DTYPE_F16, 128, 4, 2, 1, runs_ints=50) == binding.QT_E_INVALID  # run scratch too small
+    pos = (C.c_int32 * 2)(5, 9)
+
+    def da(kv, d, nq, nkv, split, pos=pos, max_pos=64, split_buf=fake, B=2):
+        return L.qt_debug_decode_attention(None, kv, d, nq, nkv, B, pos, fake, max_pos, fake, fake, fake, 1e-6, fake,
+                                           fake, fake, fake, fake, split, split_buf)
+    assert da(7, 128, 4, 2, 1) == binding.QT_E_INVALID                         # kv_dtype
+    assert da(binding.QT_DTYPE_F16, 96, 4, 2, 1) == binding.QT_E_INVALID       # head_dim
+    assert da(binding.QT_DTYPE_F16, 128, 6, 4, 1) == binding.QT_E_INVALID      # nq not a multiple of nkv
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 3) == binding.QT_E_INVALID      # kv_split not a power of two
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 4, split_buf=None) == binding.QT_E_INVALID   # split without scratch
+    assert da(binding.QT_DTYPE_F16, 64, 4, 2, 4) == binding.QT_E_INVALID       # split needs head_dim 128
+    assert da(binding.QT_DTYPE_F16, 128, 16, 2, 2) == binding.QT_E_INVALID     # and at most 4 q heads per kv head
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, max_pos=9) == binding.QT_E_INVALID   # a position past max_pos - 1
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, B=0) == binding.QT_E_INVALID          # no rows

@@ -359,3 +359,89 @@ def test_prefill_attention_tiled_matches_oracle(kv, lens, gain_scale):
     assert np.all(np.isfinite(outs[True])) and np.all(np.isfinite(outs[False]))
     assert cross <= tol_cross, cross
     assert errs[True] <= tol_oracle and errs[False] <= tol_oracle, errs
+
+
+def _cache_round(x, kv):
+    """Values as a cache of type kv holds them (rounded through float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    if kv == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    if kv == "bf16":
+        return synth.bf16_round(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def _ref_decode_attention(qkv, pos, kc, vc, q_gain, k_gain, cos, sin, nq, nkv, eps, kv):
+    """Per row r: the oracle's per-head RMSNorm and rope of the new token at
+    position pos[r] in float64, its key and value rounded to the cache type,
+    GQA attention in float64 over cached positions 0 .. pos[r] - 1 (as
+    stored) and the new one."""
+    B, d = qkv.shape[0], qkv.shape[1] // (nq + 2 * nkv)
+    out = np.empty((B, nq * d))
+    for r in range(B):
+        p = int(pos[r])
+        x = qkv[r:r + 1].astype(np.float64)
+        q = x[:, :nq * d].reshape(1, nq, d)
+        k = x[:, nq * d:(nq + nkv) * d].reshape(1, nkv, d)
+        v = x[:, (nq + nkv) * d:].reshape(1, nkv, d)
+        q = model.apply_rope(model.rms_norm(q, q_gain, eps, np.float64), [p], cos, sin, np.float64)
+        k = _cache_round(model.apply_rope(model.rms_norm(k, k_gain, eps, np.float64), [p], cos, sin, np.float64), kv)
+        v = _cache_round(v, kv)
+        K = np.concatenate([kc[r, :, :p], k.transpose(1, 0, 2)], axis=1)
+        V = np.concatenate([vc[r, :, :p], v.transpose(1, 0, 2)], axis=1)
+        out[r] = model.attention(q, K, V, [p], nkv, np.float64).reshape(nq * d)
+    return out
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("pos,nkv,G,max_pos,splits", [
+    ([0, 1, 15, 16, 17, 47, 48, 49, 63, 64, 65, 130], 8, 2, 256, (1, 2, 4, 8, 16)),
+    ([1499, 700, 3], 8, 2, 1536, (1, 4, 16)),
+    ([5, 33, 100], 4, 4, 128, (1, 2)),
+    ([3, 9], 8, 2, 16, (1,)),
+])
+def test_decode_attention_matches_oracle(kv, pos, nkv, G, max_pos, splits):
+    """One single-token decode step of the attention (the new token's
+    QK-RMSNorm and rope, its K/V into the cache, GQA over positions 0 .. pos)
+    for rows at ragged positions: empty caches, ragged tails of the 16- and
+    64-key groups the kernels stream in, a 1500-token context, every key-range
+    split, 4 q heads per kv head, and the predictor's 16-position cache;
+    against the float64 oracle over the same cache contents. Tolerance as for
+    the prefill attention: the kernel rounds its float32 rope result into the
+    cache, the oracle its float64 one, so a few stored elements of the new key
+    may sit one unit of the cache type apart (2e-3 at unit gains); split and
+    unsplit runs on one cache agree to 1e-5 (ranges added in another order)."""
+    torch = _torch()
+    nq, d, eps = nkv * G, 128, 1e-6
+    pos = np.array(pos, dtype=np.int32)
+    B = len(pos)
+    rng = np.random.default_rng(int(pos.sum()) + 11 * G + {"f16": 0, "bf16": 1, "f32": 2}[kv])
+    qkv = rng.standard_normal((B, (nq + 2 * nkv) * d)).astype(np.float32)
+    q_gain = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    k_gain = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    cos, sin = model.rope_tables(max_pos, d, 1.0e6)
+    kc = _cache_round(rng.standard_normal((B, nkv, max_pos, d)), kv)
+    vc = _cache_round(rng.standard_normal((B, nkv, max_pos, d)), kv)
+    ref = _ref_decode_attention(qkv, pos, kc, vc, q_gain, k_gain, cos, sin, nq, nkv, eps, kv)
+
+    def dev_cache(x):
+        if kv == "f16":
+            return torch.from_numpy(x.astype(np.float16)).cuda()
+        if kv == "bf16":
+            return torch.from_numpy(synth.bf16_bits(x.astype(np.float32)).view(np.int16)).cuda()
+        return torch.from_numpy(x.astype(np.float32)).cuda()
+
+    dev = [torch.from_numpy(a).cuda() for a in (qkv, q_gain, k_gain, cos, sin)]
+    kcd, vcd = dev_cache(kc), dev_cache(vc)
+    tol = 2e-3 if kv != "f32" else 1e-4
+    outs = {}
+    for S in splits:
+        print(f"decode attention kv={kv} G={G} pos={list(pos)} kv_split={S}", flush=True)
+        outs[S] = binding.debug_decode_attention(dev[0], pos, dev[1], dev[2], dev[3], dev[4], kcd, vcd, nq, nkv, eps,
+                                                 kv, S).cpu().numpy()
+        err = float(np.max(np.abs(outs[S] - ref)))
+        print(f"  max|out - oracle| {err:.3e} (tol {tol:.1e})", flush=True)
+        assert np.all(np.isfinite(outs[S])) and err <= tol, err
+    for S in splits[1:]:
+        cross = float(np.max(np.abs(outs[S] - outs[splits[0]])))
+        assert cross <= 1e-5, (S, cross)
