@@ -609,8 +609,9 @@ __device__ __forceinline__ void decode_new_rows(const AttnArgs& p, int g, int ro
 }
 
 // Decode attention for head_dim 128, one kernel launch for the NTOK new
-// tokens of every row (NTOK = 1: a talker or predictor step; NTOK = 2: the
-// predictor's two-token pass at positions 0 and 1). Block = (kv head, row).
+// tokens of every row (NTOK = 2: the predictor's two-token pass at positions
+// 0 and 1; NTOK = 1: single steps with fp32 caches or 1 or 4 q heads per kv
+// head, the others take attn_stream_kernel). Block = (kv head, row).
 // Keys older than the first new token come from the cache in chunks of KCH
 // rows (large chunks when the grid is a single wave of blocks, small ones,
 // with fewer registers, when several blocks share a compute unit) whose
@@ -1598,9 +1599,10 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
           return hipGetLastError();
         }
       }
-      // large chunks when the grid is at most one block per compute unit and
-      // contexts can be long (not the code predictor's 16 positions: 64-key
-      // chunks measured 5.1 against 5.7 us there)
+      // (the two-token pass; other caches and groupings) large chunks when
+      // the grid is at most one block per compute unit and contexts can be
+      // long (not the code predictor's 16 positions: 64-key chunks measured
+      // 5.1 against 5.7 us there)
       const bool one_wave = (long)a.nkv * a.n_runs <= 256 && a.max_pos > small;
       if (split) {
         hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, small, true>), dim3(a.nkv, a.n_runs, a.kv_split), dim3(NT), 0, s, a);
@@ -1608,9 +1610,9 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         return launch_split_combine<G>(a, s);
       }
-      // several blocks per compute unit and long contexts (the batch-64 talker):
-      // 128-key chunks, measured 6.17 against 6.20 ms per frame with 64 and
-      // 6.60 with 256
+      // several blocks per compute unit and long contexts: 128-key chunks
+      // (measured at the batch-64 talker before the wave-streaming kernel:
+      // 6.17 against 6.20 ms per frame with 64 and 6.60 with 256)
       if (nt == 2) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 2, small>), grid, dim3(NT), 0, s, a);
       else if (one_wave) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, big>), grid, dim3(NT), 0, s, a);
       else if (a.max_pos > small) hipLaunchKernelGGL((attn_step_kernel<KVT, G, 1, 2 * small>), grid, dim3(NT), 0, s, a);
