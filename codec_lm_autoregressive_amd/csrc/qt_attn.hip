@@ -844,11 +844,11 @@ __global__ __launch_bounds__(NT) void attn_step_kernel(AttnArgs p) {
 // lane l holds 16 bytes (dims 8 (l % 16) .. + 7) of key 4 i + l / 16 (i =
 // 0..3) of a chunk, for K and for V, so every load instruction reads 1 KB
 // contiguous, and NB chunks per wave are in flight (a register set reloads
-// with the wave's chunk NB steps ahead as soon as it has been used). A lane's 8 partial dot products
-// (4 keys x 2 heads) are added over the 16 lanes of its row by a
-// reduce-scatter (lane distance 8, 2, 1, then a full add at distance 4), which
-// leaves key i = 2 b3 + b1 and head b0 in lane l (b: the bits of l, lanes l
-// and l ^ 4 alike). Each wave keeps its own running max and sums; the last
+// with the wave's chunk NB steps ahead as soon as it has been used). A
+// lane's 8 partial dot products (4 keys x 2 heads) are added over the 16
+// lanes of its row by a reduce-scatter (lane distance 8, 2, 1, then a full
+// add at distance 4), which leaves key i = 2 b3 + b1 and head b0 in lane l
+// (b: the bits of l, lanes l and l ^ 4 alike). Each wave keeps its own running max and sums; the last
 // wave (the one with the fewest chunks) adds the new key from LDS, and the
 // waves are combined once at the end. SPLIT: the block's keys are one range
 // of kv_split, left as a partial for attn_split_combine_kernel.
