@@ -205,58 +205,140 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     } else {
 #pragma unroll
       for (int q = 0; q < MPT; ++q) pv[q] = tid + q * NT < V ? lv[q] / temperature : -INFINITY;
+      float rmax = -INFINITY;                // the row's largest value, once the top-k branch has run
       if (top_k > 0 && top_k < V) {
-        // radix select of the k-th largest value, 8 bits at a time from the top;
-        // per-wave histograms, then a parallel suffix count finds the digit.
-        // Two histogram buffers: a pass clears the next pass's one, so a pass
-        // costs three barriers.
-        uint32_t prefix = 0, mask = 0;
-        int kk = top_k;
+        // tau = the top_k-th largest value (values equal to it are kept). One
+        // histogram of each finite value's distance below the row's largest,
+        // in HB linear buckets between the largest and smallest: the bucket
+        // index never increases with the value, so the k-th largest lies in
+        // the bucket where the count from the top first reaches k, and that
+        // bucket's values (at most 64) are ranked exactly by one wave. A
+        // fuller bucket falls back to a radix select of the k-th largest.
+        constexpr int HB = 2 * (NT / 64) * 256;   // both radix histograms
+        int* hb = &hist[0][0];
         const int lane = tid & 63, wv = tid >> 6;
 #pragma unroll
-        for (int q = 0; q < NT / 64; ++q) hist[0][q * 256 + tid] = 0;
+        for (int q = 0; q < HB / NT; ++q) hb[q * NT + tid] = 0;
+        float lmax = -INFINITY, lmin = INFINITY;
+#pragma unroll
+        for (int q = 0; q < MPT; ++q)
+          if (pv[q] > -INFINITY) { lmax = fmaxf(lmax, pv[q]); lmin = fminf(lmin, pv[q]); }
+        lmax = wave_max(lmax);
+        lmin = -wave_max(-lmin);
+        if (lane == 0) { redf[wv] = lmax; redf[NT / 64 + wv] = lmin; }
+        if (tid == 0) { sh_int[0] = -1; sh_int[3] = 0; }
         __syncthreads();
-        for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
-          int* hb = hist[pass & 1];
+        rmax = redf[0];
+        float rmin = redf[NT / 64];
 #pragma unroll
-          for (int q = 0; q < MPT; ++q) {
-            const uint32_t key = ord_key(pv[q]);
-            if (tid + q * NT < V && (key & mask) == prefix) atomicAdd(&hb[wv * 256 + ((key >> shift) & 255u)], 1);
-          }
+        for (int w = 1; w < NT / 64; ++w) { rmax = fmaxf(rmax, redf[w]); rmin = fminf(rmin, redf[NT / 64 + w]); }
+        float bsc = (float)HB / (rmax - rmin);
+        if (!(bsc < INFINITY) || !(bsc > 0.f)) bsc = 0.f;   // one distinct finite value, or none: bucket 0
+        auto bucket = [&](float x) { return (int)fminf((rmax - x) * bsc, (float)(HB - 1)); };
 #pragma unroll
-          for (int q = 0; q < NT / 64; ++q) hist[(pass + 1) & 1][q * 256 + tid] = 0;
-          __syncthreads();
-          int h = 0;   // count of digit tid
+        for (int q = 0; q < MPT; ++q)
+          if (pv[q] > -INFINITY) atomicAdd(&hb[bucket(pv[q])], 1);
+        __syncthreads();
+        // counts of this thread's HB / NT buckets, then its place in the
+        // count from the top: inclusive prefix within the wave, then the waves
+        constexpr int BPT = HB / NT;
+        int cb[BPT], sown = 0;
 #pragma unroll
-          for (int q = 0; q < NT / 64; ++q) h += hb[q * 256 + tid];
-          int sfx = h;   // inclusive suffix count over digits >= tid, within the wave
+        for (int u = 0; u < BPT; ++u) { cb[u] = hb[tid * BPT + u]; sown += cb[u]; }
+        int incl = sown;
 #pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_down(sfx, o);
-            if (lane + o < 64) sfx += t;
-          }
-          if (lane == 0) scan[wv] = sfx;
-          __syncthreads();
-          for (int q = wv + 1; q < NT / 64; ++q) sfx += scan[q];
-          const int above = sfx - h;   // count of digits > tid
-          if (sfx >= kk && above < kk) {   // exactly one digit: the k-th largest lies in it
-            sh_int[0] = tid;
-            sh_int[1] = kk - above;
-          }
-          __syncthreads();
-          // (sh_int and scan are rewritten only after the next pass's first barrier)
-          prefix |= ((uint32_t)sh_int[0]) << shift;
-          mask |= 255u << shift;
-          kk = sh_int[1];
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
         }
-        const float tau = key_float(prefix);
+        if (lane == 63) scan[wv] = incl;
+        __syncthreads();
+        int c0 = incl - sown;
+        for (int w = 0; w < wv; ++w) c0 += scan[w];
+        if (c0 < top_k && top_k <= c0 + sown) {   // exactly one thread: the k-th largest is in its buckets
+#pragma unroll
+          for (int u = 0; u < BPT; ++u) {
+            if (c0 < top_k && top_k <= c0 + cb[u]) { sh_int[0] = tid * BPT + u; sh_int[1] = top_k - c0; sh_int[2] = cb[u]; }
+            c0 += cb[u];
+          }
+        }
+        __syncthreads();
+        const int bstar = sh_int[0];
+        float tau = -INFINITY;                   // fewer finite values than top_k: nothing is cut
+        if (bstar >= 0 && sh_int[2] <= 64) {
+          const int kk = sh_int[1], cnt = sh_int[2];
+#pragma unroll
+          for (int q = 0; q < MPT; ++q)
+            if (pv[q] > -INFINITY && bucket(pv[q]) == bstar) cp[atomicAdd(&sh_int[3], 1)] = pv[q];
+          __syncthreads();
+          if (tid < 64) {
+            // the kk-th largest of the bucket: more than kk - 1 values above it
+            // is impossible, at least kk at or above it
+            const float v = lane < cnt ? cp[lane] : -INFINITY;
+            int gt = 0, ge = 0;
+            for (int j = 0; j < cnt; ++j) {
+              const float u = cp[j];
+              gt += u > v;
+              ge += u >= v;
+            }
+            if (lane < cnt && gt < kk && kk <= ge) sh_f[0] = v;   // lanes that hold equal values write the same
+          }
+          __syncthreads();
+          tau = sh_f[0];
+        } else if (bstar >= 0) {
+          // radix select of the k-th largest value, 8 bits at a time from
+          // the top; per-wave histograms, then a parallel suffix count finds
+          // the digit. Two histogram buffers: a pass clears the next pass's
+          // one, so a pass costs three barriers.
+          uint32_t prefix = 0, mask = 0;
+          int kk = top_k;
+#pragma unroll
+          for (int q = 0; q < NT / 64; ++q) hist[0][q * 256 + tid] = 0;
+          __syncthreads();
+          for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
+            int* hb = hist[pass & 1];
+#pragma unroll
+            for (int q = 0; q < MPT; ++q) {
+              const uint32_t key = ord_key(pv[q]);
+              if (tid + q * NT < V && (key & mask) == prefix) atomicAdd(&hb[wv * 256 + ((key >> shift) & 255u)], 1);
+            }
+#pragma unroll
+            for (int q = 0; q < NT / 64; ++q) hist[(pass + 1) & 1][q * 256 + tid] = 0;
+            __syncthreads();
+            int h = 0;   // count of digit tid
+#pragma unroll
+            for (int q = 0; q < NT / 64; ++q) h += hb[q * 256 + tid];
+            int sfx = h;   // inclusive suffix count over digits >= tid, within the wave
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const int t = __shfl_down(sfx, o);
+              if (lane + o < 64) sfx += t;
+            }
+            if (lane == 0) scan[wv] = sfx;
+            __syncthreads();
+            for (int q = wv + 1; q < NT / 64; ++q) sfx += scan[q];
+            const int above = sfx - h;   // count of digits > tid
+            if (sfx >= kk && above < kk) {   // exactly one digit: the k-th largest lies in it
+              sh_int[0] = tid;
+              sh_int[1] = kk - above;
+            }
+            __syncthreads();
+            // (sh_int and scan are rewritten only after the next pass's first barrier)
+            prefix |= ((uint32_t)sh_int[0]) << shift;
+            mask |= 255u << shift;
+            kk = sh_int[1];
+          }
+          tau = key_float(prefix);
+        }
 #pragma unroll
         for (int q = 0; q < MPT; ++q) if (pv[q] < tau) pv[q] = -INFINITY;
       }
-      float mx = -INFINITY;
+      float mx = rmax;                       // the largest value survives the cut
+      if (!(top_k > 0 && top_k < V)) {
 #pragma unroll
-      for (int q = 0; q < MPT; ++q) mx = fmaxf(mx, pv[q]);
-      mx = block_max(mx, redf);
+        for (int q = 0; q < MPT; ++q) mx = fmaxf(mx, pv[q]);
+        mx = block_max(mx, redf);
+      }
       float sum = 0.f;
 #pragma unroll
       for (int q = 0; q < MPT; ++q) {

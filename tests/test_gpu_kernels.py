@@ -276,6 +276,49 @@ def test_select_topk_ties_kept():
     assert int(out[0]) in (0, 1, 2, 3, 4)
 
 
+@pytest.mark.parametrize("case", ["normal", "outlier", "ties", "suppressed"])
+def test_select_topk_cut_exact(case):
+    """The sampled selection's top-k cut keeps exactly the values at or above
+    the k-th largest, ties included. Per row one probe id (ranked around k)
+    gets Exp(1) noise 1e-30 and every other id 1, so the probe wins the race
+    if and only if it survived the cut; otherwise the row's largest value
+    (lowest id on ties) wins. Rows of normal values, a wide range (one
+    outlier far above the rest), integer values with hundreds of ties per
+    value (crowded buckets: the kernel's radix fallback), and half the ids at
+    -inf; k from 1 to V - 1 (many survivors take the block-wide path)."""
+    torch = _torch()
+    B, V = 64, 2048
+    g = np.random.default_rng({"normal": 1, "outlier": 2, "ties": 3, "suppressed": 4}[case])
+    if case == "ties":
+        L = g.integers(-3, 4, size=(B, V)).astype(np.float32)
+    else:
+        L = (g.standard_normal((B, V)) * 2).astype(np.float32)
+    if case == "outlier":
+        L[:, 7] = 40.0
+    if case == "suppressed":
+        L[:, g.permutation(V)[:V // 2]] = -np.inf
+    for k in (1, 2, 50, 300, V - 1):
+        E = np.ones((B, V), dtype=np.float32)
+        expect = np.empty(B, dtype=np.int64)
+        probes = np.empty(B, dtype=np.int64)
+        for r in range(B):
+            order = np.argsort(-L[r], kind="stable")
+            t = min(max(k - 1 + (r % 3) - 1, 0), V - 1)   # ranks k - 2, k - 1, k
+            j = int(order[t])
+            kth = L[r, order[k - 1]]
+            kept = L[r, j] >= kth and np.isfinite(L[r, j])
+            E[r, j] = 1e-30
+            probes[r] = j
+            expect[r] = j if kept else int(np.argmax(L[r]))
+        samp = dict(synth.PRED_SAMPLING, top_k=k, top_p=1.0, temperature=1.0)
+        print(f"top-k cut case={case} k={k}", flush=True)
+        out, _, st = binding.debug_select(torch.from_numpy(L).cuda(), samp, noise=torch.from_numpy(E).cuda())
+        got = out.cpu().numpy().astype(np.int64)
+        assert int(st[0]) == 0
+        bad = np.nonzero(got != expect)[0]
+        assert bad.size == 0, (case, k, [(int(r), int(probes[r]), int(got[r]), int(expect[r])) for r in bad[:5]])
+
+
 def test_select_nan_fails_closed():
     torch = _torch()
     L = np.zeros((3, 3072), dtype=np.float32)
