@@ -22,6 +22,8 @@ Measurement modes for profiler runs (rocprofv3 wraps the same command):
     --frame-counters   a prompt prefill and --counter-frames eager frames of a
                        workload, then a 64 MiB copy (byte counters per frame)
     --gemm-kernels     the batched projections at the 0.6B shapes
+    --decode-attention the talker's single-token decode attention at batch 1,
+                       8 and 64 over 28 layer caches (K/V bytes per launch)
 and a summariser of their rocprofv3 CSV output:
     --summarize DIR    per-kernel statistics of a --kernel-trace run, or the
                        counters of a --pmc run, per dispatch or per frame
@@ -157,8 +159,14 @@ def parse():
     ap.add_argument("--gemm-kernels", action="store_true",
                     help="only the batched projections (4096 prefill rows, 64-row decode) at the "
                          "0.6B shapes, timed per launch (for counter runs)")
+    ap.add_argument("--decode-attention", action="store_true",
+                    help="only the talker's decode attention at batch 1, 8 and 64 (0.6B heads, fp16 cache), "
+                         "cycling over 28 layer caches, timed per launch (for kernel traces)")
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="summarise the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="with --summarize of a kernel trace: average each kernel's dispatches in consecutive "
+                         "groups of this many")
     ap.add_argument("--per-frame", action="store_true",
                     help="with --summarize: sum counters per frame (dispatches from the first frame_start_kernel)")
     return ap.parse_args()
@@ -285,7 +293,7 @@ def roof(q, workload):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.per_frame)
+        summarize(args.summarize, args.per_frame, args.groups)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -301,6 +309,10 @@ def main():
         return
     if args.codec_only:
         print(json.dumps(codec_timing(torch, binding, synth)), flush=True)
+        return
+    if args.decode_attention:
+        for line in decode_attention_timing(torch, binding, synth):
+            print(json.dumps(line), flush=True)
         return
     if args.kernel_only:
         wl = synth.workload(args.workload)
@@ -435,16 +447,30 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize(d, per_frame):
+def summarize(d, per_frame, groups=0):
     """Print a summary of the rocprofv3 CSV output under d: kernel statistics
     (kernel_stats.csv of a --kernel-trace --stats run) and/or counters per
     kernel (counter_collection.csv of a --pmc run), with the 64 MiB copy as
     the calibration of each counter (scale = copy bytes / copy counter value).
     With per_frame, counters are also summed over the dispatches from the
     first frame_start_kernel on (runtime copy kernels excluded) and divided
-    by the number of frame_start_kernel dispatches."""
+    by the number of frame_start_kernel dispatches. With groups = N, the
+    dispatches of each kernel in a kernel trace (kernel_trace.csv) are also
+    split, in start order, into consecutive groups of N, with each group's
+    average duration (one group per case of a --decode-attention run)."""
     import glob
     stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if groups > 0:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            by = {}
+            for r in sorted(_csv_rows(path), key=lambda r: int(r["Start_Timestamp"])):
+                by.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            print(f"kernel trace ({os.path.relpath(path, d)}): groups of {groups} dispatches, average us")
+            for n, ds in by.items():
+                if len(ds) < groups:
+                    continue
+                avg = [sum(ds[i:i + groups]) / groups / 1e3 for i in range(0, len(ds) - groups + 1, groups)]
+                print(f"`{n[:90]}`: " + ", ".join(f"{a:.2f}" for a in avg))
     ctrs = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
     for path in stats:
         rows = _csv_rows(path)
@@ -695,6 +721,51 @@ def gemm_kernel_timing(torch, binding, synth, reps=10):
                         "matrix_core_TFLOPs": round(2 * flops / (us * 1e-6) / 1e12, 1),
                         "weight_GBs": round(N * K * 2 / (us * 1e-6) / 1e9, 1)})
     return out
+
+
+def decode_attention_timing(torch, binding, synth, layers=28, reps=56):
+    """The talker's single-token decode attention (16 q / 8 kv heads,
+    head_dim 128, fp16 cache) through the library's decode-attention entry
+    point, cycling over `layers` separate K/V caches as the layers of a frame
+    do (so the 256 MB last-level cache does not hold the keys between
+    launches): batch 1 at 41, 131 and 501 keys; batch 8 (8 key ranges, as the
+    frame loop runs it) and batch 64 (one range) at the workloads' prompt
+    lengths plus 0, 100 / 512 and 199 / 960 decoded frames. Reports the K/V
+    bytes each launch reads; the kernel durations come from a trace. The
+    entry point synchronises after each launch."""
+    nq, nkv, d, max_pos = 16, 8, 128, 1536
+    cos_np, sin_np = _rope_tables(max_pos, d, 1.0e6)
+    cos, sin = torch.from_numpy(cos_np).cuda(), torch.from_numpy(sin_np).cuda()
+    gain = torch.ones(d, device="cuda")
+    cases = [("b1", np.array([40]), 1), ("b1", np.array([130]), 1), ("b1", np.array([500]), 1)]
+    for name, B, S, extra in (("b8", 8, 8, (0, 100, 199)), ("b64", 64, 1, (0, 512, 960))):
+        wl = synth.workload("qwen06b_bf16_b8_sampling" if B == 8 else "qwen06b_bf16_b64_sampling")
+        lens = np.asarray(synth.prompt_lengths(B, *wl["prompt"], seed=2), dtype=np.int64)
+        for f in extra:
+            cases.append((name, lens + f, S))
+    out = []
+    for name, pos, S in cases:
+        B = len(pos)
+        g = torch.Generator(device="cuda").manual_seed(11)
+        kc = [torch.randn((B, nkv, max_pos, d), generator=g, device="cuda").half() for _ in range(layers)]
+        vc = [torch.randn((B, nkv, max_pos, d), generator=g, device="cuda").half() for _ in range(layers)]
+        qkv = torch.randn((B, (nq + 2 * nkv) * d), generator=g, device="cuda")
+        for i in range(reps):
+            binding.debug_decode_attention(qkv, pos, gain, gain, cos, sin, kc[i % layers], vc[i % layers], nq, nkv,
+                                           1e-6, "f16", S)
+        keys = int(pos.sum()) + B
+        out.append({"case": name, "rows": B, "kv_split": S, "mean_keys": round(keys / B, 1),
+                    "kv_bytes_per_launch": keys * nkv * d * 2 * 2, "launches": reps})
+        del kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
+def _rope_tables(max_pos, d, theta):
+    """cos / sin tables [max_pos, d / 2] of the rope angles (float32)."""
+    inv = (theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)).astype(np.float32)
+    ang = np.arange(max_pos, dtype=np.float32)[:, None] * inv[None, :]
+    return np.cos(ang.astype(np.float64)).astype(np.float32), np.sin(ang.astype(np.float64)).astype(np.float32)
 
 
 def _cpu_model():
