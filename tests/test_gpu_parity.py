@@ -1,6 +1,6 @@
 """End-to-end parity of the HIP frame loop with the oracle, through the C ABI.
 
-Rules (spec tolerances): raw logits max|d| <= 2e-3 for fp32 weights,
+Tolerances: raw logits max|d| <= 2e-3 for fp32 weights,
 <= 5e-2 for bf16 weights (the oracle holds the same bf16-rounded weights in
 fp32 with fp32 accumulation). Teacher-forced choices are held to two checks:
 

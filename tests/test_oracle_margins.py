@@ -1,7 +1,7 @@
 """Pins of the oracle's decision-margin helpers, which decide when a GPU
 choice that differs from the oracle's is excused in the parity tests.
 
-The rule they implement (spec tolerance rule, restated): a teacher-forced
+The rule they implement (the parity tolerance rule, restated): a teacher-forced
 choice may differ from the oracle's only where the oracle's decision could
 change under a perturbation of the logits of the size the tolerance allows.
 Each pin below fixes a value by hand or checks the helper against brute
