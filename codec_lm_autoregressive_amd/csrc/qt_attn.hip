@@ -1094,24 +1094,27 @@ static hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Single-token decode attention over at most 16 positions (the code
-// predictor's steps at batch rows > 1), head_dim 128, 16-bit cache.
-// Block = (kv head, row): waves 0..G-1 take the q heads of the group, wave G
-// the new key, wave G + 1 the new value (QK-RMSNorm + rope as in
-// attn_step_kernel, the K/V rows to the cache and LDS); after the one
-// barrier each q-head wave finishes alone. Scores: lane = (key l % 16,
+// Decode attention over at most 16 positions (the code predictor's steps at
+// batch rows > 1, NTOK = 1, and its two-token pass at positions 0 and 1,
+// NTOK = 2, activation rows 2 r and 2 r + 1), head_dim 128, 16-bit cache.
+// Block = (kv head, row), G + 2 waves per new token: waves 0..G-1 take the q
+// heads of the group, wave G the new key, wave G + 1 the new value
+// (QK-RMSNorm + rope as in attn_step_kernel, the K/V rows to the cache and
+// LDS); after the one barrier each q-head wave finishes alone (token t
+// attends to the cached keys and the new keys 0..t). Scores: lane = (key l % 16,
 // quarter l / 16 of the dims), the quarters added with two shuffles; the
 // softmax over the 16 keys stays in 16-lane groups; P.V: lane = 2 dims, the
 // key weights broadcast by shuffles. Every cache load leaves before the
 // prologue (clamped to the cached keys).
-template <typename KVT, int G>
-__global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
+template <typename KVT, int G, int NTOK = 1>
+__global__ __launch_bounds__(NTOK * (G + 2) * 64) void attn_short_kernel(AttnArgs p) {
   constexpr int D = 128, HALF = 64;
   const int g = blockIdx.x, row = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ __align__(16) float qs[G][D];
-  __shared__ __align__(16) float knew[D];
-  __shared__ __align__(16) float vnew[D];
+  const int t = wave / (G + 2), role = wave % (G + 2);   // new token, vector of it
+  __shared__ __align__(16) float qs[NTOK][G][D];
+  __shared__ __align__(16) float knew[NTOK][D];
+  __shared__ __align__(16) float vnew[NTOK][D];
   KVT* kc = (KVT*)p.kc + (long)row * p.row_stride + (long)g * p.max_pos * D;
   KVT* vc = (KVT*)p.vc + (long)row * p.row_stride + (long)g * p.max_pos * D;
   const int pos0 = p.pos_base + (p.row_pos ? p.row_pos[row] : 0);
@@ -1119,7 +1122,7 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
   const int last = max(pos0 - 1, 0);
   u32x4 kr[4];
   uint32_t vr[16];
-  if (wave < G) {
+  if (role < G) {
     const KVT* kp = kc + (long)min(jk, last) * D + 32 * qd;
 #pragma unroll
     for (int c = 0; c < 4; ++c) kr[c] = *(const u32x4*)(kp + 8 * c);
@@ -1128,7 +1131,7 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
   }
   // q/k/v of the new token: the projection's rows, its split-K partial sums,
   // or the row of the code-indexed table that the row's code selects
-  const long ar = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
+  const long ar = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off + t : row;
   const float* qrow = p.qkv + ar * p.ld_qkv;
   if (p.lut_codes) qrow = p.lut + (long)min(max(p.lut_codes[(long)row * p.lut_code_ld], 0), p.lut_rows - 1) * p.lut_ld;
   // up to PZ ranges with every load issued before the first add (ranges past
@@ -1167,22 +1170,23 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
     return v * prs;
   };
   {
+    const int pos = pos0 + t;
     float cs, sn;
     if (p.rope_rows) {
       cs = p.rope_rows[(long)row * D + lane];
       sn = p.rope_rows[(long)row * D + HALF + lane];
     } else {
-      cs = p.cos[(long)pos0 * HALF + lane];
-      sn = p.sin[(long)pos0 * HALF + lane];
+      cs = p.cos[(long)pos * HALF + lane];
+      sn = p.sin[(long)pos * HALF + lane];
     }
-    const int v = wave;
+    const int v = role;
     if (v == G + 1) {                       // value row, stored as is
       const long col = (long)(p.nq + p.nkv) * D + (long)g * D;
       const float x1 = qkv_at(col + lane), x2 = qkv_at(col + lane + HALF);
-      st_elem<KVT>(vc, (long)pos0 * D + lane, x1);
-      st_elem<KVT>(vc, (long)pos0 * D + lane + HALF, x2);
-      vnew[lane] = kv_round<KVT>(x1);
-      vnew[lane + HALF] = kv_round<KVT>(x2);
+      st_elem<KVT>(vc, (long)pos * D + lane, x1);
+      st_elem<KVT>(vc, (long)pos * D + lane + HALF, x2);
+      vnew[t][lane] = kv_round<KVT>(x1);
+      vnew[t][lane + HALF] = kv_round<KVT>(x2);
     } else {
       const long col = v < G ? (long)(g * G + v) * D : (long)p.nq * D + (long)g * D;
       const float* gain = v < G ? p.q_gain : p.k_gain;
@@ -1193,28 +1197,29 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
       const float y1 = x1 * rden * g1, y2 = x2 * rden * g2;
       const float o1 = y1 * cs - y2 * sn, o2 = y2 * cs + y1 * sn;
       if (v < G) {
-        qs[v][lane] = o1;
-        qs[v][lane + HALF] = o2;
+        qs[t][v][lane] = o1;
+        qs[t][v][lane + HALF] = o2;
       } else {
-        st_elem<KVT>(kc, (long)pos0 * D + lane, o1);
-        st_elem<KVT>(kc, (long)pos0 * D + lane + HALF, o2);
-        knew[lane] = kv_round<KVT>(o1);
-        knew[lane + HALF] = kv_round<KVT>(o2);
+        st_elem<KVT>(kc, (long)pos * D + lane, o1);
+        st_elem<KVT>(kc, (long)pos * D + lane + HALF, o2);
+        knew[t][lane] = kv_round<KVT>(o1);
+        knew[t][lane + HALF] = kv_round<KVT>(o2);
       }
     }
   }
   __syncthreads();
-  if (wave >= G) return;
-  const int hh = wave, L = pos0 + 1;
+  if (role >= G) return;
+  const int hh = role, L = pos0 + t + 1;   // keys 0 .. pos0 + t
   float x[32];
   if (jk < pos0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) unpack_chunk<KVT>(kr[c], x + 8 * c);
   } else {
+    const int jn = min(jk - pos0, NTOK - 1);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = jk == pos0 ? knew[32 * qd + e] : 0.f;
+    for (int e = 0; e < 32; ++e) x[e] = jk < L ? knew[jn][32 * qd + e] : 0.f;
   }
-  const f32x4* q4 = (const f32x4*)&qs[hh][32 * qd];
+  const f32x4* q4 = (const f32x4*)&qs[t][hh][32 * qd];
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
@@ -1251,8 +1256,9 @@ __global__ __launch_bounds__((G + 2) * 64) void attn_short_kernel(AttnArgs p) {
       } else {
         v0 = bf_lo(vr[j]); v1 = bf_hi(vr[j]);
       }
-    } else if (j == pos0) {
-      v0 = vnew[2 * lane]; v1 = vnew[2 * lane + 1];
+    } else if (j < L) {
+      const int jn = min(j - pos0, NTOK - 1);
+      v0 = vnew[jn][2 * lane]; v1 = vnew[jn][2 * lane + 1];
     } else {
       v0 = 0.f; v1 = 0.f;
     }
@@ -1574,6 +1580,12 @@ static hipError_t launch_attention_dg(const AttnArgs& a, hipStream_t s) {
     }
     if (attention_reads_lut(a)) {
       hipLaunchKernelGGL((attn_short_kernel<KVT, G>), dim3(a.nkv, a.n_runs), dim3((G + 2) * 64), 0, s, a);
+      return hipGetLastError();
+    }
+    // the predictor's two-token pass at batch rows > 1 (activation rows 2 r, 2 r + 1)
+    if (a.single_token && a.mode == ATT_WRITE_ATTEND && a.ntok == 2 && a.tok_stride == 2 && a.tok_off == 0 &&
+        a.max_pos >= 2 && a.max_pos <= 16 && a.n_runs > 1 && !a.lut_codes && !a.rope_rows && a.ld_out % 2 == 0) {
+      hipLaunchKernelGGL((attn_short_kernel<KVT, G, 2>), dim3(a.nkv, a.n_runs), dim3(2 * (G + 2) * 64), 0, s, a);
       return hipGetLastError();
     }
   }
