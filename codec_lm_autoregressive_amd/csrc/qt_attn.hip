@@ -907,6 +907,8 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(AttnArgs p) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  // (exponentials as __expf, one hardware exp2 of x log2 e: 3.50 -> 3.45 ms
+  // per batch-8 frame against expf here and in the short kernel)
   // one step of the online softmax: s is this lane's score (head b0; -inf if
   // masked; lanes l and l ^ 4 alike), counted in the lane's sum if cnt;
   // add_pv gets the lane's weight once the maxima and sums are rescaled
@@ -918,11 +920,11 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(AttnArgs p) {
     const float other = dpp_f<0xb1, 0xf>(mx, -INFINITY);
     float corr[G];
     const float mc0 = fmaxf(m[0], b0 ? other : mx), mc1 = fmaxf(m[1], b0 ? mx : other);
-    corr[0] = expf(m[0] - mc0);
-    corr[1] = expf(m[1] - mc1);
+    corr[0] = __expf(m[0] - mc0);
+    corr[1] = __expf(m[1] - mc1);
     m[0] = mc0;
     m[1] = mc1;
-    const float pw = s == -INFINITY ? 0.f : expf(s - (b0 ? mc1 : mc0));
+    const float pw = s == -INFINITY ? 0.f : __expf(s - (b0 ? mc1 : mc0));
     lsum = lsum * (b0 ? corr[1] : corr[0]) + (cnt ? pw : 0.f);
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -999,7 +1001,7 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(AttnArgs p) {
       if (ksl == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float w = expf(a[h] - m[h]);
+          const float w = __expf(a[h] - m[h]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vnew[0][dsl * 8 + e], acc[h][e]);
         }
@@ -1031,7 +1033,7 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(AttnArgs p) {
     float v = 0.f, ls = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = wm[w][hh] == -INFINITY ? 0.f : expf(wm[w][hh] - M);
+      const float f = wm[w][hh] == -INFINITY ? 0.f : __expf(wm[w][hh] - M);
       v = fmaf(f, wacc[w][hh][dim], v);
       ls = fmaf(f, wl[w][hh], ls);
     }
@@ -1074,7 +1076,7 @@ __global__ __launch_bounds__(NT) void attn_split_combine_kernel(AttnArgs p) {
   float num = 0.f, den = 0.f;
 #pragma unroll
   for (int sp = 0; sp < S; ++sp) {
-    const float w = m[sp] == -INFINITY ? 0.f : expf(m[sp] - mx);
+    const float w = m[sp] == -INFINITY ? 0.f : __expf(m[sp] - mx);
     num = fmaf(w, o[sp], num);
     den = fmaf(w, l[sp], den);
   }
@@ -1237,7 +1239,7 @@ __global__ __launch_bounds__(NTOK * (G + 2) * 64) void attn_short_kernel(AttnArg
   mx = fmaxf(mx, dpp_f<0x4e, 0xf>(mx, -INFINITY));
   mx = fmaxf(mx, dpp_f<0x141, 0xf>(mx, -INFINITY));
   mx = fmaxf(mx, dpp_f<0x140, 0xf>(mx, -INFINITY));
-  const float ew = jk < L ? expf(sc - mx) : 0.f;
+  const float ew = jk < L ? __expf(sc - mx) : 0.f;
   float lsum = ew;
   lsum += dpp_f<0xb1, 0xf>(lsum, 0.f);
   lsum += dpp_f<0x4e, 0xf>(lsum, 0.f);
@@ -1423,7 +1425,10 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
     }
   }
 
+  // scores in base-2 units (times scale log2 e): each weight is then one
+  // hardware exp2 (81 -> 74.5 us per chunk and layer at batch 64 against expf)
   float m = -INFINITY, lsum = 0.f;
+  const float sl2 = p.scale * 1.4426950408889634f;
   f32x4 acc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -1460,22 +1465,21 @@ __global__ __launch_bounds__(2 * G * 64) void attn_prefill_mfma_kernel(AttnArgs 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + 16 * kt + 4 * quad + r;
-          const float v = key <= qpos ? sc[kt][r] * p.scale : -INFINITY;
+          const float v = key <= qpos ? sc[kt][r] * sl2 : -INFINITY;   // masked: -inf, whose exp2 is 0
           sc[kt][r] = v;
           mx = fmaxf(mx, v);
         }
       mx = max_xor<16>(mx);
       mx = max_xor<32>(mx);
       const float mnew = fmaxf(m, mx);     // finite: key 0 is in every query's range
-      const float corr = expf(m - mnew);
+      const float corr = __builtin_amdgcn_exp2f(m - mnew);
       m = mnew;
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 16 * kt + 4 * quad + r;
-          const float e = key <= qpos ? expf(sc[kt][r] - mnew) : 0.f;
+          const float e = __builtin_amdgcn_exp2f(sc[kt][r] - mnew);
           sc[kt][r] = e;
           ps += e;
         }
