@@ -151,7 +151,7 @@ def lib():
             "qt_linear_noalloc": ([vp, i32, vp, i32, i32, vp, i32, vp, f32, i32, vp], i32),
             "qt_debug_prefill_attention": ([vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp,
                                             vp, i32, vp, C.c_int64], i32),
-            "qt_debug_decode_attention": ([vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp,
+            "qt_debug_decode_attention": ([vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp,
                                            vp, vp, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -469,25 +469,28 @@ def debug_prefill_attention(qkv, lens, q_gain, k_gain, cos, sin, kc, vc, nq, nkv
 
 
 def debug_decode_attention(qkv, pos, q_gain, k_gain, cos, sin, kc, vc, nq, nkv, eps=1e-6, kv_dtype="f16",
-                           kv_split=1):
-    """One single-token decode step of one layer's attention on device
-    tensors; returns out [B, nq d].
+                           kv_split=1, ntok=1):
+    """One decode step of one layer's attention on device tensors for ntok
+    (1 or 2) new tokens per row; returns out [B ntok, nq d].
 
-    qkv [B, (nq + 2 nkv) d] float32 (row r: the new token of row r); pos host
-    int [B]; kc, vc [B, nkv, max_pos, d] of the cache type (positions below
-    pos[r] hold the cache, pos[r] is written); cos, sin [max_pos, d / 2]."""
+    qkv [B ntok, (nq + 2 nkv) d] float32 (row r ntok + t: token t of row r, at
+    position pos[r] + t); pos host int [B]; kc, vc [B, nkv, max_pos, d] of the
+    cache type (positions below pos[r] hold the cache, pos[r] .. pos[r] +
+    ntok - 1 are written); cos, sin [max_pos, d / 2]."""
     import torch
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     B = int(pos.size)
     d = qkv.shape[1] // (nq + 2 * nkv)
     max_pos = kc.shape[2]
-    out = torch.zeros((B, nq * d), dtype=torch.float32, device=qkv.device)
+    if qkv.shape[0] != B * ntok:
+        raise ValueError("qkv must hold B * ntok rows")
+    out = torch.zeros((B * ntok, nq * d), dtype=torch.float32, device=qkv.device)
     pos_dev = torch.zeros(B, dtype=torch.int32, device=qkv.device)
     split = None
     if kv_split > 1:
         split = torch.zeros(B * nkv * kv_split * (nq // nkv) * (d + 2), dtype=torch.float32, device=qkv.device)
     s = torch.cuda.current_stream().cuda_stream
-    _check(lib().qt_debug_decode_attention(C.c_void_p(s), _DTYPES[kv_dtype], d, nq, nkv, B, _np_ptr(pos),
+    _check(lib().qt_debug_decode_attention(C.c_void_p(s), _DTYPES[kv_dtype], d, nq, nkv, B, int(ntok), _np_ptr(pos),
                                            _ptr(pos_dev), max_pos, _ptr(qkv), _ptr(q_gain), _ptr(k_gain), eps,
                                            _ptr(cos), _ptr(sin), _ptr(kc), _ptr(vc), _ptr(out), int(kv_split),
                                            _ptr(split) if split is not None else None))

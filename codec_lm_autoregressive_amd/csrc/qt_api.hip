@@ -1599,7 +1599,7 @@ qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t
 }
 
 qt_status qt_debug_decode_attention(void* hip_stream, int32_t kv_dtype, int32_t head_dim, int32_t nq, int32_t nkv,
-                                    int32_t B, const int32_t* pos, int32_t* pos_dev, int32_t max_pos,
+                                    int32_t B, int32_t ntok, const int32_t* pos, int32_t* pos_dev, int32_t max_pos,
                                     const float* qkv, const float* q_gain, const float* k_gain, float eps,
                                     const float* cos, const float* sin, void* kc, void* vc, float* out,
                                     int32_t kv_split, float* split_buf) {
@@ -1622,12 +1622,17 @@ qt_status qt_debug_decode_attention(void* hip_stream, int32_t kv_dtype, int32_t 
     set_err(g_err, "kv_split must be 1, or 2, 4, 8 or 16 with split_buf at head_dim 128 and nq / nkv <= 4");
     return QT_E_INVALID;
   }
+  if (!(ntok == 1 || (ntok == 2 && kv_split == 1 && head_dim <= 128))) {
+    set_err(g_err, "ntok must be 1, or 2 with kv_split 1 and head_dim <= 128");
+    return QT_E_INVALID;
+  }
   for (int r = 0; r < B; ++r)
-    if (pos[r] < 0 || pos[r] >= max_pos) { set_err(g_err, "pos[%d] out of 0..max_pos - 1", r); return QT_E_INVALID; }
+    if (pos[r] < 0 || pos[r] > max_pos - ntok) { set_err(g_err, "pos[%d] out of 0..max_pos - ntok", r); return QT_E_INVALID; }
   hipStream_t s = (hipStream_t)hip_stream;
   hipError_t e = hipMemcpyAsync(pos_dev, pos, (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice, s);
   AttnArgs t{};
-  t.mode = ATT_WRITE_ATTEND; t.single_token = 1; t.ntok = 1;
+  t.mode = ATT_WRITE_ATTEND; t.single_token = 1; t.ntok = ntok;
+  if (ntok == 2) { t.tok_stride = 2; t.tok_off = 0; }   // activation rows 2 r and 2 r + 1
   t.qkv = qkv; t.ld_qkv = (long)(nq + 2 * nkv) * head_dim; t.out = out; t.ld_out = (long)nq * head_dim;
   t.q_gain = q_gain; t.k_gain = k_gain; t.eps = eps; t.scale = (float)(1.0 / std::sqrt((double)head_dim));
   t.cos = cos; t.sin = sin; t.kc = kc; t.vc = vc; t.kvdtype = kv_dtype;

@@ -505,23 +505,25 @@ qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t
                                      const float* sin, void* kc, void* vc, float* out, int32_t tiled,
                                      int32_t* runs, int64_t runs_ints);
 
-/* One single-token decode step of one decoder layer's attention with the
- * frame's kernels (no context): for each row r the new token's q/k/v (row r
- * of qkv) go through per-head RMSNorm (q, k) and rope at position pos[r], its
- * K and V are written to cache position pos[r], and its q heads attend over
- * positions 0 .. pos[r] (GQA, scale 1/sqrt(head_dim)) (ncnn port discussion
+/* One decode step of one decoder layer's attention with the frame's kernels
+ * (no context), for ntok new tokens per row: token t of row r (row
+ * r ntok + t of qkv) goes through per-head RMSNorm (q, k) and rope at
+ * position pos[r] + t, its K and V are written to cache position pos[r] + t,
+ * and its q heads attend over positions 0 .. pos[r] + t (GQA, scale
+ * 1/sqrt(head_dim); ntok 2 is the code predictor's two-token pass) (ncnn port discussion
  * 6798, section 1 "structure": Qwen3 decoders with GQA 16/8, head_dim 128 and
  * QK-Norm; Mizuoto "Qwen3-TTS" page, "速度": decoding over a KV cache).
- *   kv_dtype, head_dim, nq, nkv as qt_debug_prefill_attention; B 1 .. 4096.
- *   pos host int32 [B], 0 .. max_pos - 1 each; pos_dev device int32 [B]
+ *   kv_dtype, head_dim, nq, nkv as qt_debug_prefill_attention; B 1 .. 4096;
+ *   ntok 1, or 2 with kv_split 1 and head_dim <= 128.
+ *   pos host int32 [B], 0 .. max_pos - ntok each; pos_dev device int32 [B]
  *   scratch (receives a copy).
- *   qkv device float [B, (nq + 2 nkv) head_dim]: q heads, then k, then v.
+ *   qkv device float [B ntok, (nq + 2 nkv) head_dim]: q heads, then k, then v.
  *   q_gain, k_gain device float [head_dim]; eps > 0.
  *   cos, sin device float [max_pos, head_dim / 2].
  *   kc, vc device [B, nkv, max_pos, head_dim] of kv_dtype: positions
  *   0 .. pos[r] - 1 of row r hold the cached keys and values as stored;
- *   position pos[r] is written, others untouched.
- *   out device float [B, nq head_dim].
+ *   positions pos[r] .. pos[r] + ntok - 1 are written, others untouched.
+ *   out device float [B ntok, nq head_dim].
  *   kv_split 1: one block per (row, kv head); 2, 4, 8 or 16 (head_dim 128,
  *   nq / nkv <= 4): that many key ranges per row, combined in range order,
  *   with split_buf device float [B, nkv, kv_split, nq / nkv, head_dim + 2]
@@ -529,7 +531,7 @@ qt_status qt_debug_prefill_attention(void* hip_stream, int32_t kv_dtype, int32_t
  * Returns after the stream has finished. QT_E_INVALID on a bad argument,
  * QT_E_HIP on a launch failure. */
 qt_status qt_debug_decode_attention(void* hip_stream, int32_t kv_dtype, int32_t head_dim, int32_t nq, int32_t nkv,
-                                    int32_t B, const int32_t* pos, int32_t* pos_dev, int32_t max_pos,
+                                    int32_t B, int32_t ntok, const int32_t* pos, int32_t* pos_dev, int32_t max_pos,
                                     const float* qkv, const float* q_gain, const float* k_gain, float eps,
                                     const float* cos, const float* sin, void* kc, void* vc, float* out,
                                     int32_t kv_split, float* split_buf);

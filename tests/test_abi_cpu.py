@@ -175,8 +175,8 @@ def test_debug_entry_points_validate_before_launch():
     assert pa(binding.QT_DTYPE_F16, 128, 4, 2, 1, runs_ints=50) == binding.QT_E_INVALID  # run scratch too small
     pos = (C.c_int32 * 2)(5, 9)
 
-    def da(kv, d, nq, nkv, split, pos=pos, max_pos=64, split_buf=fake, B=2):
-        return L.qt_debug_decode_attention(None, kv, d, nq, nkv, B, pos, fake, max_pos, fake, fake, fake, 1e-6, fake,
+    def da(kv, d, nq, nkv, split, pos=pos, max_pos=64, split_buf=fake, B=2, ntok=1):
+        return L.qt_debug_decode_attention(None, kv, d, nq, nkv, B, ntok, pos, fake, max_pos, fake, fake, fake, 1e-6, fake,
                                            fake, fake, fake, fake, split, split_buf)
     assert da(7, 128, 4, 2, 1) == binding.QT_E_INVALID                         # kv_dtype
     assert da(binding.QT_DTYPE_F16, 96, 4, 2, 1) == binding.QT_E_INVALID       # head_dim
@@ -187,3 +187,7 @@ def test_debug_entry_points_validate_before_launch():
     assert da(binding.QT_DTYPE_F16, 128, 16, 2, 2) == binding.QT_E_INVALID     # and at most 4 q heads per kv head
     assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, max_pos=9) == binding.QT_E_INVALID   # a position past max_pos - 1
     assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, B=0) == binding.QT_E_INVALID          # no rows
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, ntok=3) == binding.QT_E_INVALID       # one or two new tokens
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 2, ntok=2) == binding.QT_E_INVALID       # two tokens: no key ranges
+    assert da(binding.QT_DTYPE_F16, 256, 4, 2, 1, ntok=2) == binding.QT_E_INVALID       # nor head_dim above 128
+    assert da(binding.QT_DTYPE_F16, 128, 4, 2, 1, max_pos=10, ntok=2) == binding.QT_E_INVALID   # pos + 1 past max_pos - 1

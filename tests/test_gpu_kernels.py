@@ -488,3 +488,72 @@ def test_decode_attention_matches_oracle(kv, pos, nkv, G, max_pos, splits):
     for S in splits[1:]:
         cross = float(np.max(np.abs(outs[S] - outs[splits[0]])))
         assert cross <= 1e-5, (S, cross)
+
+
+def _ref_decode_two_tokens(qkv, pos, kc, vc, q_gain, k_gain, cos, sin, nq, nkv, eps, kv):
+    """Per row r: tokens 0 and 1 (qkv rows 2 r, 2 r + 1) at positions pos[r]
+    and pos[r] + 1, each normed, roped and its key and value rounded to the
+    cache type as in the one-token reference; token 0 attends over the cached
+    positions and itself, token 1 also over token 0's key and value."""
+    d = qkv.shape[1] // (nq + 2 * nkv)
+    out = np.empty((qkv.shape[0], nq * d))
+    for r in range(len(pos)):
+        p = int(pos[r])
+        K, V = kc[r, :, :p], vc[r, :, :p]
+        for t in range(2):
+            x = qkv[2 * r + t:2 * r + t + 1].astype(np.float64)
+            q = x[:, :nq * d].reshape(1, nq, d)
+            k = x[:, nq * d:(nq + nkv) * d].reshape(1, nkv, d)
+            v = x[:, (nq + nkv) * d:].reshape(1, nkv, d)
+            q = model.apply_rope(model.rms_norm(q, q_gain, eps, np.float64), [p + t], cos, sin, np.float64)
+            k = _cache_round(model.apply_rope(model.rms_norm(k, k_gain, eps, np.float64), [p + t], cos, sin,
+                                              np.float64), kv)
+            K = np.concatenate([K, k.transpose(1, 0, 2)], axis=1)
+            V = np.concatenate([V, _cache_round(v, kv).transpose(1, 0, 2)], axis=1)
+            out[2 * r + t] = model.attention(q, K, V, [p + t], nkv, np.float64).reshape(nq * d)
+    return out
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("pos,nkv,G,max_pos", [
+    ([0, 0, 0, 0], 8, 2, 16),
+    ([0], 8, 2, 16),
+    ([3, 9, 14], 8, 2, 16),
+    ([0, 40, 130], 8, 2, 160),
+    ([5, 33], 4, 4, 64),
+])
+def test_decode_attention_two_tokens_matches_oracle(kv, pos, nkv, G, max_pos):
+    """The code predictor's two-token pass as a decode step of two new
+    tokens per row (positions pos and pos + 1; the second attends to the
+    first's key and value): several rows at position 0 (the short kernel with
+    both tokens in one block), one row, rows with cached keys up to the
+    16-position limit, longer contexts and 4 q heads per kv head (the general
+    kernel); against the float64 oracle, tolerance as for one token."""
+    torch = _torch()
+    nq, d, eps = nkv * G, 128, 1e-6
+    pos = np.array(pos, dtype=np.int32)
+    B = len(pos)
+    rng = np.random.default_rng(int(pos.sum()) + 13 * G + 5 * B + {"f16": 0, "bf16": 1, "f32": 2}[kv])
+    qkv = rng.standard_normal((2 * B, (nq + 2 * nkv) * d)).astype(np.float32)
+    q_gain = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    k_gain = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    cos, sin = model.rope_tables(max_pos, d, 1.0e6)
+    kc = _cache_round(rng.standard_normal((B, nkv, max_pos, d)), kv)
+    vc = _cache_round(rng.standard_normal((B, nkv, max_pos, d)), kv)
+    ref = _ref_decode_two_tokens(qkv, pos, kc, vc, q_gain, k_gain, cos, sin, nq, nkv, eps, kv)
+
+    def dev_cache(x):
+        if kv == "f16":
+            return torch.from_numpy(x.astype(np.float16)).cuda()
+        if kv == "bf16":
+            return torch.from_numpy(synth.bf16_bits(x.astype(np.float32)).view(np.int16)).cuda()
+        return torch.from_numpy(x.astype(np.float32)).cuda()
+
+    dev = [torch.from_numpy(a).cuda() for a in (qkv, q_gain, k_gain, cos, sin)]
+    print(f"two-token decode attention kv={kv} G={G} pos={list(pos)} max_pos={max_pos}", flush=True)
+    out = binding.debug_decode_attention(dev[0], pos, dev[1], dev[2], dev[3], dev[4], dev_cache(kc), dev_cache(vc),
+                                         nq, nkv, eps, kv, 1, ntok=2).cpu().numpy()
+    err = float(np.max(np.abs(out - ref)))
+    tol = 2e-3 if kv != "f32" else 1e-4
+    print(f"  max|out - oracle| {err:.3e} (tol {tol:.1e})", flush=True)
+    assert np.all(np.isfinite(out)) and err <= tol, err
