@@ -526,8 +526,10 @@ __device__ __forceinline__ void decode_new_rows(const AttnArgs& p, int g, int ro
   float prs[NTOK];
   const long arow0 = p.tok_stride > 0 ? (long)row * p.tok_stride + p.tok_off : row;
   // split-K partial sums: up to PZ ranges with every load issued before the
-  // first add (clamped ranges past part_z are loaded but not added)
-  constexpr int PZ = 8;
+  // first add (clamped ranges past part_z are loaded but not added); 4 is
+  // the K = 1024 projections' split (8 clamped loads measured 1 % slower per
+  // batch-64 frame), more ranges take a loop
+  constexpr int PZ = 4;
   const bool pz_fast = p.part_z <= PZ;
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
@@ -1138,7 +1140,7 @@ __global__ __launch_bounds__(NTOK * (G + 2) * 64) void attn_short_kernel(AttnArg
   if (p.lut_codes) qrow = p.lut + (long)min(max(p.lut_codes[(long)row * p.lut_code_ld], 0), p.lut_rows - 1) * p.lut_ld;
   // up to PZ ranges with every load issued before the first add (ranges past
   // part_z are clamped loads that are not added); more ranges: a loop
-  constexpr int PZ = 8;
+  constexpr int PZ = 4;
   const bool pz_fast = p.part_z <= PZ;
   float prs = 1.f;
   if (p.part_z > 0) {
