@@ -55,10 +55,10 @@ FRAMES_PER_AUDIO_SECOND = 12.5
 #    (bench.py --frame-counters; profiles/frame_hbm_bytes_qwen06b.md).
 COUNTED = {
     "kernel": {"src_sha256_16": "799ed64ea42fd00d", "bytes": 12726309, "trace_avg_us": 4.712},
-    "frame": {"src_sha256_16": "4e2af207a7fe5c0b", "bytes_per_frame": {
+    "frame": {"src_sha256_16": "e080c0989fba5a90", "bytes_per_frame": {
         # workload: (HBM bytes per frame, mean context of the counted frames, streamed model there)
-        "qwen06b_bf16_b1": (3302200000, 35.5, 3196166144),
-        "qwen06b_bf16_b64_sampling": (11101600000, 339.9, 5701422285),
+        "qwen06b_bf16_b1": (3301200000, 35.5, 3196166144),
+        "qwen06b_bf16_b64_sampling": (11098400000, 339.9, 5701422285),
     }},
 }
 CSRC = os.path.join(ROOT, "codec_lm_autoregressive_amd", "csrc")
